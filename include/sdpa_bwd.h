@@ -1,0 +1,220 @@
+/*
+ * libsdpa_bwd: backward pass of scaled dot-product attention on MI355X (gfx950).
+ *
+ * What the library computes, per sequence and head (Q: Sq x D, K, V: Sk x D,
+ * multiplying scale s):
+ *   S = s Q K^T restricted to the admissible keys (all, causal j <= i, or the
+ *   gathered top-k blocks), P = exp(S - LSE) with LSE the row log-sum-exp,
+ *   dV = P^T dO, dP = dO V^T, dS = P o (dP - Delta) with Delta_i = sum_d dO_id O_id,
+ *   dQ = s dS K, dK = s dS^T Q.
+ * The backward takes the forward's per-row statistics instead of recomputing
+ * them (the cuDNN SDPA-backward sample notebook, introduction and stats
+ * cells: the stats tensor is (B, H, S, 1) fp32 and passes from forward to
+ * backward); the gradient formulas are those of the Ascend operator page
+ * aclnnNsaSelectedAttentionGrad ("Formula" section), whose 1/sqrt(d) factor is
+ * the case s = d^-1/2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Element types: Q, K, V, O, dO, dQ, dK, dV are all fp16 or all bf16
+ *   (sdpa_dtype); statistics are fp32.  Arithmetic is fp32 with 16-bit MFMA
+ *   operands (the sample's io=HALF, intermediate=compute=FLOAT graph).
+ * - Layout: every tensor is a strided view, strides counted in ELEMENTS.  Dense
+ *   tensors are logical (B, H, S, D) with any strides, e.g. the sample's BSHD
+ *   physical / BHSD logical strides (S*H*D, D, H*D, 1).  Packed tensors are
+ *   (T, N, D) ("TND", the Ascend page's only layout).  The last (D) stride must
+ *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
+ *   keep every row 16-byte aligned.  D is 64 or 128.
+ * - Ownership: the caller owns every buffer, including the workspace.  The
+ *   library allocates no device memory, keeps no per-call state and never
+ *   synchronises: kernels are enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) and the call returns once they are enqueued.  Host arrays
+ *   (cumulative lengths) are read during the call only.  Outputs are
+ *   overwritten, never accumulated into.  Outputs must not alias inputs.
+ * - Errors: every function returns an sdpa_status and never aborts.  Argument
+ *   errors are detected before any HIP call, in this order: NULL pointers
+ *   (SDPA_ERR_NULLPTR), invalid values (SDPA_ERR_INVALID), valid but not
+ *   implemented cases (SDPA_ERR_UNSUPPORTED), a workspace smaller than the size
+ *   query returned (SDPA_ERR_WORKSPACE).  HIP failures, including "no device",
+ *   return SDPA_ERR_HIP; sdpa_last_error() then gives the HIP error text of the
+ *   calling thread.  This mirrors the Ascend page's split of return codes into
+ *   a null-pointer error and an invalid-parameter error ("Return Value").
+ * - Thread safety: calls are independent; concurrent calls on different
+ *   streams must use different workspaces.
+ */
+#ifndef SDPA_BWD_H
+#define SDPA_BWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdpa_status {
+    SDPA_OK = 0,
+    SDPA_ERR_NULLPTR = 1,
+    SDPA_ERR_INVALID = 2,
+    SDPA_ERR_UNSUPPORTED = 3,
+    SDPA_ERR_WORKSPACE = 4,
+    SDPA_ERR_HIP = 5
+} sdpa_status;
+
+/* 16-bit element type of Q, K, V, O, dO and of the gradients (Ascend parameter
+ * table: BFLOAT16 or FLOAT16). */
+typedef enum sdpa_dtype { SDPA_F16 = 0, SDPA_BF16 = 1 } sdpa_dtype;
+
+/* Form of the per-row softmax statistics.
+ * SDPA_STATS_LSE:     one value per row, LSE_i = ln sum_j exp(S_ij) over the
+ *                     admissible keys (the cuDNN sample's "stats"; -inf for a
+ *                     row with no admissible key).
+ * SDPA_STATS_MAX_SUM: two values per row, m_i = max_j S_ij and
+ *                     l_i = sum_j exp(S_ij - m_i) (the Ascend softmaxMax and
+ *                     softmaxSum; l_i = 0 for a row with no admissible key).
+ * S is the scaled, masked score in both cases. */
+typedef enum sdpa_stats_kind { SDPA_STATS_LSE = 0, SDPA_STATS_MAX_SUM = 1 } sdpa_stats_kind;
+
+/* Dense 16-bit tensor, logical (B, H, S, D); strides in elements. */
+typedef struct sdpa_tensor4 {
+    void* data;
+    int64_t stride_b, stride_h, stride_s, stride_d;
+} sdpa_tensor4;
+
+/* Packed 16-bit tensor, logical (T, N, D); strides in elements. */
+typedef struct sdpa_tensor3 {
+    void* data;
+    int64_t stride_t, stride_n, stride_d;
+} sdpa_tensor3;
+
+/* fp32 per-row statistics.  Dense: element (b, h, i) at b*stride_b +
+ * h*stride_h + i*stride_s.  Packed: element (t, n) at t*stride_s + n*stride_h
+ * (stride_b unused).  The Ascend page's [T, N, 8] statistics (constraints
+ * section) are read as stride_s = 8N, stride_h = 8: element 0 of the 8. */
+typedef struct sdpa_stats {
+    int32_t kind;          /* sdpa_stats_kind */
+    const float* lse_or_max;
+    const float* sum;      /* SDPA_STATS_MAX_SUM only; NULL otherwise */
+    int64_t stride_b, stride_h, stride_s;
+} sdpa_stats;
+
+/* Per-row statistics output of the forward (dense layout as sdpa_stats). */
+typedef struct sdpa_stats_out {
+    float* lse;
+    int64_t stride_b, stride_h, stride_s;
+} sdpa_stats_out;
+
+/* Text for a status; for SDPA_ERR_HIP the last HIP error message of this thread. */
+const char* sdpa_status_string(int status);
+const char* sdpa_last_error(void);
+
+/*
+ * sdpa_fwd_stats: attention forward in training mode, producing O and the LSE
+ * statistics that the backward consumes (the cuDNN sample's forward graph with
+ * is_inference=False: outputs o and stats; forward-graph cell).
+ *   q: (B, Hq, Sq, D); k, v: (B, Hkv, Sk, D); o_out: (B, Hq, Sq, D) written;
+ *   lse_out: (B, Hq, Sq) written, natural-log LSE of the scaled scores.
+ *   Hq must be a multiple of Hkv; query head h reads KV head h / (Hq/Hkv).
+ *   causal: key j visible to query i iff j <= i (requires Sq == Sk).
+ * Needs no workspace.
+ */
+int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
+                   int64_t D, double scale, int causal,
+                   const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                   const sdpa_tensor4* o_out, const sdpa_stats_out* lse_out, void* stream);
+
+/*
+ * sdpa_bwd_workspace_size / sdpa_bwd: dense SDPA backward (the cuDNN sample's
+ * sdpa_backward node: inputs q, k, v, o, dO, stats, attn_scale,
+ * use_causal_mask; outputs dQ, dK, dV; backward-graph cell).
+ *   Shapes as sdpa_fwd_stats; dout, dq like q; dk, dv like k.
+ *   deterministic = 0: dQ is accumulated with fp32 atomics (run-to-run
+ *     rounding differences possible); 1: a separate dQ pass without atomics,
+ *     bitwise reproducible (the Ascend page's deterministic option,
+ *     "Constraints").
+ *   workspace: device memory of at least *bytes from the size query, any
+ *     contents on entry, 256-byte aligned.
+ */
+int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
+                            int64_t Sk, int64_t D, int deterministic, size_t* bytes);
+int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+             double scale, int causal, int deterministic,
+             const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+             const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
+             const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_bwd_varlen_workspace_size / sdpa_bwd_varlen: packed variable-length
+ * backward (TND).  `batch` sequences; cu_seqlens_q_host / cu_seqlens_kv_host
+ * are HOST arrays of `batch` int64 inclusive end offsets with no leading zero
+ * (the Ascend page's actualSeqQLen / actualSeqKvLen, "cumulative sum length
+ * of S for each batch", passed as host integer arrays; its example passes {1}
+ * and {1024} for one sequence).  Sequence b owns rows [cu[b-1], cu[b]) with
+ * cu[-1] = 0.  Causal masking uses positions local to each sequence and
+ * requires equal query and key lengths per sequence.
+ *   q, o, dout, dq: (Tq, Hq, D); k, v, dk, dv: (Tk, Hkv, D); stats per (t, h).
+ */
+int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                                   const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
+                                   int64_t D, int deterministic, size_t* bytes);
+int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                    double scale, int causal, int deterministic,
+                    const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
+                    const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
+                    const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_bwd_selected_workspace_size / sdpa_bwd_selected: NSA selected-attention
+ * backward (aclnnNsaSelectedAttentionGrad).  For every query token t and KV
+ * head h2 the keys are the block_count blocks of block_size rows named by
+ * topk[t, h2, i] (0 <= i < block_count), gathered with repetition (a block
+ * named twice counts twice; "Formula" section).  topk: DEVICE int32 tensor
+ * (T, Hkv, block_count) with element strides (tk_st, tk_sn, tk_sk); block
+ * indices are relative to the token's sequence start in K/V.
+ *   sparse_mode 0: no mask; 2: causal, key position <= query position within
+ *   the sequence (the page supports "0 or 2" without defining them).
+ *   Constraints (Ascend page, "Constraints"): block_size <= 128 and a multiple
+ *   of 16; 1 <= block_count <= 128; block_count * block_size < 8192; every KV
+ *   sequence length a multiple of block_size and >= block_count * block_size;
+ *   Hq a multiple of Hkv with Hq / Hkv <= 32.  Topk values outside the
+ *   sequence's blocks are a caller error (not checked).
+ */
+int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                                     const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int64_t block_size, int64_t block_count,
+                                     int deterministic, size_t* bytes);
+int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
+                      int deterministic,
+                      const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
+                      const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
+                      const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sdpa_selected_build_index: the inverse of the top-k choice, as used by
+ * sdpa_bwd_selected.  KV blocks are numbered over the packed KV rows (block g
+ * covers rows [g*block_size, (g+1)*block_size)); for bucket = h2 * NB + g,
+ * NB = Tk / block_size, the entries e = t * block_count + slot with
+ * topk[t, h2, slot] naming block g, sorted increasingly.
+ *   offsets_out: DEVICE int32 array of Hkv*NB + 1 CSR offsets (written);
+ *   entries_out: DEVICE int32 array of Tq*Hkv*block_count entries (written).
+ * workspace: at least the bytes returned by the selected workspace query.
+ */
+int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
+                              const int64_t* cu_seqlens_kv_host, int64_t Hkv,
+                              const int32_t* topk, int64_t tk_st, int64_t tk_sn, int64_t tk_sk,
+                              int64_t block_size, int64_t block_count,
+                              int32_t* offsets_out, int32_t* entries_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_BWD_H */

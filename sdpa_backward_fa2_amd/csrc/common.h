@@ -1,0 +1,162 @@
+// Shared device helpers for the gfx950 SDPA kernels: 16-bit element types,
+// MFMA wrappers, conversions and the kernel parameter blocks.
+//
+// MFMA register layouts used throughout (v_mfma_f32_32x32x16_{f16,bf16}, one
+// wavefront of 64 lanes, lane = 32*g + c with g in {0,1}, c in 0..31):
+//   A (32 x 16): lane (c, g) holds row c, eight k-slots (g, t), t = 0..7;
+//   B (16 x 32): lane (c, g) holds column c, the same eight k-slots (g, t);
+//   C (32 x 32): lane (c, g) holds column c, rows 8*q + 4*g + r in register 4*q + r.
+// A and B pair slot (g, t) with slot (g, t), so any one-to-one assignment of the
+// 16 k indices to the 16 slots gives the same product as long as A and B use
+// the same assignment.  Two assignments occur:
+//   "row slots":  k = 8*g + t             (operands read as 16 contiguous bytes);
+//   "acc slots":  k = 4*g + t (t < 4), 8 + 4*g + (t-4) (t >= 4), relative to a
+//                 16-row half of a C tile: this is how the rows of a C tile sit
+//                 in registers 8*h .. 8*h+7, so a C tile (rows = the contracted
+//                 index) feeds straight into the B operand of the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWave = 64;
+
+struct F16 {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint16_t cvt(float x) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+        return (uint32_t)cvt(lo) | ((uint32_t)cvt(hi) << 16);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t x) {
+        return (float)__builtin_bit_cast(_Float16, x);
+    }
+};
+
+struct BF16 {
+    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint16_t cvt(float x) {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+    static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
+        return (uint32_t)cvt(lo) | ((uint32_t)cvt(hi) << 16);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t x) {
+        return __builtin_bit_cast(float, (uint32_t)x << 16);
+    }
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+__device__ __forceinline__ uint16_t elem16(u32x4 v, int t) {
+    uint32_t w = v[t >> 1];
+    return (uint16_t)((t & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
+// Eight consecutive fp32 registers of a C tile (rows 16*h .. 16*h+15 of the
+// tile in "acc slot" order) rounded to a 16-bit B operand.
+template <class T>
+__device__ __forceinline__ u32x4 acc_to_operand(const f32x16& a, int h) {
+    u32x4 r;
+    r[0] = T::pack(a[8 * h + 0], a[8 * h + 1]);
+    r[1] = T::pack(a[8 * h + 2], a[8 * h + 3]);
+    r[2] = T::pack(a[8 * h + 4], a[8 * h + 5]);
+    r[3] = T::pack(a[8 * h + 6], a[8 * h + 7]);
+    return r;
+}
+
+// A operand in "acc slot" order from a row of a transposed LDS tile: the row
+// holds the contracted index contiguously; `base` points at element 16*h of the
+// 32-wide block, g is the lane half.
+__device__ __forceinline__ u32x4 ld_acc_slots(const uint16_t* base, int g) {
+    u32x2 lo = ld8(base + 4 * g);
+    u32x2 hi = ld8(base + 8 + 4 * g);
+    u32x4 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = hi[0]; r[3] = hi[1];
+    return r;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+// ---------------------------------------------------------------------------
+// Parameter blocks (passed by value as kernel arguments)
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxSeqArgs = 64;
+
+// Strided 16-bit tensor; the innermost (D) stride is 1.
+struct TensorArg {
+    uint16_t* p;
+    int64_t sb, sh, ss;   // dense: batch/head/row strides; packed: sb = 0, ss = token stride
+};
+
+// Sequence table.  Dense problems use n = B with q0 = k0 = 0 and the batch
+// stride; packed problems use sb = 0 and the per-sequence first rows.
+struct SeqTable {
+    int32_t n;
+    int32_t q0[kMaxSeqArgs], k0[kMaxSeqArgs], lq[kMaxSeqArgs], lk[kMaxSeqArgs];
+    const int32_t* dev;   // when n > kMaxSeqArgs: device array of 4*n ints (q0, k0, lq, lk)
+};
+
+__device__ __forceinline__ void seq_get(const SeqTable& t, int b, int& q0, int& k0, int& lq, int& lk) {
+    if (t.dev) {
+        q0 = t.dev[4 * b + 0]; k0 = t.dev[4 * b + 1]; lq = t.dev[4 * b + 2]; lk = t.dev[4 * b + 3];
+    } else {
+        q0 = t.q0[b]; k0 = t.k0[b]; lq = t.lq[b]; lk = t.lk[b];
+    }
+}
+
+struct FwdParams {
+    TensorArg q, k, v, o;
+    float* lse; int64_t lse_sb, lse_sh, lse_ss;
+    int B, Hq, Hkv, Sq, Sk;
+    float scale_log2;
+};
+
+// Row statistics workspace layout: row index R of (b, h, i)
+//   dense:  R = (b*Hq + h)*Sq + i        packed: R = (q0 + i)*Hq + h
+struct BwdParams {
+    TensorArg q, k, v, o, dout, dq, dk, dv;
+    // user statistics
+    int32_t stats_kind;
+    const float* st_a; const float* st_b; int64_t st_sb, st_sh, st_ss;
+    // workspace
+    float* lse2;      // [R] LSE * log2(e), +inf for rows without keys
+    float* delta;     // [R] sum_d dO*O
+    float* dqacc;     // [R][D] fp32 dQ accumulator (unscaled)
+    int B, Hq, Hkv, Sq, Sk;   // Sq/Sk: dense lengths (packed: Tq/Tk totals)
+    int64_t rows;             // number of statistics rows R
+    int varlen;
+    SeqTable seqs;
+    float scale, scale_log2;
+};
+
+}  // namespace sdpa

@@ -1,0 +1,27 @@
+// Launch entry points of the gfx950 kernels, called by the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace sdpa {
+
+struct BwdLaunch {
+    int dtype;            // 0 fp16, 1 bf16
+    int D;                // 64 or 128
+    bool causal;
+    bool deterministic;
+    int n_seq;            // batch (dense) or number of packed sequences
+    int max_kv_tiles;     // ceil(max key length / 128)
+    int max_q_tiles128;   // ceil(max query length / 128)
+    // Packed batches launch in chunks of sequences: the row-wise preprocess
+    // runs with the first chunk, the dQ conversion with the last.
+    static constexpr int kFirst = 1, kLast = 2;
+    int phase = kFirst | kLast;
+};
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t st);
+hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
+
+}  // namespace sdpa

@@ -1,0 +1,140 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+function include/sdpa_bwd.h declares, and rejects bad arguments with the
+documented status before making any HIP call.  Pointers here are fake aligned
+addresses; argument validation never dereferences them."""
+import ctypes
+
+import pytest
+import torch
+
+import sdpa_backward_fa2_amd as sb
+
+OK, NULLPTR, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(6)
+FAKE = 0x10000
+
+
+def lib():
+    return sb.load()
+
+
+def test_exports_every_declared_symbol():
+    names = sb.declared_functions()
+    assert len(names) >= 10, names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+    for must in ("sdpa_fwd_stats", "sdpa_bwd", "sdpa_bwd_varlen", "sdpa_bwd_selected",
+                 "sdpa_selected_build_index", "sdpa_status_string"):
+        assert must in names
+
+
+def test_status_strings():
+    for s in range(6):
+        assert lib().sdpa_status_string(s)
+
+
+def t4(ptr=FAKE, strides=(16384, 8192, 64, 1)):
+    return sb.Tensor4(ptr, *strides)
+
+
+def dense_call(**kw):
+    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, scale=0.125, causal=0, det=0,
+             q=t4(), k=t4(), v=t4(), o=t4(), do=t4(), dq=t4(), dk=t4(), dv=t4(),
+             stats=sb.Stats(0, FAKE, None, 256, 128, 1), ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    ref = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
+    return lib().sdpa_bwd(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"],
+                          a["causal"], a["det"], ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["o"]),
+                          ref(a["do"]), ref(a["stats"]), ref(a["dq"]), ref(a["dk"]), ref(a["dv"]),
+                          a["ws"], a["ws_bytes"], None)
+
+
+def test_dense_validation_order():
+    assert dense_call(q=None) == NULLPTR
+    assert dense_call(dv=t4(ptr=0)) == NULLPTR
+    assert dense_call(stats=sb.Stats(1, FAKE, None, 256, 128, 1)) == NULLPTR   # max/sum without sum
+    assert dense_call(ws=None) == NULLPTR
+    assert dense_call(dtype=7) == INVALID
+    assert dense_call(Hq=3, Hkv=2) == INVALID
+    assert dense_call(Hkv=0) == INVALID
+    assert dense_call(B=-1) == INVALID
+    assert dense_call(causal=1, Sk=64) == INVALID
+    assert dense_call(scale=float("nan")) == INVALID
+    assert dense_call(stats=sb.Stats(5, FAKE, None, 256, 128, 1)) == INVALID
+    assert dense_call(D=96) == UNSUPPORTED
+    assert dense_call(q=t4(strides=(16384, 8192, 64, 2))) == UNSUPPORTED
+    assert dense_call(k=t4(ptr=FAKE + 2)) == UNSUPPORTED
+    assert dense_call(v=t4(strides=(16384, 8192, 68, 1))) == UNSUPPORTED
+    assert dense_call(ws_bytes=16) == WORKSPACE
+    # NULL beats INVALID beats UNSUPPORTED beats WORKSPACE
+    assert dense_call(q=None, dtype=7) == NULLPTR
+    assert dense_call(dtype=7, D=96) == INVALID
+    assert dense_call(D=96, ws_bytes=16) == UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_valid_call_without_device_reports_hip_error():
+    assert dense_call() == HIP
+    assert lib().sdpa_last_error()
+
+
+def test_workspace_size_query():
+    n = ctypes.c_size_t(0)
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, ctypes.byref(n)) == OK
+    rows = 4 * 12 * 1024
+    assert n.value >= rows * 4 * 2 + rows * 64 * 4
+    m = ctypes.c_size_t(0)
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 1, ctypes.byref(m)) == OK
+    assert rows * 8 <= m.value < n.value
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 0, ctypes.byref(m)) == UNSUPPORTED
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, None) == NULLPTR
+
+
+def t3(ptr=FAKE, strides=(32 * 128, 128, 1)):
+    return sb.Tensor3(ptr, *strides)
+
+
+def varlen_call(cu_q, cu_k, **kw):
+    a = dict(dtype=1, Hq=32, Hkv=32, D=128, scale=0.088, causal=1, det=0, ws_bytes=1 << 34)
+    a.update(kw)
+    aq = (ctypes.c_int64 * len(cu_q))(*cu_q)
+    ak = (ctypes.c_int64 * len(cu_k))(*cu_k)
+    st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
+    ts = [t3() for _ in range(8)]
+    return lib().sdpa_bwd_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                 a["causal"], a["det"], *[ctypes.byref(t) for t in ts[:5]],
+                                 ctypes.byref(st), *[ctypes.byref(t) for t in ts[5:]], FAKE,
+                                 a["ws_bytes"], None)
+
+
+def test_varlen_validation():
+    assert varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
+    assert varlen_call([100, 300], [100, 200]) == INVALID         # causal with unequal lengths
+    assert varlen_call([100, 300], [100, 300], Hq=3, Hkv=2) == INVALID
+    assert varlen_call([100, 300], [100, 300], D=192) == UNSUPPORTED
+    assert varlen_call([100, 300], [100, 300], ws_bytes=8) == WORKSPACE
+    n = ctypes.c_size_t(0)
+    cu = (ctypes.c_int64 * 2)(100, 300)
+    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 0, ctypes.byref(n)) == OK
+    assert n.value >= 300 * 32 * (8 + 128 * 4)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_varlen_valid_without_device():
+    assert varlen_call([100, 300], [100, 300]) == HIP
+
+
+def fwd_call(**kw):
+    a = dict(dtype=0, B=1, Hq=2, Hkv=1, Sq=64, Sk=64, D=64, scale=0.1, causal=1)
+    a.update(kw)
+    so = sb.StatsOut(FAKE, 128, 64, 1)
+    return lib().sdpa_fwd_stats(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"],
+                                a["scale"], a["causal"], ctypes.byref(t4()), ctypes.byref(t4()),
+                                ctypes.byref(t4()), ctypes.byref(t4()), ctypes.byref(so), None)
+
+
+def test_fwd_validation():
+    assert fwd_call(Hq=3, Hkv=2) == INVALID
+    assert fwd_call(causal=1, Sk=32) == INVALID
+    assert fwd_call(D=256) == UNSUPPORTED
+    assert fwd_call(dtype=2) == INVALID
