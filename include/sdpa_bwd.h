@@ -213,6 +213,22 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
                               int32_t* offsets_out, int32_t* entries_out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing for measurement tools (not needed for computing anything).
+ * Between sdpa_profile_begin() and sdpa_profile_end() every kernel launch of
+ * this library is bracketed by a pair of HIP events recorded on its launch
+ * stream.  sdpa_profile_end() waits for the last recorded event, writes for
+ * each kernel id k < n_kernels the summed elapsed milliseconds total_ms[k]
+ * and the number of launches launches[k], and disables timing.  Kernel ids:
+ * 0 forward, 1 backward preprocess, 2 backward main, 3 dQ convert,
+ * 4 deterministic dQ, 5 NSA index build, 6 NSA dK/dV, 7 NSA dQ;
+ * sdpa_kernel_name(id) gives the kernel's symbol name stem.  Not thread-safe
+ * with respect to concurrent begin/end calls from several threads.
+ */
+int sdpa_profile_begin(void);
+int sdpa_profile_end(int n_kernels, double* total_ms, int64_t* launches);
+const char* sdpa_kernel_name(int kernel_id);
+
 #ifdef __cplusplus
 }
 #endif

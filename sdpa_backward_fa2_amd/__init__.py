@@ -86,9 +86,34 @@ _SIGS = {
     "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                   c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
                                   P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
+    "sdpa_profile_begin": (c_int, []),
+    "sdpa_profile_end": (c_int, [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
+    "sdpa_kernel_name": (ctypes.c_char_p, [c_int]),
     "sdpa_selected_build_index": (c_int, [c_i64, PI64, PI64, c_i64, c_vp, c_i64, c_i64, c_i64,
                                           c_i64, c_i64, c_vp, c_vp, c_vp, c_size, c_vp]),
 }
+
+
+N_KERNEL_IDS = 8
+
+
+class KernelTimer:
+    """Context manager: per-kernel HIP-event timing of every library launch
+    inside the block.  After exit, ``result[name] = (total_ms, launches)``."""
+
+    def __enter__(self):
+        _check(load().sdpa_profile_begin(), "sdpa_profile_begin")
+        self.result = {}
+        return self
+
+    def __exit__(self, *exc):
+        ms = (ctypes.c_double * N_KERNEL_IDS)()
+        n = (c_i64 * N_KERNEL_IDS)()
+        _check(load().sdpa_profile_end(N_KERNEL_IDS, ms, n), "sdpa_profile_end")
+        for i in range(N_KERNEL_IDS):
+            if n[i]:
+                self.result[load().sdpa_kernel_name(i).decode()] = (ms[i], n[i])
+        return False
 
 
 def library_path() -> str:
@@ -226,9 +251,11 @@ def _stats_arg(stats, packed: bool) -> Stats:
     return Stats(kind, a, b, *ref.stride()[:3])
 
 
-def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool = False,
-        dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV of dense attention.  stats: LSE (B, Hq, Sq[, 1]) or (max, sum)."""
+def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool = False,
+                dq=None, dk=None, dv=None, workspace=None):
+    """Marshal the arguments of one dense backward once; returns (call, (dq, dk, dv))
+    where call() enqueues the backward on the current stream.  The tensors must
+    stay alive and unmoved while call is used."""
     lib = load()
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
@@ -239,11 +266,28 @@ def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool
     nbytes = bwd_workspace_size(dt, B, Hq, Hkv, Sq, Sk, D, deterministic)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=False)
-    st = lib.sdpa_bwd(dt, B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal), int(deterministic),
-                      _t4(q), _t4(k), _t4(v), _t4(o), _t4(dout), ctypes.byref(sa),
-                      _t4(dq), _t4(dk), _t4(dv), ws.data_ptr(), ws.numel(), _stream_ptr(q.device))
-    _check(st, "sdpa_bwd")
-    return dq, dk, dv
+    structs = [_t4(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    args = (dt, B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal), int(deterministic),
+            *[ctypes.byref(x) for x in structs[:5]], ctypes.byref(sa),
+            *[ctypes.byref(x) for x in structs[5:]], ws.data_ptr(), ws.numel(),
+            _stream_ptr(q.device))
+    fn = lib.sdpa_bwd
+    keep = (structs, sa, ws, stats)
+
+    def call():
+        _check(fn(*args), "sdpa_bwd")
+
+    call.keep = keep
+    return call, (dq, dk, dv)
+
+
+def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool = False,
+        dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of dense attention.  stats: LSE (B, Hq, Sq[, 1]) or (max, sum)."""
+    call, outs = prepare_bwd(q, k, v, o, dout, stats, scale, causal, deterministic, dq, dk, dv,
+                             workspace)
+    call()
+    return outs
 
 
 # ----------------------------------------------------------------------------

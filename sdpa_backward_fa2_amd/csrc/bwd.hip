@@ -21,6 +21,7 @@
 // softmax gradient written with the forward output instead of P.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace sdpa {
 
@@ -400,20 +401,20 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
     const dim3 row_grid((unsigned)((row_threads + 255) / 256));
     const bool have_rows = p.rows > 0;
     if ((L.phase & BwdLaunch::kFirst) && have_rows)
-        hipLaunchKernelGGL((bwd_pre_kernel<T, D>), row_grid, dim3(256), 0, st, p, L.deterministic ? 0 : 1);
+        PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), row_grid, dim3(256), 0, st, p, L.deterministic ? 0 : 1);
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
     const bool have_main = main_grid.x > 0 && main_grid.y > 0;
     if (L.deterministic) {
         if (have_main)
-            hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
+            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
         const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
         if (dq_grid.x > 0 && dq_grid.y > 0)
-            hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
+            PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
     } else {
         if (have_main)
-            hipLaunchKernelGGL((bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
+            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
         if ((L.phase & BwdLaunch::kLast) && have_rows)
-            hipLaunchKernelGGL((bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
+            PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
     }
     return hipGetLastError();
 }

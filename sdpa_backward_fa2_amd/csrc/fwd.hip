@@ -9,6 +9,7 @@
 // lane-local and need a single exchange with the other lane half.
 #include "common.h"
 #include "kernels.h"
+#include "prof.h"
 
 namespace sdpa {
 
@@ -141,9 +142,9 @@ template <class T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, bool causal, hipStream_t st) {
     dim3 grid((p.Sq + 127) / 128, p.B * p.Hq);
     if (causal)
-        hipLaunchKernelGGL((fwd_kernel<T, D, true>), grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, true>), grid, dim3(256), 0, st, p);
     else
-        hipLaunchKernelGGL((fwd_kernel<T, D, false>), grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, false>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
