@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 256 MiB (10 launches), the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -147,6 +150,16 @@ def main():
         sys.exit(2)
     import torch
 
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
+        return
     import sdpa_backward_fa2_amd as sb
     sb.load()
     wl, call, outs, host, keep = build_inputs(args.config)

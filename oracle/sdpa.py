@@ -137,7 +137,7 @@ def dense_backward(q, k, v, do, scale: float, causal: bool, heads=None) -> dict:
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
     G = Hq // Hkv
-    todo = heads if heads is not None else [(b, hk) for b in range(B) for hk in range(Hkv)]
+    todo = sorted(set(heads)) if heads is not None else [(b, hk) for b in range(B) for hk in range(Hkv)]
     for b, hk in todo:
         for h in range(hk * G, (hk + 1) * G):
             g = head_backward(q[b, h], k[b, hk], v[b, hk], do[b, h], scale, allowed)
@@ -182,7 +182,7 @@ def varlen_backward(q, k, v, do, cu_q, cu_kv, scale: float, causal: bool, seqs=N
     _, Hkv, _ = v.shape
     dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     bounds = list(zip(_starts(cu_q), cu_q, _starts(cu_kv), cu_kv))
-    todo = range(len(bounds)) if seqs is None else seqs
+    todo = range(len(bounds)) if seqs is None else sorted(set(seqs))
     for i in todo:
         sq0, sq1, sk0, sk1 = bounds[i]
         allowed = causal_mask(sq1 - sq0, sk1 - sk0) if causal else None

@@ -45,6 +45,11 @@ __device__ __forceinline__ RowLoc row_of(const BwdParams& p, int64_t R) {
     return L;
 }
 
+// dQ accumulator row of statistics row R (head-major; see BwdParams)
+__device__ __forceinline__ int64_t acc_row(const BwdParams& p, const RowLoc& L, int64_t R) {
+    return p.varlen ? L.h * p.Sq + L.i : R;
+}
+
 __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
     return L.b * t.sb + L.h * t.sh + L.i * t.ss;
 }
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
     }
     if (zero_dq) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + R * D + part * 8);
+        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 8);
         dst[0] = z;
         dst[1] = z;
     }
@@ -96,26 +101,62 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
 // ---------------------------------------------------------------------------
 // Main backward kernel (KV-tile outer)
 // ---------------------------------------------------------------------------
+//
+// Per step (one 64-row query tile of one query head) each wavefront, owning 32
+// of the workgroup's 128 keys, computes S and dP (32 x 32 per half tile), P and
+// dS, then dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles sit row-major in
+// LDS; the transposed operands of the dV/dK products come from
+// ds_read_b64_tr_b16.  The next tile's Q/dO rows are loaded into registers
+// while the current one is consumed and written to the other half of a double
+// buffer.  In atomic mode dS^T goes to LDS and the four wavefronts split
+// dQ_tile = dS K (64 x D) between them, adding it to the fp32 accumulator with
+// global atomics.  Masks are evaluated only on tiles that need them (the
+// causal diagonal, a ragged last key tile); ragged query rows carry LSE = +inf
+// and so contribute P = 0 without a mask.
+
+// P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - Delta) for one 32x32
+// C tile held as (sa, pa); rows i = i_base + 8q + 4g + r, this lane's key my_j.
+template <bool MASKED, bool CAUSAL>
+__device__ __forceinline__ void softmax_grad_tile(f32x16& sa, f32x16& pa, const float* lse_row,
+                                                  const float* dlt_row, float scale_log2, int g,
+                                                  int i_base, int my_j, bool col_ok) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
+        const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_row[8 * q + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rg = 4 * q + r;
+            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
+            if (MASKED) {
+                const int i = i_base + 8 * q + 4 * g + r;
+                if (!col_ok || (CAUSAL && my_j > i)) pv = 0.f;
+            }
+            sa[rg] = pv;
+            pa[rg] = pv * (pa[rg] - Dr[r]);
+        }
+    }
+}
 
 template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
     constexpr int BC = 128;          // keys per workgroup: 4 wavefronts x 32
-    constexpr int BR = 64;           // query rows per inner step
+    constexpr int BR = 64;           // query rows per step
     constexpr int NW = 4;
     constexpr int KS = D / 16;       // k-steps over the head dimension
     constexpr int MB = BR / 32;      // 32-row blocks of the query tile
     constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int QP = D + 8;        // row stride of Qs, dOs     [i][d]
-    constexpr int TP = BR + 8;       // row stride of QT, dOT     [d][i]
-    constexpr int SP = BC + 8;       // row stride of dSs [i][j], KT [d][j]
-    __shared__ __align__(16) uint16_t Qs[BR * QP];
-    __shared__ __align__(16) uint16_t dOs[BR * QP];
-    __shared__ __align__(16) uint16_t QT[D * TP];
-    __shared__ __align__(16) uint16_t dOT[D * TP];
-    __shared__ __align__(16) uint16_t dSs[DQ_ATOMIC ? BR * SP : 8];
-    __shared__ __align__(16) uint16_t KT[DQ_ATOMIC ? D * SP : 8];
-    __shared__ __align__(16) float lse_s[BR];
-    __shared__ __align__(16) float dlt_s[BR];
+    constexpr int QP = D + 8;        // row stride of Qs, dOs, Ks  [row][d]
+    constexpr int SP = BR + 8;       // row stride of dST          [j][i]
+    constexpr int CH = BR * D / 8 / 256;     // 16-byte chunks per thread per tile
+    constexpr int NBLK = MB * DB / NW;       // dQ 32x32 blocks per wavefront
+    static_assert(CH >= 1 && NBLK >= 1, "tile shape");
+    __shared__ __align__(16) uint16_t Qs[2][BR * QP];
+    __shared__ __align__(16) uint16_t dOs[2][BR * QP];
+    __shared__ __align__(16) uint16_t Ks[DQ_ATOMIC ? BC * QP : 8];
+    __shared__ __align__(16) uint16_t dST[DQ_ATOMIC ? BC * SP : 8];
+    __shared__ __align__(16) float lse_s[2][BR];
+    __shared__ __align__(16) float dlt_s[2][BR];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -126,6 +167,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
     const int j0 = blockIdx.y * BC;
     if (j0 >= lk) return;
+    const bool full_cols = j0 + BC <= lk;
 
     const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
     const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
@@ -138,12 +180,259 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
         u32x4 z = {0u, 0u, 0u, 0u};
         kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
         vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
+        if (DQ_ATOMIC) st16(&Ks[(32 * w + c) * QP + 16 * s + 8 * g], kreg[s]);
     }
+
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
+
+    // steps: query heads of the group outer, query tiles from the causal start inner
+    const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
+    const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
+    const int n_steps = G * per_head;
+
+    // per-thread element offsets of its 16-byte chunks inside a tile (row r, column cc)
+    int qoff[CH], dooff[CH], crow[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + 256 * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        qoff[x] = r * (int)p.q.ss + cc;
+        dooff[x] = r * (int)p.dout.ss + cc;
+    }
+    const int64_t ws_step = p.varlen ? p.Hq : 1;
+
+    u32x4 pq[CH], pdo[CH];
+    float pl = INFINITY, pd = 0.f;
+    auto load_tile = [&](int st) {
+        const int h = hk * G + st / per_head;
+        const int i0 = i_begin + (st % per_head) * BR;
+        const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
+        const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
+        if (i0 + BR <= lq) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                pq[x] = ld16(qb + qoff[x]);
+                pdo[x] = ld16(dob + dooff[x]);
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                const bool ok = i0 + crow[x] < lq;
+                pq[x] = ok ? ld16(qb + qoff[x]) : z;
+                pdo[x] = ok ? ld16(dob + dooff[x]) : z;
+            }
+        }
+        if (tid < BR) {
+            const int i = i0 + tid;
+            const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
+            pl = i < lq ? p.lse2[ws] : INFINITY;
+            pd = i < lq ? p.delta[ws] : 0.f;
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            st16(&Qs[buf][r * QP + cc], pq[x]);
+            st16(&dOs[buf][r * QP + cc], pdo[x]);
+        }
+        if (tid < BR) {
+            lse_s[buf][tid] = pl;
+            dlt_s[buf][tid] = pd;
+        }
+    };
+
+    if (n_steps > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const int h = hk * G + st / per_head;
+        const int i0 = i_begin + (st % per_head) * BR;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+
+        const uint16_t* Qb = Qs[buf];
+        const uint16_t* dOb = dOs[buf];
+        const bool masked = (CAUSAL && i0 < j0 + BC) || !full_cols;
+        // one 32-row half of the query tile at a time keeps S and dP at 32 registers
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x16 sa = zero16(), pa = zero16();
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                sa = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
+                pa = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+            }
+            if (masked)
+                softmax_grad_tile<true, CAUSAL>(sa, pa, &lse_s[buf][mb * 32], &dlt_s[buf][mb * 32],
+                                                p.scale_log2, g, i0 + mb * 32, my_j, col_ok);
+            else
+                softmax_grad_tile<false, CAUSAL>(sa, pa, &lse_s[buf][mb * 32], &dlt_s[buf][mb * 32],
+                                                 p.scale_log2, g, i0 + mb * 32, my_j, col_ok);
+            if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 bP = acc_to_operand<T>(sa, hh);
+                const u32x4 bS = acc_to_operand<T>(pa, hh);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                    dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                }
+                if (DQ_ATOMIC) {
+                    // dS^T rows j = 32w + c; bS holds query rows 16hh + 4g + 0..3 and
+                    // 16hh + 8 + 4g + 0..3 of this half tile, packed in pairs
+                    u32x2 lo, hi;
+                    lo[0] = bS[0]; lo[1] = bS[1]; hi[0] = bS[2]; hi[1] = bS[3];
+                    st8(&dST[(32 * w + c) * SP + mb * 32 + 16 * hh + 4 * g], lo);
+                    st8(&dST[(32 * w + c) * SP + mb * 32 + 16 * hh + 8 + 4 * g], hi);
+                }
+            }
+        }
+
+        if (DQ_ATOMIC) {
+            __syncthreads();
+            f32x16 acc[NBLK];
+#pragma unroll
+            for (int x = 0; x < NBLK; ++x) acc[x] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < BC / 16; ++ks)
+#pragma unroll
+                for (int x = 0; x < NBLK; ++x) {
+                    const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
+                    acc[x] = T::mma(ld_tr<false>(dST, SP, 16 * ks, ib * 32, lane),
+                                    ld_tr<false>(Ks, QP, 16 * ks, db * 32, lane), acc[x]);
+                }
+            // accumulator rows of this (sequence, head): head-major, row stride D floats
+            const int64_t arow0 = p.varlen ? ((int64_t)h * p.Sq + q0) : (((int64_t)b * p.Hq + h) * p.Sq);
+            float* dqa = p.dqacc + (arow0 + i0) * D + c;
+            const bool full_rows = i0 + BR <= lq;
+#pragma unroll
+            for (int x = 0; x < NBLK; ++x) {
+                const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
+                float* base = dqa + (ib * 32 + 4 * g) * D + db * 32;
+                if (full_rows) {
+#pragma unroll
+                    for (int rg = 0; rg < 16; ++rg)
+                        atomicAdd(base + (8 * (rg >> 2) + (rg & 3)) * D, acc[x][rg]);
+                } else {
+#pragma unroll
+                    for (int rg = 0; rg < 16; ++rg) {
+                        const int i = i0 + ib * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3);
+                        if (i < lq) atomicAdd(base + (8 * (rg >> 2) + (rg & 3)) * D, acc[x][rg]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+    (void)ws_step;
+
+    if (!col_ok) return;
+    uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
+    uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x2 a, v;
+            a[0] = T::pack(dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale);
+            a[1] = T::pack(dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+            v[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
+            v[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
+            st8(dkp + db * 32 + 8 * q + 4 * g, a);
+            st8(dvp + db * 32 + 8 * q + 4 * g, v);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Main backward kernel, eight wavefronts (two per SIMD)
+// ---------------------------------------------------------------------------
+//
+// Same work item as bwd_main_kernel (128 keys of one KV head, every query tile
+// of every query head of its group) with eight wavefronts: wavefront
+// w = kw + 4*rh owns keys 32*kw .. 32*kw+31 and rows 32*rh .. 32*rh+31 of each
+// 64-row query tile.  Each SIMD thus runs two wavefronts, so the matrix core
+// and the vector ALU of a SIMD overlap, and every wavefront carries half the
+// softmax work.  dK/dV accumulate per wavefront over its row half; the two
+// halves are summed through LDS once, at the end.  dQ_tile = dS K uses
+// v_mfma_f32_16x16x32: wavefront w owns query rows 16*(w/2) .. +15 and head
+// dims 32*(w%2) .. +31 of the tile, with its K operand held in registers for
+// the whole kernel, so only dS^T is read from LDS per step.
+
+template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
+__global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
+    constexpr int BC = 128;          // keys per workgroup
+    constexpr int BR = 64;           // query rows per step
+    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
+    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
+    constexpr int QP = D + 8;        // row stride of Qs, dOs, Ks  [row][d]
+    constexpr int SP = BR + 8;       // row stride of dST          [j][i]
+    constexpr int CH = BR * D / 8 / 512;     // 16-byte chunks per thread per tile
+    constexpr int NQB = D / 32;      // 16-wide head-dim blocks of dQ per wavefront (2 for D=64)
+    static_assert(CH >= 1, "tile shape");
+    constexpr int TILE_B = BR * QP * 2;                  // bytes of one Q (or dO) tile
+    constexpr int OFF_Q = 0, OFF_DO = 2 * TILE_B, OFF_ST = 4 * TILE_B;
+    constexpr int OFF_STAT = OFF_ST + BC * (QP > SP ? QP : SP) * 2;
+    constexpr int LOOP_B = OFF_STAT + 4 * BR * 4;
+    constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of four wavefronts
+    constexpr int ARENA = LOOP_B > RED_B ? LOOP_B : RED_B;
+    __shared__ __align__(16) unsigned char arena[ARENA];
+    uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena + OFF_Q);
+    uint16_t* dOs0 = reinterpret_cast<uint16_t*>(arena + OFF_DO);
+    uint16_t* dST = reinterpret_cast<uint16_t*>(arena + OFF_ST);
+    float* lse_s = reinterpret_cast<float*>(arena + OFF_STAT);          // [2][BR]
+    float* dlt_s = lse_s + 2 * BR;                                        // [2][BR]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int kw = w & 3, rh = w >> 2;
+    const int g = lane >> 5, c = lane & 31;
+    const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
+    const int G = p.Hq / p.Hkv;
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
+    const int j0 = blockIdx.y * BC;
+    if (j0 >= lk) return;
+    const bool full_cols = j0 + BC <= lk;
+
+    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
+    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
+
+    const int my_j = j0 + 32 * kw + c;
+    const bool col_ok = my_j < lk;
+    u32x4 kreg[KS], vreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
+        vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
+    }
+    // K operand of the dQ product (k = key, column = head dim), via a row-major
+    // staging copy of the key tile in the dS^T area
+    u32x4 kop[BC / 32][NQB];
     if (DQ_ATOMIC) {
+        uint16_t* Ks = dST;
+        if (rh == 0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+            for (int s = 0; s < KS; ++s) st16(&Ks[(32 * kw + c) * QP + 16 * s + 8 * g], kreg[s]);
+        }
+        __syncthreads();
 #pragma unroll
-            for (int t = 0; t < 8; ++t) KT[(16 * s + 8 * g + t) * SP + 32 * w + c] = elem16(kreg[s], t);
+        for (int ks = 0; ks < BC / 32; ++ks)
+#pragma unroll
+            for (int nb = 0; nb < NQB; ++nb)
+                kop[ks][nb] = ld_tr16x16(Ks, QP, 32 * ks, (w & 1) * (16 * NQB) + 16 * nb, lane);
+        __syncthreads();
     }
 
     f32x16 dva[DB], dka[DB];
@@ -151,105 +440,165 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdParams p) {
     for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
 
     const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
-    for (int gh = 0; gh < G; ++gh) {
-        const int h = hk * G + gh;
-        const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
-        const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
-        const int64_t ws_base = p.varlen ? (int64_t)q0 * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq;
-        const int64_t ws_step = p.varlen ? p.Hq : 1;
+    const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
+    const int n_steps = G * per_head;
 
-        for (int i0 = i_begin; i0 < lq; i0 += BR) {
-            __syncthreads();
-            for (int e = tid; e < BR * D / 8; e += 256) {
-                const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-                const int i = i0 + r;
-                u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-                if (i < lq) {
-                    qv = ld16(qbase + (int64_t)i * p.q.ss + cc);
-                    dv = ld16(dobase + (int64_t)i * p.dout.ss + cc);
-                }
-                st16(&Qs[r * QP + cc], qv);
-                st16(&dOs[r * QP + cc], dv);
+    int qoff[CH], dooff[CH], crow[CH];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    QT[(cc + t) * TP + r] = elem16(qv, t);
-                    dOT[(cc + t) * TP + r] = elem16(dv, t);
-                }
-            }
-            if (tid < BR) {
-                const int i = i0 + tid;
-                lse_s[tid] = i < lq ? p.lse2[ws_base + i * ws_step] : INFINITY;
-                dlt_s[tid] = i < lq ? p.delta[ws_base + i * ws_step] : 0.f;
-            }
-            __syncthreads();
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + 512 * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        qoff[x] = r * (int)p.q.ss + cc;
+        dooff[x] = r * (int)p.dout.ss + cc;
+    }
 
-            f32x16 sa[MB], pa[MB];
+    u32x4 pq[CH], pdo[CH];
+    float pl = INFINITY, pd = 0.f;
+    auto load_tile = [&](int st) {
+        const int h = hk * G + st / per_head;
+        const int i0 = i_begin + (st % per_head) * BR;
+        const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
+        const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
+        if (i0 + BR <= lq) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                sa[mb] = zero16();
-                pa[mb] = zero16();
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    sa[mb] = T::mma(ld16(&Qs[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa[mb]);
-                    pa[mb] = T::mma(ld16(&dOs[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa[mb]);
-                }
+            for (int x = 0; x < CH; ++x) {
+                pq[x] = ld16(qb + qoff[x]);
+                pdo[x] = ld16(dob + dooff[x]);
             }
-            const bool diag = CAUSAL && (i0 < j0 + BC);
+        } else {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int x = 0; x < CH; ++x) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                const bool ok = i0 + crow[x] < lq;
+                pq[x] = ok ? ld16(qb + qoff[x]) : z;
+                pdo[x] = ok ? ld16(dob + dooff[x]) : z;
+            }
+        }
+        if (tid < BR) {
+            const int i = i0 + tid;
+            const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
+            pl = i < lq ? p.lse2[ws] : INFINITY;
+            pd = i < lq ? p.delta[ws] : 0.f;
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* Qd = Qs0 + buf * (BR * QP);
+        uint16_t* dOd = dOs0 + buf * (BR * QP);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[mb * 32 + 8 * q + 4 * g]);
-                    const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_s[mb * 32 + 8 * q + 4 * g]);
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 512 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            st16(&Qd[r * QP + cc], pq[x]);
+            st16(&dOd[r * QP + cc], pdo[x]);
+        }
+        if (tid < BR) {
+            lse_s[buf * BR + tid] = pl;
+            dlt_s[buf * BR + tid] = pd;
+        }
+    };
+
+    if (n_steps > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const int h = hk * G + st / per_head;
+        const int i0 = i_begin + (st % per_head) * BR;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+
+        const uint16_t* Qb = Qs0 + buf * (BR * QP);
+        const uint16_t* dOb = dOs0 + buf * (BR * QP);
+        const bool masked = (CAUSAL && i0 < j0 + BC) || !full_cols;
+        f32x16 sa = zero16(), pa = zero16();
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int rg = 4 * q + r;
-                        const int i = i0 + mb * 32 + 8 * q + 4 * g + r;
-                        float pv = fast_exp2(sa[mb][rg] * p.scale_log2 - Lr[r]);
-                        if (!col_ok || (diag && my_j > i)) pv = 0.f;
-                        sa[mb][rg] = pv;
-                        pa[mb][rg] = pv * (pa[mb][rg] - Dr[r]);
-                    }
-                }
+        for (int s = 0; s < KS; ++s) {
+            sa = T::mma(ld16(&Qb[(32 * rh + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
+            pa = T::mma(ld16(&dOb[(32 * rh + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+        }
+        if (masked)
+            softmax_grad_tile<true, CAUSAL>(sa, pa, &lse_s[buf * BR + 32 * rh], &dlt_s[buf * BR + 32 * rh],
+                                            p.scale_log2, g, i0 + 32 * rh, my_j, col_ok);
+        else
+            softmax_grad_tile<false, CAUSAL>(sa, pa, &lse_s[buf * BR + 32 * rh], &dlt_s[buf * BR + 32 * rh],
+                                             p.scale_log2, g, i0 + 32 * rh, my_j, col_ok);
+        if (has_next) store_tile(buf ^ 1);
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 bP = acc_to_operand<T>(sa, hh);
+            const u32x4 bS = acc_to_operand<T>(pa, hh);
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const u32x4 bP = acc_to_operand<T>(sa[mb], hh);
-                    const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int d = db * 32 + c;
-                        dva[db] = T::mma(ld_acc_slots(&dOT[d * TP + mb * 32 + 16 * hh], g), bP, dva[db]);
-                        dka[db] = T::mma(ld_acc_slots(&QT[d * TP + mb * 32 + 16 * hh], g), bS, dka[db]);
-                    }
-                }
+            for (int db = 0; db < DB; ++db) {
+                dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP, dva[db]);
+                dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS, dka[db]);
+            }
             if (DQ_ATOMIC) {
+                u32x2 lo, hi;
+                lo[0] = bS[0]; lo[1] = bS[1]; hi[0] = bS[2]; hi[1] = bS[3];
+                st8(&dST[(32 * kw + c) * SP + 32 * rh + 16 * hh + 4 * g], lo);
+                st8(&dST[(32 * kw + c) * SP + 32 * rh + 16 * hh + 8 + 4 * g], hi);
+            }
+        }
+
+        if (DQ_ATOMIC) {
+            __syncthreads();
+            const int ib = w >> 1;                 // query rows 16*ib .. +15 of the tile
+            f32x4 acc[NQB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+            for (int nb = 0; nb < NQB; ++nb) acc[nb] = zero4();
 #pragma unroll
-                    for (int rg = 0; rg < 16; ++rg)
-                        dSs[(mb * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3)) * SP + 32 * w + c] = T::cvt(pa[mb][rg]);
-                __syncthreads();
-                for (int blk = w; blk < MB * DB; blk += NW) {
-                    const int ib = blk / DB, db = blk % DB;
-                    f32x16 acc = zero16();
+            for (int ks = 0; ks < BC / 32; ++ks) {
+                const u32x4 a = ld_tr16x16(dST, SP, 32 * ks, 16 * ib, lane);
 #pragma unroll
-                    for (int ks = 0; ks < BC / 16; ++ks)
-                        acc = T::mma(ld16(&dSs[(ib * 32 + c) * SP + 16 * ks + 8 * g]),
-                                     ld16(&KT[(db * 32 + c) * SP + 16 * ks + 8 * g]), acc);
+                for (int nb = 0; nb < NQB; ++nb) acc[nb] = T::mma16(a, kop[ks][nb], acc[nb]);
+            }
+            const int64_t arow0 = p.varlen ? ((int64_t)h * p.Sq + q0) : (((int64_t)b * p.Hq + h) * p.Sq);
+            const int G16 = lane >> 4, col = lane & 15;
+            float* base = p.dqacc + (arow0 + i0 + 16 * ib + 4 * G16) * D + (w & 1) * (16 * NQB) + col;
+            if (i0 + BR <= lq) {
 #pragma unroll
-                    for (int rg = 0; rg < 16; ++rg) {
-                        const int i = i0 + ib * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3);
-                        if (i < lq)
-                            atomicAdd(&p.dqacc[(ws_base + i * ws_step) * D + db * 32 + c], acc[rg]);
-                    }
-                }
+                for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) atomicAdd(base + r * D + 16 * nb, acc[nb][r]);
+            } else {
+#pragma unroll
+                for (int nb = 0; nb < NQB; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (i0 + 16 * ib + 4 * G16 + r < lq) atomicAdd(base + r * D + 16 * nb, acc[nb][r]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // sum the two row halves' dK/dV partials through LDS, then store
+    float* red = reinterpret_cast<float*>(arena);
+    if (rh == 1) {
+#pragma unroll
+        for (int a = 0; a < 2 * DB; ++a) {
+            const f32x16& v = a < DB ? dva[a] : dka[a - DB];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 x = {v[4 * r4 + 0], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]) = x;
             }
         }
     }
-
-    if (!col_ok) return;
+    __syncthreads();
+    if (rh == 1 || !col_ok) return;
+#pragma unroll
+    for (int a = 0; a < 2 * DB; ++a) {
+        f32x16& v = a < DB ? dva[a] : dka[a - DB];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]);
+            v[4 * r4 + 0] += x[0]; v[4 * r4 + 1] += x[1]; v[4 * r4 + 2] += x[2]; v[4 * r4 + 3] += x[3];
+        }
+    }
     uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
     uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
 #pragma unroll
@@ -278,7 +627,7 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
     const int part = (int)(gt % LPR);
     if (R >= p.rows) return;
     const RowLoc L = row_of(p, R);
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.dqacc + R * D + part * 8);
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 8);
     const f32x4 a = src[0], c = src[1];
     u32x4 o;
     o[0] = T::pack(a[0] * p.scale, a[1] * p.scale);
@@ -392,6 +741,199 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dQ pass without atomics, eight wavefronts (query-tile outer)
+// ---------------------------------------------------------------------------
+//
+// One workgroup per (sequence, query head, 64-row query tile); it walks the
+// 128-key tiles the tile can see.  Wavefront w = kw + 4*rh owns query rows
+// 32*rh .. +31 and keys 32*kw .. +31 of every key tile.  Scores are computed
+// transposed, S^T = K Q^T and dP^T = V dO^T, so that each lane holds one query
+// column: its LSE and Delta are lane-uniform, and dS^T feeds
+// dQ^T += K^T dS^T directly as the B operand.  Q and dO stay in registers for
+// the whole kernel; key tiles stream through a double-buffered LDS copy whose
+// next tile is loaded into registers while the current one is used.  Each
+// wavefront accumulates dQ^T over its key slices; the four slices are summed
+// through LDS at the end and dQ is written once, scaled and rounded.
+
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
+    constexpr int BQ = 64;           // query rows per workgroup
+    constexpr int BK = 128;          // keys per step
+    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
+    constexpr int DB = D / 32;       // 32-row blocks of dQ^T
+    constexpr int KP = D + 8;        // row stride of Ks, Vs  [key][d]
+    constexpr int CH = BK * D / 8 / 512;     // 16-byte chunks per thread per key tile
+    constexpr int TILE_B = BK * KP * 2;
+    constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
+    constexpr int LOOP_B = 4 * TILE_B;
+    constexpr int RED_B = 3 * 2 * 64 * (DB * 16) * 4;    // three key slices of both row halves
+    constexpr int ARENA = LOOP_B > RED_B ? LOOP_B : RED_B;
+    __shared__ __align__(16) unsigned char arena[ARENA];
+    uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
+    uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int kw = w & 3, rh = w >> 2;
+    const int g = lane >> 5, c = lane & 31;
+    const int b = blockIdx.y / p.Hq, h = blockIdx.y % p.Hq;
+    const int hk = h / (p.Hq / p.Hkv);
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
+    const int i0 = blockIdx.x * BQ;
+    if (i0 >= lq) return;
+
+    const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
+    const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
+    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
+    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
+
+    const int my_i = i0 + 32 * rh + c;
+    const bool row_ok = my_i < lq;
+    u32x4 qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qreg[s] = row_ok ? ld16(qbase + (int64_t)my_i * p.q.ss + 16 * s + 8 * g) : z;
+        doreg[s] = row_ok ? ld16(dobase + (int64_t)my_i * p.dout.ss + 16 * s + 8 * g) : z;
+    }
+    const int64_t ws = p.varlen ? ((int64_t)(q0 + my_i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + my_i);
+    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
+    const float dl = row_ok ? p.delta[ws] : 0.f;
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+
+    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
+    const int n_steps = (kend + BK - 1) / BK;
+
+    int koff[CH], voff[CH], crow[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + 512 * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        koff[x] = r * (int)p.k.ss + cc;
+        voff[x] = r * (int)p.v.ss + cc;
+    }
+    u32x4 pk[CH], pv[CH];
+    auto load_tile = [&](int st) {
+        const int j0 = st * BK;
+        const uint16_t* kb = kbase + (int64_t)j0 * p.k.ss;
+        const uint16_t* vb = vbase + (int64_t)j0 * p.v.ss;
+        if (j0 + BK <= lk) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                pk[x] = ld16(kb + koff[x]);
+                pv[x] = ld16(vb + voff[x]);
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                const bool ok = j0 + crow[x] < lk;
+                pk[x] = ok ? ld16(kb + koff[x]) : z;
+                pv[x] = ok ? ld16(vb + voff[x]) : z;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* Kd = Ks0 + buf * (BK * KP);
+        uint16_t* Vd = Vs0 + buf * (BK * KP);
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 512 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            st16(&Kd[r * KP + cc], pk[x]);
+            st16(&Vd[r * KP + cc], pv[x]);
+        }
+    };
+
+    if (n_steps > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const int j0 = st * BK;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+        const uint16_t* Kb = Ks0 + buf * (BK * KP);
+        const uint16_t* Vb = Vs0 + buf * (BK * KP);
+
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
+            dp = T::mma(ld16(&Vb[(32 * kw + c) * KP + 16 * ks + 8 * g]), doreg[ks], dp);
+        }
+        // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
+        const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);
+        if (masked) {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const int j = j0 + 32 * kw + 8 * (rg >> 2) + 4 * g + (rg & 3);
+                float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                if (j >= lk || (CAUSAL && j > my_i)) pvv = 0.f;
+                dp[rg] = pvv * (dp[rg] - dl);
+            }
+        } else {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                dp[rg] = pvv * (dp[rg] - dl);
+            }
+        }
+        if (has_next) store_tile(buf ^ 1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 bS = acc_to_operand<T>(dp, hh);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane), bS, dq[db]);
+        }
+        __syncthreads();
+    }
+
+    // sum the four key slices through LDS (slices 1..3 write, slice 0 adds)
+    float* red = reinterpret_cast<float*>(arena);
+    if (kw != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 x = {dq[db][4 * r4 + 0], dq[db][4 * r4 + 1], dq[db][4 * r4 + 2], dq[db][4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(&red[(((((kw - 1) * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]) = x;
+            }
+    }
+    __syncthreads();
+    if (kw != 0 || !row_ok) return;
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&red[((((sl * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]);
+                dq[db][4 * r4 + 0] += x[0]; dq[db][4 * r4 + 1] += x[1];
+                dq[db][4 * r4 + 2] += x[2]; dq[db][4 * r4 + 3] += x[3];
+            }
+    uint16_t* dqp = p.dq.p + b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            u32x2 v;
+            v[0] = T::pack(dq[db][4 * q + 0] * p.scale, dq[db][4 * q + 1] * p.scale);
+            v[1] = T::pack(dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
+            st8(dqp + db * 32 + 8 * q + 4 * g, v);
+        }
+}
+
+// ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
 
@@ -404,15 +946,31 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), row_grid, dim3(256), 0, st, p, L.deterministic ? 0 : 1);
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
     const bool have_main = main_grid.x > 0 && main_grid.y > 0;
+    constexpr bool W8 = D == 64;
+    const dim3 main_block(W8 ? 512 : 256);
     if (L.deterministic) {
-        if (have_main)
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
-        const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
-        if (dq_grid.x > 0 && dq_grid.y > 0)
-            PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
+        if constexpr (W8) {
+            if (have_main)
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main8_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
+        } else if (have_main) {
+            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
+        }
+        if constexpr (W8) {
+            const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
+            if (dq_grid.x > 0 && dq_grid.y > 0)
+                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(512), 0, st, p);
+        } else {
+            const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
+            if (dq_grid.x > 0 && dq_grid.y > 0)
+                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
+        }
     } else {
-        if (have_main)
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
+        if constexpr (W8) {
+            if (have_main)
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main8_kernel<T, D, CAUSAL, true>), main_grid, main_block, 0, st, p);
+        } else if (have_main) {
+            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, main_block, 0, st, p);
+        }
         if ((L.phase & BwdLaunch::kLast) && have_rows)
             PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
     }

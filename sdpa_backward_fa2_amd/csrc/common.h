@@ -37,6 +37,10 @@ struct F16 {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
     static __device__ __forceinline__ uint16_t cvt(float x) {
         return __builtin_bit_cast(uint16_t, (_Float16)x);
     }
@@ -46,11 +50,21 @@ struct F16 {
     static __device__ __forceinline__ float to_f32(uint16_t x) {
         return (float)__builtin_bit_cast(_Float16, x);
     }
+    // MFMA operands built from fp32 intermediates (P, dS): one instruction per
+    // pair, rounding toward zero (outputs use the round-to-nearest `pack`).
+    static __device__ __forceinline__ uint32_t pack_op(float lo, float hi) {
+        typedef __fp16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
 };
 
 struct BF16 {
     static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint16_t cvt(float x) {
@@ -62,6 +76,8 @@ struct BF16 {
     static __device__ __forceinline__ float to_f32(uint16_t x) {
         return __builtin_bit_cast(float, (uint32_t)x << 16);
     }
+    // gfx950 converts a pair to bf16 with round-to-nearest-even in one instruction.
+    static __device__ __forceinline__ uint32_t pack_op(float lo, float hi) { return pack(lo, hi); }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -81,10 +97,10 @@ __device__ __forceinline__ uint16_t elem16(u32x4 v, int t) {
 template <class T>
 __device__ __forceinline__ u32x4 acc_to_operand(const f32x16& a, int h) {
     u32x4 r;
-    r[0] = T::pack(a[8 * h + 0], a[8 * h + 1]);
-    r[1] = T::pack(a[8 * h + 2], a[8 * h + 3]);
-    r[2] = T::pack(a[8 * h + 4], a[8 * h + 5]);
-    r[3] = T::pack(a[8 * h + 6], a[8 * h + 7]);
+    r[0] = T::pack_op(a[8 * h + 0], a[8 * h + 1]);
+    r[1] = T::pack_op(a[8 * h + 2], a[8 * h + 3]);
+    r[2] = T::pack_op(a[8 * h + 4], a[8 * h + 5]);
+    r[3] = T::pack_op(a[8 * h + 6], a[8 * h + 7]);
     return r;
 }
 
@@ -99,10 +115,55 @@ __device__ __forceinline__ u32x4 ld_acc_slots(const uint16_t* base, int g) {
     return r;
 }
 
+// Transposed operand from a row-major LDS tile X (row stride ld elements) whose
+// rows are the contracted index k and whose columns are the MFMA's free index:
+// this lane gets column n0 + (lane % 32) and the eight k values of its slots.
+// ds_read_b64_tr_b16 works on 16-lane groups: lane p of a group supplies the
+// address of four consecutive columns 4*(p%4).. of row p/4 and receives column
+// p of the four rows, so two reads give the eight slots.
+//   ACC = false: "row slots"  k = k0 + 8*g + t;
+//   ACC = true:  "acc slots"  k = k0 + 4*g + t (t < 4), k0 + 8 + 4*g + t - 4.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <bool ACC>
+__device__ __forceinline__ u32x4 ld_tr(const uint16_t* X, int ld, int k0, int n0, int lane) {
+    const int p = lane & 15, grp = lane >> 4;
+    const int g = grp >> 1, cb = (grp & 1) * 16;
+    const int kr0 = ACC ? (k0 + 4 * g) : (k0 + 8 * g);
+    const int kr1 = ACC ? (k0 + 8 + 4 * g) : (k0 + 8 * g + 4);
+    const int col = n0 + cb + 4 * (p & 3);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (kr0 + (p >> 2)) * ld + col));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (kr1 + (p >> 2)) * ld + col));
+    const u32x2 a = __builtin_bit_cast(u32x2, v0), b = __builtin_bit_cast(u32x2, v1);
+    u32x4 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    return r;
+}
+
+// The same for v_mfma_f32_16x16x32 operands: 16-lane group G = lane / 16 holds
+// k = k0 + 8*G + t (t = 0..7) of column n0 + lane % 16.  (16x16 C tiles: lane
+// holds column lane % 16, rows 4*G + r in register r.)
+__device__ __forceinline__ u32x4 ld_tr16x16(const uint16_t* X, int ld, int k0, int n0, int lane) {
+    const int p = lane & 15, G = lane >> 4;
+    const int col = n0 + 4 * (p & 3);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (k0 + 8 * G + (p >> 2)) * ld + col));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (k0 + 8 * G + 4 + (p >> 2)) * ld + col));
+    const u32x2 a = __builtin_bit_cast(u32x2, v0), b = __builtin_bit_cast(u32x2, v1);
+    u32x4 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll
     for (int i = 0; i < 16; ++i) z[i] = 0.f;
+    return z;
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
     return z;
 }
 
@@ -143,6 +204,9 @@ struct FwdParams {
 
 // Row statistics workspace layout: row index R of (b, h, i)
 //   dense:  R = (b*Hq + h)*Sq + i        packed: R = (q0 + i)*Hq + h
+// fp32 dQ accumulator rows (D floats each), head-major in both cases so that
+// consecutive query rows of one head are adjacent:
+//   dense:  A = (b*Hq + h)*Sq + i        packed: A = h*Tq + q0 + i
 struct BwdParams {
     TensorArg q, k, v, o, dout, dq, dk, dv;
     // user statistics
