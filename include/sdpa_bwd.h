@@ -179,8 +179,11 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   Constraints (Ascend page, "Constraints"): block_size <= 128 and a multiple
  *   of 16; 1 <= block_count <= 128; block_count * block_size < 8192; every KV
  *   sequence length a multiple of block_size and >= block_count * block_size;
- *   Hq a multiple of Hkv with Hq / Hkv <= 32.  Topk values outside the
- *   sequence's blocks are a caller error (not checked).
+ *   Hq a multiple of Hkv with Hq / Hkv <= 32; at most 64 sequences.  Topk
+ *   values outside the sequence's blocks select nothing (those slots are
+ *   ignored); the statistics must then describe the same reduced key set.
+ *   Every kernel of this path is deterministic; the flag is accepted for
+ *   symmetry with the other entry points.
  */
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,

@@ -139,6 +139,10 @@ int read_packed(int64_t batch, const int64_t* cuq, const int64_t* cuk, bool same
 
 }  // namespace
 
+namespace sdpa {
+void set_last_error(const char* msg) { g_last_error = msg ? msg : ""; }
+}  // namespace sdpa
+
 extern "C" {
 
 const char* sdpa_status_string(int status) {

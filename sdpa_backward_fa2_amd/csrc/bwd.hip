@@ -982,6 +982,20 @@ static hipError_t launch_bwd_d(const BwdParams& p, const BwdLaunch& L, hipStream
     return L.causal ? launch_bwd_t<T, D, true>(p, L, st) : launch_bwd_t<T, D, false>(p, L, st);
 }
 
+template <class T, int D>
+static hipError_t launch_pre_t(const BwdParams& p, bool zero_dq, hipStream_t st) {
+    const int64_t row_threads = p.rows * (D / 8);
+    if (row_threads > 0)
+        PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((row_threads + 255) / 256)), dim3(256),
+                    0, st, p, zero_dq ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st) {
+    if (dtype == 0) return D == 64 ? launch_pre_t<F16, 64>(p, zero_dq, st) : launch_pre_t<F16, 128>(p, zero_dq, st);
+    return D == 64 ? launch_pre_t<BF16, 64>(p, zero_dq, st) : launch_pre_t<BF16, 128>(p, zero_dq, st);
+}
+
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     if (L.dtype == 0)
         return L.D == 64 ? launch_bwd_d<F16, 64>(p, L, st) : launch_bwd_d<F16, 128>(p, L, st);

@@ -155,6 +155,20 @@ __device__ __forceinline__ u32x4 ld_tr16x16(const uint16_t* X, int ld, int k0, i
     return r;
 }
 
+// 16x16x32 operand in "acc slots" order: k = k0 + 4*G + t (t < 4) and
+// k0 + 16 + 4*G + (t - 4) (t >= 4): the rows two 16x16 C tiles (k0.., k0+16..)
+// hold in one lane, so their pair feeds the B operand of the next product.
+__device__ __forceinline__ u32x4 ld_tr16x16_acc(const uint16_t* X, int ld, int k0, int n0, int lane) {
+    const int p = lane & 15, G = lane >> 4;
+    const int col = n0 + 4 * (p & 3);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (k0 + 4 * G + (p >> 2)) * ld + col));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + (k0 + 16 + 4 * G + (p >> 2)) * ld + col));
+    const u32x2 a = __builtin_bit_cast(u32x2, v0), b = __builtin_bit_cast(u32x2, v1);
+    u32x4 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    return r;
+}
+
 __device__ __forceinline__ f32x16 zero16() {
     f32x16 z;
 #pragma unroll

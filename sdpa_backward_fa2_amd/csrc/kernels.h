@@ -24,5 +24,9 @@ struct BwdLaunch {
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
+// Delta and log2-LSE per statistics row (and the dQ accumulator clear).
+hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st);
+// Sets the text sdpa_last_error() returns on this thread.
+void set_last_error(const char* msg);
 
 }  // namespace sdpa

@@ -1,27 +1,848 @@
-// NSA selected-attention backward: placeholder entry points until the gathered
-// kernels land.
+// NSA selected-attention backward (aclnnNsaSelectedAttentionGrad) for gfx950.
+//
+// For query token t and KV head h2 the keys are the block_count blocks of
+// block_size rows that topk[t, h2, :] names, gathered with repetition (the
+// operator page's Gather over 0 <= i < selectedBlockCount, "Formula" section);
+// the gradients are the page's dV = P^T dY, dQ = dS K / sqrt(d),
+// dK = dS^T Q / sqrt(d) over those keys.
+//
+// Kernels, all on the caller's stream:
+//   nsa_index_kernel<false>  per (KV head, KV block): how many (token, slot)
+//                            choices name the block (ordered scan, no atomics)
+//   nsa_scan_kernel          CSR offsets of those lists and a table of work
+//                            pieces (at most `chunk` entries of one block each)
+//   nsa_index_kernel<true>   fills each block's list in (token, slot) order
+//   bwd_pre_kernel           Delta and log2-LSE per (token, head)  [bwd.hip]
+//   nsa_kv_kernel            per piece and 64-key half of its block: dK, dV
+//                            over the piece's tokens (G heads per token form
+//                            the query rows of a step); a block with one piece
+//                            writes dK/dV, otherwise an fp32 partial
+//   nsa_kv_reduce_kernel     sums the partials of multi-piece blocks in piece
+//                            order (deterministic); zero-fills unselected blocks
+//   nsa_dq_kernel            per (token, KV head, 16-head tile): dQ over the
+//                            gathered keys, without atomics
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <type_traits>
+#include <vector>
+
 #include "../../include/sdpa_bwd.h"
+#include "common.h"
+#include "kernels.h"
+#include "prof.h"
+
+namespace sdpa {
+
+struct NsaParams {
+    const int32_t* topk;
+    int64_t tk_st, tk_sn, tk_sk;
+    int count, bs, N2, NB, G, Hq;
+    int chunk;            // entries per work piece
+    int max_pieces;
+    SeqTable seqs;        // per sequence: first query row, first key row, lengths
+    int32_t* counts;      // [N2*NB]
+    int32_t* offsets;     // [N2*NB + 1]
+    int32_t* entries;     // [Tq*N2*count]
+    int32_t* pstart;      // [N2*NB + 1] first piece of each bucket
+    int32_t* pieces;      // [max_pieces][3]: bucket, first entry, end entry
+    // backward
+    TensorArg q, k, v, dout, dq, dk, dv;
+    const float* lse2;
+    const float* delta;
+    float* partial;       // [max_pieces][halves][64][D] for dK then dV
+    int halves;           // ceil(bs / 64)
+    int sparse_mode;
+    int Tq;
+    float scale, scale_log2;
+};
+
+__device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) {
+    int r = -1;
+    for (int i = 0; i < s.n; ++i)
+        if (key_row >= s.k0[i] && key_row < s.k0[i] + s.lk[i]) r = i;
+    return r;
+}
+
+__device__ __forceinline__ int seq_of_token(const SeqTable& s, int t) {
+    int r = -1;
+    for (int i = 0; i < s.n; ++i)
+        if (t >= s.q0[i] && t < s.q0[i] + s.lq[i]) r = i;
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Inverse index
+// ---------------------------------------------------------------------------
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void nsa_index_kernel(NsaParams p) {
+    __shared__ int wave_n[4];
+    const int g = blockIdx.x, h2 = blockIdx.y;
+    const int bucket = h2 * p.NB + g;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int s = seq_of_block(p.seqs, g * p.bs);
+    if (s < 0) {
+        if (!FILL && tid == 0) p.counts[bucket] = 0;
+        return;
+    }
+    const int gl = g - p.seqs.k0[s] / p.bs;      // block index within its sequence
+    const int64_t e0 = (int64_t)p.seqs.q0[s] * p.count;
+    const int64_t e1 = (int64_t)(p.seqs.q0[s] + p.seqs.lq[s]) * p.count;
+    int base = FILL ? p.offsets[bucket] : 0;
+    for (int64_t c0 = e0; c0 < e1; c0 += 256) {
+        const int64_t e = c0 + tid;
+        bool m = false;
+        if (e < e1) {
+            const int64_t t = e / p.count, slot = e % p.count;
+            m = p.topk[t * p.tk_st + (int64_t)h2 * p.tk_sn + slot * p.tk_sk] == gl;
+        }
+        const unsigned long long bal = __ballot(m);
+        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_n[w] = __popcll(bal);
+        __syncthreads();
+        int off = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            off += i < w ? wave_n[i] : 0;
+            tot += wave_n[i];
+        }
+        if (FILL && m) p.entries[base + off + rank] = (int32_t)e;
+        base += tot;
+        __syncthreads();
+    }
+    if (!FILL && tid == 0) p.counts[bucket] = base;
+}
+
+// Block-wide exclusive scan of one value per thread (1024 threads); returns the
+// exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wsum, int* total) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int v = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int i = 0; i < 16; ++i) {
+            const int t = wsum[i];
+            wsum[i] = acc;
+            acc += t;
+        }
+        wsum[16] = acc;
+    }
+    __syncthreads();
+    const int r = v - x + wsum[w];
+    *total = wsum[16];
+    __syncthreads();
+    return r;
+}
+
+__global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
+    __shared__ int wsum[17];
+    const int nb = p.N2 * p.NB;
+    int carry_e = 0, carry_p = 0;
+    for (int c0 = 0; c0 < nb; c0 += 1024) {
+        const int i = c0 + threadIdx.x;
+        const int cnt = i < nb ? p.counts[i] : 0;
+        const int np = (cnt + p.chunk - 1) / p.chunk;
+        int te, tp;
+        const int oe = block_exclusive_scan(cnt, wsum, &te);
+        const int op = block_exclusive_scan(np, wsum, &tp);
+        if (i < nb) {
+            const int off = carry_e + oe, ps = carry_p + op;
+            p.offsets[i] = off;
+            p.pstart[i] = ps;
+            for (int k = 0; k < np; ++k) {
+                p.pieces[(ps + k) * 3 + 0] = i;
+                p.pieces[(ps + k) * 3 + 1] = off + k * p.chunk;
+                p.pieces[(ps + k) * 3 + 2] = min(off + (k + 1) * p.chunk, off + cnt);
+            }
+        }
+        carry_e += te;
+        carry_p += tp;
+    }
+    if (threadIdx.x == 0) {
+        p.offsets[nb] = carry_e;
+        p.pstart[nb] = carry_p;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: key-block outer over pieces of the inverse lists
+// ---------------------------------------------------------------------------
+//
+// Workgroup of four wavefronts: wavefront w = kw + 2*rh owns keys 32*kw .. +31
+// of the 64-key half and rows 32*rh .. +31 of each 64-row step.  A step packs
+// E = 64 / G consecutive entries of the list; row r is head r % G of the token
+// of entry r / G.  The rest mirrors the dense main kernel: S and dP on MFMA,
+// P and dS on the vector ALU, dV^T += dO^T P and dK^T += Q^T dS with the
+// transposed operands read by ds_read_b64_tr_b16.
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
+    constexpr int BR = 64;
+    constexpr int KS = D / 16;
+    constexpr int DB = D / 32;
+    constexpr int QP = D + 8;
+    constexpr int CH = BR * D / 8 / 256;
+    constexpr int TILES_B = 4 * BR * QP * 2;             // Q and dO, double-buffered
+    constexpr int RED_B = 2 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of two wavefronts
+    constexpr int ARENA = TILES_B > RED_B ? TILES_B : RED_B;
+    __shared__ __align__(16) unsigned char arena[ARENA];
+    __shared__ __align__(16) float lse_s[2][BR];
+    __shared__ __align__(16) float dlt_s[2][BR];
+    __shared__ int tl_s[2][BR];          // sequence-local token position of each row
+    typedef uint16_t Tile[BR * QP];
+    Tile* Qs = reinterpret_cast<Tile*>(arena);
+    Tile* dOs = reinterpret_cast<Tile*>(arena + 2 * BR * QP * 2);
+
+    const int piece = blockIdx.x;
+    if (piece >= p.pstart[p.N2 * p.NB]) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int kw = w & 1, rh = w >> 1;
+    const int g = lane >> 5, c = lane & 31;
+    const int bucket = p.pieces[piece * 3 + 0];
+    const int eb = p.pieces[piece * 3 + 1], ee = p.pieces[piece * 3 + 2];
+    const int h2 = bucket / p.NB, blk = bucket % p.NB;
+    const int half = blockIdx.y;
+    const int kb0 = half * 64;                  // first key of this half inside the block
+    if (kb0 >= p.bs) return;
+    const int nkeys = min(64, p.bs - kb0);
+    const int s_idx = seq_of_block(p.seqs, blk * p.bs);
+    const int blk_local = blk - p.seqs.k0[s_idx] / p.bs;
+    const int key_row0 = blk * p.bs + kb0;      // packed KV row of key 0 of this half
+    const int kpos0 = blk_local * p.bs + kb0;   // its sequence-local position
+
+    const int myk = 32 * kw + c;
+    const bool col_ok = myk < nkeys;
+    u32x4 kreg[KS], vreg[KS];
+    const uint16_t* kp = p.k.p + h2 * p.k.sh + (int64_t)(key_row0 + myk) * p.k.ss;
+    const uint16_t* vp = p.v.p + h2 * p.v.sh + (int64_t)(key_row0 + myk) * p.v.ss;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        kreg[s] = col_ok ? ld16(kp + 16 * s + 8 * g) : z;
+        vreg[s] = col_ok ? ld16(vp + 16 * s + 8 * g) : z;
+    }
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
+
+    const int E = max(1, BR / p.G);             // entries per step
+    const int n_steps = (ee - eb + E - 1) / E;
+    const int q0s = p.seqs.q0[s_idx];
+
+    u32x4 pq[CH], pdo[CH];
+    float pl = INFINITY, pd = 0.f;
+    int ptl = 0;
+    auto load_tile = [&](int st) {
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            const int ei = eb + st * E + r / p.G;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            pq[x] = z;
+            pdo[x] = z;
+            if (r < E * p.G && ei < ee) {
+                const int t = p.entries[ei] / p.count;
+                const int h = h2 * p.G + r % p.G;
+                pq[x] = ld16(p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh + cc);
+                pdo[x] = ld16(p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh + cc);
+            }
+        }
+        if (tid < BR) {
+            const int r = tid;
+            const int ei = eb + st * E + r / p.G;
+            pl = INFINITY;
+            pd = 0.f;
+            ptl = 0;
+            if (r < E * p.G && ei < ee) {
+                const int t = p.entries[ei] / p.count;
+                const int h = h2 * p.G + r % p.G;
+                pl = p.lse2[(int64_t)t * p.Hq + h];
+                pd = p.delta[(int64_t)t * p.Hq + h];
+                ptl = t - q0s;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            st16(&Qs[buf][r * QP + cc], pq[x]);
+            st16(&dOs[buf][r * QP + cc], pdo[x]);
+        }
+        if (tid < BR) {
+            lse_s[buf][tid] = pl;
+            dlt_s[buf][tid] = pd;
+            tl_s[buf][tid] = ptl;
+        }
+    };
+
+    if (n_steps > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+    const int my_kpos = kpos0 + myk;
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+        const uint16_t* Qb = Qs[buf];
+        const uint16_t* dOb = dOs[buf];
+        f32x16 sa = zero16(), pa = zero16();
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sa = T::mma(ld16(&Qb[(32 * rh + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
+            pa = T::mma(ld16(&dOb[(32 * rh + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rb = 32 * rh + 8 * q + 4 * g;
+            const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[buf][rb]);
+            const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_s[buf][rb]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rg = 4 * q + r;
+                float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
+                const bool masked = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
+                pv = masked ? 0.f : pv;
+                sa[rg] = pv;
+                pa[rg] = pv * (pa[rg] - Dr[r]);
+            }
+        }
+        if (has_next) store_tile(buf ^ 1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 bP = acc_to_operand<T>(sa, hh);
+            const u32x4 bS = acc_to_operand<T>(pa, hh);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP, dva[db]);
+                dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS, dka[db]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // row halves -> one sum (through LDS, reusing the Q/dO tiles)
+    float* red = reinterpret_cast<float*>(arena);
+    if (rh == 1) {
+#pragma unroll
+        for (int a = 0; a < 2 * DB; ++a) {
+            const f32x16& v = a < DB ? dva[a] : dka[a - DB];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 x = {v[4 * r4 + 0], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]) = x;
+            }
+        }
+    }
+    __syncthreads();
+    if (rh == 1 || !col_ok) return;
+#pragma unroll
+    for (int a = 0; a < 2 * DB; ++a) {
+        f32x16& v = a < DB ? dva[a] : dka[a - DB];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]);
+            v[4 * r4 + 0] += x[0]; v[4 * r4 + 1] += x[1]; v[4 * r4 + 2] += x[2]; v[4 * r4 + 3] += x[3];
+        }
+    }
+    const int npieces = p.pstart[bucket + 1] - p.pstart[bucket];
+    if (npieces == 1) {
+        uint16_t* dkp = p.dk.p + h2 * p.dk.sh + (int64_t)(key_row0 + myk) * p.dk.ss;
+        uint16_t* dvp = p.dv.p + h2 * p.dv.sh + (int64_t)(key_row0 + myk) * p.dv.ss;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x2 a, v;
+                a[0] = T::pack(dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale);
+                a[1] = T::pack(dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+                v[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
+                v[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
+                st8(dkp + db * 32 + 8 * q + 4 * g, a);
+                st8(dvp + db * 32 + 8 * q + 4 * g, v);
+            }
+    } else {
+        // fp32 partial [piece][half][key][d] for dK, then the same for dV
+        float* pk = p.partial + (((int64_t)piece * p.halves + half) * 2 * 64 + myk) * D;
+        float* pv = pk + 64 * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 a = {dka[db][4 * q + 0], dka[db][4 * q + 1], dka[db][4 * q + 2], dka[db][4 * q + 3]};
+                f32x4 v = {dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2], dva[db][4 * q + 3]};
+                *reinterpret_cast<f32x4*>(pk + db * 32 + 8 * q + 4 * g) = a;
+                *reinterpret_cast<f32x4*>(pv + db * 32 + 8 * q + 4 * g) = v;
+            }
+    }
+}
+
+// Sum the partials of blocks split into several pieces (piece order), write
+// zeros for blocks no token selected.  One workgroup per (bucket, 64-key half).
+template <class T, int D>
+__global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
+    const int bucket = blockIdx.x, half = blockIdx.y;
+    const int h2 = bucket / p.NB, blk = bucket % p.NB;
+    const int kb0 = half * 64;
+    if (kb0 >= p.bs) return;
+    const int ps = p.pstart[bucket], np = p.pstart[bucket + 1] - ps;
+    if (np == 1) return;
+    const int nkeys = min(64, p.bs - kb0);
+    constexpr int LPR = D / 8;                  // threads per key row, 8 values each
+    for (int e = threadIdx.x; e < nkeys * LPR; e += 256) {
+        const int key = e / LPR, d0 = (e % LPR) * 8;
+        float ak[8], av[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
+        for (int x = 0; x < np; ++x) {
+            const float* pk = p.partial + (((int64_t)(ps + x) * p.halves + half) * 2 * 64 + key) * D + d0;
+            const float* pv = pk + 64 * D;
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ak[i] += k0[i]; ak[4 + i] += k1[i];
+                av[i] += v0[i]; av[4 + i] += v1[i];
+            }
+        }
+        u32x4 ok, ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ok[i] = T::pack(ak[2 * i] * p.scale, ak[2 * i + 1] * p.scale);
+            ov[i] = T::pack(av[2 * i], av[2 * i + 1]);
+        }
+        const int64_t row = (int64_t)blk * p.bs + kb0 + key;
+        st16(p.dk.p + h2 * p.dk.sh + row * p.dk.ss + d0, ok);
+        st16(p.dv.p + h2 * p.dv.sh + row * p.dv.ss + d0, ov);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: token outer over the gathered keys
+// ---------------------------------------------------------------------------
+//
+// Workgroup (four wavefronts) per (token, KV head, tile of 16 query heads).
+// Keys stream through LDS 128 at a time (gathered rows of K and V); wavefront
+// w takes keys 32*w .. +31 of each chunk.  Scores are computed transposed on
+// v_mfma_f32_16x16x32 (S^T = K Q^T, 16 keys x 16 heads per tile) so the heads
+// are the MFMA columns and each lane's LSE and Delta are one value; dQ^T +=
+// K^T dS^T uses the two 16-key tiles of a wavefront as one 32-deep operand.
+// The four wavefronts' partial dQ^T are summed through LDS at the end.
+
+template <class T, int D>
+__global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
+    constexpr int BK = 128;
+    constexpr int KP = D + 8;
+    constexpr int KS = D / 32;       // k-steps of 16x16x32 over the head dimension
+    constexpr int DB = D / 16;       // 16-row blocks of dQ^T
+    constexpr int CH = BK * D / 8 / 256;
+    __shared__ __align__(16) uint16_t Ks[BK * KP];
+    __shared__ __align__(16) uint16_t Vs[BK * KP];
+    __shared__ int kpos_s[BK];
+
+    const int t = blockIdx.x;
+    const int h2 = blockIdx.y / ((p.G + 15) / 16);
+    const int ht = blockIdx.y % ((p.G + 15) / 16);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 15, G16 = lane >> 4;
+    const int s_idx = seq_of_token(p.seqs, t);
+    if (s_idx < 0) return;
+    const int t_local = t - p.seqs.q0[s_idx];
+    const int krow0 = p.seqs.k0[s_idx];
+    const int nblk = p.seqs.lk[s_idx] / p.bs;   // blocks of this sequence
+    const int gh = ht * 16 + col;               // head within the group
+    const bool head_ok = gh < p.G;
+    const int h = h2 * p.G + (head_ok ? gh : 0);
+
+    u32x4 qreg[KS], doreg[KS];
+    const uint16_t* qp = p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh;
+    const uint16_t* dop = p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qreg[s] = head_ok ? ld16(qp + 32 * s + 8 * G16) : z;
+        doreg[s] = head_ok ? ld16(dop + 32 * s + 8 * G16) : z;
+    }
+    const float l2 = head_ok ? p.lse2[(int64_t)t * p.Hq + h] : INFINITY;
+    const float dl = head_ok ? p.delta[(int64_t)t * p.Hq + h] : 0.f;
+
+    f32x4 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero4();
+
+    const int nk = p.count * p.bs;
+    const int32_t* tk = p.topk + (int64_t)t * p.tk_st + (int64_t)h2 * p.tk_sn;
+    for (int c0 = 0; c0 < nk; c0 += BK) {
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            const int n = c0 + r;
+            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+            if (n < nk) {
+                const int slot = n / p.bs, rr = n % p.bs;
+                const int blk = tk[(int64_t)slot * p.tk_sk];
+                if (blk >= 0 && blk < nblk) {     // out-of-range choices are ignored
+                    const int64_t row = (int64_t)krow0 + (int64_t)blk * p.bs + rr;
+                    kv = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
+                    vv = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+                }
+            }
+            st16(&Ks[r * KP + cc], kv);
+            st16(&Vs[r * KP + cc], vv);
+        }
+        if (tid < BK) {
+            const int n = c0 + tid;
+            int kpos = 0x7fffffff;                  // masked: beyond the gathered keys
+            if (n < nk) {
+                const int blk = tk[(int64_t)(n / p.bs) * p.tk_sk];
+                if (blk >= 0 && blk < nblk) kpos = blk * p.bs + n % p.bs;
+            }
+            kpos_s[tid] = kpos;
+        }
+        __syncthreads();
+        f32x4 s[2], dp[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            s[x] = zero4();
+            dp[x] = zero4();
+            const int kr = 32 * w + 16 * x + col;       // A rows: keys
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                s[x] = T::mma16(ld16(&Ks[kr * KP + 32 * ks + 8 * G16]), qreg[ks], s[x]);
+                dp[x] = T::mma16(ld16(&Vs[kr * KP + 32 * ks + 8 * G16]), doreg[ks], dp[x]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kl = 32 * w + 16 * x + 4 * G16 + r;   // chunk-local key of this element
+                const int kpos = kpos_s[kl];
+                const bool masked = kpos == 0x7fffffff || (p.sparse_mode == 2 && kpos > t_local);
+                float pv = fast_exp2(__builtin_fmaf(s[x][r], p.scale_log2, -l2));
+                pv = masked ? 0.f : pv;
+                dp[x][r] = pv * (dp[x][r] - dl);
+            }
+        }
+        u32x4 bS;
+        bS[0] = T::pack_op(dp[0][0], dp[0][1]);
+        bS[1] = T::pack_op(dp[0][2], dp[0][3]);
+        bS[2] = T::pack_op(dp[1][0], dp[1][1]);
+        bS[3] = T::pack_op(dp[1][2], dp[1][3]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            dq[db] = T::mma16(ld_tr16x16_acc(Ks, KP, 32 * w, 16 * db, lane), bS, dq[db]);
+    }
+
+    // sum the four wavefronts' partials (through LDS, reusing Ks)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(Ks);
+    static_assert(sizeof(Ks) >= 3 * DB * 64 * 4 * 4, "reduction space");
+    if (w != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<f32x4*>(&red[((((w - 1) * DB) + db) * 64 + lane) * 4]) = dq[db];
+    }
+    __syncthreads();
+    if (w != 0 || !head_ok) return;
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&red[(((x * DB) + db) * 64 + lane) * 4]);
+            dq[db][0] += v[0]; dq[db][1] += v[1]; dq[db][2] += v[2]; dq[db][3] += v[3];
+        }
+    // dQ^T tile: lane holds head `col`, head dims 16*db + 4*G16 + r
+    uint16_t* dqp = p.dq.p + (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        u32x2 v;
+        v[0] = T::pack(dq[db][0] * p.scale, dq[db][1] * p.scale);
+        v[1] = T::pack(dq[db][2] * p.scale, dq[db][3] * p.scale);
+        st8(dqp + 16 * db + 4 * G16, v);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch
+// ---------------------------------------------------------------------------
+
+static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
+    const dim3 grid(p.NB, p.N2);
+    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<false>), grid, dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
+    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<true>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStream_t st) {
+    hipError_t e = launch_index(p, st);
+    if (e != hipSuccess) return e;
+    e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, D, false, st);
+    if (e != hipSuccess) return e;
+    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, D>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace sdpa
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kAlignN = 256;
+size_t up(size_t x) { return (x + kAlignN - 1) / kAlignN * kAlignN; }
+
+struct NsaLayout {
+    int64_t NB = 0, nbk = 0, E = 0, chunk = 1, max_pieces = 0, halves = 1;
+    size_t counts = 0, offsets = 0, entries = 0, pstart = 0, pieces = 0, lse2 = 0, delta = 0,
+           partial = 0, total = 0;
+};
+
+struct Seqs {
+    std::vector<int64_t> q0, k0, lq, lk;
+    int64_t Tq = 0, Tk = 0;
+};
+
+int read_seqs(int64_t batch, const int64_t* cuq, const int64_t* cuk, Seqs& S) {
+    int64_t pq = 0, pk = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (cuq[b] < pq || cuk[b] < pk) return SDPA_ERR_INVALID;
+        S.q0.push_back(pq); S.k0.push_back(pk);
+        S.lq.push_back(cuq[b] - pq); S.lk.push_back(cuk[b] - pk);
+        pq = cuq[b]; pk = cuk[b];
+    }
+    S.Tq = pq; S.Tk = pk;
+    return SDPA_OK;
+}
+
+// Validation shared by the size query, the backward and the index build
+// (Ascend page, "Constraints"): block_size <= 128 and a multiple of 16,
+// 1 <= block_count <= 128, count * size < 8192, every KV length a multiple of
+// block_size and >= count * size; sparse_mode 2 needs equal lengths.
+int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_t Hq, int64_t Hkv,
+                   int64_t D, int64_t bs, int64_t count, int sparse_mode, Seqs& S) {
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (Hq / Hkv > 32) return SDPA_ERR_INVALID;
+    if (bs < 16 || bs > 128 || bs % 16) return SDPA_ERR_INVALID;
+    if (count < 1 || count > 128 || count * bs >= 8192) return SDPA_ERR_INVALID;
+    if (sparse_mode != 0 && sparse_mode != 2) return SDPA_ERR_INVALID;
+    if (int s = read_seqs(batch, cuq, cuk, S)) return s;
+    for (size_t b = 0; b < S.lk.size(); ++b) {
+        if (S.lk[b] % bs) return SDPA_ERR_INVALID;
+        if (S.lk[b] < count * bs) return SDPA_ERR_INVALID;
+        if (sparse_mode == 2 && S.lq[b] != S.lk[b]) return SDPA_ERR_INVALID;
+    }
+    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (batch > sdpa::kMaxSeqArgs) return SDPA_ERR_UNSUPPORTED;
+    if (S.Tq * Hkv * count >= ((int64_t)1 << 31) || S.Tk >= ((int64_t)1 << 31)) return SDPA_ERR_UNSUPPORTED;
+    if (S.Tq > 2147483647 || Hkv * ((Hq / Hkv + 15) / 16) > 65535) return SDPA_ERR_UNSUPPORTED;
+    return SDPA_OK;
+}
+
+NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t bs, int64_t count) {
+    NsaLayout L;
+    L.NB = S.Tk / bs;
+    L.nbk = Hkv * L.NB;
+    L.E = S.Tq * Hkv * count;
+    const int64_t G = Hq / Hkv;
+    L.chunk = std::max<int64_t>(1, 2048 / G);
+    L.max_pieces = L.nbk + (L.E + L.chunk - 1) / L.chunk;
+    L.halves = (bs + 63) / 64;
+    size_t o = 0;
+    L.counts = o; o = up(o + L.nbk * 4);
+    L.offsets = o; o = up(o + (L.nbk + 1) * 4);
+    L.entries = o; o = up(o + std::max<int64_t>(L.E, 1) * 4);
+    L.pstart = o; o = up(o + (L.nbk + 1) * 4);
+    L.pieces = o; o = up(o + L.max_pieces * 3 * 4);
+    L.lse2 = o; o = up(o + S.Tq * Hq * 4);
+    L.delta = o; o = up(o + S.Tq * Hq * 4);
+    L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 2 * 64 * D * 4);
+    L.total = o;
+    return L;
+}
+
+void fill_seq_table(sdpa::SeqTable& t, const Seqs& S) {
+    t.n = (int)S.q0.size();
+    t.dev = nullptr;
+    for (int i = 0; i < t.n; ++i) {
+        t.q0[i] = (int32_t)S.q0[i]; t.k0[i] = (int32_t)S.k0[i];
+        t.lq[i] = (int32_t)S.lq[i]; t.lk[i] = (int32_t)S.lk[i];
+    }
+}
+
+thread_local std::string g_nsa_err;
+
+int hip_fail(hipError_t e, const char* where) {
+    g_nsa_err = std::string(where) + ": " + hipGetErrorString(e);
+    sdpa::set_last_error(g_nsa_err.c_str());
+    return SDPA_ERR_HIP;
+}
+
+int device_ok() {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (n <= 0) {
+        sdpa::set_last_error("no HIP device");
+        return SDPA_ERR_HIP;
+    }
+    return SDPA_OK;
+}
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int t3_ok(const sdpa_tensor3* t) {
+    if (t->stride_d != 1 || !a16(t->data) || (t->stride_t % 8) || (t->stride_n % 8)) return SDPA_ERR_UNSUPPORTED;
+    return SDPA_OK;
+}
+
+sdpa::TensorArg arg(const sdpa_tensor3* t) {
+    return sdpa::TensorArg{static_cast<uint16_t*>(t->data), 0, t->stride_n, t->stride_t};
+}
+
+}  // namespace
 
 extern "C" {
 
-int sdpa_bwd_selected_workspace_size(int, int64_t, const int64_t*, const int64_t*, int64_t, int64_t,
-                                     int64_t, int64_t, int64_t, int, size_t*) {
-    return SDPA_ERR_UNSUPPORTED;
+int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                                     const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
+                                     int64_t D, int64_t block_size, int64_t block_count,
+                                     int deterministic, size_t* bytes) {
+    (void)deterministic;
+    if (!bytes || !cu_seqlens_q_host || !cu_seqlens_kv_host) return SDPA_ERR_NULLPTR;
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    Seqs S;
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+                               block_count, 0, S))
+        return s;
+    *bytes = nsa_layout(S, Hq, Hkv, D, block_size, block_count).total;
+    return SDPA_OK;
 }
 
-int sdpa_bwd_selected(int, int64_t, const int64_t*, const int64_t*, int64_t, int64_t, int64_t, double,
-                      int, const int32_t*, int64_t, int64_t, int64_t, int64_t, int64_t, int,
-                      const sdpa_tensor3*, const sdpa_tensor3*, const sdpa_tensor3*, const sdpa_tensor3*,
-                      const sdpa_tensor3*, const sdpa_stats*, const sdpa_tensor3*, const sdpa_tensor3*,
-                      const sdpa_tensor3*, void*, size_t, void*) {
-    return SDPA_ERR_UNSUPPORTED;
+static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout& L, char* ws, const int32_t* topk,
+                              int64_t st, int64_t sn, int64_t sk, int64_t Hq, int64_t Hkv, int64_t bs, int64_t count) {
+    p.topk = topk; p.tk_st = st; p.tk_sn = sn; p.tk_sk = sk;
+    p.count = (int)count; p.bs = (int)bs; p.N2 = (int)Hkv; p.NB = (int)L.NB;
+    p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
+    p.chunk = (int)L.chunk; p.max_pieces = (int)L.max_pieces;
+    fill_seq_table(p.seqs, S);
+    p.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+    p.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    p.entries = reinterpret_cast<int32_t*>(ws + L.entries);
+    p.pstart = reinterpret_cast<int32_t*>(ws + L.pstart);
+    p.pieces = reinterpret_cast<int32_t*>(ws + L.pieces);
+    p.halves = (int)L.halves;
+    p.Tq = (int)S.Tq;
 }
 
-int sdpa_selected_build_index(int64_t, const int64_t*, const int64_t*, int64_t, const int32_t*, int64_t,
-                              int64_t, int64_t, int64_t, int64_t, int32_t*, int32_t*, void*, size_t, void*) {
-    return SDPA_ERR_UNSUPPORTED;
+int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
+                      int deterministic,
+                      const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
+                      const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
+                      const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    (void)deterministic;   // every kernel of this path is deterministic
+    if (!cu_seqlens_q_host || !cu_seqlens_kv_host || !topk) return SDPA_ERR_NULLPTR;
+    if (!q || !k || !v || !o || !dout || !stats || !dq || !dk || !dv) return SDPA_ERR_NULLPTR;
+    for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
+        if (!t->data) return SDPA_ERR_NULLPTR;
+    if (!stats->lse_or_max || (stats->kind == SDPA_STATS_MAX_SUM && !stats->sum)) return SDPA_ERR_NULLPTR;
+    if (!workspace) return SDPA_ERR_NULLPTR;
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    if (stats->kind != SDPA_STATS_LSE && stats->kind != SDPA_STATS_MAX_SUM) return SDPA_ERR_INVALID;
+    Seqs S;
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+                               block_count, sparse_mode, S))
+        return s;
+    for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
+        if (int s = t3_ok(t)) return s;
+    const NsaLayout L = nsa_layout(S, Hq, Hkv, D, block_size, block_count);
+    if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
+    if (int s = device_ok()) return s;
+    if (S.Tk == 0) return SDPA_OK;
+
+    char* ws = static_cast<char*>(workspace);
+    sdpa::NsaParams p{};
+    fill_index_params(p, S, L, ws, topk, tk_st, tk_sn, tk_sk, Hq, Hkv, block_size, block_count);
+    p.q = arg(q); p.k = arg(k); p.v = arg(v); p.dout = arg(dout);
+    p.dq = arg(dq); p.dk = arg(dk); p.dv = arg(dv);
+    p.lse2 = reinterpret_cast<float*>(ws + L.lse2);
+    p.delta = reinterpret_cast<float*>(ws + L.delta);
+    p.partial = reinterpret_cast<float*>(ws + L.partial);
+    p.sparse_mode = sparse_mode;
+    p.scale = (float)scale;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+
+    // row statistics in the packed layout (the dense preprocess kernel)
+    sdpa::BwdParams bp{};
+    bp.o = arg(o); bp.dout = arg(dout);
+    bp.stats_kind = stats->kind; bp.st_a = stats->lse_or_max; bp.st_b = stats->sum;
+    bp.st_sb = 0; bp.st_sh = stats->stride_h; bp.st_ss = stats->stride_s;
+    bp.lse2 = const_cast<float*>(p.lse2);
+    bp.delta = const_cast<float*>(p.delta);
+    bp.dqacc = nullptr;
+    bp.Hq = (int)Hq; bp.Hkv = (int)Hkv; bp.Sq = (int)S.Tq; bp.Sk = (int)S.Tk;
+    bp.rows = S.Tq * Hq;
+    bp.varlen = 1;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == SDPA_F16)
+        e = D == 64 ? sdpa::launch_nsa_t<sdpa::F16, 64>(p, bp, st) : sdpa::launch_nsa_t<sdpa::F16, 128>(p, bp, st);
+    else
+        e = D == 64 ? sdpa::launch_nsa_t<sdpa::BF16, 64>(p, bp, st) : sdpa::launch_nsa_t<sdpa::BF16, 128>(p, bp, st);
+    if (e != hipSuccess) return hip_fail(e, "selected launch");
+    return SDPA_OK;
 }
 
+int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
+                              const int64_t* cu_seqlens_kv_host, int64_t Hkv,
+                              const int32_t* topk, int64_t tk_st, int64_t tk_sn, int64_t tk_sk,
+                              int64_t block_size, int64_t block_count,
+                              int32_t* offsets_out, int32_t* entries_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!cu_seqlens_q_host || !cu_seqlens_kv_host || !topk || !offsets_out || !entries_out || !workspace)
+        return SDPA_ERR_NULLPTR;
+    Seqs S;
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hkv, Hkv, 128, block_size,
+                               block_count, 0, S))
+        return s;
+    const NsaLayout L = nsa_layout(S, Hkv, Hkv, 128, block_size, block_count);
+    if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
+    if (int s = device_ok()) return s;
+    if (L.nbk == 0) return SDPA_OK;
+    char* ws = static_cast<char*>(workspace);
+    sdpa::NsaParams p{};
+    fill_index_params(p, S, L, ws, topk, tk_st, tk_sn, tk_sk, Hkv, Hkv, block_size, block_count);
+    p.offsets = offsets_out;
+    p.entries = entries_out;
+    hipError_t e = sdpa::launch_index(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "index launch");
+    return SDPA_OK;
 }
+
+}  // extern "C"

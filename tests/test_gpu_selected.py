@@ -1,0 +1,120 @@
+"""GPU parity of the NSA selected-attention path against the fp64 oracle.
+
+* sdpa_selected_build_index: offsets and entries bit-exact against the
+  oracle's enumeration (integer work).
+* sdpa_bwd_selected: max|err|/max|ref| per tensor against the oracle's literal
+  gather (5e-3 fp16, 2e-2 bf16); the workload's statistics and O come from the
+  oracle forward, O rounded to the I/O type.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sdpa_backward_fa2_amd as sb
+import synth
+from gpu_util import assert_rel, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _topk_dev(topk):
+    return torch.from_numpy(np.ascontiguousarray(topk, dtype=np.int32)).cuda()
+
+
+def _check_index(topk, cu_q, cu_kv, bs):
+    off_ref, ent_ref = oracle.selected_block_lists(topk, cu_q, cu_kv, bs)
+    off, ent = sb.selected_build_index(_topk_dev(topk), cu_q, cu_kv, bs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(off.cpu().numpy().astype(np.int64), off_ref)
+    np.testing.assert_array_equal(ent.cpu().numpy().astype(np.int64), ent_ref)
+
+
+def test_index_config5_exact():
+    wl = synth.workload(5)
+    cu = wl.cu_seqlens()
+    _check_index(wl.topk(), cu, cu, wl.block_size)
+
+
+@pytest.mark.parametrize("lengths,N2,bs,count", [((64, 128, 48), 2, 16, 3), ((256, 512), 1, 64, 4),
+                                                  ((384,), 3, 128, 2)])
+def test_index_small_exact(lengths, N2, bs, count):
+    topk = synth.draw_topk(np.array(lengths), N2, bs, count, config_id=21)
+    # scatter some duplicates and a fully repeated row
+    topk[5 % topk.shape[0], 0, :] = topk[5 % topk.shape[0], 0, 0]
+    cu = np.cumsum(lengths)
+    _check_index(topk, cu, cu, bs)
+
+
+def _run_selected(q, k, v, o, do, stats, topk, cu, bs, scale, mode, det=False):
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    sb.bwd_selected(q, k, v, o, do, stats, _topk_dev(topk), cu, cu, bs, scale, mode,
+                    deterministic=det, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def test_config5_nsa_selected():
+    """T=4096, 16 query heads on 1 KV head, D=128 bf16, 16 blocks of 64 keys per
+    token (own block always included, padding with it when fewer exist),
+    causal within the selected keys; compared in full."""
+    wl = synth.workload(5)
+    cu = wl.cu_seqlens()
+    topk = wl.topk()
+    bits = {n: wl.packed_bits(tid, H) for n, tid, H in (("q", 0, wl.Hq), ("k", 1, wl.Hkv),
+                                                        ("v", 2, wl.Hkv), ("do", 3, wl.Hq))}
+    x = {n: synth.decode(b, wl.dtype) for n, b in bits.items()}
+    t = {n: to_device(b, wl.dtype) for n, b in bits.items()}
+    f = oracle.selected_forward(x["q"], x["k"], x["v"], topk, cu, cu, wl.block_size, wl.scale, 2)
+    g = oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], topk, cu, cu, wl.block_size, wl.scale, 2)
+    o = to_device(synth.encode(f["O"], wl.dtype), wl.dtype)
+    stats = (torch.tensor(f["m"], dtype=torch.float32, device="cuda"),
+             torch.tensor(f["l"], dtype=torch.float32, device="cuda"))
+    runs = []
+    for det in (False, True):
+        dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o, t["do"], stats, topk, cu, wl.block_size,
+                                   wl.scale, 2, det)
+        for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
+            assert_rel(to_f64(got), ref, wl.dtype, f"config5 {name} det={det}")
+        runs.append((dq, dk, dv))
+    # every kernel of this path is deterministic
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("lengths,G,N2,bs,count", [
+    ((256, 128), 2, 2, 64, 2),
+    ((96, 160, 80), 4, 1, 16, 5),
+    ((512,), 1, 1, 128, 3),
+    ((384, 192), 16, 1, 64, 3),
+])
+def test_selected_small(dtype, D, mode, lengths, G, N2, bs, count):
+    rng = np.random.default_rng(len(lengths) * 100 + G * 10 + bs + D + mode)
+    lengths = np.array(lengths)
+    cu = np.cumsum(lengths)
+    T = int(cu[-1])
+    topk = synth.draw_topk(lengths, N2, bs, count, config_id=31)
+    if mode == 0:    # without the causal mask any block of the sequence may be chosen
+        starts = np.concatenate([[0], cu[:-1]])
+        for s0, s1 in zip(starts, cu):
+            nb = (s1 - s0) // bs
+            topk[s0:s1] = rng.integers(0, nb, size=topk[s0:s1].shape)
+    Hq = G * N2
+    bits = {n: synth.encode(rng.standard_normal(shape), dtype)
+            for n, shape in (("q", (T, Hq, D)), ("k", (T, N2, D)), ("v", (T, N2, D)), ("do", (T, Hq, D)))}
+    x = {n: synth.decode(b, dtype) for n, b in bits.items()}
+    t = {n: to_device(b, dtype) for n, b in bits.items()}
+    scale = 1 / math.sqrt(D)
+    f = oracle.selected_forward(x["q"], x["k"], x["v"], topk, cu, cu, bs, scale, mode)
+    g = oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], topk, cu, cu, bs, scale, mode)
+    o = to_device(synth.encode(f["O"], dtype), dtype)
+    lse = torch.tensor(f["lse"], dtype=torch.float32, device="cuda")
+    dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o, t["do"], lse, topk, cu, bs, scale, mode)
+    for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
+        assert_rel(to_f64(got), ref, dtype, name)
