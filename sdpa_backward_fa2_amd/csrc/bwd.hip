@@ -45,6 +45,25 @@ __device__ __forceinline__ RowLoc row_of(const BwdParams& p, int64_t R) {
     return L;
 }
 
+// log2-domain LSE of one row straight from the caller's statistics: LSE*log2e,
+// or m*log2e + log2(l) for the max/sum form; +inf for a row without keys.
+__device__ __forceinline__ float stats_lse2(const BwdParams& p, int64_t so) {
+    if (p.stats_kind == 0) {
+        const float x = p.st_a[so];
+        return (x == -INFINITY) ? INFINITY : x * kLog2e;
+    }
+    const float mx = p.st_a[so], sm = p.st_b[so];
+    return (sm > 0.f) ? mx * kLog2e + log2f(sm) : INFINITY;
+}
+
+template <class T>
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc += T::to_f32(elem16(a, t)) * T::to_f32(elem16(b, t));
+    return acc;
+}
+
 // dQ accumulator row of statistics row R (head-major; see BwdParams)
 __device__ __forceinline__ int64_t acc_row(const BwdParams& p, const RowLoc& L, int64_t R) {
     return p.varlen ? L.h * p.Sq + L.i : R;
@@ -60,7 +79,7 @@ __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) {
-    constexpr int LPR = D / 8;   // lanes per row, 8 elements (16 bytes) each
+    constexpr int LPR = D / 16;  // lanes per row, 16 elements (two 16-byte chunks) each
     const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t R = gt / LPR;
     const int part = (int)(gt % LPR);
@@ -69,10 +88,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
     RowLoc L{0, 0, 0};
     if (ok) {
         L = row_of(p, R);
-        const u32x4 ov = ld16(p.o.p + toff(p.o, L) + part * 8);
-        const u32x4 dv = ld16(p.dout.p + toff(p.dout, L) + part * 8);
+        const uint16_t* op = p.o.p + toff(p.o, L) + part * 16;
+        const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * 16;
+        const u32x4 o0 = ld16(op), o1 = ld16(op + 8);
+        const u32x4 d0 = ld16(dp), d1 = ld16(dp + 8);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) acc += T::to_f32(elem16(ov, t)) * T::to_f32(elem16(dv, t));
+        for (int t = 0; t < 8; ++t) {
+            acc += T::to_f32(elem16(o0, t)) * T::to_f32(elem16(d0, t));
+            acc += T::to_f32(elem16(o1, t)) * T::to_f32(elem16(d1, t));
+        }
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -92,9 +116,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
     }
     if (zero_dq) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 8);
+        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 16);
         dst[0] = z;
         dst[1] = z;
+        dst[2] = z;
+        dst[3] = z;
     }
 }
 
@@ -129,8 +155,10 @@ __device__ __forceinline__ void softmax_grad_tile(f32x16& sa, f32x16& pa, const 
             const int rg = 4 * q + r;
             float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
             if (MASKED) {
+                // branch-free: keep = key valid and (not causal or key <= row)
                 const int i = i_base + 8 * q + 4 * g + r;
-                if (!col_ok || (CAUSAL && my_j > i)) pv = 0.f;
+                const bool keep = col_ok & (!CAUSAL | (my_j <= i));
+                pv = keep ? pv : 0.f;
             }
             sa[rg] = pv;
             pa[rg] = pv * (pa[rg] - Dr[r]);
@@ -369,8 +397,19 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 // dims 32*(w%2) .. +31 of the tile, with its K operand held in registers for
 // the whole kernel, so only dS^T is read from LDS per step.
 
+template <int D>
+struct Main8Lds {
+    static constexpr int BC = 128, BR = 64, QP = D + 8, SP = BR + 8, DB = D / 32;
+    static constexpr int TILE_B = BR * QP * 2;
+    static constexpr int OFF_ST = 4 * TILE_B;
+    static constexpr int OFF_STAT = OFF_ST + BC * (QP > SP ? QP : SP) * 2;
+    static constexpr int LOOP_B = OFF_STAT + 4 * BR * 4;
+    static constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;
+    static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
+};
+
 template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     constexpr int BC = 128;          // keys per workgroup
     constexpr int BR = 64;           // query rows per step
     constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
@@ -385,8 +424,7 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
     constexpr int OFF_STAT = OFF_ST + BC * (QP > SP ? QP : SP) * 2;
     constexpr int LOOP_B = OFF_STAT + 4 * BR * 4;
     constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of four wavefronts
-    constexpr int ARENA = LOOP_B > RED_B ? LOOP_B : RED_B;
-    __shared__ __align__(16) unsigned char arena[ARENA];
+    static_assert(Main8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
     uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena + OFF_Q);
     uint16_t* dOs0 = reinterpret_cast<uint16_t*>(arena + OFF_DO);
     uint16_t* dST = reinterpret_cast<uint16_t*>(arena + OFF_ST);
@@ -397,11 +435,11 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
     const int lane = tid & 63, w = tid >> 6;
     const int kw = w & 3, rh = w >> 2;
     const int g = lane >> 5, c = lane & 31;
-    const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
+    const int b = bx / p.Hkv, hk = bx % p.Hkv;
     const int G = p.Hq / p.Hkv;
     int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
     if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int j0 = blockIdx.y * BC;
+    const int j0 = by * BC;
     if (j0 >= lk) return;
     const bool full_cols = j0 + BC <= lk;
 
@@ -443,7 +481,7 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
     const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
     const int n_steps = G * per_head;
 
-    int qoff[CH], dooff[CH], crow[CH];
+    int qoff[CH], dooff[CH], ooff[CH], crow[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + 512 * x;
@@ -451,20 +489,26 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
         crow[x] = r;
         qoff[x] = r * (int)p.q.ss + cc;
         dooff[x] = r * (int)p.dout.ss + cc;
+        ooff[x] = r * (int)p.o.ss + cc;
     }
 
-    u32x4 pq[CH], pdo[CH];
-    float pl = INFINITY, pd = 0.f;
+    // Each step's 64 rows arrive as 16-byte chunks of Q, dO and O; the row's
+    // Delta = sum_d dO*O is reduced across the D/8 consecutive lanes holding
+    // it, and its LSE is read from the caller's statistics: no separate pass.
+    u32x4 pq[CH], pdo[CH], po[CH];
+    float pl = INFINITY;
     auto load_tile = [&](int st) {
         const int h = hk * G + st / per_head;
         const int i0 = i_begin + (st % per_head) * BR;
         const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
         const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
+        const uint16_t* ob = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + i0) * p.o.ss;
         if (i0 + BR <= lq) {
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
                 pq[x] = ld16(qb + qoff[x]);
                 pdo[x] = ld16(dob + dooff[x]);
+                po[x] = ld16(ob + ooff[x]);
             }
         } else {
 #pragma unroll
@@ -473,13 +517,12 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
                 const bool ok = i0 + crow[x] < lq;
                 pq[x] = ok ? ld16(qb + qoff[x]) : z;
                 pdo[x] = ok ? ld16(dob + dooff[x]) : z;
+                po[x] = ok ? ld16(ob + ooff[x]) : z;
             }
         }
         if (tid < BR) {
             const int i = i0 + tid;
-            const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
-            pl = i < lq ? p.lse2[ws] : INFINITY;
-            pd = i < lq ? p.delta[ws] : 0.f;
+            pl = i < lq ? stats_lse2(p, b * p.st_sb + h * p.st_sh + (int64_t)(q0 + i) * p.st_ss) : INFINITY;
         }
     };
     auto store_tile = [&](int buf) {
@@ -491,11 +534,12 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
             st16(&Qd[r * QP + cc], pq[x]);
             st16(&dOd[r * QP + cc], pdo[x]);
+            float dsum = dot8<T>(pdo[x], po[x]);
+#pragma unroll
+            for (int o = D / 16; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o);
+            if (cc == 0) dlt_s[buf * BR + r] = dsum;
         }
-        if (tid < BR) {
-            lse_s[buf * BR + tid] = pl;
-            dlt_s[buf * BR + tid] = pd;
-        }
+        if (tid < BR) lse_s[buf * BR + tid] = pl;
     };
 
     if (n_steps > 0) {
@@ -613,6 +657,12 @@ __global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
             st8(dkp + db * 32 + 8 * q + 4 * g, a);
             st8(dvp + db * 32 + 8 * q + 4 * g, v);
         }
+}
+
+template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
+__global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
+    __shared__ __align__(16) unsigned char arena[Main8Lds<D>::BYTES];
+    bwd_main8_body<T, D, CAUSAL, DQ_ATOMIC>(p, arena, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -755,8 +805,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
 // wavefront accumulates dQ^T over its key slices; the four slices are summed
 // through LDS at the end and dQ is written once, scaled and rounded.
 
+template <int D>
+struct Dq8Lds {
+    static constexpr int BK = 128, KP = D + 8, DB = D / 32;
+    static constexpr int TILE_B = BK * KP * 2;
+    static constexpr int LOOP_B = 4 * TILE_B;
+    static constexpr int RED_B = 3 * 2 * 64 * (DB * 16) * 4;
+    static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
+};
+
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
+__device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     constexpr int BQ = 64;           // query rows per workgroup
     constexpr int BK = 128;          // keys per step
     constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
@@ -767,8 +826,7 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
     constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
     constexpr int LOOP_B = 4 * TILE_B;
     constexpr int RED_B = 3 * 2 * 64 * (DB * 16) * 4;    // three key slices of both row halves
-    constexpr int ARENA = LOOP_B > RED_B ? LOOP_B : RED_B;
-    __shared__ __align__(16) unsigned char arena[ARENA];
+    static_assert(Dq8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
     uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
     uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
 
@@ -776,11 +834,11 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
     const int lane = tid & 63, w = tid >> 6;
     const int kw = w & 3, rh = w >> 2;
     const int g = lane >> 5, c = lane & 31;
-    const int b = blockIdx.y / p.Hq, h = blockIdx.y % p.Hq;
+    const int b = by / p.Hq, h = by % p.Hq;
     const int hk = h / (p.Hq / p.Hkv);
     int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
     if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int i0 = blockIdx.x * BQ;
+    const int i0 = bx * BQ;
     if (i0 >= lq) return;
 
     const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
@@ -797,9 +855,17 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
         qreg[s] = row_ok ? ld16(qbase + (int64_t)my_i * p.q.ss + 16 * s + 8 * g) : z;
         doreg[s] = row_ok ? ld16(dobase + (int64_t)my_i * p.dout.ss + 16 * s + 8 * g) : z;
     }
-    const int64_t ws = p.varlen ? ((int64_t)(q0 + my_i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + my_i);
-    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
-    const float dl = row_ok ? p.delta[ws] : 0.f;
+    // this row's LSE from the caller's statistics and Delta = sum_d dO*O: the two
+    // lane halves hold alternate 8-element chunks of the row
+    const float l2 = row_ok ? stats_lse2(p, b * p.st_sb + h * p.st_sh + (int64_t)(q0 + my_i) * p.st_ss) : INFINITY;
+    float dl = 0.f;
+    {
+        const uint16_t* orow = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + my_i) * p.o.ss;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            if (row_ok) dl += dot8<T>(doreg[s], ld16(orow + 16 * s + 8 * g));
+        dl += __shfl_xor(dl, 32);
+    }
 
     f32x16 dq[DB];
 #pragma unroll
@@ -877,7 +943,8 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
             for (int rg = 0; rg < 16; ++rg) {
                 const int j = j0 + 32 * kw + 8 * (rg >> 2) + 4 * g + (rg & 3);
                 float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
-                if (j >= lk || (CAUSAL && j > my_i)) pvv = 0.f;
+                const bool keep = (j < lk) & (!CAUSAL | (j <= my_i));
+                pvv = keep ? pvv : 0.f;
                 dp[rg] = pvv * (dp[rg] - dl);
             }
         } else {
@@ -933,6 +1000,40 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
         }
 }
 
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
+    __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
+    bwd_dq8_body<T, D, CAUSAL>(p, arena, blockIdx.x, blockIdx.y);
+}
+
+// dK/dV and dQ in one launch: the first n_main workgroups run the key-tile
+// outer kernel (key tiles in ascending order, so the longest causal ranges
+// start first), the rest the query-tile outer dQ kernel (query tiles in
+// descending order).  The dQ workgroups fill the CUs the long dK/dV
+// workgroups leave idle near the end.
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y) {
+    constexpr int A = Main8Lds<D>::BYTES > Dq8Lds<D>::BYTES ? Main8Lds<D>::BYTES : Dq8Lds<D>::BYTES;
+    __shared__ __align__(16) unsigned char arena[A];
+    const int id = blockIdx.x;
+    const int n_main = main_x * main_y;
+    if (id < n_main) {
+        bwd_main8_body<T, D, CAUSAL, false>(p, arena, id % main_x, id / main_x);
+    } else {
+        const int r = id - n_main;
+        bwd_dq8_body<T, D, CAUSAL>(p, arena, dq_x - 1 - r / dq_y, r % dq_y);
+    }
+}
+
+// fp32 zero fill (16 bytes per thread) of the dQ accumulator in atomic mode
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* dst, int64_t n4) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        reinterpret_cast<f32x4*>(dst)[i] = z;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
@@ -940,26 +1041,35 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     const int64_t row_threads = p.rows * (D / 8);
-    const dim3 row_grid((unsigned)((row_threads + 255) / 256));
+    const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
     const bool have_rows = p.rows > 0;
-    if ((L.phase & BwdLaunch::kFirst) && have_rows)
-        PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), row_grid, dim3(256), 0, st, p, L.deterministic ? 0 : 1);
+    constexpr bool W8 = D == 64;   // eight-wavefront kernels read the statistics and O themselves
+    if ((L.phase & BwdLaunch::kFirst) && have_rows) {
+        if constexpr (W8) {
+            if (!L.deterministic) {
+                const int64_t n4 = p.rows * D / 4;
+                PROF_LAUNCH(KID_BWD_PRE, st, fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                            p.dqacc, n4);
+            }
+        } else {
+            PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((p.rows * (D / 16) + 255) / 256)),
+                        dim3(256), 0, st, p, L.deterministic ? 0 : 1);
+        }
+    }
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
     const bool have_main = main_grid.x > 0 && main_grid.y > 0;
-    constexpr bool W8 = D == 64;
     const dim3 main_block(W8 ? 512 : 256);
     if (L.deterministic) {
         if constexpr (W8) {
-            if (have_main)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main8_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
-        } else if (have_main) {
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
-        }
-        if constexpr (W8) {
-            const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
-            if (dq_grid.x > 0 && dq_grid.y > 0)
-                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(512), 0, st, p);
+            const int mx = (int)main_grid.x, my = (int)main_grid.y;
+            const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
+            const int n = mx * my + qx * qy;
+            if (n > 0)
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p,
+                            mx, my, qx, qy);
         } else {
+            if (have_main)
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
             const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
             if (dq_grid.x > 0 && dq_grid.y > 0)
                 PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
@@ -984,7 +1094,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, const BwdLaunch& L, hipStream
 
 template <class T, int D>
 static hipError_t launch_pre_t(const BwdParams& p, bool zero_dq, hipStream_t st) {
-    const int64_t row_threads = p.rows * (D / 8);
+    const int64_t row_threads = p.rows * (D / 16);
     if (row_threads > 0)
         PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((row_threads + 255) / 256)), dim3(256),
                     0, st, p, zero_dq ? 1 : 0);

@@ -201,12 +201,18 @@ struct SeqTable {
     const int32_t* dev;   // when n > kMaxSeqArgs: device array of 4*n ints (q0, k0, lq, lk)
 };
 
+// The values are uniform across the workgroup; readfirstlane keeps them (and
+// everything derived from them, such as loop bounds) in scalar registers.
 __device__ __forceinline__ void seq_get(const SeqTable& t, int b, int& q0, int& k0, int& lq, int& lk) {
     if (t.dev) {
         q0 = t.dev[4 * b + 0]; k0 = t.dev[4 * b + 1]; lq = t.dev[4 * b + 2]; lk = t.dev[4 * b + 3];
     } else {
         q0 = t.q0[b]; k0 = t.k0[b]; lq = t.lq[b]; lk = t.lk[b];
     }
+    q0 = __builtin_amdgcn_readfirstlane(q0);
+    k0 = __builtin_amdgcn_readfirstlane(k0);
+    lq = __builtin_amdgcn_readfirstlane(lq);
+    lk = __builtin_amdgcn_readfirstlane(lk);
 }
 
 struct FwdParams {
