@@ -45,23 +45,23 @@ __device__ __forceinline__ RowLoc row_of(const BwdParams& p, int64_t R) {
     return L;
 }
 
-// log2-domain LSE of one row straight from the caller's statistics: LSE*log2e,
-// or m*log2e + log2(l) for the max/sum form; +inf for a row without keys.
+// log2-domain LSE of one row from the caller's statistics (a = LSE, or a = row
+// max and b = row sum): LSE*log2e, or m*log2e + log2(l); +inf for a row
+// without keys, so that its P is exactly zero.
+__device__ __forceinline__ float stats_to_lse2(int kind, float a, float b) {
+    if (kind == 0) return (a == -INFINITY) ? INFINITY : a * kLog2e;
+    return (b > 0.f) ? a * kLog2e + log2f(b) : INFINITY;
+}
 __device__ __forceinline__ float stats_lse2(const BwdParams& p, int64_t so) {
-    if (p.stats_kind == 0) {
-        const float x = p.st_a[so];
-        return (x == -INFINITY) ? INFINITY : x * kLog2e;
-    }
-    const float mx = p.st_a[so], sm = p.st_b[so];
-    return (sm > 0.f) ? mx * kLog2e + log2f(sm) : INFINITY;
+    return stats_to_lse2(p.stats_kind, p.st_a[so], p.stats_kind ? p.st_b[so] : 0.f);
 }
 
 template <class T>
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) acc += T::to_f32(elem16(a, t)) * T::to_f32(elem16(b, t));
-    return acc;
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc = 0.f) {
+    acc = T::dot2(a[0], b[0], acc);
+    acc = T::dot2(a[1], b[1], acc);
+    acc = T::dot2(a[2], b[2], acc);
+    return T::dot2(a[3], b[3], acc);
 }
 
 // dQ accumulator row of statistics row R (head-major; see BwdParams)
@@ -162,6 +162,26 @@ __device__ __forceinline__ void softmax_grad_tile(f32x16& sa, f32x16& pa, const 
             }
             sa[rg] = pv;
             pa[rg] = pv * (pa[rg] - Dr[r]);
+        }
+    }
+}
+
+// The same for a tile whose dP accumulator started from -Delta (pa already
+// holds dP - Delta).  Element (q, r) is kept when 8q + r >= t, with t the first
+// kept row offset of this lane's key (INT_MAX for a key past the end).
+template <bool MASKED>
+__device__ __forceinline__ void softmax_grad_tile_nd(f32x16& sa, f32x16& pa, const float* lse_row,
+                                                     float scale_log2, int g, int t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rg = 4 * q + r;
+            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
+            if (MASKED) pv = (8 * q + r >= t) ? pv : 0.f;
+            sa[rg] = pv;
+            pa[rg] = pv * pa[rg];
         }
     }
 }
@@ -383,53 +403,48 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel, eight wavefronts (two per SIMD)
+// dK/dV body, eight wavefronts (two per SIMD), software-pipelined
 // ---------------------------------------------------------------------------
 //
-// Same work item as bwd_main_kernel (128 keys of one KV head, every query tile
-// of every query head of its group) with eight wavefronts: wavefront
-// w = kw + 4*rh owns keys 32*kw .. 32*kw+31 and rows 32*rh .. 32*rh+31 of each
-// 64-row query tile.  Each SIMD thus runs two wavefronts, so the matrix core
-// and the vector ALU of a SIMD overlap, and every wavefront carries half the
-// softmax work.  dK/dV accumulate per wavefront over its row half; the two
-// halves are summed through LDS once, at the end.  dQ_tile = dS K uses
-// v_mfma_f32_16x16x32: wavefront w owns query rows 16*(w/2) .. +15 and head
-// dims 32*(w%2) .. +31 of the tile, with its K operand held in registers for
-// the whole kernel, so only dS^T is read from LDS per step.
+// Work item: 128 keys of one KV head against every 64-row query tile of every
+// query head of its group (causal: from the tile holding the diagonal on).
+// Wavefront w = kw + 4*rh owns keys 32*kw .. +31 and rows 32*rh .. +31 of each
+// tile; K and V of its keys stay in registers and dK^T, dV^T accumulate in
+// registers across all tiles.  Step k runs the softmax gradient of tile k
+// (vector ALU) next to S^T and dP^T of tile k+1 (matrix cores, independent of
+// it), then dV^T += P^T dO and dK^T += dS^T Q of tile k; P^T and dS^T feed the
+// B operand straight from the accumulator layout.  Q/dO tiles rotate through
+// three LDS buffers: tile k (read by dV/dK), k+1 (read by S/dP), and k+2, which
+// is loaded into registers at the start of the step and stored at its end with
+// its rows' negated Delta = -sum_d dO*O and log2-domain LSE.  The two row
+// halves' dK/dV partials are summed through LDS at the end.  dQ is left to
+// the query-outer body.
 
 template <int D>
 struct Main8Lds {
-    static constexpr int BC = 128, BR = 64, QP = D + 8, SP = BR + 8, DB = D / 32;
-    static constexpr int TILE_B = BR * QP * 2;
-    static constexpr int OFF_ST = 4 * TILE_B;
-    static constexpr int OFF_STAT = OFF_ST + BC * (QP > SP ? QP : SP) * 2;
-    static constexpr int LOOP_B = OFF_STAT + 4 * BR * 4;
-    static constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;
+    static constexpr int BR = 64, QP = D + 8, DB = D / 32, NBUF = 3;
+    static constexpr int TILE_B = BR * QP * 2;            // one Q or dO tile
+    static constexpr int OFF_STAT = 2 * NBUF * TILE_B;    // lse [NBUF][BR], -Delta [NBUF][BR]
+    static constexpr int LOOP_B = OFF_STAT + 2 * NBUF * BR * 4;
+    static constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of four wavefronts
     static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
 };
 
-template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
+template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    using L = Main8Lds<D>;
     constexpr int BC = 128;          // keys per workgroup
-    constexpr int BR = 64;           // query rows per step
+    constexpr int BR = L::BR;        // query rows per step
     constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
-    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int QP = D + 8;        // row stride of Qs, dOs, Ks  [row][d]
-    constexpr int SP = BR + 8;       // row stride of dST          [j][i]
+    constexpr int DB = L::DB;        // 32-row blocks of dK^T / dV^T
+    constexpr int QP = L::QP;        // row stride of the Q and dO tiles  [row][d]
+    constexpr int TILE = BR * QP;    // elements of one tile
     constexpr int CH = BR * D / 8 / 512;     // 16-byte chunks per thread per tile
-    constexpr int NQB = D / 32;      // 16-wide head-dim blocks of dQ per wavefront (2 for D=64)
     static_assert(CH >= 1, "tile shape");
-    constexpr int TILE_B = BR * QP * 2;                  // bytes of one Q (or dO) tile
-    constexpr int OFF_Q = 0, OFF_DO = 2 * TILE_B, OFF_ST = 4 * TILE_B;
-    constexpr int OFF_STAT = OFF_ST + BC * (QP > SP ? QP : SP) * 2;
-    constexpr int LOOP_B = OFF_STAT + 4 * BR * 4;
-    constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of four wavefronts
-    static_assert(Main8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
-    uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena + OFF_Q);
-    uint16_t* dOs0 = reinterpret_cast<uint16_t*>(arena + OFF_DO);
-    uint16_t* dST = reinterpret_cast<uint16_t*>(arena + OFF_ST);
-    float* lse_s = reinterpret_cast<float*>(arena + OFF_STAT);          // [2][BR]
-    float* dlt_s = lse_s + 2 * BR;                                        // [2][BR]
+    uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena);
+    uint16_t* dOs0 = Qs0 + L::NBUF * TILE;
+    float* lse_s = reinterpret_cast<float*>(arena + L::OFF_STAT);
+    float* dlt_s = lse_s + L::NBUF * BR;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -448,30 +463,6 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
 
     const int my_j = j0 + 32 * kw + c;
     const bool col_ok = my_j < lk;
-    u32x4 kreg[KS], vreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
-        vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
-    }
-    // K operand of the dQ product (k = key, column = head dim), via a row-major
-    // staging copy of the key tile in the dS^T area
-    u32x4 kop[BC / 32][NQB];
-    if (DQ_ATOMIC) {
-        uint16_t* Ks = dST;
-        if (rh == 0) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) st16(&Ks[(32 * kw + c) * QP + 16 * s + 8 * g], kreg[s]);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int ks = 0; ks < BC / 32; ++ks)
-#pragma unroll
-            for (int nb = 0; nb < NQB; ++nb)
-                kop[ks][nb] = ld_tr16x16(Ks, QP, 32 * ks, (w & 1) * (16 * NQB) + 16 * nb, lane);
-        __syncthreads();
-    }
 
     f32x16 dva[DB], dka[DB];
 #pragma unroll
@@ -481,142 +472,177 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
     const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
     const int n_steps = G * per_head;
 
-    int qoff[CH], dooff[CH], ooff[CH], crow[CH];
+    int qoff[CH], dooff[CH], ooff[CH], crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + 512 * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
+        ccol[x] = cc;
         qoff[x] = r * (int)p.q.ss + cc;
         dooff[x] = r * (int)p.dout.ss + cc;
         ooff[x] = r * (int)p.o.ss + cc;
     }
 
-    // Each step's 64 rows arrive as 16-byte chunks of Q, dO and O; the row's
-    // Delta = sum_d dO*O is reduced across the D/8 consecutive lanes holding
-    // it, and its LSE is read from the caller's statistics: no separate pass.
-    u32x4 pq[CH], pdo[CH], po[CH];
-    float pl = INFINITY;
-    auto load_tile = [&](int st) {
-        const int h = hk * G + st / per_head;
-        const int i0 = i_begin + (st % per_head) * BR;
-        const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
-        const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
-        const uint16_t* ob = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + i0) * p.o.ss;
-        if (i0 + BR <= lq) {
-#pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                pq[x] = ld16(qb + qoff[x]);
-                pdo[x] = ld16(dob + dooff[x]);
-                po[x] = ld16(ob + ooff[x]);
-            }
+    // Pointers of the tile being loaded (head ld_h, rows from ld_i0), advanced
+    // by one tile per step in scalar registers.
+    const uint16_t* const q_seq = p.q.p + b * p.q.sb + (int64_t)q0 * p.q.ss;
+    const uint16_t* const do_seq = p.dout.p + b * p.dout.sb + (int64_t)q0 * p.dout.ss;
+    const uint16_t* const o_seq = p.o.p + b * p.o.sb + (int64_t)q0 * p.o.ss;
+    const float* const sa_seq = p.st_a + b * p.st_sb + (int64_t)q0 * p.st_ss;
+    const float* const sb_seq = (p.stats_kind ? p.st_b : p.st_a) + b * p.st_sb + (int64_t)q0 * p.st_ss;
+    const int64_t q_step = BR * p.q.ss, do_step = BR * p.dout.ss, o_step = BR * p.o.ss, st_step = BR * p.st_ss;
+    int ld_h = hk * G, ld_i0 = i_begin;
+    const uint16_t *ld_q, *ld_do, *ld_o;
+    const float *ld_sa, *ld_sb;
+    auto seek = [&]() {
+        ld_q = q_seq + ld_h * p.q.sh + (int64_t)ld_i0 * p.q.ss;
+        ld_do = do_seq + ld_h * p.dout.sh + (int64_t)ld_i0 * p.dout.ss;
+        ld_o = o_seq + ld_h * p.o.sh + (int64_t)ld_i0 * p.o.ss;
+        ld_sa = sa_seq + ld_h * p.st_sh + (int64_t)ld_i0 * p.st_ss;
+        ld_sb = sb_seq + ld_h * p.st_sh + (int64_t)ld_i0 * p.st_ss;
+    };
+    // the query rows of one head from i_begin to the end of the sequence, then
+    // the next head of the group
+    auto advance = [&]() {
+        ld_i0 += BR;
+        if (ld_i0 >= lq) {
+            ld_i0 = i_begin;
+            ++ld_h;
+            seek();
         } else {
-#pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                const bool ok = i0 + crow[x] < lq;
-                pq[x] = ok ? ld16(qb + qoff[x]) : z;
-                pdo[x] = ok ? ld16(dob + dooff[x]) : z;
-                po[x] = ok ? ld16(ob + ooff[x]) : z;
-            }
-        }
-        if (tid < BR) {
-            const int i = i0 + tid;
-            pl = i < lq ? stats_lse2(p, b * p.st_sb + h * p.st_sh + (int64_t)(q0 + i) * p.st_ss) : INFINITY;
+            ld_q += q_step; ld_do += do_step; ld_o += o_step; ld_sa += st_step; ld_sb += st_step;
         }
     };
-    auto store_tile = [&](int buf) {
-        uint16_t* Qd = Qs0 + buf * (BR * QP);
-        uint16_t* dOd = dOs0 + buf * (BR * QP);
+    seek();
+
+    // Tile loads are unconditional: rows past the end of the sequence re-read
+    // its last row and get LSE = +inf when stored, so their P is exactly zero.
+    // Nothing loaded is used before the tile is stored.
+    struct TileRegs { u32x4 q[CH], d[CH], o[CH]; float sa, sb; };
+    const int srow = tid & (BR - 1);
+    const int srow_off = srow * (int)p.st_ss;
+    auto load_tile = [&](TileRegs& t) {
+        int oq[CH], odo[CH], oo[CH], so = srow_off;
+        if (ld_i0 + BR <= lq) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; oo[x] = ooff[x]; }
+        } else {
+            const int last = lq - 1 - ld_i0;
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                const int r = min(crow[x], last);
+                oq[x] = r * (int)p.q.ss + ccol[x];
+                odo[x] = r * (int)p.dout.ss + ccol[x];
+                oo[x] = r * (int)p.o.ss + ccol[x];
+            }
+            so = min(srow, last) * (int)p.st_ss;
+        }
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            const int e = tid + 512 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Qd[r * QP + cc], pq[x]);
-            st16(&dOd[r * QP + cc], pdo[x]);
-            float dsum = dot8<T>(pdo[x], po[x]);
-#pragma unroll
-            for (int o = D / 16; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o);
-            if (cc == 0) dlt_s[buf * BR + r] = dsum;
+            t.q[x] = ld16(ld_q + oq[x]);
+            t.d[x] = ld16(ld_do + odo[x]);
+            t.o[x] = ld16(ld_o + oo[x]);
         }
-        if (tid < BR) lse_s[buf * BR + tid] = pl;
+        t.sa = ld_sa[so];
+        t.sb = ld_sb[so];
     };
-
-    if (n_steps > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int st = 0; st < n_steps; ++st) {
-        const int buf = st & 1;
-        const int h = hk * G + st / per_head;
-        const int i0 = i_begin + (st % per_head) * BR;
-        const bool has_next = st + 1 < n_steps;
-        if (has_next) load_tile(st + 1);
-
-        const uint16_t* Qb = Qs0 + buf * (BR * QP);
-        const uint16_t* dOb = dOs0 + buf * (BR * QP);
-        const bool masked = (CAUSAL && i0 < j0 + BC) || !full_cols;
-        f32x16 sa = zero16(), pa = zero16();
+    auto store_tile = [&](const TileRegs& t, int buf, int i0) {
+        uint16_t* Qd = Qs0 + buf * TILE;
+        uint16_t* dOd = dOs0 + buf * TILE;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            st16(&Qd[crow[x] * QP + ccol[x]], t.q[x]);
+            st16(&dOd[crow[x] * QP + ccol[x]], t.d[x]);
+            const float dsum = lane_group_sum<D / 8>(dot8<T>(t.d[x], t.o[x]));
+            if (ccol[x] == 0) dlt_s[buf * BR + crow[x]] = -dsum;
+        }
+        if (tid < BR)
+            lse_s[buf * BR + tid] = (i0 + tid < lq) ? stats_to_lse2(p.stats_kind, t.sa, t.sb) : INFINITY;
+    };
+    u32x4 kreg[KS], vreg[KS];            // this wavefront's keys, loaded in the prologue
+    // S^T and dP^T - Delta of the tile in buffer buf; dP^T accumulates onto
+    // the rows' -Delta
+    auto s_dp = [&](int buf, f32x16& sa, f32x16& pa) {
+        const uint16_t* Qb = Qs0 + buf * TILE;
+        const uint16_t* dOb = dOs0 + buf * TILE;
+        sa = zero16();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf * BR + 32 * rh + 8 * q + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             sa = T::mma(ld16(&Qb[(32 * rh + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
             pa = T::mma(ld16(&dOb[(32 * rh + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
         }
-        if (masked)
-            softmax_grad_tile<true, CAUSAL>(sa, pa, &lse_s[buf * BR + 32 * rh], &dlt_s[buf * BR + 32 * rh],
-                                            p.scale_log2, g, i0 + 32 * rh, my_j, col_ok);
-        else
-            softmax_grad_tile<false, CAUSAL>(sa, pa, &lse_s[buf * BR + 32 * rh], &dlt_s[buf * BR + 32 * rh],
-                                             p.scale_log2, g, i0 + 32 * rh, my_j, col_ok);
-        if (has_next) store_tile(buf ^ 1);
+    };
+
+    // Prologue: the first two tiles and this wavefront's K and V rows are all
+    // requested before anything waits for memory.
+    int i0_k = i_begin, i0_k1 = i_begin;   // first rows of tiles k and k+1
+    TileRegs tr0, tr1;
+    if (n_steps > 0) { load_tile(tr0); i0_k = ld_i0; advance(); }
+    if (n_steps > 1) { load_tile(tr1); i0_k1 = ld_i0; advance(); }
+    {
+        const int jr = min(my_j, lk - 1);   // keys past the end are masked and not stored
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 bP = acc_to_operand<T>(sa, hh);
-            const u32x4 bS = acc_to_operand<T>(pa, hh);
+        for (int s = 0; s < KS; ++s) {
+            kreg[s] = ld16(kbase + (int64_t)jr * p.k.ss + 16 * s + 8 * g);
+            vreg[s] = ld16(vbase + (int64_t)jr * p.v.ss + 16 * s + 8 * g);
+        }
+    }
+    if (n_steps > 0) store_tile(tr0, 0, i0_k);
+    if (n_steps > 1) store_tile(tr1, 1, i0_k1);
+    wait_all_memory();
+    __syncthreads();
+
+    // this lane's first kept row offset within its 32-row half, before the
+    // 8q+4g part: key my_j needs row >= my_j; a key past the end keeps nothing
+    const int t_key = col_ok ? (CAUSAL ? my_j - 32 * rh - 4 * g : INT_MIN / 2) : INT_MAX / 2;
+
+    f32x16 sa, pa;
+    if (n_steps > 0) s_dp(0, sa, pa);
+    int bk = 0, bk1 = 1, bk2 = 2;          // buffers of tiles k, k+1, k+2
+    for (int k = 0; k < n_steps; ++k) {
+        const bool has2 = k + 2 < n_steps;
+        int i0_k2 = i0_k1;
+        TileRegs trn;
+        if (has2) { load_tile(trn); i0_k2 = ld_i0; advance(); }
+
+        // softmax gradient of tile k next to S^T/dP^T of tile k+1 (on the last
+        // step the latter reads a stale buffer and is discarded)
+        const bool masked = (CAUSAL && i0_k < j0 + BC) || !full_cols;
+        u32x4 bP[2], bS[2];
+        if (masked) {
+            softmax_grad_tile_nd<true>(sa, pa, &lse_s[bk * BR + 32 * rh], p.scale_log2, g, t_key - i0_k);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP, dva[db]);
-                dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS, dka[db]);
-            }
-            if (DQ_ATOMIC) {
-                u32x2 lo, hi;
-                lo[0] = bS[0]; lo[1] = bS[1]; hi[0] = bS[2]; hi[1] = bS[3];
-                st8(&dST[(32 * kw + c) * SP + 32 * rh + 16 * hh + 4 * g], lo);
-                st8(&dST[(32 * kw + c) * SP + 32 * rh + 16 * hh + 8 + 4 * g], hi);
-            }
+            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
+            s_dp(bk1, sa, pa);
+        } else {
+            softmax_grad_tile_nd<false>(sa, pa, &lse_s[bk * BR + 32 * rh], p.scale_log2, g, 0);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
+            s_dp(bk1, sa, pa);
         }
 
-        if (DQ_ATOMIC) {
-            __syncthreads();
-            const int ib = w >> 1;                 // query rows 16*ib .. +15 of the tile
-            f32x4 acc[NQB];
+        // dV^T += P^T dO, dK^T += dS^T Q of tile k
+        const uint16_t* Qb = Qs0 + bk * TILE;
+        const uint16_t* dOb = dOs0 + bk * TILE;
 #pragma unroll
-            for (int nb = 0; nb < NQB; ++nb) acc[nb] = zero4();
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int ks = 0; ks < BC / 32; ++ks) {
-                const u32x4 a = ld_tr16x16(dST, SP, 32 * ks, 16 * ib, lane);
-#pragma unroll
-                for (int nb = 0; nb < NQB; ++nb) acc[nb] = T::mma16(a, kop[ks][nb], acc[nb]);
+            for (int db = 0; db < DB; ++db) {
+                dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP[hh], dva[db]);
+                dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS[hh], dka[db]);
             }
-            const int64_t arow0 = p.varlen ? ((int64_t)h * p.Sq + q0) : (((int64_t)b * p.Hq + h) * p.Sq);
-            const int G16 = lane >> 4, col = lane & 15;
-            float* base = p.dqacc + (arow0 + i0 + 16 * ib + 4 * G16) * D + (w & 1) * (16 * NQB) + col;
-            if (i0 + BR <= lq) {
-#pragma unroll
-                for (int nb = 0; nb < NQB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) atomicAdd(base + r * D + 16 * nb, acc[nb][r]);
-            } else {
-#pragma unroll
-                for (int nb = 0; nb < NQB; ++nb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (i0 + 16 * ib + 4 * G16 + r < lq) atomicAdd(base + r * D + 16 * nb, acc[nb][r]);
-            }
-        }
+        if (has2) store_tile(trn, bk2, i0_k2);
         __syncthreads();
+        const int t = bk; bk = bk1; bk1 = bk2; bk2 = t;
+        i0_k = i0_k1;
+        i0_k1 = i0_k2;
     }
 
     // sum the two row halves' dK/dV partials through LDS, then store
@@ -657,12 +683,6 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
             st8(dkp + db * 32 + 8 * q + 4 * g, a);
             st8(dvp + db * 32 + 8 * q + 4 * g, v);
         }
-}
-
-template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(512) void bwd_main8_kernel(BwdParams p) {
-    __shared__ __align__(16) unsigned char arena[Main8Lds<D>::BYTES];
-    bwd_main8_body<T, D, CAUSAL, DQ_ATOMIC>(p, arena, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -846,81 +866,98 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
     const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
 
-    const int my_i = i0 + 32 * rh + c;
-    const bool row_ok = my_i < lq;
-    u32x4 qreg[KS], doreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qreg[s] = row_ok ? ld16(qbase + (int64_t)my_i * p.q.ss + 16 * s + 8 * g) : z;
-        doreg[s] = row_ok ? ld16(dobase + (int64_t)my_i * p.dout.ss + 16 * s + 8 * g) : z;
-    }
-    // this row's LSE from the caller's statistics and Delta = sum_d dO*O: the two
-    // lane halves hold alternate 8-element chunks of the row
-    const float l2 = row_ok ? stats_lse2(p, b * p.st_sb + h * p.st_sh + (int64_t)(q0 + my_i) * p.st_ss) : INFINITY;
-    float dl = 0.f;
-    {
-        const uint16_t* orow = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + my_i) * p.o.ss;
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            if (row_ok) dl += dot8<T>(doreg[s], ld16(orow + 16 * s + 8 * g));
-        dl += __shfl_xor(dl, 32);
-    }
-
-    f32x16 dq[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dq[db] = zero16();
-
     const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
     const int n_steps = (kend + BK - 1) / BK;
 
-    int koff[CH], voff[CH], crow[CH];
+    int koff[CH], voff[CH], crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + 512 * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
+        ccol[x] = cc;
         koff[x] = r * (int)p.k.ss + cc;
         voff[x] = r * (int)p.v.ss + cc;
     }
+    // Unconditional loads: keys past the end of the sequence re-read its last
+    // key and are masked out (P = 0), so nothing is waited for before the tile
+    // is stored after the step's products.
     u32x4 pk[CH], pv[CH];
+    const uint16_t* kb = kbase;          // key tile being loaded, advanced per step
+    const uint16_t* vb = vbase;
+    const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
     auto load_tile = [&](int st) {
         const int j0 = st * BK;
-        const uint16_t* kb = kbase + (int64_t)j0 * p.k.ss;
-        const uint16_t* vb = vbase + (int64_t)j0 * p.v.ss;
+        int ok_[CH], ov_[CH];
         if (j0 + BK <= lk) {
 #pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                pk[x] = ld16(kb + koff[x]);
-                pv[x] = ld16(vb + voff[x]);
-            }
+            for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
         } else {
+            const int last = lk - 1 - j0;
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                const bool ok = j0 + crow[x] < lk;
-                pk[x] = ok ? ld16(kb + koff[x]) : z;
-                pv[x] = ok ? ld16(vb + voff[x]) : z;
+                const int r = min(crow[x], last);
+                ok_[x] = r * (int)p.k.ss + ccol[x];
+                ov_[x] = r * (int)p.v.ss + ccol[x];
             }
         }
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            pk[x] = ld16(kb + ok_[x]);
+            pv[x] = ld16(vb + ov_[x]);
+        }
+        kb += k_step;
+        vb += v_step;
     };
     auto store_tile = [&](int buf) {
         uint16_t* Kd = Ks0 + buf * (BK * KP);
         uint16_t* Vd = Vs0 + buf * (BK * KP);
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            const int e = tid + 512 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Kd[r * KP + cc], pk[x]);
-            st16(&Vd[r * KP + cc], pv[x]);
+            st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
+            st16(&Vd[crow[x] * KP + ccol[x]], pv[x]);
         }
     };
 
-    if (n_steps > 0) {
-        load_tile(0);
-        store_tile(0);
+    // Prologue: the first key tile and this lane's query row are requested
+    // before anything waits for memory.
+    if (n_steps > 0) load_tile(0);
+    const int my_i = i0 + 32 * rh + c;
+    const bool row_ok = my_i < lq;
+    // a row past the end of the sequence re-reads its last row; its LSE is
+    // +inf (P = 0) and its dQ is not stored
+    const int my_ic = min(my_i, lq - 1);
+    u32x4 qreg[KS], doreg[KS], oreg[KS];
+    const uint16_t* orow = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + my_ic) * p.o.ss;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
+        doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
+        oreg[s] = ld16(orow + 16 * s + 8 * g);
     }
+    const int64_t so = b * p.st_sb + h * p.st_sh + (int64_t)(q0 + my_ic) * p.st_ss;
+    const float sa_raw = p.st_a[so];
+    const float sb_raw = (p.stats_kind ? p.st_b : p.st_a)[so];
+    // this row's LSE and Delta = sum_d dO*O; the two lane halves hold
+    // alternate 8-element chunks of the row
+    const float l2 = row_ok ? stats_to_lse2(p.stats_kind, sa_raw, sb_raw) : INFINITY;
+    float dl = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) dl = dot8<T>(doreg[s], oreg[s], dl);
+    dl += __shfl_xor(dl, 32);
+
+    f32x16 dq[DB], ndl16;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
+
+    if (n_steps > 0) store_tile(0);
+    wait_all_memory();
     __syncthreads();
+
+    // last key this lane's row keeps, relative to the 8q+4g part of a tile row
+    const int t_row = min(lk - 1, CAUSAL ? my_i : INT_MAX) - 32 * kw - 4 * g;
 
     for (int st = 0; st < n_steps; ++st) {
         const int buf = st & 1;
@@ -930,7 +967,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         const uint16_t* Kb = Ks0 + buf * (BK * KP);
         const uint16_t* Vb = Vs0 + buf * (BK * KP);
 
-        f32x16 s = zero16(), dp = zero16();
+        f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
@@ -939,19 +976,18 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
         const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);
         if (masked) {
+            const int t = t_row - j0;
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) {
-                const int j = j0 + 32 * kw + 8 * (rg >> 2) + 4 * g + (rg & 3);
                 float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
-                const bool keep = (j < lk) & (!CAUSAL | (j <= my_i));
-                pvv = keep ? pvv : 0.f;
-                dp[rg] = pvv * (dp[rg] - dl);
+                pvv = (8 * (rg >> 2) + (rg & 3) <= t) ? pvv : 0.f;
+                dp[rg] = pvv * dp[rg];
             }
         } else {
 #pragma unroll
             for (int rg = 0; rg < 16; ++rg) {
                 const float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
-                dp[rg] = pvv * (dp[rg] - dl);
+                dp[rg] = pvv * dp[rg];
             }
         }
         if (has_next) store_tile(buf ^ 1);
@@ -1000,12 +1036,6 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         }
 }
 
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
-    __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
-    bwd_dq8_body<T, D, CAUSAL>(p, arena, blockIdx.x, blockIdx.y);
-}
-
 // dK/dV and dQ in one launch: the first n_main workgroups run the key-tile
 // outer kernel (key tiles in ascending order, so the longest causal ranges
 // start first), the rest the query-tile outer dQ kernel (query tiles in
@@ -1018,19 +1048,10 @@ __global__ __launch_bounds__(512) void bwd_fused8_kernel(BwdParams p, int main_x
     const int id = blockIdx.x;
     const int n_main = main_x * main_y;
     if (id < n_main) {
-        bwd_main8_body<T, D, CAUSAL, false>(p, arena, id % main_x, id / main_x);
+        bwd_main8_body<T, D, CAUSAL>(p, arena, id % main_x, id / main_x);
     } else {
         const int r = id - n_main;
         bwd_dq8_body<T, D, CAUSAL>(p, arena, dq_x - 1 - r / dq_y, r % dq_y);
-    }
-}
-
-// fp32 zero fill (16 bytes per thread) of the dQ accumulator in atomic mode
-__global__ __launch_bounds__(256) void fill_zero_kernel(float* dst, int64_t n4) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < n4) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        reinterpret_cast<f32x4*>(dst)[i] = z;
     }
 }
 
@@ -1040,51 +1061,40 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* dst, int64_t n4) 
 
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    const int64_t row_threads = p.rows * (D / 8);
-    const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
-    const bool have_rows = p.rows > 0;
-    constexpr bool W8 = D == 64;   // eight-wavefront kernels read the statistics and O themselves
-    if ((L.phase & BwdLaunch::kFirst) && have_rows) {
-        if constexpr (W8) {
-            if (!L.deterministic) {
-                const int64_t n4 = p.rows * D / 4;
-                PROF_LAUNCH(KID_BWD_PRE, st, fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                            p.dqacc, n4);
-            }
-        } else {
+    if constexpr (D == 64) {
+        // One launch, no workspace traffic: the kernel reads the statistics
+        // and O itself and computes dQ without atomics, so it is deterministic
+        // whatever the caller asked for.
+        const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles;
+        const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
+        const int n = mx * my + qx * qy;
+        if (n > 0)
+            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p, mx, my, qx,
+                        qy);
+        return hipGetLastError();
+    } else {
+        const int64_t row_threads = p.rows * (D / 8);
+        const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
+        const bool have_rows = p.rows > 0;
+        if ((L.phase & BwdLaunch::kFirst) && have_rows)
             PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((p.rows * (D / 16) + 255) / 256)),
                         dim3(256), 0, st, p, L.deterministic ? 0 : 1);
-        }
-    }
-    const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
-    const bool have_main = main_grid.x > 0 && main_grid.y > 0;
-    const dim3 main_block(W8 ? 512 : 256);
-    if (L.deterministic) {
-        if constexpr (W8) {
-            const int mx = (int)main_grid.x, my = (int)main_grid.y;
-            const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
-            const int n = mx * my + qx * qy;
-            if (n > 0)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p,
-                            mx, my, qx, qy);
-        } else {
+        const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
+        const bool have_main = main_grid.x > 0 && main_grid.y > 0;
+        if (L.deterministic) {
             if (have_main)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, main_block, 0, st, p);
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
             const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
             if (dq_grid.x > 0 && dq_grid.y > 0)
                 PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
-        }
-    } else {
-        if constexpr (W8) {
+        } else {
             if (have_main)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main8_kernel<T, D, CAUSAL, true>), main_grid, main_block, 0, st, p);
-        } else if (have_main) {
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, main_block, 0, st, p);
+                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
+            if ((L.phase & BwdLaunch::kLast) && have_rows)
+                PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
         }
-        if ((L.phase & BwdLaunch::kLast) && have_rows)
-            PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
+        return hipGetLastError();
     }
-    return hipGetLastError();
 }
 
 template <class T, int D>

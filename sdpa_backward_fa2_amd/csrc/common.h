@@ -56,6 +56,11 @@ struct F16 {
         typedef __fp16 h2 __attribute__((ext_vector_type(2)));
         return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
     }
+    // c + a.lo*b.lo + a.hi*b.hi in fp32 (one v_dot2 instruction)
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+    }
 };
 
 struct BF16 {
@@ -78,9 +83,34 @@ struct BF16 {
     }
     // gfx950 converts a pair to bf16 with round-to-nearest-even in one instruction.
     static __device__ __forceinline__ uint32_t pack_op(float lo, float hi) { return pack(lo, hi); }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+    }
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// lane exchange inside a row of 16 lanes (DPP control word CTRL)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N (8 or 16) consecutive lanes; every lane of the
+// group receives the sum.  Quad swaps, then the half-row and row mirrors.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group size");
+    x += dpp_f32<0xB1>(x);    // quad_perm 1,0,3,2
+    x += dpp_f32<0x4E>(x);    // quad_perm 2,3,0,1
+    x += dpp_f32<0x141>(x);   // row_half_mirror
+    if (N == 16) x += dpp_f32<0x140>(x);   // row_mirror
+    return x;
+}
+
+// Wait for every outstanding memory operation of the wavefront.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
