@@ -90,10 +90,79 @@ def build_inputs(cid: int):
             ts[name], host[name] = t, x
         o, lse = sb.fwd_stats(ts["q"], ts["k"], ts["v"], wl.scale, wl.causal)
         torch.cuda.synchronize()
-        call, outs = sb.prepare_bwd(ts["q"], ts["k"], ts["v"], o, ts["do"], lse, wl.scale,
-                                    wl.causal, deterministic=False)
-        return wl, call, outs, host, (ts, o, lse)
-    raise SystemExit(f"config {cid}: bench line not implemented yet")
+
+        def prep(det):
+            return sb.prepare_bwd(ts["q"], ts["k"], ts["v"], o, ts["do"], lse, wl.scale, wl.causal,
+                                  deterministic=det)
+        return wl, prep, host
+
+    ts = {}
+    for name, tid, H in (("q", synth.TID_Q, wl.Hq), ("k", synth.TID_K, wl.Hkv),
+                         ("v", synth.TID_V, wl.Hkv), ("do", synth.TID_DO, wl.Hq)):
+        bits = wl.packed_bits(tid, H)
+        ts[name], host[name] = dev(bits), bits
+    cu = wl.cu_seqlens()
+    T = wl.T
+    if wl.kind == "varlen":
+        # O and the LSE per sequence from the library's dense forward, written
+        # straight into the packed buffers (outside the timed region)
+        o = torch.empty_like(ts["q"])
+        lse = torch.empty((T, wl.Hq), dtype=torch.float32, device="cuda")
+        start = 0
+        for end in cu:
+            end = int(end)
+            if end > start:
+                def v4(x):
+                    return x[start:end].unsqueeze(0).permute(0, 2, 1, 3)
+                sb.fwd_stats(v4(ts["q"]), v4(ts["k"]), v4(ts["v"]), wl.scale, wl.causal,
+                             o=v4(o), lse=lse[start:end].t().unsqueeze(0))
+            start = end
+        torch.cuda.synchronize()
+
+        def prep(det):
+            return sb.prepare_varlen(ts["q"], ts["k"], ts["v"], o, ts["do"], lse, cu, cu, wl.scale,
+                                     wl.causal, deterministic=det)
+        return wl, prep, host
+
+    # selected (NSA): O and the (max, sum) statistics over the gathered keys,
+    # prepared with torch fp32 products on the GPU in the dense-with-bias form
+    # (bias ln m_b on a block chosen m_b times, -inf elsewhere and above the
+    # diagonal), outside the timed region
+    topk_np = wl.topk()
+    topk = torch.from_numpy(np.ascontiguousarray(topk_np, dtype=np.int32)).cuda()
+    bs, G = wl.block_size, wl.Hq // wl.Hkv
+    o = torch.empty_like(ts["q"])
+    m = torch.empty((T, wl.Hq), dtype=torch.float32, device="cuda")
+    l = torch.empty_like(m)
+    starts = np.concatenate([[0], cu[:-1]])
+    for s0, s1 in zip(starts.tolist(), cu.tolist()):
+        L = s1 - s0
+        if L == 0:
+            continue
+        nb = L // bs
+        for h2 in range(wl.Hkv):
+            mult = torch.zeros((L, nb), dtype=torch.float32, device="cuda")
+            mult.scatter_add_(1, topk[s0:s1, h2].long(), torch.ones((L, topk.shape[2]), device="cuda"))
+            bias = torch.log(mult).repeat_interleave(bs, dim=1)
+            bias = torch.cat([bias, torch.full((L, L - nb * bs), -math.inf, device="cuda")], 1)
+            if wl.extra.get("sparse_mode", 2) == 2:
+                bias = bias.masked_fill(torch.ones(L, L, dtype=torch.bool, device="cuda").triu(1), -math.inf)
+            kk = ts["k"][s0:s1, h2].float()
+            vv = ts["v"][s0:s1, h2].float()
+            for h in range(h2 * G, (h2 + 1) * G):
+                sc = (ts["q"][s0:s1, h].float() @ kk.t()) * wl.scale
+                mx = torch.where(torch.isfinite(bias), sc, torch.full_like(sc, -math.inf)).amax(1)
+                pw = torch.exp(sc + bias - mx[:, None])
+                sm = pw.sum(1)
+                o[s0:s1, h] = ((pw @ vv) / sm[:, None]).to(o.dtype)
+                m[s0:s1, h], l[s0:s1, h] = mx, sm
+    torch.cuda.synchronize()
+
+    def prep(det):
+        return sb.prepare_selected(ts["q"], ts["k"], ts["v"], o, ts["do"], (m, l), topk, cu, cu, bs,
+                                   wl.scale, wl.extra.get("sparse_mode", 2), deterministic=det)
+    host["topk"] = topk_np
+    return wl, prep, host
 
 
 def cpu_baseline(wl, host) -> dict:
@@ -101,30 +170,72 @@ def cpu_baseline(wl, host) -> dict:
     import numpy as np
 
     import oracle
+    import synth
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    B, Hq = wl.B, wl.Hq
-    heads = [(b, h) for b in range(B) for h in range(wl.Hkv)]
-    # size the sample: time one head, then take enough heads for ~10 s per repetition
+    x = {k: synth.decode(v, wl.dtype) if wl.kind != "dense" else v
+         for k, v in host.items() if k in ("q", "k", "v", "do")}
+    if wl.kind == "dense":
+        units = [(b, h) for b in range(wl.B) for h in range(wl.Hkv)]
+        what = "(batch, KV head) slices"
+
+        def run(sel):
+            oracle.dense_backward(x["q"], x["k"], x["v"], x["do"], wl.scale, wl.causal, heads=sel)
+
+        def share(sel):
+            return len(sel) / len(units)
+    elif wl.kind == "varlen":
+        cu = wl.cu_seqlens()
+        units = list(range(len(cu)))
+        what = "sequences"
+
+        def run(sel):
+            oracle.varlen_backward(x["q"], x["k"], x["v"], x["do"], cu, cu, wl.scale, wl.causal, seqs=sel)
+
+        lens = np.diff(np.concatenate([[0], cu])).astype(np.float64)
+
+        def share(sel):
+            return float(np.sum(lens[sel] ** 2) / np.sum(lens ** 2))
+    else:
+        cu = wl.cu_seqlens()
+        units = [0]
+        what = "the whole problem"
+
+        def run(sel):
+            oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], host["topk"], cu, cu,
+                                     wl.block_size, wl.scale, wl.extra.get("sparse_mode", 2))
+
+        def share(sel):
+            return 1.0
+    # size the sample: time one unit, then take enough units for ~10 s per repetition
     t0 = time.perf_counter()
-    oracle.dense_backward(host["q"], host["k"], host["v"], host["do"], wl.scale, wl.causal, heads=heads[:1])
-    t_head = time.perf_counter() - t0
-    n = int(min(len(heads), max(1, math.ceil(10.0 / max(t_head, 1e-3)))))
-    reps = 3 if n == len(heads) and t_head * n < 8 else 1
+    run(units[:1])
+    t_one = time.perf_counter() - t0
+    n = int(min(len(units), max(1, math.ceil(10.0 / max(t_one, 1e-3)))))
+    reps = 3 if n == len(units) and t_one * n < 8 else 1
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        oracle.dense_backward(host["q"], host["k"], host["v"], host["do"], wl.scale, wl.causal,
-                              heads=heads[:n])
+        run(units[:n])
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
-    flops = wl.counted_flops() * n / len(heads)
+    flops = wl.counted_flops() * share(units[:n])
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n} of {len(heads)} (batch, head) slices of the same problem, fp64 numpy "
-                      f"oracle, median of {reps} run(s), {t:.2f} s per run"}
+            "sample": f"{n} of {len(units)} {what} of the same problem, fp64 numpy oracle, "
+                      f"median of {reps} run(s), {t:.2f} s per run"}
+
+
+# Share of the counted contractions (S, dP, dV, dK, dQ) each kernel performs;
+# recomputed S and dP in the deterministic dQ kernels are not counted.
+KERNEL_FLOP_SHARE = {
+    ("bwd_main_kernel", "fused"): 1.0,
+    ("bwd_main_kernel", False): 1.0, ("bwd_main_kernel", True): 0.8, ("bwd_dq_kernel", True): 0.2,
+    ("nsa_bwd_kv_kernel", False): 0.8, ("nsa_bwd_kv_kernel", True): 0.8,
+    ("nsa_bwd_dq_kernel", False): 0.2, ("nsa_bwd_dq_kernel", True): 0.2,
+}
 
 
 def traffic_for(kernel: str, workload: str):
@@ -162,11 +273,8 @@ def main():
         return
     import sdpa_backward_fa2_amd as sb
     sb.load()
-    wl, call, outs, host, keep = build_inputs(args.config)
-    if args.deterministic:
-        ts, o, lse = keep
-        call, outs = sb.prepare_bwd(ts["q"], ts["k"], ts["v"], o, ts["do"], lse, wl.scale, wl.causal,
-                                    deterministic=True)
+    wl, prep, host = build_inputs(args.config)
+    call, outs = prep(args.deterministic)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -186,22 +294,33 @@ def main():
             call()
     torch.cuda.synchronize()
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in kt.result.items()}
-    main_name = "bwd_main_kernel"
+    # the dominant kernel, with the counted contractions it performs
+    main_name = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
+    fused = wl.kind != "selected" and wl.D == 64
+    share = KERNEL_FLOP_SHARE.get((main_name, "fused" if fused else args.deterministic), 0.0)
     main_us = kernels[main_name]["avg_us"]
-    achieved = flops / (main_us * 1e-6) / 1e12
+    per_launch = flops * share * args.steps / kernels[main_name]["launches"]
+    achieved = per_launch / (main_us * 1e-6) / 1e12
     workload_name = f"config{args.config}"
     roofline = {"bound": "mfma", "kernel": main_name, "achieved": achieved,
                 "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_16BIT_TFLOPS,
                 "traffic": traffic_for(main_name, workload_name)}
+    if wl.kind == "dense":
+        cfg = {"workload": wl.name, "B": wl.B, "H": wl.Hq, "S": wl.S, "D": wl.D, "causal": wl.causal,
+               "layout": wl.layout}
+    else:
+        cfg = {"workload": wl.name, "T": wl.T, "sequences": len(wl.lengths), "Hq": wl.Hq, "Hkv": wl.Hkv,
+               "D": wl.D, "causal": wl.causal}
+        if wl.kind == "selected":
+            cfg.update(block_size=wl.block_size, block_count=wl.block_count)
+    cfg.update(deterministic=args.deterministic, counted_gflop=flops / 1e9)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
-        "config": {"workload": wl.name, "B": wl.B, "H": wl.Hq, "S": wl.S, "D": wl.D,
-                   "causal": wl.causal, "layout": wl.layout, "deterministic": args.deterministic,
-                   "counted_gflop": flops / 1e9},
+        "config": cfg,
         "pct_of_mfma_peak": 100.0 * value / PEAK_MFMA_16BIT_TFLOPS,
         "roofline": roofline,
         "kernels": kernels,

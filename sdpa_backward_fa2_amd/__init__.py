@@ -308,10 +308,11 @@ def bwd_varlen_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, deterministic) -> 
     return out.value
 
 
-def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
-               deterministic: bool = False, dq=None, dk=None, dv=None, workspace=None):
-    """Packed (T, N, D) backward; cu_q / cu_kv: host sequences of inclusive end
-    offsets; stats: LSE (T, Hq) or a (max, sum) pair of (T, Hq[, 8]) tensors."""
+def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
+                   deterministic: bool = False, dq=None, dk=None, dv=None, workspace=None):
+    """Marshal one packed (T, N, D) backward once; returns (call, (dq, dk, dv)).
+    cu_q / cu_kv: host sequences of inclusive end offsets; stats: LSE (T, Hq)
+    or a (max, sum) pair of (T, Hq[, 8]) tensors."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
@@ -324,12 +325,28 @@ def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
     nbytes = bwd_varlen_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, deterministic)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
-    st = lib.sdpa_bwd_varlen(dt, n, aq, ak, Hq, Hkv, D, float(scale), int(causal), int(deterministic),
-                             _t3(q), _t3(k), _t3(v), _t3(o), _t3(dout), ctypes.byref(sa),
-                             _t3(dq), _t3(dk), _t3(dv), ws.data_ptr(), ws.numel(),
-                             _stream_ptr(q.device))
-    _check(st, "sdpa_bwd_varlen")
-    return dq, dk, dv
+    structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(causal), int(deterministic),
+            *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
+            _stream_ptr(q.device))
+    fn = lib.sdpa_bwd_varlen
+    keep = (structs, sa, ws, stats, aq, ak)
+
+    def call():
+        _check(fn(*args), "sdpa_bwd_varlen")
+
+    call.keep = keep
+    return call, (dq, dk, dv)
+
+
+def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
+               deterministic: bool = False, dq=None, dk=None, dv=None, workspace=None):
+    """Packed (T, N, D) backward; cu_q / cu_kv: host sequences of inclusive end
+    offsets; stats: LSE (T, Hq) or a (max, sum) pair of (T, Hq[, 8]) tensors."""
+    call, outs = prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale, causal, deterministic,
+                                dq, dk, dv, workspace)
+    call()
+    return outs
 
 
 # ----------------------------------------------------------------------------
@@ -347,10 +364,11 @@ def bwd_selected_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, block_size, bloc
     return out.value
 
 
-def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
-                 sparse_mode: int, deterministic: bool = False, dq=None, dk=None, dv=None,
-                 workspace=None):
-    """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device."""
+def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
+                     sparse_mode: int, deterministic: bool = False, dq=None, dk=None, dv=None,
+                     workspace=None):
+    """Marshal one NSA selected-attention backward once; returns (call, (dq, dk, dv)).
+    topk: int32 (T, Hkv, count) on the device."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
@@ -364,13 +382,29 @@ def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, sc
     nbytes = bwd_selected_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, block_size, count, deterministic)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
-    st = lib.sdpa_bwd_selected(dt, n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
-                               topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic),
-                               _t3(q), _t3(k), _t3(v), _t3(o), _t3(dout), ctypes.byref(sa),
-                               _t3(dq), _t3(dk), _t3(dv), ws.data_ptr(), ws.numel(),
-                               _stream_ptr(q.device))
-    _check(st, "sdpa_bwd_selected")
-    return dq, dk, dv
+    structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
+            topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic),
+            *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
+            _stream_ptr(q.device))
+    fn = lib.sdpa_bwd_selected
+    keep = (structs, sa, ws, stats, topk, aq, ak)
+
+    def call():
+        _check(fn(*args), "sdpa_bwd_selected")
+
+    call.keep = keep
+    return call, (dq, dk, dv)
+
+
+def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
+                 sparse_mode: int, deterministic: bool = False, dq=None, dk=None, dv=None,
+                 workspace=None):
+    """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device."""
+    call, outs = prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size, scale,
+                                  sparse_mode, deterministic, dq, dk, dv, workspace)
+    call()
+    return outs
 
 
 def selected_build_index(topk, cu_q, cu_kv, block_size: int, workspace=None):
