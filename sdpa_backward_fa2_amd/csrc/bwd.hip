@@ -1036,6 +1036,12 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         }
 }
 
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
+    __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
+    bwd_dq8_body<T, D, CAUSAL>(p, arena, blockIdx.x, blockIdx.y);
+}
+
 // dK/dV and dQ in one launch: the first n_main workgroups run the key-tile
 // outer kernel (key tiles in ascending order, so the longest causal ranges
 // start first), the rest the query-tile outer dQ kernel (query tiles in
@@ -1084,9 +1090,9 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         if (L.deterministic) {
             if (have_main)
                 PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
-            const dim3 dq_grid(L.max_q_tiles128, L.n_seq * p.Hq);
+            const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
             if (dq_grid.x > 0 && dq_grid.y > 0)
-                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq_kernel<T, D, CAUSAL>), dq_grid, dim3(256), 0, st, p);
+                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(512), 0, st, p);
         } else {
             if (have_main)
                 PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);

@@ -8,7 +8,7 @@
 //
 // Kernels, all on the caller's stream:
 //   nsa_index_kernel<false>  per (KV head, KV block): how many (token, slot)
-//                            choices name the block (ordered scan, no atomics)
+//                            choices name the block (ballot counts, no atomics)
 //   nsa_scan_kernel          CSR offsets of those lists and a table of work
 //                            pieces (at most `chunk` entries of one block each)
 //   nsa_index_kernel<true>   fills each block's list in (token, slot) order
@@ -78,9 +78,15 @@ __device__ __forceinline__ int seq_of_token(const SeqTable& s, int t) {
 // Inverse index
 // ---------------------------------------------------------------------------
 
+// One workgroup of 16 wavefronts per (KV block, KV head).  The sequence's
+// (token, slot) entries are split into 16 contiguous spans, one per wavefront;
+// a wavefront walks its span 64 entries at a time with coalesced loads and a
+// ballot.  The counting pass writes the block's total; the filling pass
+// counts again, takes the wavefronts' exclusive prefix and writes each match
+// at its rank, so every list comes out in (token, slot) order without atomics.
 template <bool FILL>
-__global__ __launch_bounds__(256) void nsa_index_kernel(NsaParams p) {
-    __shared__ int wave_n[4];
+__global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
+    __shared__ int wave_n[16];
     const int g = blockIdx.x, h2 = blockIdx.y;
     const int bucket = h2 * p.NB + g;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -92,29 +98,53 @@ __global__ __launch_bounds__(256) void nsa_index_kernel(NsaParams p) {
     const int gl = g - p.seqs.k0[s] / p.bs;      // block index within its sequence
     const int64_t e0 = (int64_t)p.seqs.q0[s] * p.count;
     const int64_t e1 = (int64_t)(p.seqs.q0[s] + p.seqs.lq[s]) * p.count;
-    int base = FILL ? p.offsets[bucket] : 0;
-    for (int64_t c0 = e0; c0 < e1; c0 += 256) {
-        const int64_t e = c0 + tid;
-        bool m = false;
-        if (e < e1) {
-            const int64_t t = e / p.count, slot = e % p.count;
-            m = p.topk[t * p.tk_st + (int64_t)h2 * p.tk_sn + slot * p.tk_sk] == gl;
-        }
-        const unsigned long long bal = __ballot(m);
-        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_n[w] = __popcll(bal);
-        __syncthreads();
-        int off = 0, tot = 0;
+    const int64_t span = ((e1 - e0 + 15) / 16 + 63) / 64 * 64;
+    const int64_t a = e0 + w * span;
+    const int64_t b = min(a + span, e1);
+    const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
+    const double inv_count = 1.0 / p.count;
+    auto match = [&](int64_t e) -> bool {
+        if (e >= b) return false;
+        // t = e / count through a double reciprocal, corrected to the exact quotient
+        int64_t t = (int64_t)((double)e * inv_count);
+        t += (t + 1) * p.count <= e;
+        t -= t * p.count > e;
+        const int64_t slot = e - t * p.count;
+        return tk[t * p.tk_st + slot * p.tk_sk] == gl;
+    };
+    // eight chunks per iteration so that their loads are in flight together
+    int n = 0;
+    for (int64_t c = a; c < b; c += 512) {
+        bool m[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            off += i < w ? wave_n[i] : 0;
-            tot += wave_n[i];
-        }
-        if (FILL && m) p.entries[base + off + rank] = (int32_t)e;
-        base += tot;
-        __syncthreads();
+        for (int u = 0; u < 8; ++u) m[u] = match(c + 64 * u + lane);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) n += __popcll(__ballot(m[u]));
     }
-    if (!FILL && tid == 0) p.counts[bucket] = base;
+    if (lane == 0) wave_n[w] = n;
+    __syncthreads();
+    if (!FILL) {
+        if (tid == 0) {
+            int tot = 0;
+            for (int i = 0; i < 16; ++i) tot += wave_n[i];
+            p.counts[bucket] = tot;
+        }
+        return;
+    }
+    int base = p.offsets[bucket];
+    for (int i = 0; i < w; ++i) base += wave_n[i];
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int64_t c = a; c < b; c += 512) {
+        bool m[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m[u] = match(c + 64 * u + lane);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const unsigned long long bal = __ballot(m[u]);
+            if (m[u]) p.entries[base + __popcll(bal & below)] = (int32_t)(c + 64 * u + lane);
+            base += __popcll(bal);
+        }
+    }
 }
 
 // Block-wide exclusive scan of one value per thread (1024 threads); returns the
@@ -584,9 +614,9 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 
 static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
     const dim3 grid(p.NB, p.N2);
-    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<false>), grid, dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<false>), grid, dim3(1024), 0, st, p);
     PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
-    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<true>), grid, dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<true>), grid, dim3(1024), 0, st, p);
     return hipGetLastError();
 }
 
