@@ -231,10 +231,10 @@ def cpu_baseline(wl, host) -> dict:
 # Share of the counted contractions (S, dP, dV, dK, dQ) each kernel performs;
 # recomputed S and dP in the deterministic dQ kernels are not counted.
 KERNEL_FLOP_SHARE = {
-    ("bwd_main_kernel", "fused"): 1.0,
-    ("bwd_main_kernel", False): 1.0, ("bwd_main_kernel", True): 0.8, ("bwd_dq_kernel", True): 0.2,
-    ("nsa_bwd_kv_kernel", False): 0.8, ("nsa_bwd_kv_kernel", True): 0.8,
-    ("nsa_bwd_dq_kernel", False): 0.2, ("nsa_bwd_dq_kernel", True): 0.2,
+    ("bwd_fused8_kernel", False): 1.0, ("bwd_fused8_kernel", True): 1.0,
+    ("bwd_main_kernel", False): 1.0, ("bwd_main_kernel", True): 0.8, ("bwd_dq8_kernel", True): 0.2,
+    ("nsa_kv_kernel", False): 0.8, ("nsa_kv_kernel", True): 0.8,
+    ("nsa_dq_kernel", False): 0.2, ("nsa_dq_kernel", True): 0.2,
 }
 
 
@@ -296,8 +296,7 @@ def main():
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in kt.result.items()}
     # the dominant kernel, with the counted contractions it performs
     main_name = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-    fused = wl.kind != "selected" and wl.D == 64
-    share = KERNEL_FLOP_SHARE.get((main_name, "fused" if fused else args.deterministic), 0.0)
+    share = KERNEL_FLOP_SHARE.get((main_name, args.deterministic), 0.0)
     main_us = kernels[main_name]["avg_us"]
     per_launch = flops * share * args.steps / kernels[main_name]["launches"]
     achieved = per_launch / (main_us * 1e-6) / 1e12

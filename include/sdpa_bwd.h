@@ -223,8 +223,9 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
  * stream.  sdpa_profile_end() waits for the last recorded event, writes for
  * each kernel id k < n_kernels the summed elapsed milliseconds total_ms[k]
  * and the number of launches launches[k], and disables timing.  Kernel ids:
- * 0 forward, 1 backward preprocess, 2 backward main, 3 dQ convert,
- * 4 deterministic dQ, 5 NSA index build, 6 NSA dK/dV, 7 NSA dQ;
+ * 0 forward, 1 backward preprocess, 2 backward main (D=128), 3 dQ convert,
+ * 4 deterministic dQ (D=128), 5 NSA index build (three launches), 6 NSA dK/dV,
+ * 7 NSA dQ, 8 fused dK/dV and dQ (D=64), 9 NSA dK/dV partial reduction;
  * sdpa_kernel_name(id) gives the kernel's symbol name stem.  Not thread-safe
  * with respect to concurrent begin/end calls from several threads.
  */

@@ -94,7 +94,7 @@ _SIGS = {
 }
 
 
-N_KERNEL_IDS = 8
+N_KERNEL_IDS = 10
 
 
 class KernelTimer:

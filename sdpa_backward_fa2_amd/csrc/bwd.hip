@@ -1,19 +1,24 @@
 // SDPA backward, FlashAttention-2 style, for gfx950.
 //
 // Kernels (all on the caller's stream):
-//   bwd_pre_kernel     per row: Delta = sum_d dO*O, the statistics turned into
+//   bwd_fused8_kernel  D=64: one launch of eight-wavefront workgroups; the
+//                      first ones run the key-tile outer body (dK, dV of 128
+//                      keys over every query tile of every query head of the
+//                      group), the rest the query-tile outer body (dQ of 64
+//                      rows over the key tiles they see).  Both read O and the
+//                      caller's statistics themselves; no atomics, no
+//                      workspace traffic.                               [MFMA]
+//   bwd_pre_kernel     D=128, per row: Delta = sum_d dO*O, the statistics as
 //                      log2-domain LSE, and (atomic mode) the fp32 dQ
 //                      accumulator row cleared.                   [HBM-bound]
-//   bwd_main_kernel    one workgroup per (sequence, KV head, 128-key tile): K
-//                      and V of the tile stay in registers, dK and dV
-//                      accumulate in registers across every query tile of
-//                      every query head of the group; per 64-row query tile it
-//                      runs the five contractions S = Q K^T, dP = dO V^T,
-//                      dV += P^T dO, dK += dS^T Q, dQ += dS K (the last through
-//                      fp32 atomics, or skipped in deterministic mode). [MFMA]
-//   bwd_dq_convert     dQ = scale * accumulator, rounded to the I/O type.
-//   bwd_dq_kernel      deterministic dQ: query-tile outer, recomputes S, P, dP
-//                      and dS per key tile and keeps dQ in registers.
+//   bwd_main_kernel    D=128: one four-wavefront workgroup per (sequence, KV
+//                      head, 128-key tile); dK and dV accumulate in registers
+//                      across every query tile of every query head of the
+//                      group; per 64-row query tile S, dP, dV, dK and, in
+//                      atomic mode, dQ += dS K through fp32 atomics.     [MFMA]
+//   bwd_dq_convert     D=128 atomic mode: dQ = scale * accumulator, rounded.
+//   bwd_dq8_kernel     D=128 deterministic mode: the query-tile outer dQ body
+//                      as its own launch.                                [MFMA]
 //
 // The formulas: dV = P^T dO, dQ = s dS K, dK = s dS^T Q (Ascend
 // aclnnNsaSelectedAttentionGrad page, "Formula" section), with
@@ -708,109 +713,6 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Deterministic dQ (query-tile outer)
-// ---------------------------------------------------------------------------
-
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-    constexpr int BQ = 128;          // 4 wavefronts x 32 query rows
-    constexpr int BK = 64;           // keys per LDS tile
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
-    constexpr int KP = D + 8;        // Ks, Vs  [key][d]
-    constexpr int TP = BK + 8;       // KT      [d][key]
-    __shared__ __align__(16) uint16_t Ks[BK * KP];
-    __shared__ __align__(16) uint16_t Vs[BK * KP];
-    __shared__ __align__(16) uint16_t KT[D * TP];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 5, c = lane & 31;
-    const int b = blockIdx.y / p.Hq, h = blockIdx.y % p.Hq;
-    const int hk = h / (p.Hq / p.Hkv);
-    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
-    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int i0 = blockIdx.x * BQ;
-    if (i0 >= lq) return;
-
-    const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
-    const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
-    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
-    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
-    const int64_t ws_base = p.varlen ? (int64_t)q0 * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq;
-    const int64_t ws_step = p.varlen ? p.Hq : 1;
-
-    const int my_i = i0 + 32 * w + c;
-    const bool row_ok = my_i < lq;
-    u32x4 qreg[KS], doreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qreg[s] = row_ok ? ld16(qbase + (int64_t)my_i * p.q.ss + 16 * s + 8 * g) : z;
-        doreg[s] = row_ok ? ld16(dobase + (int64_t)my_i * p.dout.ss + 16 * s + 8 * g) : z;
-    }
-    const float l2 = row_ok ? p.lse2[ws_base + my_i * ws_step] : INFINITY;
-    const float dl = row_ok ? p.delta[ws_base + my_i * ws_step] : 0.f;
-
-    f32x16 dq[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dq[db] = zero16();
-
-    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
-    for (int j0 = 0; j0 < kend; j0 += BK) {
-        __syncthreads();
-        for (int e = tid; e < BK * D / 8; e += 256) {
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            const int j = j0 + r;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (j < lk) {
-                kv = ld16(kbase + (int64_t)j * p.k.ss + cc);
-                vv = ld16(vbase + (int64_t)j * p.v.ss + cc);
-            }
-            st16(&Ks[r * KP + cc], kv);
-            st16(&Vs[r * KP + cc], vv);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) KT[(cc + t) * TP + r] = elem16(kv, t);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-            for (int st = 0; st < KS; ++st) {
-                s = T::mma(ld16(&Ks[(kb * 32 + c) * KP + 16 * st + 8 * g]), qreg[st], s);
-                dp = T::mma(ld16(&Vs[(kb * 32 + c) * KP + 16 * st + 8 * g]), doreg[st], dp);
-            }
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-                const int j = j0 + kb * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3);
-                float pv = fast_exp2(s[rg] * p.scale_log2 - l2);
-                if (j >= lk || (CAUSAL && j > my_i)) pv = 0.f;
-                dp[rg] = pv * (dp[rg] - dl);
-            }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const u32x4 bS = acc_to_operand<T>(dp, hh);
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    dq[db] = T::mma(ld_acc_slots(&KT[(db * 32 + c) * TP + kb * 32 + 16 * hh], g), bS, dq[db]);
-            }
-        }
-    }
-    if (!row_ok) return;
-    uint16_t* dqp = p.dq.p + b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u32x2 v;
-            v[0] = T::pack(dq[db][4 * q + 0] * p.scale, dq[db][4 * q + 1] * p.scale);
-            v[1] = T::pack(dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
-            st8(dqp + db * 32 + 8 * q + 4 * g, v);
-        }
-}
-
-// ---------------------------------------------------------------------------
 // dQ pass without atomics, eight wavefronts (query-tile outer)
 // ---------------------------------------------------------------------------
 //
@@ -1075,7 +977,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
         const int n = mx * my + qx * qy;
         if (n > 0)
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p, mx, my, qx,
+            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p, mx, my, qx,
                         qy);
         return hipGetLastError();
     } else {

@@ -627,7 +627,7 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, D, false, st);
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, D>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
-    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves), dim3(256), 0, st, p);
     PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
     return hipGetLastError();
 }

@@ -18,7 +18,9 @@ enum KernelId {
     KID_NSA_INDEX = 5,
     KID_NSA_KV = 6,
     KID_NSA_DQ = 7,
-    KID_COUNT = 8
+    KID_BWD_FUSED = 8,
+    KID_NSA_KV_REDUCE = 9,
+    KID_COUNT = 10
 };
 
 bool prof_enabled();
