@@ -220,6 +220,7 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
         p.seqs.dev = nullptr;
         L.n_seq = (int)B;
         L.max_kv_tiles = (int)((Sk + 127) / 128);
+        L.max_kv_tiles64 = (int)((Sk + 63) / 64);
         L.max_q_tiles128 = (int)((Sq + 127) / 128);
         L.max_q_tiles64 = (int)((Sq + 63) / 64);
         hipError_t e = sdpa::launch_bwd(p, L, st);
@@ -245,6 +246,7 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
         }
         L.n_seq = (int)(c1 - c0);
         L.max_kv_tiles = (int)((mlk + 127) / 128);
+        L.max_kv_tiles64 = (int)((mlk + 63) / 64);
         L.max_q_tiles128 = (int)((mlq + 127) / 128);
         L.max_q_tiles64 = (int)((mlq + 63) / 64);
         L.phase = (c0 == 0 ? sdpa::BwdLaunch::kFirst : 0) | (c1 == n ? sdpa::BwdLaunch::kLast : 0);

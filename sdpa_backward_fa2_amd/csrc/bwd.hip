@@ -425,26 +425,34 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 // halves' dK/dV partials are summed through LDS at the end.  dQ is left to
 // the query-outer body.
 
+// Wavefronts per workgroup of the D=64 kernel and the dQ body: two row halves
+// of NKW key slices.  Four wavefronts let two workgroups share a CU (two
+// wavefronts per SIMD), so one workgroup's memory waits and barriers overlap
+// the other's arithmetic.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeySlices = kWaves / 2;
+
 template <int D>
 struct Main8Lds {
     static constexpr int BR = 64, QP = D + 8, DB = D / 32, NBUF = 3;
     static constexpr int TILE_B = BR * QP * 2;            // one Q or dO tile
     static constexpr int OFF_STAT = 2 * NBUF * TILE_B;    // lse [NBUF][BR], -Delta [NBUF][BR]
     static constexpr int LOOP_B = OFF_STAT + 2 * NBUF * BR * 4;
-    static constexpr int RED_B = 4 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of four wavefronts
+    static constexpr int RED_B = kKeySlices * 64 * (2 * DB * 16) * 4;   // dK/dV partials of one row half
     static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
 };
 
 template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     using L = Main8Lds<D>;
-    constexpr int BC = 128;          // keys per workgroup
+    constexpr int BC = 32 * kKeySlices;   // keys per workgroup
     constexpr int BR = L::BR;        // query rows per step
     constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
     constexpr int DB = L::DB;        // 32-row blocks of dK^T / dV^T
     constexpr int QP = L::QP;        // row stride of the Q and dO tiles  [row][d]
     constexpr int TILE = BR * QP;    // elements of one tile
-    constexpr int CH = BR * D / 8 / 512;     // 16-byte chunks per thread per tile
+    constexpr int CH = BR * D / 8 / kThreads;   // 16-byte chunks per thread per tile
     static_assert(CH >= 1, "tile shape");
     uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena);
     uint16_t* dOs0 = Qs0 + L::NBUF * TILE;
@@ -453,7 +461,7 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int kw = w & 3, rh = w >> 2;
+    const int kw = w % kKeySlices, rh = w / kKeySlices;
     const int g = lane >> 5, c = lane & 31;
     const int b = bx / p.Hkv, hk = bx % p.Hkv;
     const int G = p.Hq / p.Hkv;
@@ -480,7 +488,7 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
     int qoff[CH], dooff[CH], ooff[CH], crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
-        const int e = tid + 512 * x;
+        const int e = tid + kThreads * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
         ccol[x] = cc;
@@ -729,32 +737,32 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 
 template <int D>
 struct Dq8Lds {
-    static constexpr int BK = 128, KP = D + 8, DB = D / 32;
+    static constexpr int BK = 32 * kKeySlices, KP = D + 8, DB = D / 32;
     static constexpr int TILE_B = BK * KP * 2;
     static constexpr int LOOP_B = 4 * TILE_B;
-    static constexpr int RED_B = 3 * 2 * 64 * (DB * 16) * 4;
+    static constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;
     static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
 };
 
 template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     constexpr int BQ = 64;           // query rows per workgroup
-    constexpr int BK = 128;          // keys per step
+    constexpr int BK = 32 * kKeySlices;   // keys per step
     constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
     constexpr int DB = D / 32;       // 32-row blocks of dQ^T
     constexpr int KP = D + 8;        // row stride of Ks, Vs  [key][d]
-    constexpr int CH = BK * D / 8 / 512;     // 16-byte chunks per thread per key tile
+    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per key tile
     constexpr int TILE_B = BK * KP * 2;
     constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
     constexpr int LOOP_B = 4 * TILE_B;
-    constexpr int RED_B = 3 * 2 * 64 * (DB * 16) * 4;    // three key slices of both row halves
+    constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;   // key slices 1.. of both row halves
     static_assert(Dq8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
     uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
     uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
-    const int kw = w & 3, rh = w >> 2;
+    const int kw = w % kKeySlices, rh = w / kKeySlices;
     const int g = lane >> 5, c = lane & 31;
     const int b = by / p.Hq, h = by % p.Hq;
     const int hk = h / (p.Hq / p.Hkv);
@@ -774,7 +782,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     int koff[CH], voff[CH], crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
-        const int e = tid + 512 * x;
+        const int e = tid + kThreads * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
         ccol[x] = cc;
@@ -917,7 +925,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     __syncthreads();
     if (kw != 0 || !row_ok) return;
 #pragma unroll
-    for (int sl = 0; sl < 3; ++sl)
+    for (int sl = 0; sl < kKeySlices - 1; ++sl)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -939,7 +947,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
 }
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
     __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
     bwd_dq8_body<T, D, CAUSAL>(p, arena, blockIdx.x, blockIdx.y);
 }
@@ -950,7 +958,7 @@ __global__ __launch_bounds__(512) void bwd_dq8_kernel(BwdParams p) {
 // descending order).  The dQ workgroups fill the CUs the long dK/dV
 // workgroups leave idle near the end.
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y) {
     constexpr int A = Main8Lds<D>::BYTES > Dq8Lds<D>::BYTES ? Main8Lds<D>::BYTES : Dq8Lds<D>::BYTES;
     __shared__ __align__(16) unsigned char arena[A];
     const int id = blockIdx.x;
@@ -973,11 +981,12 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         // One launch, no workspace traffic: the kernel reads the statistics
         // and O itself and computes dQ without atomics, so it is deterministic
         // whatever the caller asked for.
-        const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles;
+        const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
+        static_assert(32 * kKeySlices == 64, "key tile of the fused kernel");
         const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
         const int n = mx * my + qx * qy;
         if (n > 0)
-            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(512), 0, st, p, mx, my, qx,
+            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(kThreads), 0, st, p, mx, my, qx,
                         qy);
         return hipGetLastError();
     } else {
@@ -994,7 +1003,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
                 PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
             const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
             if (dq_grid.x > 0 && dq_grid.y > 0)
-                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(512), 0, st, p);
+                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
         } else {
             if (have_main)
                 PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);

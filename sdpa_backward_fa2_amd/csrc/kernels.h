@@ -14,6 +14,7 @@ struct BwdLaunch {
     bool deterministic;
     int n_seq;            // batch (dense) or number of packed sequences
     int max_kv_tiles;     // ceil(max key length / 128)
+    int max_kv_tiles64;   // ceil(max key length / 64)
     int max_q_tiles128;   // ceil(max query length / 128)
     int max_q_tiles64;    // ceil(max query length / 64)
     // Packed batches launch in chunks of sequences: the row-wise preprocess
