@@ -257,34 +257,41 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     }
     const int64_t ws_step = p.varlen ? p.Hq : 1;
 
+    // Tile loads are unconditional (rows past the end re-read the last row),
+    // and nothing loaded is used before store_tile, so the prefetch of the next
+    // tile is not waited for until the current step's products are issued.
     u32x4 pq[CH], pdo[CH];
     float pl = INFINITY, pd = 0.f;
+    int pi0 = 0;
     auto load_tile = [&](int st) {
         const int h = hk * G + st / per_head;
         const int i0 = i_begin + (st % per_head) * BR;
         const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
         const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
+        int oq[CH], odo[CH];
         if (i0 + BR <= lq) {
 #pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                pq[x] = ld16(qb + qoff[x]);
-                pdo[x] = ld16(dob + dooff[x]);
-            }
+            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
         } else {
+            const int last = lq - 1 - i0;
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                const bool ok = i0 + crow[x] < lq;
-                pq[x] = ok ? ld16(qb + qoff[x]) : z;
-                pdo[x] = ok ? ld16(dob + dooff[x]) : z;
+                const int e = tid + 256 * x;
+                const int r = min(crow[x], last), cc = (e % (D / 8)) * 8;
+                oq[x] = r * (int)p.q.ss + cc;
+                odo[x] = r * (int)p.dout.ss + cc;
             }
         }
-        if (tid < BR) {
-            const int i = i0 + tid;
-            const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
-            pl = i < lq ? p.lse2[ws] : INFINITY;
-            pd = i < lq ? p.delta[ws] : 0.f;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            pq[x] = ld16(qb + oq[x]);
+            pdo[x] = ld16(dob + odo[x]);
         }
+        const int i = min(i0 + (tid & (BR - 1)), lq - 1);
+        const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
+        pl = p.lse2[ws];
+        pd = p.delta[ws];
+        pi0 = i0;
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -295,8 +302,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
             st16(&dOs[buf][r * QP + cc], pdo[x]);
         }
         if (tid < BR) {
-            lse_s[buf][tid] = pl;
-            dlt_s[buf][tid] = pd;
+            const bool ok = pi0 + tid < lq;     // a row past the end has P = 0
+            lse_s[buf][tid] = ok ? pl : INFINITY;
+            dlt_s[buf][tid] = ok ? pd : 0.f;
         }
     };
 
@@ -304,6 +312,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         load_tile(0);
         store_tile(0);
     }
+    wait_all_memory();
     __syncthreads();
 
     for (int st = 0; st < n_steps; ++st) {
