@@ -16,7 +16,7 @@ Prints ONE JSON line:
               the MI355X dense fp16/bf16 MFMA peak of 2516.6 TFLOP/s;
   cpu_baseline the fp64 CPU oracle on the same inputs, timed on this host.
 
-    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--deterministic]
+    python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--dq-mode 0|1|2]
 """
 from __future__ import annotations
 
@@ -55,7 +55,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
-    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--deterministic", action="store_true", help="dQ mode 1 (same as --dq-mode 1)")
+    ap.add_argument("--dq-mode", type=int, choices=[0, 1, 2], default=None,
+                    help="0 fastest (default), 1 bitwise reproducible, 2 fp32 atomic accumulation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 256 MiB (10 launches), the reference "
@@ -228,13 +230,13 @@ def cpu_baseline(wl, host) -> dict:
                       f"median of {reps} run(s), {t:.2f} s per run"}
 
 
-# Share of the counted contractions (S, dP, dV, dK, dQ) each kernel performs;
-# recomputed S and dP in the deterministic dQ kernels are not counted.
+# Share of the counted contractions (S, dP, dV, dK, dQ) each kernel performs,
+# keyed by (kernel, dQ formed without atomics); recomputed S and dP in the
+# query-outer dQ kernels are not counted.
 KERNEL_FLOP_SHARE = {
-    ("bwd_fused8_kernel", False): 1.0, ("bwd_fused8_kernel", True): 1.0,
+    ("bwd_fused8_kernel", True): 1.0,
     ("bwd_main_kernel", False): 1.0, ("bwd_main_kernel", True): 0.8, ("bwd_dq8_kernel", True): 0.2,
-    ("nsa_kv_kernel", False): 0.8, ("nsa_kv_kernel", True): 0.8,
-    ("nsa_dq_kernel", False): 0.2, ("nsa_dq_kernel", True): 0.2,
+    ("nsa_kv_kernel", True): 0.8, ("nsa_dq_kernel", True): 0.2,
 }
 
 
@@ -273,8 +275,9 @@ def main():
         return
     import sdpa_backward_fa2_amd as sb
     sb.load()
+    mode = args.dq_mode if args.dq_mode is not None else (1 if args.deterministic else 0)
     wl, prep, host = build_inputs(args.config)
-    call, outs = prep(args.deterministic)
+    call, outs = prep(mode)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -296,7 +299,8 @@ def main():
     kernels = {k: {"avg_us": 1e3 * t / n, "launches": n} for k, (t, n) in kt.result.items()}
     # the dominant kernel, with the counted contractions it performs
     main_name = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches"])
-    share = KERNEL_FLOP_SHARE.get((main_name, args.deterministic), 0.0)
+    atomic = mode == 2 and wl.D == 128 and wl.kind != "selected"
+    share = KERNEL_FLOP_SHARE.get((main_name, not atomic), 0.0)
     main_us = kernels[main_name]["avg_us"]
     per_launch = flops * share * args.steps / kernels[main_name]["launches"]
     achieved = per_launch / (main_us * 1e-6) / 1e12
@@ -313,7 +317,7 @@ def main():
                "D": wl.D, "causal": wl.causal}
         if wl.kind == "selected":
             cfg.update(block_size=wl.block_size, block_count=wl.block_count)
-    cfg.update(deterministic=args.deterministic, counted_gflop=flops / 1e9)
+    cfg.update(dq_mode=mode, counted_gflop=flops / 1e9)
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,

@@ -128,10 +128,16 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
  * sdpa_backward node: inputs q, k, v, o, dO, stats, attn_scale,
  * use_causal_mask; outputs dQ, dK, dV; backward-graph cell).
  *   Shapes as sdpa_fwd_stats; dout, dq like q; dk, dv like k.
- *   deterministic = 0: dQ is accumulated with fp32 atomics (run-to-run
- *     rounding differences possible); 1: a separate dQ pass without atomics,
- *     bitwise reproducible (the Ascend page's deterministic option,
- *     "Constraints").
+ *   deterministic selects how dQ is formed (the Ascend page's deterministic
+ *     option, "Constraints", extended):
+ *     0: the library's fastest method; today that is the atomic-free query-
+ *        outer pass for every head size, so results are reproducible;
+ *     1: guaranteed bitwise reproducible: the atomic-free query-outer pass;
+ *     2: fp32 atomic accumulation inside the key-outer kernel and a final
+ *        conversion (FlashAttention-2's method; run-to-run rounding
+ *        differences possible); D=128 only, D=64 has no atomic kernel and
+ *        runs mode 1.
+ *     Any other value: SDPA_ERR_INVALID.  The workspace size depends on it.
  *   workspace: device memory of at least *bytes from the size query, any
  *     contents on entry, 256-byte aligned.
  */
@@ -154,6 +160,7 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
  * cu[-1] = 0.  Causal masking uses positions local to each sequence and
  * requires equal query and key lengths per sequence.
  *   q, o, dout, dq: (Tq, Hq, D); k, v, dk, dv: (Tk, Hkv, D); stats per (t, h).
+ *   deterministic: as for sdpa_bwd (0, 1 or 2).
  */
 int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
@@ -182,8 +189,8 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   Hq a multiple of Hkv with Hq / Hkv <= 32; at most 64 sequences.  Topk
  *   values outside the sequence's blocks select nothing (those slots are
  *   ignored); the statistics must then describe the same reduced key set.
- *   Every kernel of this path is deterministic; the flag is accepted for
- *   symmetry with the other entry points.
+ *   Every kernel of this path is deterministic; the flag (0, 1 or 2, else
+ *   SDPA_ERR_INVALID) is accepted for symmetry with the other entry points.
  */
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,

@@ -227,7 +227,13 @@ def fwd_stats(q, k, v, scale: float, causal: bool, o=None, lse=None):
 # Dense backward
 # ----------------------------------------------------------------------------
 
-def bwd_workspace_size(dtype: int, B, Hq, Hkv, Sq, Sk, D, deterministic: bool) -> int:
+# dQ modes (the `deterministic` argument of the backward entry points)
+DQ_FASTEST = 0          # the library's fastest method (atomic-free today)
+DQ_DETERMINISTIC = 1    # bitwise reproducible
+DQ_ATOMIC = 2           # fp32 atomic accumulation (D=128; D=64 runs mode 1)
+
+
+def bwd_workspace_size(dtype: int, B, Hq, Hkv, Sq, Sk, D, deterministic: int) -> int:
     n = c_size(0)
     _check(load().sdpa_bwd_workspace_size(dtype, B, Hq, Hkv, Sq, Sk, D, int(deterministic),
                                           ctypes.byref(n)), "sdpa_bwd_workspace_size")
@@ -251,7 +257,7 @@ def _stats_arg(stats, packed: bool) -> Stats:
     return Stats(kind, a, b, *ref.stride()[:3])
 
 
-def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool = False,
+def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
                 dq=None, dk=None, dv=None, workspace=None):
     """Marshal the arguments of one dense backward once; returns (call, (dq, dk, dv))
     where call() enqueues the backward on the current stream.  The tensors must
@@ -281,9 +287,11 @@ def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, determinist
     return call, (dq, dk, dv)
 
 
-def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: bool = False,
+def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
         dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV of dense attention.  stats: LSE (B, Hq, Sq[, 1]) or (max, sum)."""
+    """dQ, dK, dV of dense attention.  stats: LSE (B, Hq, Sq[, 1]) or (max, sum).
+    deterministic: DQ_FASTEST (0), DQ_DETERMINISTIC (1) or DQ_ATOMIC (2); a
+    bool is read as 0 or 1."""
     call, outs = prepare_bwd(q, k, v, o, dout, stats, scale, causal, deterministic, dq, dk, dv,
                              workspace)
     call()
@@ -309,7 +317,7 @@ def bwd_varlen_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, deterministic) -> 
 
 
 def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
-                   deterministic: bool = False, dq=None, dk=None, dv=None, workspace=None):
+                   deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None):
     """Marshal one packed (T, N, D) backward once; returns (call, (dq, dk, dv)).
     cu_q / cu_kv: host sequences of inclusive end offsets; stats: LSE (T, Hq)
     or a (max, sum) pair of (T, Hq[, 8]) tensors."""
@@ -340,7 +348,7 @@ def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: b
 
 
 def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
-               deterministic: bool = False, dq=None, dk=None, dv=None, workspace=None):
+               deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None):
     """Packed (T, N, D) backward; cu_q / cu_kv: host sequences of inclusive end
     offsets; stats: LSE (T, Hq) or a (max, sum) pair of (T, Hq[, 8]) tensors."""
     call, outs = prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale, causal, deterministic,
@@ -365,7 +373,7 @@ def bwd_selected_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, block_size, bloc
 
 
 def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
-                     sparse_mode: int, deterministic: bool = False, dq=None, dk=None, dv=None,
+                     sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
                      workspace=None):
     """Marshal one NSA selected-attention backward once; returns (call, (dq, dk, dv)).
     topk: int32 (T, Hkv, count) on the device."""
@@ -398,7 +406,7 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
 
 
 def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
-                 sparse_mode: int, deterministic: bool = False, dq=None, dk=None, dv=None,
+                 sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
                  workspace=None):
     """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device."""
     call, outs = prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size, scale,

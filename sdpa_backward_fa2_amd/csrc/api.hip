@@ -93,6 +93,13 @@ Carve carve_bwd(int64_t rows, int64_t D, bool deterministic) {
     return c;
 }
 
+// dQ mode of the dense and packed entry points: 0 = the library's fastest
+// method, 1 = bitwise reproducible, 2 = fp32 atomic accumulation (FA2's
+// method; D=128 only, other head sizes have no atomic kernel and run mode 1).
+// Every method the library picks today is the atomic-free one.
+bool dq_mode_ok(int mode) { return mode >= 0 && mode <= 2; }
+bool dq_atomic(int mode, int64_t D) { return mode == 2 && D == 128; }
+
 int check_stats(const sdpa_stats* s) {
     if (!s->lse_or_max) return SDPA_ERR_NULLPTR;
     if (s->kind == SDPA_STATS_MAX_SUM && !s->sum) return SDPA_ERR_NULLPTR;
@@ -205,8 +212,9 @@ int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
     if (!bytes) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
-    *bytes = carve_bwd(B * Hq * Sq, D, deterministic != 0).total;
+    *bytes = carve_bwd(B * Hq * Sq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
 
@@ -272,13 +280,14 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     if (Hq % Hkv) return SDPA_ERR_INVALID;
     if (causal && Sq != Sk) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor4_ok(t)) return s;
     if (Sq >= kMaxLen || Sk >= kMaxLen || (Sk + 127) / 128 > kMaxGridY || B * Hq > kMaxGridY)
         return SDPA_ERR_UNSUPPORTED;
-    const bool det = deterministic != 0;
+    const bool det = !dq_atomic(deterministic, D);
     const int64_t rows = B * Hq * Sq;
     const Carve cv = carve_bwd(rows, D, det);
     if (workspace_bytes < cv.total) return SDPA_ERR_WORKSPACE;
@@ -316,8 +325,9 @@ int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_s
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, false, P)) return s;
+    if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
-    *bytes = carve_bwd(P.Tq * Hq, D, deterministic != 0).total;
+    *bytes = carve_bwd(P.Tq * Hq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
 
@@ -337,6 +347,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, causal != 0, P)) return s;
@@ -344,7 +355,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;
     if (P.max_lk / 128 + 1 > kMaxGridY || Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
-    const bool det = deterministic != 0;
+    const bool det = !dq_atomic(deterministic, D);
     const int64_t rows = P.Tq * Hq;
     const Carve cv = carve_bwd(rows, D, det);
     if (workspace_bytes < cv.total) return SDPA_ERR_WORKSPACE;

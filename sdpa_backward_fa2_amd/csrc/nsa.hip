@@ -759,9 +759,9 @@ int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
                                      int64_t D, int64_t block_size, int64_t block_count,
                                      int deterministic, size_t* bytes) {
-    (void)deterministic;
     if (!bytes || !cu_seqlens_q_host || !cu_seqlens_kv_host) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (deterministic < 0 || deterministic > 2) return SDPA_ERR_INVALID;
     Seqs S;
     if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
                                block_count, 0, S))
@@ -795,7 +795,6 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
                       const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
                       const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
                       void* workspace, size_t workspace_bytes, void* stream) {
-    (void)deterministic;   // every kernel of this path is deterministic
     if (!cu_seqlens_q_host || !cu_seqlens_kv_host || !topk) return SDPA_ERR_NULLPTR;
     if (!q || !k || !v || !o || !dout || !stats || !dq || !dk || !dv) return SDPA_ERR_NULLPTR;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
@@ -804,6 +803,8 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (!workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    // every kernel of this path is deterministic, whatever dQ mode is asked for
+    if (deterministic < 0 || deterministic > 2) return SDPA_ERR_INVALID;
     if (stats->kind != SDPA_STATS_LSE && stats->kind != SDPA_STATS_MAX_SUM) return SDPA_ERR_INVALID;
     Seqs S;
     if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,

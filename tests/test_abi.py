@@ -60,6 +60,8 @@ def test_dense_validation_order():
     assert dense_call(B=-1) == INVALID
     assert dense_call(causal=1, Sk=64) == INVALID
     assert dense_call(scale=float("nan")) == INVALID
+    assert dense_call(det=3) == INVALID          # dQ mode outside 0..2
+    assert dense_call(det=-1) == INVALID
     assert dense_call(stats=sb.Stats(5, FAKE, None, 256, 128, 1)) == INVALID
     assert dense_call(D=96) == UNSUPPORTED
     assert dense_call(q=t4(strides=(16384, 8192, 64, 2))) == UNSUPPORTED
@@ -79,13 +81,20 @@ def test_valid_call_without_device_reports_hip_error():
 
 
 def test_workspace_size_query():
-    n = ctypes.c_size_t(0)
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, ctypes.byref(n)) == OK
     rows = 4 * 12 * 1024
-    assert n.value >= rows * 4 * 2 + rows * 64 * 4
+
+    def size(D, mode):
+        n = ctypes.c_size_t(0)
+        assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, D, mode, ctypes.byref(n)) == OK
+        return n.value
+    # atomic-free modes: LSE and Delta rows; the atomic mode (D=128 only) adds
+    # the fp32 dQ accumulator
+    for D in (64, 128):
+        assert size(D, 0) == size(D, 1) >= rows * 8
+    assert size(64, 2) == size(64, 1)
+    assert size(128, 2) >= size(128, 1) + rows * 128 * 4
     m = ctypes.c_size_t(0)
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 1, ctypes.byref(m)) == OK
-    assert rows * 8 <= m.value < n.value
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 3, ctypes.byref(m)) == INVALID
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 0, ctypes.byref(m)) == UNSUPPORTED
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, None) == NULLPTR
 
@@ -116,7 +125,10 @@ def test_varlen_validation():
     n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 2)(100, 300)
     assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 0, ctypes.byref(n)) == OK
-    assert n.value >= 300 * 32 * (8 + 128 * 4)
+    assert n.value >= 300 * 32 * 8                      # LSE and Delta per (token, head)
+    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 2, ctypes.byref(n)) == OK
+    assert n.value >= 300 * 32 * (8 + 128 * 4)         # plus the fp32 dQ accumulator
+    assert varlen_call([100, 300], [100, 300], det=5) == INVALID
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")

@@ -60,7 +60,7 @@ def _check_case(B, Hq, Hkv, Sq, Sk, D, dtype, causal, layout, seed=0, stats="gpu
         o = to_device(synth.encode(f["O"], dtype), dtype)
         lse = torch.tensor(f["lse"], dtype=torch.float32, device="cuda")
     g = oracle.dense_backward(qx, kx, vx, dox, scale, causal)
-    for det in (False, True):
+    for det in (0, 1, 2):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, scale, causal, det)
         for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
             assert_rel(to_f64(got), ref, dtype, f"{name} det={det}")
@@ -81,7 +81,7 @@ def test_config1_tiny_dense():
     o = to_device(synth.encode(f["O"], wl.dtype), wl.dtype)
     lse = torch.tensor(f["lse"][..., None], dtype=torch.float32, device="cuda")   # (B,H,S,1)
     g = oracle.dense_backward(qx, kx, vx, dox, wl.scale, wl.causal)
-    for det in (False, True):
+    for det in (0, 1, 2):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, det)
         for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
             assert_rel(to_f64(got), ref, wl.dtype, f"config1 {name} det={det}")
@@ -114,7 +114,7 @@ def test_config2_gpt2_shape():
     assert np.max(np.abs(to_f64(lse) - f["lse"])) <= STATS_ABS_TOL
     assert_rel(to_f64(o), f["O"], wl.dtype, "config2 O")
     g = oracle.dense_backward(qx, kx, vx, dox, wl.scale, wl.causal)
-    for det in (False, True):
+    for det in (0, 1, 2):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, det)
         for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
             assert_rel(to_f64(got), ref, wl.dtype, f"config2 {name} det={det}")
@@ -131,7 +131,7 @@ def test_config3_long_context_sampled_heads():
         assert np.max(np.abs(lse_np[b, h] - f["lse"])) <= STATS_ABS_TOL
         assert_rel(to_f64(o[b, h]), f["O"], wl.dtype, f"config3 O[{b},{h}]")
     g = oracle.dense_backward(qx, kx, vx, dox, wl.scale, wl.causal, heads=heads)
-    for det in (False, True):
+    for det in (0, 1, 2):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, det)
         for b, h in heads:
             for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
@@ -178,14 +178,19 @@ def test_oracle_stats_max_sum_form():
         assert_rel(to_f64(got), ref, "f16", name)
 
 
-def test_deterministic_is_bitwise_stable():
-    wl, (q, k, v, do, o, lse), _ = _gpu_stats_config(2)
-    a = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, True)
-    b = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, True)
-    for x, y in zip(a, b):
+@pytest.mark.parametrize("cid", [2, 3])
+def test_dq_modes(cid):
+    """Mode 1 is bitwise stable; mode 0 (fastest) is today the same atomic-free
+    pass, so bitwise equal to it; mode 2 (fp32 atomics, D=128) agrees within
+    the tolerance."""
+    wl, (q, k, v, do, o, lse), _ = _gpu_stats_config(cid)
+    a = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, 1)
+    b = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, 1)
+    f = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, 0)
+    for x, y, z in zip(a, b, f):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
-    # the atomic path agrees with the deterministic one within the tolerance
-    c = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, False)
+        assert torch.equal(x.view(torch.int16), z.view(torch.int16))
+    c = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, 2)
     for x, y in zip(a, c):
         e = float((x.float() - y.float()).abs().max() / x.float().abs().max())
-        assert e <= REL_TOL["f16"]
+        assert e <= REL_TOL[wl.dtype]

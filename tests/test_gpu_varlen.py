@@ -30,7 +30,7 @@ def _run(q, k, v, o, do, stats, cu_q, cu_k, scale, causal, det):
     return dq, dk, dv
 
 
-def _case(lq, lk, Hq, Hkv, D, dtype, causal, seed, stats_form="max_sum", dets=(False, True)):
+def _case(lq, lk, Hq, Hkv, D, dtype, causal, seed, stats_form="max_sum", dets=(0, 1, 2)):
     rng = np.random.default_rng(seed)
     cu_q, cu_k = np.cumsum(lq), np.cumsum(lk)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
@@ -79,7 +79,7 @@ def test_config4_packed_varlen_sampled():
     m = torch.tensor(m_np, dtype=torch.float32, device="cuda")
     l = torch.tensor(l_np, dtype=torch.float32, device="cuda")
     g = oracle.varlen_backward(qx, kx, vx, dox, cu, cu, wl.scale, wl.causal, seqs=seqs)
-    for det in (False, True):
+    for det in (0, 1, 2):
         dq, dk, dv = _run(q, k, v, o, do, (m, l), cu, cu, wl.scale, wl.causal, det)
         for s in seqs:
             sl = slice(int(starts[s]), int(cu[s]))
