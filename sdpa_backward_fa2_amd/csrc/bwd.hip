@@ -967,10 +967,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
 // descending order).  The dQ workgroups fill the CUs the long dK/dV
 // workgroups leave idle near the end.
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y,
+                                                                   int alternate) {
     constexpr int A = Main8Lds<D>::BYTES > Dq8Lds<D>::BYTES ? Main8Lds<D>::BYTES : Dq8Lds<D>::BYTES;
     __shared__ __align__(16) unsigned char arena[A];
     const int id = blockIdx.x;
+    if (alternate) {
+        // main_x == dq_y and main_y == dq_x: segment 2k is key tile k (k+1-th
+        // longest causal range), segment 2k+1 the query tile with as many key
+        // steps, so work items are dispatched roughly longest first
+        const int seg = id / main_x, within = id % main_x;
+        if (!(seg & 1)) bwd_main8_body<T, D, CAUSAL>(p, arena, within, seg >> 1);
+        else bwd_dq8_body<T, D, CAUSAL>(p, arena, dq_x - 1 - (seg >> 1), within);
+        return;
+    }
     const int n_main = main_x * main_y;
     if (id < n_main) {
         bwd_main8_body<T, D, CAUSAL>(p, arena, id % main_x, id / main_x);
@@ -995,8 +1005,15 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
         const int n = mx * my + qx * qy;
         if (n > 0)
-            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(kThreads), 0, st, p, mx, my, qx,
-                        qy);
+        {
+            // Causal with one query head per KV head: main key tile k has as many
+            // steps as query tile n-1-k has key steps, so the two kinds alternate
+            // in decreasing length; otherwise the key-tile items (the longer
+            // ones) go first.
+            const int alternate = (CAUSAL && mx == qy && my == qx) ? 1 : 0;
+            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(kThreads), 0, st, p, mx, my,
+                        qx, qy, alternate);
+        }
         return hipGetLastError();
     } else {
         const int64_t row_threads = p.rows * (D / 8);

@@ -37,9 +37,12 @@
 
 namespace sdpa {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 struct NsaParams {
     const int32_t* topk;
     int64_t tk_st, tk_sn, tk_sk;
+    int tk_vec4;          // slots contiguous, count % 4 == 0, 16-byte aligned rows
     int count, bs, N2, NB, G, Hq;
     int chunk;            // entries per work piece
     int max_pieces;
@@ -98,10 +101,69 @@ __global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
     const int gl = g - p.seqs.k0[s] / p.bs;      // block index within its sequence
     const int64_t e0 = (int64_t)p.seqs.q0[s] * p.count;
     const int64_t e1 = (int64_t)(p.seqs.q0[s] + p.seqs.lq[s]) * p.count;
+    const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    if (p.tk_vec4) {
+        // Four consecutive slots of one token per lane and 16-byte load (the
+        // slots of a token are contiguous and count is a multiple of 4); a
+        // wavefront's span is a multiple of 256 entries.
+        const int64_t span = ((e1 - e0 + 15) / 16 + 255) / 256 * 256;
+        const int64_t a = e0 + w * span;
+        const int64_t b = min(a + span, e1);
+        const int cnt4 = p.count / 4;
+        auto hits = [&](int64_t c) -> int {   // match bits of entries c .. c+3
+            if (c >= b) return 0;
+            const int64_t t = (int64_t)((uint32_t)(c >> 2) / (uint32_t)cnt4);
+            const int slot = (int)(c - t * p.count);
+            const i32x4 v = *reinterpret_cast<const i32x4*>(tk + t * p.tk_st + slot);
+            return (v[0] == gl) | ((v[1] == gl) << 1) | ((v[2] == gl) << 2) | ((v[3] == gl) << 3);
+        };
+        int n = 0;
+        for (int64_t c = a; c < b; c += 1024) {
+            int m[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m[u] = hits(c + 256 * u + 4 * lane);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) n += __popc(m[u]);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
+        if (lane == 0) wave_n[w] = n;
+        __syncthreads();
+        if (!FILL) {
+            if (tid == 0) {
+                int tot = 0;
+                for (int i = 0; i < 16; ++i) tot += wave_n[i];
+                p.counts[bucket] = tot;
+            }
+            return;
+        }
+        int base = p.offsets[bucket];
+        for (int i = 0; i < w; ++i) base += wave_n[i];
+        for (int64_t c = a; c < b; c += 1024) {
+            int m[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) m[u] = hits(c + 256 * u + 4 * lane);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                // exclusive prefix of the lanes' match counts from the bits of
+                // their 3-bit counts
+                const int k = __popc(m[u]);
+                const unsigned long long b0 = __ballot(k & 1), b1 = __ballot(k & 2), b2 = __ballot(k & 4);
+                int r = base + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
+                const int64_t e = c + 256 * u + 4 * lane;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (m[u] & (1 << q)) p.entries[r++] = (int32_t)(e + q);
+                base += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+            }
+        }
+        return;
+    }
+    // General strides: one entry per lane, eight chunks in flight.
     const int64_t span = ((e1 - e0 + 15) / 16 + 63) / 64 * 64;
     const int64_t a = e0 + w * span;
     const int64_t b = min(a + span, e1);
-    const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
     const double inv_count = 1.0 / p.count;
     auto match = [&](int64_t e) -> bool {
         if (e >= b) return false;
@@ -112,7 +174,6 @@ __global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
         const int64_t slot = e - t * p.count;
         return tk[t * p.tk_st + slot * p.tk_sk] == gl;
     };
-    // eight chunks per iteration so that their loads are in flight together
     int n = 0;
     for (int64_t c = a; c < b; c += 512) {
         bool m[8];
@@ -133,7 +194,6 @@ __global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
     }
     int base = p.offsets[bucket];
     for (int i = 0; i < w; ++i) base += wave_n[i];
-    const unsigned long long below = (1ull << lane) - 1ull;
     for (int64_t c = a; c < b; c += 512) {
         bool m[8];
 #pragma unroll
@@ -773,6 +833,8 @@ int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu
 static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout& L, char* ws, const int32_t* topk,
                               int64_t st, int64_t sn, int64_t sk, int64_t Hq, int64_t Hkv, int64_t bs, int64_t count) {
     p.topk = topk; p.tk_st = st; p.tk_sn = sn; p.tk_sk = sk;
+    p.tk_vec4 = (sk == 1 && count % 4 == 0 && st % 4 == 0 && sn % 4 == 0 &&
+                 reinterpret_cast<uintptr_t>(topk) % 16 == 0 && S.Tq * count < (int64_t(1) << 33)) ? 1 : 0;
     p.count = (int)count; p.bs = (int)bs; p.N2 = (int)Hkv; p.NB = (int)L.NB;
     p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
     p.chunk = (int)L.chunk; p.max_pieces = (int)L.max_pieces;
