@@ -290,6 +290,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     __shared__ __align__(16) float lse_s[2][BR];
     __shared__ __align__(16) float dlt_s[2][BR];
     __shared__ int tl_s[2][BR];          // sequence-local token position of each row
+    __shared__ int tok_s[2048];          // token of each entry of the piece (<= 2048 / G entries)
     typedef uint16_t Tile[BR * QP];
     Tile* Qs = reinterpret_cast<Tile*>(arena);
     Tile* dOs = reinterpret_cast<Tile*>(arena + 2 * BR * QP * 2);
@@ -331,38 +332,39 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     const int n_steps = (ee - eb + E - 1) / E;
     const int q0s = p.seqs.q0[s_idx];
 
+    // The tokens of the piece's entries go to LDS once, so that a step's
+    // row addresses need no dependent global load.
+    const int n_e = ee - eb;                    // >= 1: pieces are never empty
+    for (int i = tid; i < n_e; i += 256) tok_s[i] = p.entries[eb + i] / p.count;
+    __syncthreads();
+
+    // Row r of step st is head r % G of entry st*E + r/G.  Loads are
+    // unconditional: padding rows re-read the piece's last entry and are
+    // given LSE = +inf when stored, so their P is exactly zero; nothing loaded
+    // is used before store_tile.
     u32x4 pq[CH], pdo[CH];
     float pl = INFINITY, pd = 0.f;
     int ptl = 0;
+    bool pok = false;
     auto load_tile = [&](int st) {
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
             const int e = tid + 256 * x;
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            const int ei = eb + st * E + r / p.G;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            pq[x] = z;
-            pdo[x] = z;
-            if (r < E * p.G && ei < ee) {
-                const int t = p.entries[ei] / p.count;
-                const int h = h2 * p.G + r % p.G;
-                pq[x] = ld16(p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh + cc);
-                pdo[x] = ld16(p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh + cc);
-            }
+            const int t = tok_s[min(st * E + r / p.G, n_e - 1)];
+            const int h = h2 * p.G + r % p.G;
+            pq[x] = ld16(p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh + cc);
+            pdo[x] = ld16(p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh + cc);
         }
-        if (tid < BR) {
-            const int r = tid;
-            const int ei = eb + st * E + r / p.G;
-            pl = INFINITY;
-            pd = 0.f;
-            ptl = 0;
-            if (r < E * p.G && ei < ee) {
-                const int t = p.entries[ei] / p.count;
-                const int h = h2 * p.G + r % p.G;
-                pl = p.lse2[(int64_t)t * p.Hq + h];
-                pd = p.delta[(int64_t)t * p.Hq + h];
-                ptl = t - q0s;
-            }
+        {
+            const int r = tid & (BR - 1);
+            const int li = st * E + r / p.G;
+            const int t = tok_s[min(li, n_e - 1)];
+            const int h = h2 * p.G + r % p.G;
+            pl = p.lse2[(int64_t)t * p.Hq + h];
+            pd = p.delta[(int64_t)t * p.Hq + h];
+            ptl = t - q0s;
+            pok = r < E * p.G && li < n_e;
         }
     };
     auto store_tile = [&](int buf) {
@@ -374,8 +376,8 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             st16(&dOs[buf][r * QP + cc], pdo[x]);
         }
         if (tid < BR) {
-            lse_s[buf][tid] = pl;
-            dlt_s[buf][tid] = pd;
+            lse_s[buf][tid] = pok ? pl : INFINITY;
+            dlt_s[buf][tid] = pok ? pd : 0.f;
             tl_s[buf][tid] = ptl;
         }
     };
@@ -384,6 +386,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
         load_tile(0);
         store_tile(0);
     }
+    wait_all_memory();
     __syncthreads();
     const int my_kpos = kpos0 + myk;
     for (int st = 0; st < n_steps; ++st) {
@@ -545,6 +548,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     __shared__ __align__(16) uint16_t Ks[BK * KP];
     __shared__ __align__(16) uint16_t Vs[BK * KP];
     __shared__ int kpos_s[BK];
+    __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
 
     const int t = blockIdx.x;
     const int h2 = blockIdx.y / ((p.G + 15) / 16);
@@ -576,38 +580,68 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero4();
 
+    // The token's chosen blocks go to LDS once (as first packed key rows, or
+    // -1 for a choice outside the sequence), so chunk addresses need no
+    // dependent global load.  Each chunk's K/V rows are loaded into registers
+    // while the previous chunk is being used; loads are unconditional (rows of
+    // an ignored choice or past the gathered keys re-read key row krow0 and
+    // are masked through kpos).
     const int nk = p.count * p.bs;
     const int32_t* tk = p.topk + (int64_t)t * p.tk_st + (int64_t)h2 * p.tk_sn;
+    for (int i = tid; i < p.count; i += 256) {
+        const int blk = tk[(int64_t)i * p.tk_sk];
+        blk_s[i] = (blk >= 0 && blk < nblk) ? blk : -1;
+    }
+    __syncthreads();
+    u32x4 kv[CH], vv[CH];
+    int kpos_r = 0x7fffffff;
+    // slot and row-in-block of gathered key n: when block_size divides the
+    // chunk, chunk c0 starts at slot c0 / block_size and a row's part of that
+    // is fixed, so the divisions are done once
+    const bool bs_divides = BK % p.bs == 0;
+    int rq[CH], rr[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int r = (tid + 256 * x) / (D / 8);
+        rq[x] = r / p.bs;
+        rr[x] = r % p.bs;
+    }
+    const int rq_k = (tid & (BK - 1)) / p.bs, rr_k = (tid & (BK - 1)) % p.bs;
+    auto load_chunk = [&](int c0) {
+        const int cs = bs_divides ? c0 / p.bs : 0;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            int slot, rb;
+            if (bs_divides) { slot = cs + rq[x]; rb = rr[x]; }
+            else { const int n = c0 + r; slot = n / p.bs; rb = n % p.bs; }
+            const int blk = blk_s[min(slot, p.count - 1)];
+            const bool ok = c0 + r < nk && blk >= 0;
+            const int64_t row = (int64_t)krow0 + (ok ? (int64_t)blk * p.bs + rb : 0);
+            kv[x] = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
+            vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+        }
+        const int n = c0 + (tid & (BK - 1));
+        int slot, rb;
+        if (bs_divides) { slot = cs + rq_k; rb = rr_k; }
+        else { slot = n / p.bs; rb = n % p.bs; }
+        const int blk = blk_s[min(slot, p.count - 1)];
+        kpos_r = (n < nk && blk >= 0) ? blk * p.bs + rb : 0x7fffffff;   // masked: no key there
+    };
+    load_chunk(0);
     for (int c0 = 0; c0 < nk; c0 += BK) {
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
             const int e = tid + 256 * x;
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            const int n = c0 + r;
-            u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (n < nk) {
-                const int slot = n / p.bs, rr = n % p.bs;
-                const int blk = tk[(int64_t)slot * p.tk_sk];
-                if (blk >= 0 && blk < nblk) {     // out-of-range choices are ignored
-                    const int64_t row = (int64_t)krow0 + (int64_t)blk * p.bs + rr;
-                    kv = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
-                    vv = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
-                }
-            }
-            st16(&Ks[r * KP + cc], kv);
-            st16(&Vs[r * KP + cc], vv);
+            st16(&Ks[r * KP + cc], kv[x]);
+            st16(&Vs[r * KP + cc], vv[x]);
         }
-        if (tid < BK) {
-            const int n = c0 + tid;
-            int kpos = 0x7fffffff;                  // masked: beyond the gathered keys
-            if (n < nk) {
-                const int blk = tk[(int64_t)(n / p.bs) * p.tk_sk];
-                if (blk >= 0 && blk < nblk) kpos = blk * p.bs + n % p.bs;
-            }
-            kpos_s[tid] = kpos;
-        }
+        if (tid < BK) kpos_s[tid] = kpos_r;
         __syncthreads();
+        if (c0 + BK < nk) load_chunk(c0 + BK);
         f32x4 s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {

@@ -39,7 +39,7 @@ def test_index_config5_exact():
 
 
 @pytest.mark.parametrize("lengths,N2,bs,count", [((64, 128, 48), 2, 16, 3), ((256, 512), 1, 64, 4),
-                                                  ((384,), 3, 128, 2)])
+                                                  ((384,), 3, 128, 2), ((384, 480), 2, 48, 8)])
 def test_index_small_exact(lengths, N2, bs, count):
     topk = synth.draw_topk(np.array(lengths), N2, bs, count, config_id=21)
     # scatter some duplicates and a fully repeated row
@@ -93,6 +93,7 @@ def test_config5_nsa_selected():
     ((96, 160, 80), 4, 1, 16, 5),
     ((512,), 1, 1, 128, 3),
     ((384, 192), 16, 1, 64, 3),
+    ((96, 192), 2, 1, 48, 2),      # block size that does not divide a 128-key chunk
 ])
 def test_selected_small(dtype, D, mode, lengths, G, N2, bs, count):
     rng = np.random.default_rng(len(lengths) * 100 + G * 10 + bs + D + mode)
