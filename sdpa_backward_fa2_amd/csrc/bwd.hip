@@ -146,33 +146,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
 // and so contribute P = 0 without a mask.
 
 // P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - Delta) for one 32x32
-// C tile held as (sa, pa); rows i = i_base + 8q + 4g + r, this lane's key my_j.
-template <bool MASKED, bool CAUSAL>
-__device__ __forceinline__ void softmax_grad_tile(f32x16& sa, f32x16& pa, const float* lse_row,
-                                                  const float* dlt_row, float scale_log2, int g,
-                                                  int i_base, int my_j, bool col_ok) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
-        const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_row[8 * q + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rg = 4 * q + r;
-            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
-            if (MASKED) {
-                // branch-free: keep = key valid and (not causal or key <= row)
-                const int i = i_base + 8 * q + 4 * g + r;
-                const bool keep = col_ok & (!CAUSAL | (my_j <= i));
-                pv = keep ? pv : 0.f;
-            }
-            sa[rg] = pv;
-            pa[rg] = pv * (pa[rg] - Dr[r]);
-        }
-    }
-}
-
-// The same for a tile whose dP accumulator started from -Delta (pa already
-// holds dP - Delta).  Element (q, r) is kept when 8q + r >= t, with t the first
+// C tile held as (sa, pa), whose dP accumulator started from -Delta (pa
+// already holds dP - Delta); rows 8q + 4g + r of the tile, this lane's key.  Element (q, r) is kept when 8q + r >= t, with t the first
 // kept row offset of this lane's key (INT_MAX for a key past the end).
 template <bool MASKED>
 __device__ __forceinline__ void softmax_grad_tile_nd(f32x16& sa, f32x16& pa, const float* lse_row,
@@ -304,7 +279,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         if (tid < BR) {
             const bool ok = pi0 + tid < lq;     // a row past the end has P = 0
             lse_s[buf][tid] = ok ? pl : INFINITY;
-            dlt_s[buf][tid] = ok ? pd : 0.f;
+            dlt_s[buf][tid] = ok ? -pd : 0.f;       // stored negated: it seeds dP - Delta
         }
     };
 
@@ -314,6 +289,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     }
     wait_all_memory();
     __syncthreads();
+
+    // first kept row offset of this lane's key within a 32-row half, before
+    // the 8q+4g part: key my_j needs row >= my_j; a key past the end keeps nothing
+    const int t_key = col_ok ? (CAUSAL ? my_j - 4 * g : INT_MIN / 2) : INT_MAX / 2;
 
     for (int st = 0; st < n_steps; ++st) {
         const int buf = st & 1;
@@ -328,18 +307,23 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         // one 32-row half of the query tile at a time keeps S and dP at 32 registers
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-            f32x16 sa = zero16(), pa = zero16();
+            // dP^T accumulates onto the rows' -Delta: pa ends as dP - Delta
+            f32x16 sa = zero16(), pa;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+            }
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 sa = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
                 pa = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
             }
             if (masked)
-                softmax_grad_tile<true, CAUSAL>(sa, pa, &lse_s[buf][mb * 32], &dlt_s[buf][mb * 32],
-                                                p.scale_log2, g, i0 + mb * 32, my_j, col_ok);
+                softmax_grad_tile_nd<true>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
             else
-                softmax_grad_tile<false, CAUSAL>(sa, pa, &lse_s[buf][mb * 32], &dlt_s[buf][mb * 32],
-                                                 p.scale_log2, g, i0 + mb * 32, my_j, col_ok);
+                softmax_grad_tile_nd<false>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, 0);
             if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
