@@ -158,10 +158,11 @@ def test_sweep_rectangular_noncausal(Sq, Sk):
     _check_case(1, 3, 3, Sq, Sk, 64, "f16", False, "bhsd", seed=Sq * Sk)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_gqa(Hq, Hkv, causal):
-    _check_case(2, Hq, Hkv, 160, 160, 128, "bf16", causal, "bshd", seed=Hq)
+def test_gqa(Hq, Hkv, causal, D):
+    _check_case(2, Hq, Hkv, 160, 160, D, "bf16", causal, "bshd", seed=Hq + D)
 
 
 def test_oracle_stats_max_sum_form():

@@ -105,9 +105,10 @@ def test_zero_length_query_sequence_zeroes_its_keys():
     _case([50, 0, 70], [50, 90, 70], 2, 2, 64, "bf16", False, seed=6)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (16, 1)])
-def test_gqa(Hq, Hkv):
-    _case([130, 257], [130, 257], Hq, Hkv, 128, "bf16", True, seed=Hq)
+def test_gqa(Hq, Hkv, D):
+    _case([130, 257], [130, 257], Hq, Hkv, D, "bf16", True, seed=Hq + D)
 
 
 @pytest.mark.parametrize("form", ["lse", "t_n_8"])
