@@ -36,13 +36,16 @@ METRIC = "SDPA-backward TFLOP/s on 1 MI355X (GPT-2 shape, causal); % of MFMA pea
 PEAK_MFMA_16BIT_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dense fp16/bf16
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f)
-                  for f in ("common.h", "bwd.hip", "nsa.hip")]
+def kernel_sources(kernel: str) -> list:
+    """The source files a kernel is built from (NSA kernels also use the
+    dense preprocess)."""
+    files = ("common.h", "bwd.hip", "nsa.hip") if kernel.startswith("nsa") else ("common.h", "bwd.hip")
+    return [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f) for f in files]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str = "bwd_fused8_kernel") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(kernel):
         if os.path.exists(f):
             with open(f, "rb") as fh:
                 h.update(fh.read())
@@ -249,7 +252,7 @@ def traffic_for(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     e = rec.get(kernel, {}).get(workload)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
