@@ -278,7 +278,11 @@ __global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
-    constexpr int BR = 64;
+    // rows per step: 128 at D=128 (each wavefront takes two 32-row blocks of
+    // its 64-row half, so a step's barrier and loads cover twice the
+    // products), 64 at D=64 (two workgroups per CU)
+    constexpr int BR = D == 128 ? 128 : 64;
+    constexpr int NSB = BR / 64;               // 32-row blocks per wavefront and step
     constexpr int KS = D / 16;
     constexpr int DB = D / 32;
     constexpr int QP = D + 8;
@@ -395,36 +399,40 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
         if (has_next) load_tile(st + 1);
         const uint16_t* Qb = Qs[buf];
         const uint16_t* dOb = dOs[buf];
-        f32x16 sa = zero16(), pa = zero16();
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            sa = T::mma(ld16(&Qb[(32 * rh + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
-            pa = T::mma(ld16(&dOb[(32 * rh + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
-        }
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int r0 = (BR / 2) * rh + 32 * sb;     // first row of this 32-row block
+            f32x16 sa = zero16(), pa = zero16();
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rb = 32 * rh + 8 * q + 4 * g;
-            const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[buf][rb]);
-            const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_s[buf][rb]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rg = 4 * q + r;
-                float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
-                const bool masked = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
-                pv = masked ? 0.f : pv;
-                sa[rg] = pv;
-                pa[rg] = pv * (pa[rg] - Dr[r]);
+            for (int s = 0; s < KS; ++s) {
+                sa = T::mma(ld16(&Qb[(r0 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
+                pa = T::mma(ld16(&dOb[(r0 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
             }
-        }
-        if (has_next) store_tile(buf ^ 1);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 bP = acc_to_operand<T>(sa, hh);
-            const u32x4 bS = acc_to_operand<T>(pa, hh);
+            for (int q = 0; q < 4; ++q) {
+                const int rb = r0 + 8 * q + 4 * g;
+                const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[buf][rb]);
+                const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_s[buf][rb]);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP, dva[db]);
-                dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS, dka[db]);
+                for (int r = 0; r < 4; ++r) {
+                    const int rg = 4 * q + r;
+                    float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
+                    const bool masked = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
+                    pv = masked ? 0.f : pv;
+                    sa[rg] = pv;
+                    pa[rg] = pv * (pa[rg] - Dr[r]);
+                }
+            }
+            if (sb == NSB - 1 && has_next) store_tile(buf ^ 1);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 bP = acc_to_operand<T>(sa, hh);
+                const u32x4 bS = acc_to_operand<T>(pa, hh);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dva[db] = T::mma(ld_tr<true>(dOb, QP, r0 + 16 * hh, db * 32, lane), bP, dva[db]);
+                    dka[db] = T::mma(ld_tr<true>(Qb, QP, r0 + 16 * hh, db * 32, lane), bS, dka[db]);
+                }
             }
         }
         __syncthreads();
