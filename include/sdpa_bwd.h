@@ -24,7 +24,9 @@
  *   physical / BHSD logical strides (S*H*D, D, H*D, 1).  Packed tensors are
  *   (T, N, D) ("TND", the Ascend page's only layout).  The last (D) stride must
  *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
- *   keep every row 16-byte aligned.  D is 64 or 128.
+ *   keep every row 16-byte aligned.  The row stride (S or T) of every tensor
+ *   and of the statistics must lie in [0, 2^23) elements.  D is 64 or 128.
+ *   Any other layout returns SDPA_ERR_UNSUPPORTED.
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library allocates no device memory, keeps no per-call state and never
  *   synchronises: kernels are enqueued on `stream` (a hipStream_t; NULL is the

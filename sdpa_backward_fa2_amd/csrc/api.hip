@@ -58,6 +58,7 @@ int tensor4_ok(const sdpa_tensor4* t) {
     if (t->stride_d != 1) return SDPA_ERR_UNSUPPORTED;
     if (!aligned16(t->data)) return SDPA_ERR_UNSUPPORTED;
     if ((t->stride_b % 8) || (t->stride_h % 8) || (t->stride_s % 8)) return SDPA_ERR_UNSUPPORTED;
+    if (!sdpa::row_stride_ok(t->stride_s)) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
 }
 
@@ -65,6 +66,7 @@ int tensor3_ok(const sdpa_tensor3* t) {
     if (t->stride_d != 1) return SDPA_ERR_UNSUPPORTED;
     if (!aligned16(t->data)) return SDPA_ERR_UNSUPPORTED;
     if ((t->stride_t % 8) || (t->stride_n % 8)) return SDPA_ERR_UNSUPPORTED;
+    if (!sdpa::row_stride_ok(t->stride_t)) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
 }
 
@@ -109,6 +111,10 @@ int check_stats(const sdpa_stats* s) {
 int check_stats_kind(const sdpa_stats* s) {
     if (s->kind != SDPA_STATS_LSE && s->kind != SDPA_STATS_MAX_SUM) return SDPA_ERR_INVALID;
     return SDPA_OK;
+}
+
+int check_stats_stride(const sdpa_stats* s) {
+    return sdpa::row_stride_ok(s->stride_s) ? SDPA_OK : SDPA_ERR_UNSUPPORTED;
 }
 
 void fill_stats(sdpa::BwdParams& p, const sdpa_stats* s) {
@@ -285,6 +291,7 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor4_ok(t)) return s;
+    if (int s = check_stats_stride(stats)) return s;
     if (Sq >= kMaxLen || Sk >= kMaxLen || (Sk + 127) / 128 > kMaxGridY || B * Hq > kMaxGridY)
         return SDPA_ERR_UNSUPPORTED;
     const bool det = !dq_atomic(deterministic, D);
@@ -354,6 +361,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;
+    if (int s = check_stats_stride(stats)) return s;
     if (P.max_lk / 128 + 1 > kMaxGridY || Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
     const bool det = !dq_atomic(deterministic, D);
     const int64_t rows = P.Tq * Hq;

@@ -401,12 +401,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV body, eight wavefronts (two per SIMD), software-pipelined
+// dK/dV body, four wavefronts (two workgroups per CU), software-pipelined
 // ---------------------------------------------------------------------------
 //
-// Work item: 128 keys of one KV head against every 64-row query tile of every
+// Work item: 64 keys of one KV head against every 64-row query tile of every
 // query head of its group (causal: from the tile holding the diagonal on).
-// Wavefront w = kw + 4*rh owns keys 32*kw .. +31 and rows 32*rh .. +31 of each
+// Wavefront w = kw + 2*rh owns keys 32*kw .. +31 and rows 32*rh .. +31 of each
 // tile; K and V of its keys stay in registers and dK^T, dV^T accumulate in
 // registers across all tiles.  Step k runs the softmax gradient of tile k
 // (vector ALU) next to S^T and dP^T of tile k+1 (matrix cores, independent of
@@ -478,16 +478,20 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
     const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
     const int n_steps = G * per_head;
 
-    int qoff[CH], dooff[CH], ooff[CH], crow[CH], ccol[CH];
+    // byte offsets of this thread's chunks within a tile (row strides are
+    // below 2^23 elements, so 128 rows fit in 32 bits)
+    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss, oss = 2u * (uint32_t)p.o.ss;
+    uint32_t qoff[CH], dooff[CH], ooff[CH];
+    int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + kThreads * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
         ccol[x] = cc;
-        qoff[x] = r * (int)p.q.ss + cc;
-        dooff[x] = r * (int)p.dout.ss + cc;
-        ooff[x] = r * (int)p.o.ss + cc;
+        qoff[x] = r * qss + 2 * cc;
+        dooff[x] = r * doss + 2 * cc;
+        ooff[x] = r * oss + 2 * cc;
     }
 
     // Pointers of the tile being loaded (head ld_h, rows from ld_i0), advanced
@@ -527,9 +531,10 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
     // Nothing loaded is used before the tile is stored.
     struct TileRegs { u32x4 q[CH], d[CH], o[CH]; float sa, sb; };
     const int srow = tid & (BR - 1);
-    const int srow_off = srow * (int)p.st_ss;
+    const uint32_t sss = 4u * (uint32_t)p.st_ss;
+    const uint32_t srow_off = srow * sss;
     auto load_tile = [&](TileRegs& t) {
-        int oq[CH], odo[CH], oo[CH], so = srow_off;
+        uint32_t oq[CH], odo[CH], oo[CH], so = srow_off;
         if (ld_i0 + BR <= lq) {
 #pragma unroll
             for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; oo[x] = ooff[x]; }
@@ -537,21 +542,21 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
             const int last = lq - 1 - ld_i0;
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
-                const int r = min(crow[x], last);
-                oq[x] = r * (int)p.q.ss + ccol[x];
-                odo[x] = r * (int)p.dout.ss + ccol[x];
-                oo[x] = r * (int)p.o.ss + ccol[x];
+                const uint32_t r = min(crow[x], last);
+                oq[x] = r * qss + 2 * ccol[x];
+                odo[x] = r * doss + 2 * ccol[x];
+                oo[x] = r * oss + 2 * ccol[x];
             }
-            so = min(srow, last) * (int)p.st_ss;
+            so = (uint32_t)min(srow, last) * sss;
         }
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            t.q[x] = ld16(ld_q + oq[x]);
-            t.d[x] = ld16(ld_do + odo[x]);
-            t.o[x] = ld16(ld_o + oo[x]);
+            t.q[x] = ld16_at(ld_q, oq[x]);
+            t.d[x] = ld16_at(ld_do, odo[x]);
+            t.o[x] = ld16_at(ld_o, oo[x]);
         }
-        t.sa = ld_sa[so];
-        t.sb = ld_sb[so];
+        t.sa = ldf_at(ld_sa, so);
+        t.sb = ldf_at(ld_sb, so);
     };
     auto store_tile = [&](const TileRegs& t, int buf, int i0) {
         uint16_t* Qd = Qs0 + buf * TILE;
@@ -714,19 +719,19 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass without atomics, eight wavefronts (query-tile outer)
+// dQ pass without atomics, four wavefronts (query-tile outer)
 // ---------------------------------------------------------------------------
 //
 // One workgroup per (sequence, query head, 64-row query tile); it walks the
-// 128-key tiles the tile can see.  Wavefront w = kw + 4*rh owns query rows
+// 64-key tiles the tile can see.  Wavefront w = kw + 2*rh owns query rows
 // 32*rh .. +31 and keys 32*kw .. +31 of every key tile.  Scores are computed
 // transposed, S^T = K Q^T and dP^T = V dO^T, so that each lane holds one query
 // column: its LSE and Delta are lane-uniform, and dS^T feeds
 // dQ^T += K^T dS^T directly as the B operand.  Q and dO stay in registers for
 // the whole kernel; key tiles stream through a double-buffered LDS copy whose
 // next tile is loaded into registers while the current one is used.  Each
-// wavefront accumulates dQ^T over its key slices; the four slices are summed
-// through LDS at the end and dQ is written once, scaled and rounded.
+// wavefront accumulates dQ^T over its key slice; the two slices' partials are
+// summed through LDS at the end and dQ is written once, scaled and rounded.
 
 template <int D>
 struct Dq8Lds {
@@ -772,15 +777,18 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
     const int n_steps = (kend + BK - 1) / BK;
 
-    int koff[CH], voff[CH], crow[CH], ccol[CH];
+    // byte offsets of this thread's chunks within a key tile
+    const uint32_t kss = 2u * (uint32_t)p.k.ss, vss = 2u * (uint32_t)p.v.ss;
+    uint32_t koff[CH], voff[CH];
+    int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + kThreads * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
         ccol[x] = cc;
-        koff[x] = r * (int)p.k.ss + cc;
-        voff[x] = r * (int)p.v.ss + cc;
+        koff[x] = r * kss + 2 * cc;
+        voff[x] = r * vss + 2 * cc;
     }
     // Unconditional loads: keys past the end of the sequence re-read its last
     // key and are masked out (P = 0), so nothing is waited for before the tile
@@ -791,7 +799,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
     auto load_tile = [&](int st) {
         const int j0 = st * BK;
-        int ok_[CH], ov_[CH];
+        uint32_t ok_[CH], ov_[CH];
         if (j0 + BK <= lk) {
 #pragma unroll
             for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
@@ -799,15 +807,15 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
             const int last = lk - 1 - j0;
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
-                const int r = min(crow[x], last);
-                ok_[x] = r * (int)p.k.ss + ccol[x];
-                ov_[x] = r * (int)p.v.ss + ccol[x];
+                const uint32_t r = min(crow[x], last);
+                ok_[x] = r * kss + 2 * ccol[x];
+                ov_[x] = r * vss + 2 * ccol[x];
             }
         }
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            pk[x] = ld16(kb + ok_[x]);
-            pv[x] = ld16(vb + ov_[x]);
+            pk[x] = ld16_at(kb, ok_[x]);
+            pv[x] = ld16_at(vb, ov_[x]);
         }
         kb += k_step;
         vb += v_step;
@@ -904,7 +912,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         __syncthreads();
     }
 
-    // sum the four key slices through LDS (slices 1..3 write, slice 0 adds)
+    // sum the key slices through LDS (slices 1..3 write, slice 0 adds)
     float* red = reinterpret_cast<float*>(arena);
     if (kw != 0) {
 #pragma unroll

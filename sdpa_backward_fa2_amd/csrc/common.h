@@ -115,6 +115,15 @@ __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+// Loads at an unsigned 32-bit byte offset from a base every lane shares: they
+// take the scalar-base + vector-offset addressing form, with no 64-bit
+// address arithmetic per lane.
+__device__ __forceinline__ u32x4 ld16_at(const void* base, uint32_t off) {
+    return *reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(base) + off);
+}
+__device__ __forceinline__ float ldf_at(const float* base, uint32_t off) {
+    return *reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(base) + off);
+}
 __device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
 __device__ __forceinline__ uint16_t elem16(u32x4 v, int t) {

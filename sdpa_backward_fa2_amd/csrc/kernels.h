@@ -7,6 +7,12 @@
 
 namespace sdpa {
 
+// Kernels address the rows of one tile (at most 128) as 32-bit byte offsets
+// from the tile's first row, so a row (sequence or token) stride must lie in
+// [0, 2^23) elements; the host entry points reject other strides.
+constexpr int64_t kMaxRowStride = (int64_t)1 << 23;
+inline bool row_stride_ok(int64_t s) { return s >= 0 && s < kMaxRowStride; }
+
 struct BwdLaunch {
     int dtype;            // 0 fp16, 1 bf16
     int D;                // 64 or 128

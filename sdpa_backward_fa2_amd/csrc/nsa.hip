@@ -846,6 +846,7 @@ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int t3_ok(const sdpa_tensor3* t) {
     if (t->stride_d != 1 || !a16(t->data) || (t->stride_t % 8) || (t->stride_n % 8)) return SDPA_ERR_UNSUPPORTED;
+    if (!sdpa::row_stride_ok(t->stride_t)) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
 }
 
@@ -916,6 +917,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
         return s;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = t3_ok(t)) return s;
+    if (!sdpa::row_stride_ok(stats->stride_s)) return SDPA_ERR_UNSUPPORTED;
     const NsaLayout L = nsa_layout(S, Hq, Hkv, D, block_size, block_count);
     if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
     if (int s = device_ok()) return s;

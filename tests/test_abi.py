@@ -67,6 +67,9 @@ def test_dense_validation_order():
     assert dense_call(q=t4(strides=(16384, 8192, 64, 2))) == UNSUPPORTED
     assert dense_call(k=t4(ptr=FAKE + 2)) == UNSUPPORTED
     assert dense_call(v=t4(strides=(16384, 8192, 68, 1))) == UNSUPPORTED
+    assert dense_call(q=t4(strides=(16384, 8192, -64, 1))) == UNSUPPORTED     # row stride < 0
+    assert dense_call(dq=t4(strides=(1 << 40, 1 << 30, 1 << 23, 1))) == UNSUPPORTED
+    assert dense_call(stats=sb.Stats(0, FAKE, None, 256, 128, 1 << 23)) == UNSUPPORTED
     assert dense_call(ws_bytes=16) == WORKSPACE
     # NULL beats INVALID beats UNSUPPORTED beats WORKSPACE
     assert dense_call(q=None, dtype=7) == NULLPTR
@@ -129,6 +132,14 @@ def test_varlen_validation():
     assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 2, ctypes.byref(n)) == OK
     assert n.value >= 300 * 32 * (8 + 128 * 4)         # plus the fp32 dQ accumulator
     assert varlen_call([100, 300], [100, 300], det=5) == INVALID
+    big = sb.Tensor3(FAKE, 1 << 23, 128, 1)                          # token stride 2^23
+    cu = (ctypes.c_int64 * 2)(100, 300)
+    st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
+    ts = [t3() for _ in range(8)]
+    ts[2] = big
+    assert lib().sdpa_bwd_varlen(1, 2, cu, cu, 32, 32, 128, 0.088, 1, 0,
+                                 *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
+                                 *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None) == UNSUPPORTED
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
