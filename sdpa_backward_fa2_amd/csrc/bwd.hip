@@ -1,16 +1,15 @@
 // SDPA backward, FlashAttention-2 style, for gfx950.
 //
 // Kernels (all on the caller's stream):
-//   bwd_fused8_kernel  D=64: one launch of eight-wavefront workgroups; the
-//                      first ones run the key-tile outer body (dK, dV of 128
-//                      keys over every query tile of every query head of the
-//                      group), the rest the query-tile outer body (dQ of 64
-//                      rows over the key tiles they see).  Both read O and the
-//                      caller's statistics themselves; no atomics, no
-//                      workspace traffic.                               [MFMA]
-//   bwd_pre_kernel     D=128, per row: Delta = sum_d dO*O, the statistics as
-//                      log2-domain LSE, and (atomic mode) the fp32 dQ
+//   bwd_pre_kernel     per row: Delta = sum_d dO*O, the statistics as
+//                      log2-domain LSE, and (D=128 atomic mode) the fp32 dQ
 //                      accumulator row cleared.                   [HBM-bound]
+//   bwd_fused8_kernel  D=64: one launch of four-wavefront workgroups, two per
+//                      CU; the first ones run the key-tile outer body (dK, dV
+//                      of 64 keys over every query tile of every query head
+//                      of the group), the rest the query-tile outer body (dQ
+//                      of 64 rows over the key tiles they see).  No atomics.
+//                                                                       [MFMA]
 //   bwd_main_kernel    D=128: one four-wavefront workgroup per (sequence, KV
 //                      head, 128-key tile); dK and dV accumulate in registers
 //                      across every query tile of every query head of the
@@ -57,9 +56,6 @@ __device__ __forceinline__ float stats_to_lse2(int kind, float a, float b) {
     if (kind == 0) return (a == -INFINITY) ? INFINITY : a * kLog2e;
     return (b > 0.f) ? a * kLog2e + log2f(b) : INFINITY;
 }
-__device__ __forceinline__ float stats_lse2(const BwdParams& p, int64_t so) {
-    return stats_to_lse2(p.stats_kind, p.st_a[so], p.stats_kind ? p.st_b[so] : 0.f);
-}
 
 template <class T>
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc = 0.f) {
@@ -82,42 +78,36 @@ __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
 // Preprocess
 // ---------------------------------------------------------------------------
 
+// Grid: x = chunks of kPreRows rows, y = (batch, head) when dense, head when
+// packed (rows are then tokens); D/16 lanes per row, 16 elements each.
+template <int D>
+constexpr int pre_rows_per_block() { return 256 / (D / 16); }
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) {
-    constexpr int LPR = D / 16;  // lanes per row, 16 elements (two 16-byte chunks) each
-    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t R = gt / LPR;
-    const int part = (int)(gt % LPR);
-    const bool ok = R < p.rows;
-    float acc = 0.f;
-    RowLoc L{0, 0, 0};
-    if (ok) {
-        L = row_of(p, R);
-        const uint16_t* op = p.o.p + toff(p.o, L) + part * 16;
-        const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * 16;
-        const u32x4 o0 = ld16(op), o1 = ld16(op + 8);
-        const u32x4 d0 = ld16(dp), d1 = ld16(dp + 8);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            acc += T::to_f32(elem16(o0, t)) * T::to_f32(elem16(d0, t));
-            acc += T::to_f32(elem16(o1, t)) * T::to_f32(elem16(d1, t));
-        }
-    }
+    constexpr int LPR = D / 16;
+    constexpr int RPB = pre_rows_per_block<D>();
+    const int part = threadIdx.x % LPR;
+    const int i = blockIdx.x * RPB + threadIdx.x / LPR;   // row (dense) or token (packed)
+    const int y = blockIdx.y;
+    const int b = p.varlen ? 0 : y / p.Hq, h = p.varlen ? y : y % p.Hq;
+    const bool ok = i < p.Sq;
+    const RowLoc L{b, h, min(i, p.Sq - 1)};               // rows past the end re-read the last
+    const uint16_t* op = p.o.p + toff(p.o, L) + part * 16;
+    const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * 16;
+    const u32x4 o0 = ld16(op), o1 = ld16(op + 8);
+    const u32x4 d0 = ld16(dp), d1 = ld16(dp + 8);
+    const int64_t so = L.b * p.st_sb + L.h * p.st_sh + L.i * p.st_ss;
+    const float sa = p.st_a[so];
+    const float sb = p.stats_kind ? p.st_b[so] : 0.f;
+    float acc = dot8<T>(d1, o1, dot8<T>(d0, o0));
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (!ok) return;
+    const int64_t R = p.varlen ? (int64_t)i * p.Hq + h : (int64_t)y * p.Sq + i;
     if (part == 0) {
         p.delta[R] = acc;
-        const int64_t so = L.b * p.st_sb + L.h * p.st_sh + L.i * p.st_ss;
-        float l2;
-        if (p.stats_kind == 0) {
-            const float x = p.st_a[so];
-            l2 = (x == -INFINITY) ? INFINITY : x * kLog2e;
-        } else {
-            const float mx = p.st_a[so], sm = p.st_b[so];
-            l2 = (sm > 0.f) ? mx * kLog2e + log2f(sm) : INFINITY;
-        }
-        p.lse2[R] = l2;
+        p.lse2[R] = stats_to_lse2(p.stats_kind, sa, sb);
     }
     if (zero_dq) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -127,6 +117,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
         dst[2] = z;
         dst[3] = z;
     }
+}
+
+template <class T, int D>
+static void launch_pre(const BwdParams& p, int zero_dq, hipStream_t st) {
+    constexpr int RPB = pre_rows_per_block<D>();
+    const dim3 grid((unsigned)((p.Sq + RPB - 1) / RPB), (unsigned)(p.varlen ? p.Hq : p.B * p.Hq));
+    if (grid.x > 0 && grid.y > 0)
+        PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), grid, dim3(256), 0, st, p, zero_dq);
 }
 
 // ---------------------------------------------------------------------------
@@ -414,12 +412,12 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 // B operand straight from the accumulator layout.  Q/dO tiles rotate through
 // three LDS buffers: tile k (read by dV/dK), k+1 (read by S/dP), and k+2, which
 // is loaded into registers at the start of the step and stored at its end with
-// its rows' negated Delta = -sum_d dO*O and log2-domain LSE.  The two row
+// its rows' log2-domain LSE and negated Delta from the row pass.  The two row
 // halves' dK/dV partials are summed through LDS at the end.  dQ is left to
 // the query-outer body.
 
 // Wavefronts per workgroup of the D=64 kernel and the dQ body: two row halves
-// of NKW key slices.  Four wavefronts let two workgroups share a CU (two
+// of kKeySlices key slices.  Four wavefronts let two workgroups share a CU (two
 // wavefronts per SIMD), so one workgroup's memory waits and barriers overlap
 // the other's arithmetic.
 constexpr int kWaves = 4;
@@ -480,8 +478,8 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
 
     // byte offsets of this thread's chunks within a tile (row strides are
     // below 2^23 elements, so 128 rows fit in 32 bits)
-    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss, oss = 2u * (uint32_t)p.o.ss;
-    uint32_t qoff[CH], dooff[CH], ooff[CH];
+    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
+    uint32_t qoff[CH], dooff[CH];
     int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
@@ -491,26 +489,26 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
         ccol[x] = cc;
         qoff[x] = r * qss + 2 * cc;
         dooff[x] = r * doss + 2 * cc;
-        ooff[x] = r * oss + 2 * cc;
     }
 
     // Pointers of the tile being loaded (head ld_h, rows from ld_i0), advanced
     // by one tile per step in scalar registers.
     const uint16_t* const q_seq = p.q.p + b * p.q.sb + (int64_t)q0 * p.q.ss;
     const uint16_t* const do_seq = p.dout.p + b * p.dout.sb + (int64_t)q0 * p.dout.ss;
-    const uint16_t* const o_seq = p.o.p + b * p.o.sb + (int64_t)q0 * p.o.ss;
-    const float* const sa_seq = p.st_a + b * p.st_sb + (int64_t)q0 * p.st_ss;
-    const float* const sb_seq = (p.stats_kind ? p.st_b : p.st_a) + b * p.st_sb + (int64_t)q0 * p.st_ss;
-    const int64_t q_step = BR * p.q.ss, do_step = BR * p.dout.ss, o_step = BR * p.o.ss, st_step = BR * p.st_ss;
+    // per-row log2-domain LSE and Delta from the row pass, rows (token, head)
+    // when packed, (batch, head, row) when dense
+    const int64_t ws_ss = p.varlen ? p.Hq : 1;
+    const int64_t q_step = BR * p.q.ss, do_step = BR * p.dout.ss, st_step = BR * ws_ss;
     int ld_h = hk * G, ld_i0 = i_begin;
-    const uint16_t *ld_q, *ld_do, *ld_o;
+    const uint16_t *ld_q, *ld_do;
     const float *ld_sa, *ld_sb;
     auto seek = [&]() {
         ld_q = q_seq + ld_h * p.q.sh + (int64_t)ld_i0 * p.q.ss;
         ld_do = do_seq + ld_h * p.dout.sh + (int64_t)ld_i0 * p.dout.ss;
-        ld_o = o_seq + ld_h * p.o.sh + (int64_t)ld_i0 * p.o.ss;
-        ld_sa = sa_seq + ld_h * p.st_sh + (int64_t)ld_i0 * p.st_ss;
-        ld_sb = sb_seq + ld_h * p.st_sh + (int64_t)ld_i0 * p.st_ss;
+        const int64_t ws = p.varlen ? (int64_t)(q0 + ld_i0) * p.Hq + ld_h
+                                    : ((int64_t)b * p.Hq + ld_h) * p.Sq + ld_i0;
+        ld_sa = p.lse2 + ws;
+        ld_sb = p.delta + ws;
     };
     // the query rows of one head from i_begin to the end of the sequence, then
     // the next head of the group
@@ -521,7 +519,7 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
             ++ld_h;
             seek();
         } else {
-            ld_q += q_step; ld_do += do_step; ld_o += o_step; ld_sa += st_step; ld_sb += st_step;
+            ld_q += q_step; ld_do += do_step; ld_sa += st_step; ld_sb += st_step;
         }
     };
     seek();
@@ -529,15 +527,15 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
     // Tile loads are unconditional: rows past the end of the sequence re-read
     // its last row and get LSE = +inf when stored, so their P is exactly zero.
     // Nothing loaded is used before the tile is stored.
-    struct TileRegs { u32x4 q[CH], d[CH], o[CH]; float sa, sb; };
+    struct TileRegs { u32x4 q[CH], d[CH]; float sa, sb; };
     const int srow = tid & (BR - 1);
-    const uint32_t sss = 4u * (uint32_t)p.st_ss;
+    const uint32_t sss = 4u * (uint32_t)ws_ss;
     const uint32_t srow_off = srow * sss;
     auto load_tile = [&](TileRegs& t) {
-        uint32_t oq[CH], odo[CH], oo[CH], so = srow_off;
+        uint32_t oq[CH], odo[CH], so = srow_off;
         if (ld_i0 + BR <= lq) {
 #pragma unroll
-            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; oo[x] = ooff[x]; }
+            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
         } else {
             const int last = lq - 1 - ld_i0;
 #pragma unroll
@@ -545,7 +543,6 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
                 const uint32_t r = min(crow[x], last);
                 oq[x] = r * qss + 2 * ccol[x];
                 odo[x] = r * doss + 2 * ccol[x];
-                oo[x] = r * oss + 2 * ccol[x];
             }
             so = (uint32_t)min(srow, last) * sss;
         }
@@ -553,7 +550,6 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
         for (int x = 0; x < CH; ++x) {
             t.q[x] = ld16_at(ld_q, oq[x]);
             t.d[x] = ld16_at(ld_do, odo[x]);
-            t.o[x] = ld16_at(ld_o, oo[x]);
         }
         t.sa = ldf_at(ld_sa, so);
         t.sb = ldf_at(ld_sb, so);
@@ -565,11 +561,12 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
         for (int x = 0; x < CH; ++x) {
             st16(&Qd[crow[x] * QP + ccol[x]], t.q[x]);
             st16(&dOd[crow[x] * QP + ccol[x]], t.d[x]);
-            const float dsum = lane_group_sum<D / 8>(dot8<T>(t.d[x], t.o[x]));
-            if (ccol[x] == 0) dlt_s[buf * BR + crow[x]] = -dsum;
         }
-        if (tid < BR)
-            lse_s[buf * BR + tid] = (i0 + tid < lq) ? stats_to_lse2(p.stats_kind, t.sa, t.sb) : INFINITY;
+        if (tid < BR) {
+            const bool ok = i0 + tid < lq;      // a row past the end has P = 0
+            lse_s[buf * BR + tid] = ok ? t.sa : INFINITY;
+            dlt_s[buf * BR + tid] = ok ? -t.sb : 0.f;   // stored negated: it seeds dP - Delta
+        }
     };
     u32x4 kreg[KS], vreg[KS];            // this wavefront's keys, loaded in the prologue
     // S^T and dP^T - Delta of the tile in buffer buf; dP^T accumulates onto
@@ -838,24 +835,16 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     // a row past the end of the sequence re-reads its last row; its LSE is
     // +inf (P = 0) and its dQ is not stored
     const int my_ic = min(my_i, lq - 1);
-    u32x4 qreg[KS], doreg[KS], oreg[KS];
-    const uint16_t* orow = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + my_ic) * p.o.ss;
+    u32x4 qreg[KS], doreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
         qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
         doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
-        oreg[s] = ld16(orow + 16 * s + 8 * g);
     }
-    const int64_t so = b * p.st_sb + h * p.st_sh + (int64_t)(q0 + my_ic) * p.st_ss;
-    const float sa_raw = p.st_a[so];
-    const float sb_raw = (p.stats_kind ? p.st_b : p.st_a)[so];
-    // this row's LSE and Delta = sum_d dO*O; the two lane halves hold
-    // alternate 8-element chunks of the row
-    const float l2 = row_ok ? stats_to_lse2(p.stats_kind, sa_raw, sb_raw) : INFINITY;
-    float dl = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) dl = dot8<T>(doreg[s], oreg[s], dl);
-    dl += __shfl_xor(dl, 32);
+    // this row's log2-domain LSE and Delta from the row pass
+    const int64_t ws = p.varlen ? (int64_t)(q0 + my_ic) * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq + my_ic;
+    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
+    const float dl = p.delta[ws];
 
     f32x16 dq[DB], ndl16;
 #pragma unroll
@@ -989,9 +978,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, in
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     if constexpr (D == 64) {
-        // One launch, no workspace traffic: the kernel reads the statistics
-        // and O itself and computes dQ without atomics, so it is deterministic
-        // whatever the caller asked for.
+        // The row pass, then one launch of both bodies; dQ is computed without
+        // atomics, so the result is deterministic whatever the caller asked for.
+        if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
         const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
         static_assert(32 * kKeySlices == 64, "key tile of the fused kernel");
         const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
@@ -1011,9 +1000,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         const int64_t row_threads = p.rows * (D / 8);
         const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
         const bool have_rows = p.rows > 0;
-        if ((L.phase & BwdLaunch::kFirst) && have_rows)
-            PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((p.rows * (D / 16) + 255) / 256)),
-                        dim3(256), 0, st, p, L.deterministic ? 0 : 1);
+        if ((L.phase & BwdLaunch::kFirst) && have_rows) launch_pre<T, D>(p, L.deterministic ? 0 : 1, st);
         const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
         const bool have_main = main_grid.x > 0 && main_grid.y > 0;
         if (L.deterministic) {
@@ -1039,10 +1026,7 @@ static hipError_t launch_bwd_d(const BwdParams& p, const BwdLaunch& L, hipStream
 
 template <class T, int D>
 static hipError_t launch_pre_t(const BwdParams& p, bool zero_dq, hipStream_t st) {
-    const int64_t row_threads = p.rows * (D / 16);
-    if (row_threads > 0)
-        PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), dim3((unsigned)((row_threads + 255) / 256)), dim3(256),
-                    0, st, p, zero_dq ? 1 : 0);
+    launch_pre<T, D>(p, zero_dq ? 1 : 0, st);
     return hipGetLastError();
 }
 
