@@ -78,8 +78,9 @@ __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
 // Preprocess
 // ---------------------------------------------------------------------------
 
-// Grid: x = chunks of kPreRows rows, y = (batch, head) when dense, head when
-// packed (rows are then tokens); D/16 lanes per row, 16 elements each.
+// Grid, D/16 lanes per row (16 elements each): dense, x = chunks of rows of
+// one (batch, head) = y; packed, x = chunks of the (token, head) rows in
+// memory order (the heads of a token are adjacent in the packed layout).
 template <int D>
 constexpr int pre_rows_per_block() { return 256 / (D / 16); }
 
@@ -88,11 +89,21 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
     constexpr int LPR = D / 16;
     constexpr int RPB = pre_rows_per_block<D>();
     const int part = threadIdx.x % LPR;
-    const int i = blockIdx.x * RPB + threadIdx.x / LPR;   // row (dense) or token (packed)
-    const int y = blockIdx.y;
-    const int b = p.varlen ? 0 : y / p.Hq, h = p.varlen ? y : y % p.Hq;
-    const bool ok = i < p.Sq;
-    const RowLoc L{b, h, min(i, p.Sq - 1)};               // rows past the end re-read the last
+    int64_t R;
+    bool ok;
+    RowLoc L;
+    if (p.varlen) {
+        R = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+        ok = R < p.rows;
+        const int64_t Rc = ok ? R : p.rows - 1;           // rows past the end re-read the last
+        L = RowLoc{0, Rc % p.Hq, Rc / p.Hq};
+    } else {
+        const int i = blockIdx.x * RPB + threadIdx.x / LPR;
+        const int y = blockIdx.y;
+        ok = i < p.Sq;
+        R = (int64_t)y * p.Sq + i;
+        L = RowLoc{y / p.Hq, y % p.Hq, min(i, p.Sq - 1)};
+    }
     const uint16_t* op = p.o.p + toff(p.o, L) + part * 16;
     const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * 16;
     const u32x4 o0 = ld16(op), o1 = ld16(op + 8);
@@ -104,7 +115,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (!ok) return;
-    const int64_t R = p.varlen ? (int64_t)i * p.Hq + h : (int64_t)y * p.Sq + i;
     if (part == 0) {
         p.delta[R] = acc;
         p.lse2[R] = stats_to_lse2(p.stats_kind, sa, sb);
@@ -122,7 +132,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
 template <class T, int D>
 static void launch_pre(const BwdParams& p, int zero_dq, hipStream_t st) {
     constexpr int RPB = pre_rows_per_block<D>();
-    const dim3 grid((unsigned)((p.Sq + RPB - 1) / RPB), (unsigned)(p.varlen ? p.Hq : p.B * p.Hq));
+    const dim3 grid = p.varlen ? dim3((unsigned)((p.rows + RPB - 1) / RPB), 1)
+                               : dim3((unsigned)((p.Sq + RPB - 1) / RPB), (unsigned)(p.B * p.Hq));
     if (grid.x > 0 && grid.y > 0)
         PROF_LAUNCH(KID_BWD_PRE, st, (bwd_pre_kernel<T, D>), grid, dim3(256), 0, st, p, zero_dq);
 }
