@@ -37,10 +37,11 @@ PEAK_MFMA_16BIT_TFLOPS = 2516.6      # 256 CU x 4096 FLOP/clk/CU x 2.4 GHz, dens
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def kernel_sources(kernel: str) -> list:
-    """The source files a kernel is built from (NSA kernels also use the
-    dense preprocess)."""
+    """The files a kernel's code comes from: its sources (NSA kernels also use
+    the dense preprocess) and the build script, which holds the compiler flags."""
     files = ("common.h", "bwd.hip", "nsa.hip") if kernel.startswith("nsa") else ("common.h", "bwd.hip")
-    return [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f) for f in files]
+    return [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f) for f in files] + [
+        os.path.join(ROOT, "sdpa_backward_fa2_amd", "build.py")]
 
 
 def kernel_source_hash(kernel: str = "bwd_fused8_kernel") -> str:

@@ -5,7 +5,12 @@
 Every HIP source under csrc/ is compiled into one shared library next to this
 file.  Packed fp32 instructions are disabled for device code
 (``-packed-fp32-ops``); hipcc's host pass warns that it does not know that
-feature, which is harmless.
+feature, which is harmless.  Matrix-core results are allocated in ordinary
+vector registers (``-amdgpu-mfma-vgpr-form``): the score tiles feed vector-ALU
+code right after their products, and with accumulation registers the compiler
+copies every element across (about 130 copies per step of the D=128 dK/dV
+kernel); the dK/dV accumulators still land in accumulation registers when the
+vector file is full.
 """
 from __future__ import annotations
 
@@ -32,6 +37,7 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     flags = [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-result", "-Wno-unused-command-line-argument",
     ] + list(extra or [])
     procs = []
