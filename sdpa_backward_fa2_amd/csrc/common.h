@@ -75,13 +75,17 @@ struct BF16 {
     static __device__ __forceinline__ uint16_t cvt(float x) {
         return __builtin_bit_cast(uint16_t, (__bf16)x);
     }
+    // a pair as one vector conversion, so that it is one gfx950 instruction
+    // (round to nearest even, as the scalar conversion)
     static __device__ __forceinline__ uint32_t pack(float lo, float hi) {
-        return (uint32_t)cvt(lo) | ((uint32_t)cvt(hi) << 16);
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+        const f2 v = {lo, hi};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
     }
     static __device__ __forceinline__ float to_f32(uint16_t x) {
         return __builtin_bit_cast(float, (uint32_t)x << 16);
     }
-    // gfx950 converts a pair to bf16 with round-to-nearest-even in one instruction.
     static __device__ __forceinline__ uint32_t pack_op(float lo, float hi) { return pack(lo, hi); }
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
         typedef __bf16 b2 __attribute__((ext_vector_type(2)));
