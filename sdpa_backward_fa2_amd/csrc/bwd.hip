@@ -229,17 +229,37 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
     const int n_steps = G * per_head;
 
-    // per-thread element offsets of its 16-byte chunks inside a tile (row r, column cc)
-    int qoff[CH], dooff[CH], crow[CH];
+    // per-thread byte offsets of its 16-byte chunks inside a tile (row r,
+    // column cc); row strides are below 2^23 elements, so they fit 32 bits
+    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
+    const int64_t ws_ss = p.varlen ? p.Hq : 1;      // row stride of lse2 / delta
+    const uint32_t wss = 4u * (uint32_t)ws_ss;
+    uint32_t qoff[CH], dooff[CH];
+    int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + 256 * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
-        qoff[x] = r * (int)p.q.ss + cc;
-        dooff[x] = r * (int)p.dout.ss + cc;
+        ccol[x] = cc;
+        qoff[x] = r * qss + 2 * cc;
+        dooff[x] = r * doss + 2 * cc;
     }
-    const int64_t ws_step = p.varlen ? p.Hq : 1;
+
+    // Cursor of the tile to load next (head ld_h, rows from ld_i0): the query
+    // rows of one head from i_begin to the end, then the next head of the
+    // group; pointers advance in scalar registers.
+    int ld_h = hk * G, ld_i0 = i_begin;
+    const uint16_t *ld_q, *ld_do;
+    const float *ld_l, *ld_d;
+    auto seek = [&]() {
+        ld_q = p.q.p + b * p.q.sb + ld_h * p.q.sh + (int64_t)(q0 + ld_i0) * p.q.ss;
+        ld_do = p.dout.p + b * p.dout.sb + ld_h * p.dout.sh + (int64_t)(q0 + ld_i0) * p.dout.ss;
+        const int64_t ws = p.varlen ? (int64_t)(q0 + ld_i0) * p.Hq + ld_h : ((int64_t)b * p.Hq + ld_h) * p.Sq + ld_i0;
+        ld_l = p.lse2 + ws;
+        ld_d = p.delta + ws;
+    };
+    seek();
 
     // Tile loads are unconditional (rows past the end re-read the last row),
     // and nothing loaded is used before store_tile, so the prefetch of the next
@@ -247,35 +267,38 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     u32x4 pq[CH], pdo[CH];
     float pl = INFINITY, pd = 0.f;
     int pi0 = 0;
-    auto load_tile = [&](int st) {
-        const int h = hk * G + st / per_head;
-        const int i0 = i_begin + (st % per_head) * BR;
-        const uint16_t* qb = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)(q0 + i0) * p.q.ss;
-        const uint16_t* dob = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)(q0 + i0) * p.dout.ss;
-        int oq[CH], odo[CH];
-        if (i0 + BR <= lq) {
+    auto load_tile = [&]() {
+        uint32_t oq[CH], odo[CH];
+        uint32_t so = (uint32_t)(tid & (BR - 1)) * wss;
+        if (ld_i0 + BR <= lq) {
 #pragma unroll
             for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
         } else {
-            const int last = lq - 1 - i0;
+            const int last = lq - 1 - ld_i0;
 #pragma unroll
             for (int x = 0; x < CH; ++x) {
-                const int e = tid + 256 * x;
-                const int r = min(crow[x], last), cc = (e % (D / 8)) * 8;
-                oq[x] = r * (int)p.q.ss + cc;
-                odo[x] = r * (int)p.dout.ss + cc;
+                const uint32_t r = min(crow[x], last);
+                oq[x] = r * qss + 2 * ccol[x];
+                odo[x] = r * doss + 2 * ccol[x];
             }
+            so = (uint32_t)min(tid & (BR - 1), last) * wss;
         }
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            pq[x] = ld16(qb + oq[x]);
-            pdo[x] = ld16(dob + odo[x]);
+            pq[x] = ld16_at(ld_q, oq[x]);
+            pdo[x] = ld16_at(ld_do, odo[x]);
         }
-        const int i = min(i0 + (tid & (BR - 1)), lq - 1);
-        const int64_t ws = p.varlen ? ((int64_t)(q0 + i) * p.Hq + h) : (((int64_t)b * p.Hq + h) * p.Sq + i);
-        pl = p.lse2[ws];
-        pd = p.delta[ws];
-        pi0 = i0;
+        pl = ldf_at(ld_l, so);
+        pd = ldf_at(ld_d, so);
+        pi0 = ld_i0;
+        ld_i0 += BR;
+        if (ld_i0 >= lq) {
+            ld_i0 = i_begin;
+            ++ld_h;
+            seek();
+        } else {
+            ld_q += BR * p.q.ss; ld_do += BR * p.dout.ss; ld_l += BR * ws_ss; ld_d += BR * ws_ss;
+        }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -293,7 +316,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     };
 
     if (n_steps > 0) {
-        load_tile(0);
+        load_tile();
         store_tile(0);
     }
     wait_all_memory();
@@ -303,12 +326,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     // the 8q+4g part: key my_j needs row >= my_j; a key past the end keeps nothing
     const int t_key = col_ok ? (CAUSAL ? my_j - 4 * g : INT_MIN / 2) : INT_MAX / 2;
 
+    int h = hk * G, i0 = i_begin;          // the step's tile
     for (int st = 0; st < n_steps; ++st) {
         const int buf = st & 1;
-        const int h = hk * G + st / per_head;
-        const int i0 = i_begin + (st % per_head) * BR;
         const bool has_next = st + 1 < n_steps;
-        if (has_next) load_tile(st + 1);
+        if (has_next) load_tile();
 
         const uint16_t* Qb = Qs[buf];
         const uint16_t* dOb = dOs[buf];
@@ -389,8 +411,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
             }
         }
         __syncthreads();
+        i0 += BR;
+        if (i0 >= lq) { i0 = i_begin; ++h; }
     }
-    (void)ws_step;
 
     if (!col_ok) return;
     uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
