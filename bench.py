@@ -110,19 +110,8 @@ def build_inputs(cid: int):
     cu = wl.cu_seqlens()
     T = wl.T
     if wl.kind == "varlen":
-        # O and the LSE per sequence from the library's dense forward, written
-        # straight into the packed buffers (outside the timed region)
-        o = torch.empty_like(ts["q"])
-        lse = torch.empty((T, wl.Hq), dtype=torch.float32, device="cuda")
-        start = 0
-        for end in cu:
-            end = int(end)
-            if end > start:
-                def v4(x):
-                    return x[start:end].unsqueeze(0).permute(0, 2, 1, 3)
-                sb.fwd_stats(v4(ts["q"]), v4(ts["k"]), v4(ts["v"]), wl.scale, wl.causal,
-                             o=v4(o), lse=lse[start:end].t().unsqueeze(0))
-            start = end
+        # O and the LSE from the library's packed forward (outside the timed region)
+        o, lse = sb.fwd_stats_varlen(ts["q"], ts["k"], ts["v"], cu, cu, wl.scale, wl.causal)
         torch.cuda.synchronize()
 
         def prep(det):

@@ -126,6 +126,27 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
                    const sdpa_tensor4* o_out, const sdpa_stats_out* lse_out, void* stream);
 
 /*
+ * sdpa_fwd_stats_varlen: the same forward for a packed (TND) batch, one call
+ * for all sequences (the Ascend page's packed layout and host cumulative
+ * lengths, "Parameters" table; its softmaxMax/softmaxSum are given here as
+ * the equivalent LSE = max + ln(sum)).
+ *   cu_seqlens_q_host, cu_seqlens_kv_host: host arrays of `batch` inclusive
+ *   end offsets (no leading zero), non-decreasing; read during the call only.
+ *   q: (Tq, Hq, D); k, v: (Tk, Hkv, D); o_out: (Tq, Hq, D) written.
+ *   lse_out: natural-log LSE of token t, head n at t*stride_s + n*stride_h
+ *   (stride_b unused), written for every query token.
+ *   causal: per sequence, key j visible to query i iff j <= i (equal lengths
+ *   per sequence required, else SDPA_ERR_INVALID).  A query with no visible
+ *   key (empty key sequence) gets O = 0 and LSE = -inf.
+ * Needs no workspace; errors as sdpa_fwd_stats.
+ */
+int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                          double scale, int causal, const sdpa_tensor3* q, const sdpa_tensor3* k,
+                          const sdpa_tensor3* v, const sdpa_tensor3* o_out, const sdpa_stats_out* lse_out,
+                          void* stream);
+
+/*
  * sdpa_bwd_workspace_size / sdpa_bwd: dense SDPA backward (the cuDNN sample's
  * sdpa_backward node: inputs q, k, v, o, dO, stats, attn_scale,
  * use_causal_mask; outputs dQ, dK, dV; backward-graph cell).

@@ -73,6 +73,8 @@ _SIGS = {
     "sdpa_last_error": (ctypes.c_char_p, []),
     "sdpa_fwd_stats": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                P4, P4, P4, P4, ctypes.POINTER(StatsOut), c_vp]),
+    "sdpa_fwd_stats_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
+                                      P3, P3, P3, P3, ctypes.POINTER(StatsOut), c_vp]),
     "sdpa_bwd_workspace_size": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
                                         ctypes.POINTER(c_size)]),
     "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int,
@@ -220,6 +222,25 @@ def fwd_stats(q, k, v, scale: float, causal: bool, o=None, lse=None):
     st = lib.sdpa_fwd_stats(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal),
                             _t4(q), _t4(k), _t4(v), _t4(o), ctypes.byref(so), _stream_ptr(q.device))
     _check(st, "sdpa_fwd_stats")
+    return o, lse
+
+
+def fwd_stats_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, o=None, lse=None):
+    """O and the natural-log LSE (Tq, Hq) fp32 for a packed (T, N, D) batch;
+    cu_q / cu_kv: host sequences of inclusive end offsets."""
+    lib = load()
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=q.device)
+    so = StatsOut(lse.data_ptr(), 0, lse.stride(1), lse.stride(0))
+    aq, n = _cu_host(cu_q)
+    ak, _ = _cu_host(cu_kv)
+    st = lib.sdpa_fwd_stats_varlen(_dtype_code(q), n, aq, ak, Hq, Hkv, D, float(scale), int(causal),
+                                   _t3(q), _t3(k), _t3(v), _t3(o), ctypes.byref(so), _stream_ptr(q.device))
+    _check(st, "sdpa_fwd_stats_varlen")
     return o, lse
 
 

@@ -200,12 +200,61 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
     p.lse_sb = lse_out->stride_b; p.lse_sh = lse_out->stride_h; p.lse_ss = lse_out->stride_s;
     p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.Sq = (int)Sq; p.Sk = (int)Sk;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
-    hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, causal != 0, static_cast<hipStream_t>(stream));
+    hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)Sq, causal != 0, static_cast<hipStream_t>(stream));
     if (log_enabled())
         std::fprintf(stderr, "[sdpa_bwd] fwd_stats dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld causal=%d grid=(%lld,%lld)\n",
                      dtype, (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq, (long long)Sk,
                      (long long)D, causal, (long long)((Sq + 127) / 128), (long long)(B * Hq));
     if (e != hipSuccess) return fail_hip(e, "fwd launch");
+    return SDPA_OK;
+}
+
+int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                          double scale, int causal, const sdpa_tensor3* q, const sdpa_tensor3* k,
+                          const sdpa_tensor3* v, const sdpa_tensor3* o_out, const sdpa_stats_out* lse_out,
+                          void* stream) {
+    if (!cu_seqlens_q_host || !cu_seqlens_kv_host) return SDPA_ERR_NULLPTR;
+    if (!q || !k || !v || !o_out || !lse_out) return SDPA_ERR_NULLPTR;
+    if (!q->data || !k->data || !v->data || !o_out->data || !lse_out->lse) return SDPA_ERR_NULLPTR;
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    Packed P;
+    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, causal != 0, P)) return s;
+    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    for (const sdpa_tensor3* t : {q, k, v, o_out})
+        if (int s = tensor3_ok(t)) return s;
+    if (std::min<int64_t>(batch, sdpa::kMaxSeqArgs) * Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
+    if (int s = check_device()) return s;
+    if (P.Tq == 0) return SDPA_OK;
+
+    sdpa::FwdParams p{};
+    p.q = arg3(q); p.k = arg3(k); p.v = arg3(v); p.o = arg3(o_out);
+    p.lse = lse_out->lse;
+    p.lse_sb = 0; p.lse_sh = lse_out->stride_h; p.lse_ss = lse_out->stride_s;
+    p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.Sq = (int)P.Tq; p.Sk = (int)P.Tk;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    p.varlen = 1;
+    // one launch per chunk of up to kMaxSeqArgs sequences
+    const int64_t n = (int64_t)P.q0.size();
+    for (int64_t c0 = 0; c0 < n; c0 += sdpa::kMaxSeqArgs) {
+        const int64_t c1 = std::min<int64_t>(n, c0 + sdpa::kMaxSeqArgs);
+        int64_t mlq = 0;
+        p.seqs.n = (int)(c1 - c0);
+        p.seqs.dev = nullptr;
+        for (int64_t b = c0; b < c1; ++b) {
+            p.seqs.q0[b - c0] = (int32_t)P.q0[b];
+            p.seqs.k0[b - c0] = (int32_t)P.k0[b];
+            p.seqs.lq[b - c0] = (int32_t)P.lq[b];
+            p.seqs.lk[b - c0] = (int32_t)P.lk[b];
+            mlq = std::max(mlq, P.lq[b]);
+        }
+        p.B = (int)(c1 - c0);
+        if (mlq == 0) continue;
+        hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)mlq, causal != 0, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail_hip(e, "fwd varlen launch");
+    }
     return SDPA_OK;
 }
 

@@ -261,8 +261,10 @@ __device__ __forceinline__ void seq_get(const SeqTable& t, int b, int& q0, int& 
 struct FwdParams {
     TensorArg q, k, v, o;
     float* lse; int64_t lse_sb, lse_sh, lse_ss;
-    int B, Hq, Hkv, Sq, Sk;
+    int B, Hq, Hkv, Sq, Sk;   // packed: B = sequences of this launch, Sq/Sk unused
     float scale_log2;
+    int varlen;               // rows of sequence b: tokens seqs.q0[b] .. + seqs.lq[b]
+    SeqTable seqs;
 };
 
 // Row statistics workspace layout: row index R of (b, h, i)

@@ -4,7 +4,8 @@
 // forward graph with is_inference=False emits o and stats; forward-graph cell).
 // It is a FlashAttention-style forward: each wavefront owns 32 query rows,
 // keys stream through LDS 64 at a time, and a running max and sum give the
-// softmax without materialising it.  Scores are computed transposed
+// softmax without materialising it.  Packed batches read each sequence's
+// token range from the sequence table.  Scores are computed transposed
 // (S^T = K Q^T) so that every lane holds one query column: row statistics are
 // lane-local and need a single exchange with the other lane half.
 #include "common.h"
@@ -30,15 +31,17 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     const int bh = blockIdx.y;
     const int b = bh / p.Hq, h = bh % p.Hq;
     const int hk = h / (p.Hq / p.Hkv);
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
     const int i0 = blockIdx.x * BQ;
-    if (i0 >= p.Sq) return;
+    if (i0 >= lq) return;
 
-    const uint16_t* qp = p.q.p + b * p.q.sb + h * p.q.sh;
-    const uint16_t* kp = p.k.p + b * p.k.sb + hk * p.k.sh;
-    const uint16_t* vp = p.v.p + b * p.v.sb + hk * p.v.sh;
+    const uint16_t* qp = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
+    const uint16_t* kp = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
+    const uint16_t* vp = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
 
     const int my_i = i0 + 32 * w + c;
-    const bool row_ok = my_i < p.Sq;
+    const bool row_ok = my_i < lq;
     u32x4 qreg[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -51,14 +54,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = zero16();
 
-    const int kend = CAUSAL ? min(p.Sk, i0 + BQ) : p.Sk;
+    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
     for (int j0 = 0; j0 < kend; j0 += BK) {
         __syncthreads();
         for (int e = tid; e < BK * D / 8; e += 256) {
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
             const int j = j0 + r;
             u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-            if (j < p.Sk) {
+            if (j < lk) {
                 kv = ld16(kp + (int64_t)j * p.k.ss + cc);
                 vv = ld16(vp + (int64_t)j * p.v.ss + cc);
             }
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
             for (int rg = 0; rg < 16; ++rg) {
                 const int j = j0 + kb * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3);
                 float x = s[kb][rg] * p.scale_log2;
-                if (j >= p.Sk || (CAUSAL && j > my_i)) x = -INFINITY;
+                if (j >= lk || (CAUSAL && j > my_i)) x = -INFINITY;
                 s[kb][rg] = x;
                 tmax = fmaxf(tmax, x);
             }
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 
     if (!row_ok) return;
     const float inv_l = l > 0.f ? 1.f / l : 0.f;
-    uint16_t* op = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)my_i * p.o.ss;
+    uint16_t* op = p.o.p + b * p.o.sb + h * p.o.sh + (int64_t)(q0 + my_i) * p.o.ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -134,13 +137,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
         }
     if (g == 0) {
         const float lse = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-        p.lse[b * p.lse_sb + h * p.lse_sh + (int64_t)my_i * p.lse_ss] = lse;
+        p.lse[b * p.lse_sb + h * p.lse_sh + (int64_t)(q0 + my_i) * p.lse_ss] = lse;
     }
 }
 
+// grid.x covers the longest sequence (dense: Sq) in 128-row tiles
 template <class T, int D>
-static hipError_t launch_fwd_t(const FwdParams& p, bool causal, hipStream_t st) {
-    dim3 grid((p.Sq + 127) / 128, p.B * p.Hq);
+static hipError_t launch_fwd_t(const FwdParams& p, int max_lq, bool causal, hipStream_t st) {
+    dim3 grid((max_lq + 127) / 128, p.B * p.Hq);
     if (causal)
         PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, true>), grid, dim3(256), 0, st, p);
     else
@@ -148,10 +152,10 @@ static hipError_t launch_fwd_t(const FwdParams& p, bool causal, hipStream_t st) 
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t st) {
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st) {
     if (dtype == 0)
-        return D == 64 ? launch_fwd_t<F16, 64>(p, causal, st) : launch_fwd_t<F16, 128>(p, causal, st);
-    return D == 64 ? launch_fwd_t<BF16, 64>(p, causal, st) : launch_fwd_t<BF16, 128>(p, causal, st);
+        return D == 64 ? launch_fwd_t<F16, 64>(p, max_lq, causal, st) : launch_fwd_t<F16, 128>(p, max_lq, causal, st);
+    return D == 64 ? launch_fwd_t<BF16, 64>(p, max_lq, causal, st) : launch_fwd_t<BF16, 128>(p, max_lq, causal, st);
 }
 
 }  // namespace sdpa

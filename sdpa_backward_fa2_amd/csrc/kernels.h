@@ -29,7 +29,7 @@ struct BwdLaunch {
     int phase = kFirst | kLast;
 };
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, bool causal, hipStream_t st);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // Delta and log2-LSE per statistics row (and the dQ accumulator clear).
 hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st);

@@ -161,3 +161,28 @@ def test_fwd_validation():
     assert fwd_call(causal=1, Sk=32) == INVALID
     assert fwd_call(D=256) == UNSUPPORTED
     assert fwd_call(dtype=2) == INVALID
+
+
+def fwd_varlen_call(cu_q, cu_k, **kw):
+    a = dict(dtype=1, Hq=4, Hkv=2, D=128, scale=0.088, causal=1, lse=FAKE)
+    a.update(kw)
+    aq = (ctypes.c_int64 * len(cu_q))(*cu_q)
+    ak = (ctypes.c_int64 * len(cu_k))(*cu_k)
+    so = sb.StatsOut(a["lse"], 0, 1, 4)
+    ts = [t3() for _ in range(4)]
+    return lib().sdpa_fwd_stats_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                       a["causal"], *[ctypes.byref(t) for t in ts], ctypes.byref(so), None)
+
+
+def test_fwd_varlen_validation():
+    assert fwd_varlen_call([100, 300], [100, 300], lse=None) == NULLPTR
+    assert fwd_varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
+    assert fwd_varlen_call([100, 300], [100, 200]) == INVALID         # causal, unequal lengths
+    assert fwd_varlen_call([100, 300], [100, 300], Hq=3) == INVALID   # heads not grouped
+    assert fwd_varlen_call([100, 300], [100, 300], dtype=4) == INVALID
+    assert fwd_varlen_call([100, 300], [100, 300], D=96) == UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_fwd_varlen_valid_without_device():
+    assert fwd_varlen_call([100, 300], [100, 200], causal=0) == HIP
