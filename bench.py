@@ -119,38 +119,13 @@ def build_inputs(cid: int):
                                      wl.causal, deterministic=det)
         return wl, prep, host
 
-    # selected (NSA): O and the (max, sum) statistics over the gathered keys,
-    # prepared with torch fp32 products on the GPU in the dense-with-bias form
-    # (bias ln m_b on a block chosen m_b times, -inf elsewhere and above the
-    # diagonal), outside the timed region
+    # selected (NSA): O and the (max, sum) statistics over the gathered keys
+    # from the library's selected forward, outside the timed region
     topk_np = wl.topk()
     topk = torch.from_numpy(np.ascontiguousarray(topk_np, dtype=np.int32)).cuda()
-    bs, G = wl.block_size, wl.Hq // wl.Hkv
-    o = torch.empty_like(ts["q"])
-    m = torch.empty((T, wl.Hq), dtype=torch.float32, device="cuda")
-    l = torch.empty_like(m)
-    starts = np.concatenate([[0], cu[:-1]])
-    for s0, s1 in zip(starts.tolist(), cu.tolist()):
-        L = s1 - s0
-        if L == 0:
-            continue
-        nb = L // bs
-        for h2 in range(wl.Hkv):
-            mult = torch.zeros((L, nb), dtype=torch.float32, device="cuda")
-            mult.scatter_add_(1, topk[s0:s1, h2].long(), torch.ones((L, topk.shape[2]), device="cuda"))
-            bias = torch.log(mult).repeat_interleave(bs, dim=1)
-            bias = torch.cat([bias, torch.full((L, L - nb * bs), -math.inf, device="cuda")], 1)
-            if wl.extra.get("sparse_mode", 2) == 2:
-                bias = bias.masked_fill(torch.ones(L, L, dtype=torch.bool, device="cuda").triu(1), -math.inf)
-            kk = ts["k"][s0:s1, h2].float()
-            vv = ts["v"][s0:s1, h2].float()
-            for h in range(h2 * G, (h2 + 1) * G):
-                sc = (ts["q"][s0:s1, h].float() @ kk.t()) * wl.scale
-                mx = torch.where(torch.isfinite(bias), sc, torch.full_like(sc, -math.inf)).amax(1)
-                pw = torch.exp(sc + bias - mx[:, None])
-                sm = pw.sum(1)
-                o[s0:s1, h] = ((pw @ vv) / sm[:, None]).to(o.dtype)
-                m[s0:s1, h], l[s0:s1, h] = mx, sm
+    bs = wl.block_size
+    o, m, l = sb.fwd_selected(ts["q"], ts["k"], ts["v"], topk, cu, cu, bs, wl.scale,
+                              wl.extra.get("sparse_mode", 2))
     torch.cuda.synchronize()
 
     def prep(det):

@@ -230,6 +230,27 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_fwd_selected: the NSA selected-attention forward in training mode,
+ * producing O and the softmaxMax / softmaxSum statistics that
+ * sdpa_bwd_selected consumes (Ascend page, "Formula": P is the softmax of the
+ * scaled scores over the gathered blocks; "Parameters": softmaxMax,
+ * softmaxSum).  Arguments, topk, sparse_mode and constraints as
+ * sdpa_bwd_selected; o_out: (Tq, Hq, D) written.
+ *   max_out[t*stats_stride_s + h*stats_stride_h]: max over the admissible
+ *   gathered keys of the scaled score (natural units); sum_out at the same
+ *   offset: sum of exp(score - max).  A token with no admissible key gets
+ *   O = 0, max = -inf, sum = 0.  Both arrays are caller-owned device fp32.
+ * Needs no workspace; errors as sdpa_bwd_selected.
+ */
+int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
+                      const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
+                      const sdpa_tensor3* o_out, float* max_out, float* sum_out,
+                      int64_t stats_stride_s, int64_t stats_stride_h, void* stream);
+
+/*
  * sdpa_selected_build_index: the inverse of the top-k choice, as used by
  * sdpa_bwd_selected.  KV blocks are numbered over the packed KV rows (block g
  * covers rows [g*block_size, (g+1)*block_size)); for bucket = h2 * NB + g,

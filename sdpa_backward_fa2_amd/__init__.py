@@ -88,6 +88,9 @@ _SIGS = {
     "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                   c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
                                   P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
+    "sdpa_fwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
+                                  c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                  P3, P3, P3, P3, c_vp, c_vp, c_i64, c_i64, c_vp]),
     "sdpa_profile_begin": (c_int, []),
     "sdpa_profile_end": (c_int, [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
     "sdpa_kernel_name": (ctypes.c_char_p, [c_int]),
@@ -434,6 +437,31 @@ def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, sc
                                   sparse_mode, deterministic, dq, dk, dv, workspace)
     call()
     return outs
+
+
+def fwd_selected(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float, sparse_mode: int,
+                 o=None, m=None, l=None):
+    """NSA selected-attention forward: O and the (max, sum) statistics (T, Hq)
+    fp32 over each token's gathered keys; topk: int32 (T, Hkv, count) on the device."""
+    lib = load()
+    Hq, D = q.shape[1], q.shape[2]
+    Hkv = k.shape[1]
+    count = topk.shape[2]
+    if o is None:
+        o = torch.empty_like(q)
+    if m is None:
+        m = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=q.device)
+    if l is None:
+        l = torch.empty_like(m)
+    assert m.stride() == l.stride()
+    aq, n = _cu_host(cu_q)
+    ak, _ = _cu_host(cu_kv)
+    st = lib.sdpa_fwd_selected(_dtype_code(q), n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
+                               topk.data_ptr(), *topk.stride(), int(block_size), count,
+                               _t3(q), _t3(k), _t3(v), _t3(o), m.data_ptr(), l.data_ptr(),
+                               m.stride(0), m.stride(1), _stream_ptr(q.device))
+    _check(st, "sdpa_fwd_selected")
+    return o, m, l
 
 
 def selected_build_index(topk, cu_q, cu_kv, block_size: int, workspace=None):

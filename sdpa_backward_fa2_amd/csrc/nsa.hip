@@ -61,6 +61,11 @@ struct NsaParams {
     int sparse_mode;
     int Tq;
     float scale, scale_log2;
+    // forward outputs
+    TensorArg o;
+    float* m_out;         // softmax max of the scaled scores, natural units
+    float* l_out;         // sum of exp(score - max)
+    int64_t st_ss, st_sh; // token and head strides of m_out / l_out
 };
 
 __device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) {
@@ -711,6 +716,197 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Forward: O and the (max, sum) statistics over each token's gathered keys
+// ---------------------------------------------------------------------------
+//
+// The selected-attention forward in training mode (Ascend
+// aclnnNsaSelectedAttentionGrad page, "Formula": P is the softmax of the scaled
+// scores over the gathered blocks; its softmaxMax / softmaxSum parameters are
+// this kernel's statistics).  One workgroup per (token, 16 query heads of a KV
+// head), as the dQ kernel: the token's chosen blocks stream through LDS 128
+// gathered keys at a time; wavefront w scores keys 32w .. +31 of a chunk
+// against the 16 heads (S^T = K Q^T, so each lane holds one head column) and
+// keeps a running max and sum per head and an O^T partial; the four partials
+// are merged at the end.
+template <class T, int D>
+__global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
+    constexpr int BK = 128;
+    constexpr int KP = D + 8;
+    constexpr int KS = D / 32;       // k-steps of 16x16x32 over the head dimension
+    constexpr int DB = D / 16;       // 16-row blocks of O^T
+    constexpr int CH = BK * D / 8 / 256;
+    __shared__ __align__(16) uint16_t Ks[BK * KP];
+    __shared__ __align__(16) uint16_t Vs[BK * KP];
+    __shared__ int kpos_s[BK];
+    __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
+
+    const int t = blockIdx.x;
+    const int h2 = blockIdx.y / ((p.G + 15) / 16);
+    const int ht = blockIdx.y % ((p.G + 15) / 16);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 15, G16 = lane >> 4;
+    const int s_idx = seq_of_token(p.seqs, t);
+    if (s_idx < 0) return;
+    const int t_local = t - p.seqs.q0[s_idx];
+    const int krow0 = p.seqs.k0[s_idx];
+    const int nblk = p.seqs.lk[s_idx] / p.bs;
+    const int gh = ht * 16 + col;
+    const bool head_ok = gh < p.G;
+    const int h = h2 * p.G + (head_ok ? gh : 0);
+
+    u32x4 qreg[KS];
+    const uint16_t* qp = p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qreg[s] = head_ok ? ld16(qp + 32 * s + 8 * G16) : z;
+    }
+
+    f32x4 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = zero4();
+    float m = -INFINITY, l = 0.f;       // this wavefront's running max (log2 domain) and sum
+
+    const int nk = p.count * p.bs;
+    const int32_t* tk = p.topk + (int64_t)t * p.tk_st + (int64_t)h2 * p.tk_sn;
+    for (int i = tid; i < p.count; i += 256) {
+        const int blk = tk[(int64_t)i * p.tk_sk];
+        blk_s[i] = (blk >= 0 && blk < nblk) ? blk : -1;
+    }
+    __syncthreads();
+    // chunk loads as in the dQ kernel: unconditional, an ignored choice or a
+    // row past the gathered keys re-reads key row krow0 and is masked
+    u32x4 kv[CH], vv[CH];
+    int kpos_r = 0x7fffffff;
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            const int n = c0 + r;
+            const int blk = blk_s[min(n / p.bs, p.count - 1)];
+            const bool ok = n < nk && blk >= 0;
+            const int64_t row = (int64_t)krow0 + (ok ? (int64_t)blk * p.bs + n % p.bs : 0);
+            kv[x] = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
+            vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+        }
+        const int n = c0 + (tid & (BK - 1));
+        const int blk = blk_s[min(n / p.bs, p.count - 1)];
+        kpos_r = (n < nk && blk >= 0) ? blk * p.bs + n % p.bs : 0x7fffffff;
+    };
+    load_chunk(0);
+    for (int c0 = 0; c0 < nk; c0 += BK) {
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            st16(&Ks[r * KP + cc], kv[x]);
+            st16(&Vs[r * KP + cc], vv[x]);
+        }
+        if (tid < BK) kpos_s[tid] = kpos_r;
+        __syncthreads();
+        if (c0 + BK < nk) load_chunk(c0 + BK);
+        // scores of keys 32w + 16x + 4*G16 + r against head `col`, log2 domain
+        f32x4 sc[2];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            sc[x] = zero4();
+            const int kr = 32 * w + 16 * x + col;       // A rows: keys
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sc[x] = T::mma16(ld16(&Ks[kr * KP + 32 * ks + 8 * G16]), qreg[ks], sc[x]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int kpos = kpos_s[32 * w + 16 * x + 4 * G16 + r];
+                const bool masked = kpos == 0x7fffffff || (p.sparse_mode == 2 && kpos > t_local);
+                sc[x][r] = masked ? -INFINITY : sc[x][r] * p.scale_log2;
+                tmax = fmaxf(tmax, sc[x][r]);
+            }
+        }
+        // the head's keys of this wavefront sit in the four 16-lane groups
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m, tmax);
+        const float msub = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+        float rs = 0.f;
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sc[x][r] = fast_exp2(sc[x][r] - msub);
+                rs += sc[x][r];
+            }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        l = l * alpha + rs;
+        m = m_new;
+        // O^T += V^T P^T over this wavefront's 32 keys (acc-slot order)
+        u32x4 bP;
+        bP[0] = T::pack_op(sc[0][0], sc[0][1]);
+        bP[1] = T::pack_op(sc[0][2], sc[0][3]);
+        bP[2] = T::pack_op(sc[1][0], sc[1][1]);
+        bP[3] = T::pack_op(sc[1][2], sc[1][3]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            o[db][0] *= alpha; o[db][1] *= alpha; o[db][2] *= alpha; o[db][3] *= alpha;
+            o[db] = T::mma16(ld_tr16x16_acc(Vs, KP, 32 * w, 16 * db, lane), bP, o[db]);
+        }
+    }
+
+    // merge the four wavefronts: M = max m_w, L = sum l_w 2^(m_w - M),
+    // O = sum O_w 2^(m_w - M) / L  (through LDS, reusing Ks and kpos_s)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(Ks);
+    float* ml = reinterpret_cast<float*>(kpos_s);   // [4 waves][16 heads][m, l]
+    static_assert(sizeof(Ks) >= 3 * DB * 64 * 4 * 4, "merge space");
+    static_assert(sizeof(kpos_s) >= 4 * 16 * 2 * 4, "merge space");
+    if (w != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<f32x4*>(&red[((((w - 1) * DB) + db) * 64 + lane) * 4]) = o[db];
+    }
+    if (G16 == 0) { ml[(w * 16 + col) * 2] = m; ml[(w * 16 + col) * 2 + 1] = l; }
+    __syncthreads();
+    if (w != 0 || !head_ok) return;
+    float M = m;
+#pragma unroll
+    for (int x = 1; x < 4; ++x) M = fmaxf(M, ml[(x * 16 + col) * 2]);
+    const float f0 = m == -INFINITY ? 0.f : fast_exp2(m - M);
+    float L = l * f0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { o[db][0] *= f0; o[db][1] *= f0; o[db][2] *= f0; o[db][3] *= f0; }
+#pragma unroll
+    for (int x = 1; x < 4; ++x) {
+        const float mx = ml[(x * 16 + col) * 2];
+        const float fx = mx == -INFINITY ? 0.f : fast_exp2(mx - M);
+        L += ml[(x * 16 + col) * 2 + 1] * fx;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&red[((((x - 1) * DB) + db) * 64 + lane) * 4]);
+            o[db][0] += v[0] * fx; o[db][1] += v[1] * fx; o[db][2] += v[2] * fx; o[db][3] += v[3] * fx;
+        }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    // O^T tile: lane holds head `col`, head dims 16*db + 4*G16 + r
+    uint16_t* op = p.o.p + (int64_t)t * p.o.ss + (int64_t)h * p.o.sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        u32x2 v;
+        v[0] = T::pack(o[db][0] * inv, o[db][1] * inv);
+        v[1] = T::pack(o[db][2] * inv, o[db][3] * inv);
+        st8(op + 16 * db + 4 * G16, v);
+    }
+    if (G16 == 0) {
+        const int64_t so = (int64_t)t * p.st_ss + (int64_t)h * p.st_sh;
+        p.m_out[so] = M == -INFINITY ? -INFINITY : M * kLn2;
+        p.l_out[so] = L;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launch
 // ---------------------------------------------------------------------------
 
@@ -719,6 +915,12 @@ static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
     PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<false>), grid, dim3(1024), 0, st, p);
     PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
     PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<true>), grid, dim3(1024), 0, st, p);
+    return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_nsa_fwd_t(const NsaParams& p, hipStream_t st) {
+    PROF_LAUNCH(KID_FWD, st, (nsa_fwd_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -889,6 +1091,50 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
     p.pieces = reinterpret_cast<int32_t*>(ws + L.pieces);
     p.halves = (int)L.halves;
     p.Tq = (int)S.Tq;
+}
+
+int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
+                      const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
+                      const sdpa_tensor3* o_out, float* max_out, float* sum_out,
+                      int64_t stats_stride_s, int64_t stats_stride_h, void* stream) {
+    if (!cu_seqlens_q_host || !cu_seqlens_kv_host || !topk) return SDPA_ERR_NULLPTR;
+    if (!q || !k || !v || !o_out || !max_out || !sum_out) return SDPA_ERR_NULLPTR;
+    for (const sdpa_tensor3* t : {q, k, v, o_out})
+        if (!t->data) return SDPA_ERR_NULLPTR;
+    if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
+    Seqs S;
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+                               block_count, sparse_mode, S))
+        return s;
+    for (const sdpa_tensor3* t : {q, k, v, o_out})
+        if (int s = t3_ok(t)) return s;
+    if (int s = device_ok()) return s;
+    if (S.Tq == 0) return SDPA_OK;
+
+    sdpa::NsaParams p{};
+    p.topk = topk; p.tk_st = tk_st; p.tk_sn = tk_sn; p.tk_sk = tk_sk;
+    p.count = (int)block_count; p.bs = (int)block_size; p.N2 = (int)Hkv;
+    p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
+    fill_seq_table(p.seqs, S);
+    p.Tq = (int)S.Tq;
+    p.q = arg(q); p.k = arg(k); p.v = arg(v); p.o = arg(o_out);
+    p.m_out = max_out; p.l_out = sum_out;
+    p.st_ss = stats_stride_s; p.st_sh = stats_stride_h;
+    p.sparse_mode = sparse_mode;
+    p.scale = (float)scale;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (dtype == SDPA_F16)
+        e = D == 64 ? sdpa::launch_nsa_fwd_t<sdpa::F16, 64>(p, st) : sdpa::launch_nsa_fwd_t<sdpa::F16, 128>(p, st);
+    else
+        e = D == 64 ? sdpa::launch_nsa_fwd_t<sdpa::BF16, 64>(p, st) : sdpa::launch_nsa_fwd_t<sdpa::BF16, 128>(p, st);
+    if (e != hipSuccess) return hip_fail(e, "selected forward launch");
+    return SDPA_OK;
 }
 
 int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,

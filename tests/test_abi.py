@@ -186,3 +186,28 @@ def test_fwd_varlen_validation():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_fwd_varlen_valid_without_device():
     assert fwd_varlen_call([100, 300], [100, 200], causal=0) == HIP
+
+
+def fwd_selected_call(**kw):
+    a = dict(dtype=1, cu=[512], Hq=16, Hkv=1, D=128, bs=64, count=4, mode=2, m=FAKE, l=FAKE)
+    a.update(kw)
+    cu = (ctypes.c_int64 * len(a["cu"]))(*a["cu"])
+    ts = [t3() for _ in range(4)]
+    return lib().sdpa_fwd_selected(a["dtype"], len(a["cu"]), cu, cu, a["Hq"], a["Hkv"], a["D"], 0.088,
+                                   a["mode"], FAKE, 4 * a["count"], a["count"], 1, a["bs"], a["count"],
+                                   *[ctypes.byref(t) for t in ts], a["m"], a["l"], 16, 1, None)
+
+
+def test_fwd_selected_validation():
+    assert fwd_selected_call(m=None) == NULLPTR
+    assert fwd_selected_call(dtype=3) == INVALID
+    assert fwd_selected_call(bs=40) == INVALID          # not a multiple of 16
+    assert fwd_selected_call(cu=[500]) == INVALID       # KV length not a multiple of block_size
+    assert fwd_selected_call(mode=1) == INVALID
+    assert fwd_selected_call(Hq=64) == INVALID          # more than 32 query heads per KV head
+    assert fwd_selected_call(D=96) == UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_fwd_selected_valid_without_device():
+    assert fwd_selected_call() == HIP
