@@ -44,6 +44,7 @@ struct NsaParams {
     int64_t tk_st, tk_sn, tk_sk;
     int tk_vec4;          // slots contiguous, count % 4 == 0, 16-byte aligned rows
     int count, bs, N2, NB, G, Hq;
+    int g_mul;            // ceil(2^16 / G): r / G == (r * g_mul) >> 16 for 0 <= r < 256
     int chunk;            // entries per work piece
     int max_pieces;
     SeqTable seqs;        // per sequence: first query row, first key row, lengths
@@ -355,21 +356,26 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     float pl = INFINITY, pd = 0.f;
     int ptl = 0;
     bool pok = false;
+    // row r of a tile: entry r / G, head r % G (r < 256, G <= 32: a multiply
+    // and shift divide exactly)
+    auto div_g = [&](int r) { return (r * p.g_mul) >> 16; };
     auto load_tile = [&](int st) {
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
             const int e = tid + 256 * x;
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            const int t = tok_s[min(st * E + r / p.G, n_e - 1)];
-            const int h = h2 * p.G + r % p.G;
+            const int rq = div_g(r);
+            const int t = tok_s[min(st * E + rq, n_e - 1)];
+            const int h = h2 * p.G + r - rq * p.G;
             pq[x] = ld16(p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh + cc);
             pdo[x] = ld16(p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh + cc);
         }
         {
             const int r = tid & (BR - 1);
-            const int li = st * E + r / p.G;
+            const int rq = div_g(r);
+            const int li = st * E + rq;
             const int t = tok_s[min(li, n_e - 1)];
-            const int h = h2 * p.G + r % p.G;
+            const int h = h2 * p.G + r - rq * p.G;
             pl = p.lse2[(int64_t)t * p.Hq + h];
             pd = p.delta[(int64_t)t * p.Hq + h];
             ptl = t - q0s;
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
         }
         if (tid < BR) {
             lse_s[buf][tid] = pok ? pl : INFINITY;
-            dlt_s[buf][tid] = pok ? pd : 0.f;
+            dlt_s[buf][tid] = pok ? -pd : 0.f;      // stored negated: it seeds dP - Delta
             tl_s[buf][tid] = ptl;
         }
     };
@@ -398,36 +404,53 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     wait_all_memory();
     __syncthreads();
     const int my_kpos = kpos0 + myk;
+    const int last_kpos = kpos0 + nkeys - 1;   // the half block's last key position
     for (int st = 0; st < n_steps; ++st) {
         const int buf = st & 1;
         const bool has_next = st + 1 < n_steps;
         if (has_next) load_tile(st + 1);
         const uint16_t* Qb = Qs[buf];
         const uint16_t* dOb = dOs[buf];
+        // a bucket's entries are sorted by token, so row 0 holds the step's
+        // first token: when it sees the whole half block, no element is masked
+        const bool masked = nkeys < 64 || (p.sparse_mode == 2 && last_kpos > tl_s[buf][0]);
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             const int r0 = (BR / 2) * rh + 32 * sb;     // first row of this 32-row block
-            f32x16 sa = zero16(), pa = zero16();
+            // dP^T accumulates onto the rows' -Delta: pa ends as dP - Delta
+            f32x16 sa = zero16(), pa;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][r0 + 8 * q + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+            }
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 sa = T::mma(ld16(&Qb[(r0 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
                 pa = T::mma(ld16(&dOb[(r0 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
             }
+            auto grad = [&](auto masked_tag) {
+                constexpr bool MK = decltype(masked_tag)::value;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rb = r0 + 8 * q + 4 * g;
-                const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[buf][rb]);
-                const f32x4 Dr = *reinterpret_cast<const f32x4*>(&dlt_s[buf][rb]);
+                for (int q = 0; q < 4; ++q) {
+                    const int rb = r0 + 8 * q + 4 * g;
+                    const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_s[buf][rb]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int rg = 4 * q + r;
-                    float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
-                    const bool masked = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
-                    pv = masked ? 0.f : pv;
-                    sa[rg] = pv;
-                    pa[rg] = pv * (pa[rg] - Dr[r]);
+                    for (int r = 0; r < 4; ++r) {
+                        const int rg = 4 * q + r;
+                        float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
+                        if (MK) {
+                            const bool off = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
+                            pv = off ? 0.f : pv;
+                        }
+                        sa[rg] = pv;
+                        pa[rg] = pv * pa[rg];
+                    }
                 }
-            }
+            };
+            if (masked) grad(std::true_type{});
+            else grad(std::false_type{});
             if (sb == NSB - 1 && has_next) store_tile(buf ^ 1);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -1082,6 +1105,7 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
                  reinterpret_cast<uintptr_t>(topk) % 16 == 0 && S.Tq * count < (int64_t(1) << 33)) ? 1 : 0;
     p.count = (int)count; p.bs = (int)bs; p.N2 = (int)Hkv; p.NB = (int)L.NB;
     p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
+    p.g_mul = (65536 + p.G - 1) / p.G;
     p.chunk = (int)L.chunk; p.max_pieces = (int)L.max_pieces;
     fill_seq_table(p.seqs, S);
     p.counts = reinterpret_cast<int32_t*>(ws + L.counts);
