@@ -643,6 +643,10 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
         rr[x] = r % p.bs;
     }
     const int rq_k = (tid & (BK - 1)) / p.bs, rr_k = (tid & (BK - 1)) % p.bs;
+    // row strides are below 2^23 elements: 32 x 32 -> 64-bit row offsets
+    const int kss = (int)p.k.ss, vss = (int)p.v.ss;
+    const uint16_t* const kh = p.k.p + (int64_t)h2 * p.k.sh;
+    const uint16_t* const vh = p.v.p + (int64_t)h2 * p.v.sh;
     auto load_chunk = [&](int c0) {
         const int cs = bs_divides ? c0 / p.bs : 0;
 #pragma unroll
@@ -654,9 +658,9 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
             else { const int n = c0 + r; slot = n / p.bs; rb = n % p.bs; }
             const int blk = blk_s[min(slot, p.count - 1)];
             const bool ok = c0 + r < nk && blk >= 0;
-            const int64_t row = (int64_t)krow0 + (ok ? (int64_t)blk * p.bs + rb : 0);
-            kv[x] = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
-            vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+            const int row = krow0 + (ok ? blk * p.bs + rb : 0);
+            kv[x] = ld16(kh + (int64_t)row * kss + cc);
+            vv[x] = ld16(vh + (int64_t)row * vss + cc);
         }
         const int n = c0 + (tid & (BK - 1));
         int slot, rb;
@@ -676,27 +680,34 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
             st16(&Vs[r * KP + cc], vv[x]);
         }
         if (tid < BK) kpos_s[tid] = kpos_r;
-        __syncthreads();
+        // whether any key of the chunk is masked for this token
+        const bool masked = __syncthreads_or(tid < BK && (kpos_r == 0x7fffffff ||
+                                                          (p.sparse_mode == 2 && kpos_r > t_local)));
         if (c0 + BK < nk) load_chunk(c0 + BK);
         f32x4 s[2], dp[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             s[x] = zero4();
-            dp[x] = zero4();
+            dp[x][0] = dp[x][1] = dp[x][2] = dp[x][3] = -dl;   // dP^T accumulates onto -Delta
             const int kr = 32 * w + 16 * x + col;       // A rows: keys
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 s[x] = T::mma16(ld16(&Ks[kr * KP + 32 * ks + 8 * G16]), qreg[ks], s[x]);
                 dp[x] = T::mma16(ld16(&Vs[kr * KP + 32 * ks + 8 * G16]), doreg[ks], dp[x]);
             }
+            if (masked) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int kl = 32 * w + 16 * x + 4 * G16 + r;   // chunk-local key of this element
-                const int kpos = kpos_s[kl];
-                const bool masked = kpos == 0x7fffffff || (p.sparse_mode == 2 && kpos > t_local);
-                float pv = fast_exp2(__builtin_fmaf(s[x][r], p.scale_log2, -l2));
-                pv = masked ? 0.f : pv;
-                dp[x][r] = pv * (dp[x][r] - dl);
+                for (int r = 0; r < 4; ++r) {
+                    const int kl = 32 * w + 16 * x + 4 * G16 + r;   // chunk-local key of this element
+                    const int kpos = kpos_s[kl];
+                    const bool off = kpos == 0x7fffffff || (p.sparse_mode == 2 && kpos > t_local);
+                    const float pv = fast_exp2(__builtin_fmaf(s[x][r], p.scale_log2, -l2));
+                    dp[x][r] = off ? 0.f : pv * dp[x][r];
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dp[x][r] = fast_exp2(__builtin_fmaf(s[x][r], p.scale_log2, -l2)) * dp[x][r];
             }
         }
         u32x4 bS;
