@@ -359,6 +359,8 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     // row r of a tile: entry r / G, head r % G (r < 256, G <= 32: a multiply
     // and shift divide exactly)
     auto div_g = [&](int r) { return (r * p.g_mul) >> 16; };
+    // token and head strides are below 2^23 elements: 32 x 32 -> 64-bit products
+    const int qss = (int)p.q.ss, qsh = (int)p.q.sh, dss = (int)p.dout.ss, dsh = (int)p.dout.sh;
     auto load_tile = [&](int st) {
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
@@ -367,8 +369,8 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             const int rq = div_g(r);
             const int t = tok_s[min(st * E + rq, n_e - 1)];
             const int h = h2 * p.G + r - rq * p.G;
-            pq[x] = ld16(p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh + cc);
-            pdo[x] = ld16(p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh + cc);
+            pq[x] = ld16(p.q.p + ((int64_t)t * qss + (int64_t)h * qsh + cc));
+            pdo[x] = ld16(p.dout.p + ((int64_t)t * dss + (int64_t)h * dsh + cc));
         }
         {
             const int r = tid & (BR - 1);
@@ -1082,7 +1084,7 @@ bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int t3_ok(const sdpa_tensor3* t) {
     if (t->stride_d != 1 || !a16(t->data) || (t->stride_t % 8) || (t->stride_n % 8)) return SDPA_ERR_UNSUPPORTED;
-    if (!sdpa::row_stride_ok(t->stride_t)) return SDPA_ERR_UNSUPPORTED;
+    if (!sdpa::row_stride_ok(t->stride_t) || !sdpa::row_stride_ok(t->stride_n)) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
 }
 

@@ -206,6 +206,12 @@ def test_fwd_selected_validation():
     assert fwd_selected_call(mode=1) == INVALID
     assert fwd_selected_call(Hq=64) == INVALID          # more than 32 query heads per KV head
     assert fwd_selected_call(D=96) == UNSUPPORTED
+    big = sb.Tensor3(FAKE, 128, 1 << 23, 1)                  # head stride 2^23
+    cu = (ctypes.c_int64 * 1)(512)
+    ts = [t3() for _ in range(4)]
+    ts[1] = big
+    assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 0.088, 2, FAKE, 64, 16, 1, 64, 4,
+                                   *[ctypes.byref(t) for t in ts], FAKE, FAKE, 16, 1, None) == UNSUPPORTED
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
