@@ -524,10 +524,18 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     }
 }
 
-// Sum the partials of blocks split into several pieces (piece order), write
-// zeros for blocks no token selected.  One workgroup per (bucket, 64-key half).
+// Sum the partials of blocks split into several pieces, in piece order; a
+// block no token chose (no piece) gets zeros, and a block with one piece was
+// written by the dK/dV kernel itself.  Grid:
+// (bucket, 64-key half, key group); one (key, 8 values) item per thread,
+// 256 / (D/8) keys per workgroup; the pieces' partials are read four at a
+// time so that their loads are in flight together.
+template <int D>
+constexpr int reduce_key_groups() { return 64 / (256 / (D / 8)); }
+
 template <class T, int D>
 __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
+    constexpr int LPR = D / 8;                  // threads per key row, 8 values each
     const int bucket = blockIdx.x, half = blockIdx.y;
     const int h2 = bucket / p.NB, blk = bucket % p.NB;
     const int kb0 = half * 64;
@@ -535,33 +543,38 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
     const int ps = p.pstart[bucket], np = p.pstart[bucket + 1] - ps;
     if (np == 1) return;
     const int nkeys = min(64, p.bs - kb0);
-    constexpr int LPR = D / 8;                  // threads per key row, 8 values each
-    for (int e = threadIdx.x; e < nkeys * LPR; e += 256) {
-        const int key = e / LPR, d0 = (e % LPR) * 8;
-        float ak[8], av[8];
+    const int key = blockIdx.z * (256 / LPR) + threadIdx.x / LPR, d0 = (threadIdx.x % LPR) * 8;
+    if (key >= nkeys) return;
+    float ak[8], av[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
-        for (int x = 0; x < np; ++x) {
-            const float* pk = p.partial + (((int64_t)(ps + x) * p.halves + half) * 2 * 64 + key) * D + d0;
-            const float* pv = pk + 64 * D;
-            const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ak[i] += k0[i]; ak[4 + i] += k1[i];
-                av[i] += v0[i]; av[4 + i] += v1[i];
-            }
-        }
-        u32x4 ok, ov;
+    for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
+    const float* base = p.partial + ((int64_t)ps * p.halves + half) * 2 * 64 * D + key * D + d0;
+    const int64_t pstride = (int64_t)p.halves * 2 * 64 * D;   // between consecutive pieces
+    auto add = [&](const float* pk) {
+        const float* pv = pk + 64 * D;
+        const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ok[i] = T::pack(ak[2 * i] * p.scale, ak[2 * i + 1] * p.scale);
-            ov[i] = T::pack(av[2 * i], av[2 * i + 1]);
+            ak[i] += k0[i]; ak[4 + i] += k1[i];
+            av[i] += v0[i]; av[4 + i] += v1[i];
         }
-        const int64_t row = (int64_t)blk * p.bs + kb0 + key;
-        st16(p.dk.p + h2 * p.dk.sh + row * p.dk.ss + d0, ok);
-        st16(p.dv.p + h2 * p.dv.sh + row * p.dv.ss + d0, ov);
+    };
+    int x = 0;
+    for (; x + 4 <= np; x += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) add(base + (x + u) * pstride);
     }
+    for (; x < np; ++x) add(base + x * pstride);
+    u32x4 ok, ov;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        ok[i] = T::pack(ak[2 * i] * p.scale, ak[2 * i + 1] * p.scale);
+        ov[i] = T::pack(av[2 * i], av[2 * i + 1]);
+    }
+    const int64_t row = (int64_t)blk * p.bs + kb0 + key;
+    st16(p.dk.p + h2 * p.dk.sh + row * p.dk.ss + d0, ok);
+    st16(p.dv.p + h2 * p.dv.sh + row * p.dv.ss + d0, ov);
 }
 
 // ---------------------------------------------------------------------------
@@ -967,7 +980,8 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, D, false, st);
     if (e != hipSuccess) return e;
     PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, D>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
-    PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves, reduce_key_groups<D>()),
+                dim3(256), 0, st, p);
     PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
