@@ -673,6 +673,7 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
         // dV^T += P^T dO, dK^T += dS^T Q of tile k
         const uint16_t* Qb = Qs0 + bk * TILE;
         const uint16_t* dOb = dOs0 + bk * TILE;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -680,6 +681,7 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
                 dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rh + 16 * hh, db * 32, lane), bP[hh], dva[db]);
                 dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rh + 16 * hh, db * 32, lane), bS[hh], dka[db]);
             }
+        __builtin_amdgcn_s_setprio(0);
         if (has2) store_tile(trn, bk2, i0_k2);
         __syncthreads();
         const int t = bk; bk = bk1; bk1 = bk2; bk2 = t;
@@ -925,6 +927,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
             }
         }
         if (has_next) store_tile(buf ^ 1);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const u32x4 bS = acc_to_operand<T>(dp, hh);
@@ -932,6 +935,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
             for (int db = 0; db < DB; ++db)
                 dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane), bS, dq[db]);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();
     }
 
