@@ -117,7 +117,9 @@ const char* sdpa_last_error(void);
  *   q: (B, Hq, Sq, D); k, v: (B, Hkv, Sk, D); o_out: (B, Hq, Sq, D) written;
  *   lse_out: (B, Hq, Sq) written, natural-log LSE of the scaled scores.
  *   Hq must be a multiple of Hkv; query head h reads KV head h / (Hq/Hkv).
- *   causal: key j visible to query i iff j <= i (requires Sq == Sk).
+ *   causal: key j visible to query i iff j <= i, for any Sq and Sk (aligned
+ *   at the top left, as the PyTorch is_causal reference that the cuDNN sample
+ *   checks against, last code cell): queries i >= Sk see every key.
  * Needs no workspace.
  */
 int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
@@ -135,9 +137,9 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
  *   q: (Tq, Hq, D); k, v: (Tk, Hkv, D); o_out: (Tq, Hq, D) written.
  *   lse_out: natural-log LSE of token t, head n at t*stride_s + n*stride_h
  *   (stride_b unused), written for every query token.
- *   causal: per sequence, key j visible to query i iff j <= i (equal lengths
- *   per sequence required, else SDPA_ERR_INVALID).  A query with no visible
- *   key (empty key sequence) gets O = 0 and LSE = -inf.
+ *   causal: per sequence, key j visible to query i iff j <= i in local
+ *   positions (top-left aligned; the lengths may differ).  A query with no
+ *   visible key (empty key sequence) gets O = 0 and LSE = -inf.
  * Needs no workspace; errors as sdpa_fwd_stats.
  */
 int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
@@ -180,8 +182,8 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
  * (the Ascend page's actualSeqQLen / actualSeqKvLen, "cumulative sum length
  * of S for each batch", passed as host integer arrays; its example passes {1}
  * and {1024} for one sequence).  Sequence b owns rows [cu[b-1], cu[b]) with
- * cu[-1] = 0.  Causal masking uses positions local to each sequence and
- * requires equal query and key lengths per sequence.
+ * cu[-1] = 0.  Causal masking uses positions local to each sequence (j <= i,
+ * top-left aligned when the query and key lengths differ).
  *   q, o, dout, dq: (Tq, Hq, D); k, v, dk, dv: (Tk, Hkv, D); stats per (t, h).
  *   deterministic: as for sdpa_bwd (0, 1 or 2).
  */

@@ -44,7 +44,10 @@ __all__ = [
 
 def causal_mask(sq: int, sk: int) -> np.ndarray:
     """Admissible set of the causal mask: key j is visible to query i iff j <= i
-    (the cuDNN sample's ``use_causal_mask``; only Sq == Sk occurs)."""
+    (the cuDNN sample's ``use_causal_mask``).  For Sq != Sk this is the top-left
+    alignment of the PyTorch ``is_causal`` reference that the sample checks
+    against (cudnn-frontend notebook, last code cell): queries i >= Sk see
+    every key, keys j >= Sq are seen by no query."""
     return np.arange(sk)[None, :] <= np.arange(sq)[:, None]
 
 

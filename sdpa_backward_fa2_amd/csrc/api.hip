@@ -132,13 +132,12 @@ struct Packed {
     int64_t Tq = 0, Tk = 0, max_lq = 0, max_lk = 0;
 };
 
-int read_packed(int64_t batch, const int64_t* cuq, const int64_t* cuk, bool same_len, Packed& P) {
+int read_packed(int64_t batch, const int64_t* cuq, const int64_t* cuk, Packed& P) {
     int64_t pq = 0, pk = 0;
     for (int64_t b = 0; b < batch; ++b) {
         const int64_t eq = cuq[b], ek = cuk[b];
         if (eq < pq || ek < pk) return SDPA_ERR_INVALID;
         const int64_t lq = eq - pq, lk = ek - pk;
-        if (same_len && lq != lk) return SDPA_ERR_INVALID;
         if (lq >= kMaxLen || lk >= kMaxLen) return SDPA_ERR_UNSUPPORTED;
         P.q0.push_back(pq); P.k0.push_back(pk); P.lq.push_back(lq); P.lk.push_back(lk);
         P.max_lq = std::max(P.max_lq, lq);
@@ -185,7 +184,6 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
-    if (causal && Sq != Sk) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o_out})
@@ -221,7 +219,7 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     Packed P;
-    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, causal != 0, P)) return s;
+    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o_out})
         if (int s = tensor3_ok(t)) return s;
@@ -333,7 +331,6 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
-    if (causal && Sq != Sk) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
@@ -380,7 +377,7 @@ int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_s
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     Packed P;
-    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, false, P)) return s;
+    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     *bytes = carve_bwd(P.Tq * Hq, D, !dq_atomic(deterministic, D)).total;
@@ -406,7 +403,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
     Packed P;
-    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, causal != 0, P)) return s;
+    if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
     if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;

@@ -58,7 +58,7 @@ def test_dense_validation_order():
     assert dense_call(Hq=3, Hkv=2) == INVALID
     assert dense_call(Hkv=0) == INVALID
     assert dense_call(B=-1) == INVALID
-    assert dense_call(causal=1, Sk=64) == INVALID
+    assert dense_call(causal=1, Sk=64) == HIP     # causal Sq != Sk is valid (top-left); no device here
     assert dense_call(scale=float("nan")) == INVALID
     assert dense_call(det=3) == INVALID          # dQ mode outside 0..2
     assert dense_call(det=-1) == INVALID
@@ -121,7 +121,7 @@ def varlen_call(cu_q, cu_k, **kw):
 
 def test_varlen_validation():
     assert varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
-    assert varlen_call([100, 300], [100, 200]) == INVALID         # causal with unequal lengths
+    assert varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths: valid; no device
     assert varlen_call([100, 300], [100, 300], Hq=3, Hkv=2) == INVALID
     assert varlen_call([100, 300], [100, 300], D=192) == UNSUPPORTED
     assert varlen_call([100, 300], [100, 300], ws_bytes=8) == WORKSPACE
@@ -158,7 +158,7 @@ def fwd_call(**kw):
 
 def test_fwd_validation():
     assert fwd_call(Hq=3, Hkv=2) == INVALID
-    assert fwd_call(causal=1, Sk=32) == INVALID
+    assert fwd_call(causal=1, Sk=32) == HIP       # causal Sq != Sk is valid; no device here
     assert fwd_call(D=256) == UNSUPPORTED
     assert fwd_call(dtype=2) == INVALID
 
@@ -177,7 +177,7 @@ def fwd_varlen_call(cu_q, cu_k, **kw):
 def test_fwd_varlen_validation():
     assert fwd_varlen_call([100, 300], [100, 300], lse=None) == NULLPTR
     assert fwd_varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
-    assert fwd_varlen_call([100, 300], [100, 200]) == INVALID         # causal, unequal lengths
+    assert fwd_varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths: valid
     assert fwd_varlen_call([100, 300], [100, 300], Hq=3) == INVALID   # heads not grouped
     assert fwd_varlen_call([100, 300], [100, 300], dtype=4) == INVALID
     assert fwd_varlen_call([100, 300], [100, 300], D=96) == UNSUPPORTED

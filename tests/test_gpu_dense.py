@@ -158,6 +158,18 @@ def test_sweep_rectangular_noncausal(Sq, Sk):
     _check_case(1, 3, 3, Sq, Sk, 64, "f16", False, "bhsd", seed=Sq * Sk)
 
 
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16")])
+@pytest.mark.parametrize("Sq,Sk", [(64, 300), (257, 129), (5, 1), (1, 77), (200, 64), (130, 131)])
+def test_sweep_rectangular_causal(Sq, Sk, D, dtype):
+    """Causal with Sq != Sk, top-left aligned: keys past the last query get
+    dK = dV = 0, queries past the last key see every key."""
+    _check_case(1, 3, 3, Sq, Sk, D, dtype, True, "bshd", seed=Sq * Sk + D)
+
+
+def test_rectangular_causal_gqa():
+    _check_case(2, 4, 2, 96, 230, 128, "f16", True, "bhsd", seed=77)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1)])
 @pytest.mark.parametrize("causal", [False, True])

@@ -68,6 +68,12 @@ def test_noncausal_unequal_and_empty_key_sequence():
     _fwd_case([100, 7, 250], [37, 0, 129], 3, 3, 64, "f16", False, seed=21, backward=False)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_unequal_lengths(D):
+    # top-left causal per sequence; the third sequence has no keys
+    _fwd_case([100, 7, 64, 250], [37, 300, 0, 129], 2, 2, D, "f16", True, seed=25 + D)
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (16, 1)])
 def test_gqa(Hq, Hkv):
     _fwd_case([130, 257], [130, 257], Hq, Hkv, 128, "bf16", True, seed=22 + Hq)

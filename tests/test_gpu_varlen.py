@@ -100,6 +100,14 @@ def test_noncausal_unequal_lengths():
     _case([100, 1, 250], [37, 300, 129], 3, 3, 64, "f16", False, seed=5)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_causal_unequal_lengths(D):
+    """Causal per sequence with different query and key lengths (top-left in
+    local positions); a sequence without keys gives dQ = 0 and one without
+    queries dK = dV = 0."""
+    _case([100, 1, 250, 0, 64, 9], [37, 300, 129, 20, 0, 9], 2, 2, D, "bf16", True, seed=30 + D)
+
+
 def test_zero_length_query_sequence_zeroes_its_keys():
     # a sequence with keys but no queries gets dK = dV = 0
     _case([50, 0, 70], [50, 90, 70], 2, 2, 64, "bf16", False, seed=6)

@@ -44,10 +44,8 @@ def _finite_diff(q, k, v, do, scale, allowed, h=1e-6):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("sq,sk,d,dv", [(5, 5, 3, 3), (7, 7, 4, 2), (3, 6, 2, 4)])
+@pytest.mark.parametrize("sq,sk,d,dv", [(5, 5, 3, 3), (7, 7, 4, 2), (3, 6, 2, 4), (6, 3, 3, 2)])
 def test_finite_differences(causal, sq, sk, d, dv):
-    if causal and sq != sk:
-        pytest.skip("causal is only defined for Sq == Sk")
     q, k, v, do = _rand(sq, d), _rand(sk, d), _rand(sk, dv), _rand(sq, dv)
     scale = 0.7
     allowed = oracle.causal_mask(sq, sk) if causal else None
@@ -183,6 +181,28 @@ def test_against_torch_fp64(causal, hq, hkv):
         .masked_fill(~torch.tensor(oracle.causal_mask(S, S)) if causal else torch.zeros(S, S, dtype=torch.bool),
                      float("-inf")), dim=-1).numpy()
     np.testing.assert_allclose(f["lse"], ref_lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("sq,sk", [(19, 45), (45, 19)])
+def test_causal_unequal_lengths_against_torch_fp64(sq, sk):
+    """Causal with Sq != Sk: the top-left alignment of torch's is_causal (the
+    sample's checking recipe).  Keys past the last query get no gradient, and
+    queries past the last key equal the unmasked rows."""
+    B, H, D = 2, 2, 8
+    q, do = _rand(B, H, sq, D), _rand(B, H, sq, D)
+    k, v = _rand(B, H, sk, D), _rand(B, H, sk, D)
+    scale = 0.3
+    f = oracle.dense_forward(q, k, v, scale, True)
+    g = oracle.dense_backward(q, k, v, do, scale, True)
+    o_t, dq_t, dk_t, dv_t = _torch_reference(q, k, v, do, scale, True)
+    for got, ref in ((f["O"], o_t), (g["dq"], dq_t), (g["dk"], dk_t), (g["dv"], dv_t)):
+        np.testing.assert_allclose(got, ref, atol=1e-12)
+    if sk > sq:
+        assert np.all(g["dk"][:, :, sq:] == 0) and np.all(g["dv"][:, :, sq:] == 0)
+    else:
+        full = oracle.dense_forward(q, k, v, scale, False)
+        np.testing.assert_allclose(f["O"][:, :, sk:], full["O"][:, :, sk:], atol=1e-13)
+        np.testing.assert_allclose(f["lse"][:, :, sk:], full["lse"][:, :, sk:], atol=1e-13)
 
 
 def test_dense_heads_subset_matches_full():
