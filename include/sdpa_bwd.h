@@ -16,9 +16,12 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - Element types: Q, K, V, O, dO, dQ, dK, dV are all fp16 or all bf16
- *   (sdpa_dtype); statistics are fp32.  Arithmetic is fp32 with 16-bit MFMA
- *   operands (the sample's io=HALF, intermediate=compute=FLOAT graph).
+ * - Element types: Q, K, V, O and dO are all fp16 or all bf16 (sdpa_dtype);
+ *   the gradients dQ, dK, dV are that type or fp32 (grad_dtype of the
+ *   backward entry points; the Ascend parameter table lists FLOAT16, BFLOAT16
+ *   and FLOAT32 for dqOut, dkOut and dvOut); statistics are fp32.  Arithmetic
+ *   is fp32 with 16-bit MFMA operands (the sample's io=HALF,
+ *   intermediate=compute=FLOAT graph).
  * - Layout: every tensor is a strided view, strides counted in ELEMENTS.  Dense
  *   tensors are logical (B, H, S, D) with any strides, e.g. the sample's BSHD
  *   physical / BHSD logical strides (S*H*D, D, H*D, 1).  Packed tensors are
@@ -63,9 +66,10 @@ typedef enum sdpa_status {
     SDPA_ERR_HIP = 5
 } sdpa_status;
 
-/* 16-bit element type of Q, K, V, O, dO and of the gradients (Ascend parameter
- * table: BFLOAT16 or FLOAT16). */
-typedef enum sdpa_dtype { SDPA_F16 = 0, SDPA_BF16 = 1 } sdpa_dtype;
+/* Element types (Ascend parameter table): Q, K, V, O and dO are BFLOAT16 or
+ * FLOAT16; the gradients are that type or, as grad_dtype = SDPA_F32, FLOAT32
+ * (the fp32 accumulators written without rounding to 16 bits). */
+typedef enum sdpa_dtype { SDPA_F16 = 0, SDPA_BF16 = 1, SDPA_F32 = 2 } sdpa_dtype;
 
 /* Form of the per-row softmax statistics.
  * SDPA_STATS_LSE:     one value per row, LSE_i = ln sum_j exp(S_ij) over the
@@ -163,13 +167,16 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  *        differences possible); D=128 only, D=64 has no atomic kernel and
  *        runs mode 1.
  *     Any other value: SDPA_ERR_INVALID.  The workspace size depends on it.
+ *   grad_dtype: element type of dq, dk and dv: `dtype`, or SDPA_F32 for fp32
+ *     gradients (same layout rules, strides in fp32 elements); anything else
+ *     is SDPA_ERR_INVALID.  It does not change the workspace size.
  *   workspace: device memory of at least *bytes from the size query, any
  *     contents on entry, 256-byte aligned.
  */
 int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
                             int64_t Sk, int64_t D, int deterministic, size_t* bytes);
 int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-             double scale, int causal, int deterministic,
+             double scale, int causal, int deterministic, int grad_dtype,
              const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
              const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
              const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
@@ -185,14 +192,14 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
  * cu[-1] = 0.  Causal masking uses positions local to each sequence (j <= i,
  * top-left aligned when the query and key lengths differ).
  *   q, o, dout, dq: (Tq, Hq, D); k, v, dk, dv: (Tk, Hkv, D); stats per (t, h).
- *   deterministic: as for sdpa_bwd (0, 1 or 2).
+ *   deterministic, grad_dtype: as for sdpa_bwd.
  */
 int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
                                    int64_t D, int deterministic, size_t* bytes);
 int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                     const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
-                    double scale, int causal, int deterministic,
+                    double scale, int causal, int deterministic, int grad_dtype,
                     const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                     const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
                     const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
@@ -217,6 +224,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   ignored); the statistics must then describe the same reduced key set.
  *   Every kernel of this path is deterministic; the flag (0, 1 or 2, else
  *   SDPA_ERR_INVALID) is accepted for symmetry with the other entry points.
+ *   grad_dtype: `dtype` or SDPA_F32, as for sdpa_bwd.
  */
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
@@ -226,7 +234,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
-                      int deterministic,
+                      int deterministic, int grad_dtype,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                       const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
                       const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,

@@ -29,7 +29,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "sdpa_bwd.h")
 
 STATUS = {0: "SDPA_OK", 1: "SDPA_ERR_NULLPTR", 2: "SDPA_ERR_INVALID", 3: "SDPA_ERR_UNSUPPORTED",
           4: "SDPA_ERR_WORKSPACE", 5: "SDPA_ERR_HIP"}
-F16, BF16 = 0, 1
+F16, BF16, F32 = 0, 1, 2
 STATS_LSE, STATS_MAX_SUM = 0, 1
 
 c_i64 = ctypes.c_int64
@@ -77,16 +77,16 @@ _SIGS = {
                                       P3, P3, P3, P3, ctypes.POINTER(StatsOut), c_vp]),
     "sdpa_bwd_workspace_size": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
                                         ctypes.POINTER(c_size)]),
-    "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int,
+    "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                          P4, P4, P4, P4, P4, PS, P4, P4, P4, c_vp, c_size, c_vp]),
     "sdpa_bwd_varlen_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_int,
                                                ctypes.POINTER(c_size)]),
-    "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int,
+    "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                                 P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
     "sdpa_bwd_selected_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64,
                                                  c_i64, c_i64, c_int, ctypes.POINTER(c_size)]),
     "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
-                                  c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
+                                  c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int, c_int,
                                   P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
     "sdpa_fwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                   c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
@@ -178,6 +178,23 @@ def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
     raise TypeError(f"expected float16 or bfloat16, got {t.dtype}")
+
+
+def _grads(q, k, v, dq, dk, dv, grad_dtype):
+    """The gradient tensors (allocated like q, k, v when not given, in
+    grad_dtype or the input dtype) and their element-type code: the input
+    type or fp32, the same for all three."""
+    want = q.dtype if grad_dtype is None else grad_dtype
+    dq = torch.empty_like(q, dtype=want) if dq is None else dq
+    dk = torch.empty_like(k, dtype=want) if dk is None else dk
+    dv = torch.empty_like(v, dtype=want) if dv is None else dv
+    if not (dq.dtype == dk.dtype == dv.dtype):
+        raise TypeError(f"gradients differ in dtype: {dq.dtype}, {dk.dtype}, {dv.dtype}")
+    if dq.dtype == torch.float32:
+        return dq, dk, dv, F32
+    if dq.dtype != q.dtype:
+        raise TypeError(f"gradients must be {q.dtype} or float32, got {dq.dtype}")
+    return dq, dk, dv, _dtype_code(q)
 
 
 def _stream_ptr(device: torch.device) -> int:
@@ -282,22 +299,21 @@ def _stats_arg(stats, packed: bool) -> Stats:
 
 
 def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
-                dq=None, dk=None, dv=None, workspace=None):
+                dq=None, dk=None, dv=None, workspace=None, grad_dtype=None):
     """Marshal the arguments of one dense backward once; returns (call, (dq, dk, dv))
     where call() enqueues the backward on the current stream.  The tensors must
-    stay alive and unmoved while call is used."""
+    stay alive and unmoved while call is used.  Gradients are q's dtype or
+    float32 (given tensors, else grad_dtype)."""
     lib = load()
     B, Hq, Sq, D = q.shape
     Hkv, Sk = k.shape[1], k.shape[2]
     dt = _dtype_code(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     nbytes = bwd_workspace_size(dt, B, Hq, Hkv, Sq, Sk, D, deterministic)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=False)
     structs = [_t4(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal), int(deterministic),
+    args = (dt, B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal), int(deterministic), gdt,
             *[ctypes.byref(x) for x in structs[:5]], ctypes.byref(sa),
             *[ctypes.byref(x) for x in structs[5:]], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
@@ -312,12 +328,13 @@ def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, determinist
 
 
 def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
-        dq=None, dk=None, dv=None, workspace=None):
+        dq=None, dk=None, dv=None, workspace=None, grad_dtype=None):
     """dQ, dK, dV of dense attention.  stats: LSE (B, Hq, Sq[, 1]) or (max, sum).
     deterministic: DQ_FASTEST (0), DQ_DETERMINISTIC (1) or DQ_ATOMIC (2); a
-    bool is read as 0 or 1."""
+    bool is read as 0 or 1.  grad_dtype: torch.float32 for fp32 gradients
+    (default: q's dtype, or that of the given dq, dk, dv)."""
     call, outs = prepare_bwd(q, k, v, o, dout, stats, scale, causal, deterministic, dq, dk, dv,
-                             workspace)
+                             workspace, grad_dtype)
     call()
     return outs
 
@@ -341,7 +358,8 @@ def bwd_varlen_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, deterministic) -> 
 
 
 def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
-                   deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None):
+                   deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None,
+                   grad_dtype=None):
     """Marshal one packed (T, N, D) backward once; returns (call, (dq, dk, dv)).
     cu_q / cu_kv: host sequences of inclusive end offsets; stats: LSE (T, Hq)
     or a (max, sum) pair of (T, Hq[, 8]) tensors."""
@@ -349,16 +367,14 @@ def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: b
     Hq, D = q.shape[1], q.shape[2]
     Hkv = k.shape[1]
     dt = _dtype_code(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
     nbytes = bwd_varlen_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, deterministic)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
     structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(causal), int(deterministic),
+    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(causal), int(deterministic), gdt,
             *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
     fn = lib.sdpa_bwd_varlen
@@ -372,11 +388,12 @@ def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: b
 
 
 def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
-               deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None):
+               deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None, workspace=None,
+               grad_dtype=None):
     """Packed (T, N, D) backward; cu_q / cu_kv: host sequences of inclusive end
     offsets; stats: LSE (T, Hq) or a (max, sum) pair of (T, Hq[, 8]) tensors."""
     call, outs = prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale, causal, deterministic,
-                                dq, dk, dv, workspace)
+                                dq, dk, dv, workspace, grad_dtype)
     call()
     return outs
 
@@ -398,7 +415,7 @@ def bwd_selected_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, block_size, bloc
 
 def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
                      sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
-                     workspace=None):
+                     workspace=None, grad_dtype=None):
     """Marshal one NSA selected-attention backward once; returns (call, (dq, dk, dv)).
     topk: int32 (T, Hkv, count) on the device."""
     lib = load()
@@ -406,9 +423,7 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
     Hkv = k.shape[1]
     count = topk.shape[2]
     dt = _dtype_code(q)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
     nbytes = bwd_selected_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, block_size, count, deterministic)
@@ -416,7 +431,7 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
     sa = _stats_arg(stats, packed=True)
     structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
     args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
-            topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic),
+            topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic), gdt,
             *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
     fn = lib.sdpa_bwd_selected
@@ -431,10 +446,11 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
 
 def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
                  sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
-                 workspace=None):
-    """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device."""
+                 workspace=None, grad_dtype=None):
+    """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device;
+    gradients in q's dtype or float32 (grad_dtype, or the given tensors')."""
     call, outs = prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size, scale,
-                                  sparse_mode, deterministic, dq, dk, dv, workspace)
+                                  sparse_mode, deterministic, dq, dk, dv, workspace, grad_dtype)
     call()
     return outs
 

@@ -318,7 +318,7 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
 }
 
 int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-             double scale, int causal, int deterministic,
+             double scale, int causal, int deterministic, int grad_dtype,
              const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
              const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
              const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
@@ -329,6 +329,7 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     if (int s = check_stats(stats)) return s;
     if (!workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
@@ -351,6 +352,7 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     sdpa::BwdParams p{};
     p.q = arg4(q); p.k = arg4(k); p.v = arg4(v); p.o = arg4(o); p.dout = arg4(dout);
     p.dq = arg4(dq); p.dk = arg4(dk); p.dv = arg4(dv);
+    p.grad_f32 = grad_dtype == SDPA_F32;
     fill_stats(p, stats);
     p.lse2 = reinterpret_cast<float*>(ws + cv.lse2);
     p.delta = reinterpret_cast<float*>(ws + cv.delta);
@@ -386,7 +388,7 @@ int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_s
 
 int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                     const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
-                    double scale, int causal, int deterministic,
+                    double scale, int causal, int deterministic, int grad_dtype,
                     const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                     const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
                     const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
@@ -398,6 +400,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (int s = check_stats(stats)) return s;
     if (!workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
@@ -419,6 +422,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     sdpa::BwdParams p{};
     p.q = arg3(q); p.k = arg3(k); p.v = arg3(v); p.o = arg3(o); p.dout = arg3(dout);
     p.dq = arg3(dq); p.dk = arg3(dk); p.dv = arg3(dv);
+    p.grad_f32 = grad_dtype == SDPA_F32;
     fill_stats(p, stats);
     p.st_sb = 0;
     p.lse2 = reinterpret_cast<float*>(ws + cv.lse2);

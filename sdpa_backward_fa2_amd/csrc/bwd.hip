@@ -416,19 +416,17 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     }
 
     if (!col_ok) return;
-    uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
-    uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
+    const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
+    const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            u32x2 a, v;
-            a[0] = T::pack(dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale);
-            a[1] = T::pack(dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-            v[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
-            v[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
-            st8(dkp + db * 32 + 8 * q + 4 * g, a);
-            st8(dvp + db * 32 + 8 * q + 4 * g, v);
+            const int e = db * 32 + 8 * q + 4 * g;
+            st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
+                        dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+            st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
+                        dva[db][4 * q + 3]);
         }
 }
 
@@ -713,19 +711,17 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
             v[4 * r4 + 0] += x[0]; v[4 * r4 + 1] += x[1]; v[4 * r4 + 2] += x[2]; v[4 * r4 + 3] += x[3];
         }
     }
-    uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
-    uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
+    const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
+    const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            u32x2 a, v;
-            a[0] = T::pack(dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale);
-            a[1] = T::pack(dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-            v[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
-            v[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
-            st8(dkp + db * 32 + 8 * q + 4 * g, a);
-            st8(dvp + db * 32 + 8 * q + 4 * g, v);
+            const int e = db * 32 + 8 * q + 4 * g;
+            st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
+                        dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+            st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
+                        dva[db][4 * q + 3]);
         }
 }
 
@@ -743,12 +739,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
     const RowLoc L = row_of(p, R);
     const f32x4* src = reinterpret_cast<const f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 8);
     const f32x4 a = src[0], c = src[1];
-    u32x4 o;
-    o[0] = T::pack(a[0] * p.scale, a[1] * p.scale);
-    o[1] = T::pack(a[2] * p.scale, a[3] * p.scale);
-    o[2] = T::pack(c[0] * p.scale, c[1] * p.scale);
-    o[3] = T::pack(c[2] * p.scale, c[3] * p.scale);
-    st16(p.dq.p + toff(p.dq, L) + part * 8, o);
+    const float x[8] = {a[0] * p.scale, a[1] * p.scale, a[2] * p.scale, a[3] * p.scale,
+                        c[0] * p.scale, c[1] * p.scale, c[2] * p.scale, c[3] * p.scale};
+    st_grad8<T>(p.dq.p, toff(p.dq, L) + part * 8, p.grad_f32, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -962,16 +955,13 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
                 dq[db][4 * r4 + 0] += x[0]; dq[db][4 * r4 + 1] += x[1];
                 dq[db][4 * r4 + 2] += x[2]; dq[db][4 * r4 + 3] += x[3];
             }
-    uint16_t* dqp = p.dq.p + b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
+    const int64_t dqo = b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            u32x2 v;
-            v[0] = T::pack(dq[db][4 * q + 0] * p.scale, dq[db][4 * q + 1] * p.scale);
-            v[1] = T::pack(dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
-            st8(dqp + db * 32 + 8 * q + 4 * g, v);
-        }
+        for (int q = 0; q < 4; ++q)
+            st_grad4<T>(p.dq.p, dqo + db * 32 + 8 * q + 4 * g, p.grad_f32, dq[db][4 * q + 0] * p.scale,
+                        dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
 }
 
 template <class T, int D, bool CAUSAL>

@@ -130,6 +130,35 @@ __device__ __forceinline__ float ldf_at(const float* base, uint32_t off) {
 }
 __device__ __forceinline__ void st8(uint16_t* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// Gradient outputs hold either the input dtype T (f32 == 0) or fp32; `off`
+// counts elements from `base`, so both forms use the caller's element strides.
+template <class T>
+__device__ __forceinline__ void st_grad4(uint16_t* base, int64_t off, int f32, float a, float b, float c, float d) {
+    if (f32) {
+        const f32x4 v = {a, b, c, d};
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off) = v;
+    } else {
+        u32x2 v;
+        v[0] = T::pack(a, b);
+        v[1] = T::pack(c, d);
+        st8(base + off, v);
+    }
+}
+template <class T>
+__device__ __forceinline__ void st_grad8(uint16_t* base, int64_t off, int f32, const float* x) {
+    if (f32) {
+        const f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+        f32x4* d = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off);
+        d[0] = lo;
+        d[1] = hi;
+    } else {
+        u32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = T::pack(x[2 * i], x[2 * i + 1]);
+        st16(base + off, v);
+    }
+}
+
 __device__ __forceinline__ uint16_t elem16(u32x4 v, int t) {
     uint32_t w = v[t >> 1];
     return (uint16_t)((t & 1) ? (w >> 16) : (w & 0xffffu));
@@ -284,6 +313,7 @@ struct BwdParams {
     int B, Hq, Hkv, Sq, Sk;   // Sq/Sk: dense lengths (packed: Tq/Tk totals)
     int64_t rows;             // number of statistics rows R
     int varlen;
+    int grad_f32;             // dQ, dK, dV are fp32 (else the input dtype)
     SeqTable seqs;
     float scale, scale_log2;
 };

@@ -61,6 +61,7 @@ struct NsaParams {
     int halves;           // ceil(bs / 64)
     int sparse_mode;
     int Tq;
+    int grad_f32;         // dQ, dK, dV are fp32 (else the input dtype)
     float scale, scale_log2;
     // forward outputs
     TensorArg o;
@@ -494,19 +495,17 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     }
     const int npieces = p.pstart[bucket + 1] - p.pstart[bucket];
     if (npieces == 1) {
-        uint16_t* dkp = p.dk.p + h2 * p.dk.sh + (int64_t)(key_row0 + myk) * p.dk.ss;
-        uint16_t* dvp = p.dv.p + h2 * p.dv.sh + (int64_t)(key_row0 + myk) * p.dv.ss;
+        const int64_t dko = h2 * p.dk.sh + (int64_t)(key_row0 + myk) * p.dk.ss;
+        const int64_t dvo = h2 * p.dv.sh + (int64_t)(key_row0 + myk) * p.dv.ss;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                u32x2 a, v;
-                a[0] = T::pack(dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale);
-                a[1] = T::pack(dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-                v[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
-                v[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
-                st8(dkp + db * 32 + 8 * q + 4 * g, a);
-                st8(dvp + db * 32 + 8 * q + 4 * g, v);
+                const int e = db * 32 + 8 * q + 4 * g;
+                st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
+                            dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+                st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
+                            dva[db][4 * q + 3]);
             }
     } else {
         // fp32 partial [piece][half][key][d] for dK, then the same for dV
@@ -566,15 +565,11 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
         for (int u = 0; u < 4; ++u) add(base + (x + u) * pstride);
     }
     for (; x < np; ++x) add(base + x * pstride);
-    u32x4 ok, ov;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        ok[i] = T::pack(ak[2 * i] * p.scale, ak[2 * i + 1] * p.scale);
-        ov[i] = T::pack(av[2 * i], av[2 * i + 1]);
-    }
+    for (int i = 0; i < 8; ++i) ak[i] *= p.scale;
     const int64_t row = (int64_t)blk * p.bs + kb0 + key;
-    st16(p.dk.p + h2 * p.dk.sh + row * p.dk.ss + d0, ok);
-    st16(p.dv.p + h2 * p.dv.sh + row * p.dv.ss + d0, ov);
+    st_grad8<T>(p.dk.p, h2 * p.dk.sh + row * p.dk.ss + d0, p.grad_f32, ak);
+    st_grad8<T>(p.dv.p, h2 * p.dv.sh + row * p.dv.ss + d0, p.grad_f32, av);
 }
 
 // ---------------------------------------------------------------------------
@@ -754,14 +749,11 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
             dq[db][0] += v[0]; dq[db][1] += v[1]; dq[db][2] += v[2]; dq[db][3] += v[3];
         }
     // dQ^T tile: lane holds head `col`, head dims 16*db + 4*G16 + r
-    uint16_t* dqp = p.dq.p + (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
+    const int64_t dqo = (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-        u32x2 v;
-        v[0] = T::pack(dq[db][0] * p.scale, dq[db][1] * p.scale);
-        v[1] = T::pack(dq[db][2] * p.scale, dq[db][3] * p.scale);
-        st8(dqp + 16 * db + 4 * G16, v);
-    }
+    for (int db = 0; db < DB; ++db)
+        st_grad4<T>(p.dq.p, dqo + 16 * db + 4 * G16, p.grad_f32, dq[db][0] * p.scale, dq[db][1] * p.scale,
+                    dq[db][2] * p.scale, dq[db][3] * p.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -1192,7 +1184,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
-                      int deterministic,
+                      int deterministic, int grad_dtype,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                       const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
                       const sdpa_tensor3* dq, const sdpa_tensor3* dk, const sdpa_tensor3* dv,
@@ -1204,6 +1196,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (!stats->lse_or_max || (stats->kind == SDPA_STATS_MAX_SUM && !stats->sum)) return SDPA_ERR_NULLPTR;
     if (!workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
+    if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     // every kernel of this path is deterministic, whatever dQ mode is asked for
     if (deterministic < 0 || deterministic > 2) return SDPA_ERR_INVALID;
@@ -1225,6 +1218,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     fill_index_params(p, S, L, ws, topk, tk_st, tk_sn, tk_sk, Hq, Hkv, block_size, block_count);
     p.q = arg(q); p.k = arg(k); p.v = arg(v); p.dout = arg(dout);
     p.dq = arg(dq); p.dk = arg(dk); p.dv = arg(dv);
+    p.grad_f32 = grad_dtype == SDPA_F32;
     p.lse2 = reinterpret_cast<float*>(ws + L.lse2);
     p.delta = reinterpret_cast<float*>(ws + L.delta);
     p.partial = reinterpret_cast<float*>(ws + L.partial);

@@ -38,13 +38,14 @@ def t4(ptr=FAKE, strides=(16384, 8192, 64, 1)):
 
 
 def dense_call(**kw):
-    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, scale=0.125, causal=0, det=0,
+    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, scale=0.125, causal=0, det=0, grad=None,
              q=t4(), k=t4(), v=t4(), o=t4(), do=t4(), dq=t4(), dk=t4(), dv=t4(),
              stats=sb.Stats(0, FAKE, None, 256, 128, 1), ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     ref = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
+    grad = a["dtype"] if a["grad"] is None else a["grad"]
     return lib().sdpa_bwd(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"],
-                          a["causal"], a["det"], ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["o"]),
+                          a["causal"], a["det"], grad, ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["o"]),
                           ref(a["do"]), ref(a["stats"]), ref(a["dq"]), ref(a["dk"]), ref(a["dv"]),
                           a["ws"], a["ws_bytes"], None)
 
@@ -58,7 +59,8 @@ def test_dense_validation_order():
     assert dense_call(Hq=3, Hkv=2) == INVALID
     assert dense_call(Hkv=0) == INVALID
     assert dense_call(B=-1) == INVALID
-    assert dense_call(causal=1, Sk=64) == HIP     # causal Sq != Sk is valid (top-left); no device here
+    assert dense_call(grad=1) == INVALID          # gradients: the input dtype or fp32
+    assert dense_call(grad=3) == INVALID
     assert dense_call(scale=float("nan")) == INVALID
     assert dense_call(det=3) == INVALID          # dQ mode outside 0..2
     assert dense_call(det=-1) == INVALID
@@ -81,6 +83,8 @@ def test_dense_validation_order():
 def test_valid_call_without_device_reports_hip_error():
     assert dense_call() == HIP
     assert lib().sdpa_last_error()
+    assert dense_call(causal=1, Sk=64) == HIP     # causal with Sq != Sk (top-left) is valid
+    assert dense_call(grad=2) == HIP              # fp32 gradients
 
 
 def test_workspace_size_query():
@@ -107,21 +111,21 @@ def t3(ptr=FAKE, strides=(32 * 128, 128, 1)):
 
 
 def varlen_call(cu_q, cu_k, **kw):
-    a = dict(dtype=1, Hq=32, Hkv=32, D=128, scale=0.088, causal=1, det=0, ws_bytes=1 << 34)
+    a = dict(dtype=1, Hq=32, Hkv=32, D=128, scale=0.088, causal=1, det=0, grad=1, ws_bytes=1 << 34)
     a.update(kw)
     aq = (ctypes.c_int64 * len(cu_q))(*cu_q)
     ak = (ctypes.c_int64 * len(cu_k))(*cu_k)
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
     ts = [t3() for _ in range(8)]
     return lib().sdpa_bwd_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], a["scale"],
-                                 a["causal"], a["det"], *[ctypes.byref(t) for t in ts[:5]],
+                                 a["causal"], a["det"], a["grad"], *[ctypes.byref(t) for t in ts[:5]],
                                  ctypes.byref(st), *[ctypes.byref(t) for t in ts[5:]], FAKE,
                                  a["ws_bytes"], None)
 
 
 def test_varlen_validation():
     assert varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
-    assert varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths: valid; no device
+    assert varlen_call([100, 300], [100, 300], grad=0) == INVALID  # bf16 inputs, fp16 gradients
     assert varlen_call([100, 300], [100, 300], Hq=3, Hkv=2) == INVALID
     assert varlen_call([100, 300], [100, 300], D=192) == UNSUPPORTED
     assert varlen_call([100, 300], [100, 300], ws_bytes=8) == WORKSPACE
@@ -137,7 +141,7 @@ def test_varlen_validation():
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
     ts = [t3() for _ in range(8)]
     ts[2] = big
-    assert lib().sdpa_bwd_varlen(1, 2, cu, cu, 32, 32, 128, 0.088, 1, 0,
+    assert lib().sdpa_bwd_varlen(1, 2, cu, cu, 32, 32, 128, 0.088, 1, 0, 1,
                                  *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
                                  *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None) == UNSUPPORTED
 
@@ -145,6 +149,8 @@ def test_varlen_validation():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_varlen_valid_without_device():
     assert varlen_call([100, 300], [100, 300]) == HIP
+    assert varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths
+    assert varlen_call([100, 300], [100, 300], grad=2) == HIP     # fp32 gradients
 
 
 def fwd_call(**kw):
@@ -158,7 +164,6 @@ def fwd_call(**kw):
 
 def test_fwd_validation():
     assert fwd_call(Hq=3, Hkv=2) == INVALID
-    assert fwd_call(causal=1, Sk=32) == HIP       # causal Sq != Sk is valid; no device here
     assert fwd_call(D=256) == UNSUPPORTED
     assert fwd_call(dtype=2) == INVALID
 
@@ -177,7 +182,6 @@ def fwd_varlen_call(cu_q, cu_k, **kw):
 def test_fwd_varlen_validation():
     assert fwd_varlen_call([100, 300], [100, 300], lse=None) == NULLPTR
     assert fwd_varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
-    assert fwd_varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths: valid
     assert fwd_varlen_call([100, 300], [100, 300], Hq=3) == INVALID   # heads not grouped
     assert fwd_varlen_call([100, 300], [100, 300], dtype=4) == INVALID
     assert fwd_varlen_call([100, 300], [100, 300], D=96) == UNSUPPORTED
@@ -186,6 +190,8 @@ def test_fwd_varlen_validation():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_fwd_varlen_valid_without_device():
     assert fwd_varlen_call([100, 300], [100, 200], causal=0) == HIP
+    assert fwd_varlen_call([100, 300], [100, 200]) == HIP             # causal, unequal lengths
+    assert fwd_call(causal=1, Sk=32) == HIP                           # dense causal, Sq != Sk
 
 
 def fwd_selected_call(**kw):
@@ -212,6 +218,29 @@ def test_fwd_selected_validation():
     ts[1] = big
     assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 0.088, 2, FAKE, 64, 16, 1, 64, 4,
                                    *[ctypes.byref(t) for t in ts], FAKE, FAKE, 16, 1, None) == UNSUPPORTED
+
+
+def bwd_selected_call(**kw):
+    a = dict(dtype=1, grad=1, det=0)
+    a.update(kw)
+    cu = (ctypes.c_int64 * 1)(512)
+    st = sb.Stats(1, FAKE, FAKE, 0, 1, 16)
+    ts = [t3() for _ in range(8)]
+    return lib().sdpa_bwd_selected(a["dtype"], 1, cu, cu, 16, 1, 128, 0.088, 2, FAKE, 16, 4, 1, 64, 4,
+                                   a["det"], a["grad"], *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
+                                   *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None)
+
+
+def test_bwd_selected_validation():
+    assert bwd_selected_call(grad=0) == INVALID       # bf16 inputs, fp16 gradients
+    assert bwd_selected_call(grad=7) == INVALID
+    assert bwd_selected_call(det=3) == INVALID
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_bwd_selected_valid_without_device():
+    assert bwd_selected_call() == HIP
+    assert bwd_selected_call(grad=2) == HIP           # fp32 gradients
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
