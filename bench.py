@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--deterministic", action="store_true", help="dQ mode 1 (same as --dq-mode 1)")
     ap.add_argument("--dq-mode", type=int, choices=[0, 1, 2], default=None,
                     help="0 fastest (default), 1 bitwise reproducible, 2 fp32 atomic accumulation")
+    ap.add_argument("--head-dims", default=None, metavar="D,DV",
+                    help="selected workload only: query/key and value head dims, e.g. 192,128 "
+                         "(the NSA page's unequal head dims); default the workload's own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of 256 MiB (10 launches), the reference "
@@ -69,15 +72,17 @@ def parse():
     return ap.parse_args()
 
 
-def build_inputs(cid: int):
-    """Device inputs and a prepared call for workload `cid`; also the fp64
-    host copies the CPU baseline needs."""
+def build_inputs(cid: int, head_dims=None):
+    """Device inputs and a prepared call for workload `cid` (with other head
+    dims when given); also the fp64 host copies the CPU baseline needs."""
     import numpy as np
     import torch
 
     import sdpa_backward_fa2_amd as sb
     import synth
     wl = synth.workload(cid)
+    if head_dims is not None:
+        wl = synth.with_head_dims(wl, *head_dims)
     dt = {"f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
 
     def dev(bits):
@@ -244,7 +249,12 @@ def main():
     import sdpa_backward_fa2_amd as sb
     sb.load()
     mode = args.dq_mode if args.dq_mode is not None else (1 if args.deterministic else 0)
-    wl, prep, host = build_inputs(args.config)
+    head_dims = None
+    if args.head_dims:
+        head_dims = tuple(int(x) for x in args.head_dims.split(","))
+        if args.config != 5 or len(head_dims) != 2:
+            sys.exit("--head-dims D,DV applies to the selected workload (--config 5) only")
+    wl, prep, host = build_inputs(args.config, head_dims)
     call, outs = prep(mode)
     for _ in range(args.warmup):
         call()
@@ -272,7 +282,7 @@ def main():
     main_us = kernels[main_name]["avg_us"]
     per_launch = flops * share * args.steps / kernels[main_name]["launches"]
     achieved = per_launch / (main_us * 1e-6) / 1e12
-    workload_name = f"config{args.config}"
+    workload_name = f"config{args.config}" + (f"_d{wl.D}_dv{wl.Dv}" if head_dims else "")
     roofline = {"bound": "mfma", "kernel": main_name, "achieved": achieved,
                 "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_MFMA_16BIT_TFLOPS,
@@ -283,6 +293,8 @@ def main():
     else:
         cfg = {"workload": wl.name, "T": wl.T, "sequences": len(wl.lengths), "Hq": wl.Hq, "Hkv": wl.Hkv,
                "D": wl.D, "causal": wl.causal}
+        if wl.Dv != wl.D:
+            cfg["Dv"] = wl.Dv
         if wl.kind == "selected":
             cfg.update(block_size=wl.block_size, block_count=wl.block_count)
     cfg.update(dq_mode=mode, counted_gflop=flops / 1e9)

@@ -28,7 +28,8 @@
  *   (T, N, D) ("TND", the Ascend page's only layout).  The last (D) stride must
  *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
  *   keep every row 16-byte aligned.  The row stride (S or T) of every tensor
- *   and of the statistics must lie in [0, 2^23) elements.  D is 64 or 128.
+ *   and of the statistics must lie in [0, 2^23) elements.  D is 64 or 128
+ *   (the selected backward also takes D = 192 with a value head dim of 128).
  *   Any other layout returns SDPA_ERR_UNSUPPORTED.
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library allocates no device memory, keeps no per-call state and never
@@ -225,13 +226,16 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   Every kernel of this path is deterministic; the flag (0, 1 or 2, else
  *   SDPA_ERR_INVALID) is accepted for symmetry with the other entry points.
  *   grad_dtype: `dtype` or SDPA_F32, as for sdpa_bwd.
+ *   D: head dim of q, k, dq, dk; Dv: of v, o, dout, dv (the page: D is 192
+ *   or 128, and K and V may differ).  Kernels exist for (D, Dv) = (64, 64),
+ *   (128, 128) and (192, 128); other valid pairs return SDPA_ERR_UNSUPPORTED.
  */
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
-                                     int64_t D, int64_t block_size, int64_t block_count,
+                                     int64_t D, int64_t Dv, int64_t block_size, int64_t block_count,
                                      int deterministic, size_t* bytes);
 int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       int deterministic, int grad_dtype,
@@ -245,8 +249,8 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
  * producing O and the softmaxMax / softmaxSum statistics that
  * sdpa_bwd_selected consumes (Ascend page, "Formula": P is the softmax of the
  * scaled scores over the gathered blocks; "Parameters": softmaxMax,
- * softmaxSum).  Arguments, topk, sparse_mode and constraints as
- * sdpa_bwd_selected; o_out: (Tq, Hq, D) written.
+ * softmaxSum).  Arguments, topk, sparse_mode, head dims (D, Dv) and
+ * constraints as sdpa_bwd_selected; o_out: (Tq, Hq, Dv) written.
  *   max_out[t*stats_stride_s + h*stats_stride_h]: max over the admissible
  *   gathered keys of the scaled score (natural units); sum_out at the same
  *   offset: sum of exp(score - max).  A token with no admissible key gets
@@ -254,7 +258,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
  * Needs no workspace; errors as sdpa_bwd_selected.
  */
 int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,

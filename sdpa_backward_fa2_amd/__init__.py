@@ -83,12 +83,12 @@ _SIGS = {
                                                ctypes.POINTER(c_size)]),
     "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                                 P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
-    "sdpa_bwd_selected_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64,
+    "sdpa_bwd_selected_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64,
                                                  c_i64, c_i64, c_int, ctypes.POINTER(c_size)]),
-    "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
+    "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                   c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int, c_int,
                                   P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
-    "sdpa_fwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
+    "sdpa_fwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                   c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                   P3, P3, P3, P3, c_vp, c_vp, c_i64, c_i64, c_vp]),
     "sdpa_profile_begin": (c_int, []),
@@ -403,11 +403,14 @@ def bwd_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: bool,
 # ----------------------------------------------------------------------------
 
 def bwd_selected_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, block_size, block_count,
-                                deterministic) -> int:
+                                deterministic, Dv=None) -> int:
+    """Bytes of workspace for the selected backward; D: q/k head dim, Dv: v's
+    (default D)."""
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
     out = c_size(0)
-    _check(load().sdpa_bwd_selected_workspace_size(dtype, n, aq, ak, Hq, Hkv, D, block_size,
+    Dv = D if Dv is None else Dv
+    _check(load().sdpa_bwd_selected_workspace_size(dtype, n, aq, ak, Hq, Hkv, D, Dv, block_size,
                                                    block_count, int(deterministic), ctypes.byref(out)),
            "sdpa_bwd_selected_workspace_size")
     return out.value
@@ -420,17 +423,17 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
     topk: int32 (T, Hkv, count) on the device."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
-    Hkv = k.shape[1]
+    Hkv, Dv = k.shape[1], v.shape[2]
     count = topk.shape[2]
     dt = _dtype_code(q)
     dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
-    nbytes = bwd_selected_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, block_size, count, deterministic)
+    nbytes = bwd_selected_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, block_size, count, deterministic, Dv)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
     structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
+    args = (dt, n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(sparse_mode),
             topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic), gdt,
             *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
@@ -458,13 +461,14 @@ def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, sc
 def fwd_selected(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float, sparse_mode: int,
                  o=None, m=None, l=None):
     """NSA selected-attention forward: O and the (max, sum) statistics (T, Hq)
-    fp32 over each token's gathered keys; topk: int32 (T, Hkv, count) on the device."""
+    fp32 over each token's gathered keys; topk: int32 (T, Hkv, count) on the device.
+    O has v's head dim."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
-    Hkv = k.shape[1]
+    Hkv, Dv = k.shape[1], v.shape[2]
     count = topk.shape[2]
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty((q.shape[0], Hq, Dv), dtype=q.dtype, device=q.device)
     if m is None:
         m = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=q.device)
     if l is None:
@@ -472,7 +476,7 @@ def fwd_selected(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float, spar
     assert m.stride() == l.stride()
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
-    st = lib.sdpa_fwd_selected(_dtype_code(q), n, aq, ak, Hq, Hkv, D, float(scale), int(sparse_mode),
+    st = lib.sdpa_fwd_selected(_dtype_code(q), n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(sparse_mode),
                                topk.data_ptr(), *topk.stride(), int(block_size), count,
                                _t3(q), _t3(k), _t3(v), _t3(o), m.data_ptr(), l.data_ptr(),
                                m.stride(0), m.stride(1), _stream_ptr(q.device))

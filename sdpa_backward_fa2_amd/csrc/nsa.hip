@@ -283,28 +283,32 @@ __global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
 // P and dS on the vector ALU, dV^T += dO^T P and dK^T += Q^T dS with the
 // transposed operands read by ds_read_b64_tr_b16.
 
-template <class T, int D>
+template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
-    // rows per step: 128 at D=128 (each wavefront takes two 32-row blocks of
-    // its 64-row half, so a step's barrier and loads cover twice the
-    // products), 64 at D=64 (two workgroups per CU)
-    constexpr int BR = D == 128 ? 128 : 64;
+    // DK: head dim of Q and K; DV: of V, O and dO.  Rows per step: 128 at
+    // DK = DV = 128 (each wavefront takes two 32-row blocks of its 64-row
+    // half, so a step's barrier and loads cover twice the products), 64
+    // otherwise (D=64: two workgroups per CU; DK=192: the tiles' LDS)
+    constexpr int BR = (DK == 128 && DV == 128) ? 128 : 64;
     constexpr int NSB = BR / 64;               // 32-row blocks per wavefront and step
-    constexpr int KS = D / 16;
-    constexpr int DB = D / 32;
-    constexpr int QP = D + 8;
-    constexpr int CH = BR * D / 8 / 256;
-    constexpr int TILES_B = 4 * BR * QP * 2;             // Q and dO, double-buffered
-    constexpr int RED_B = 2 * 64 * (2 * DB * 16) * 4;   // dK/dV partials of two wavefronts
+    constexpr int KSK = DK / 16, KSV = DV / 16;   // k-steps of S (over DK) and of dP (over DV)
+    constexpr int KSM = KSK > KSV ? KSK : KSV;
+    constexpr int DBK = DK / 32, DBV = DV / 32;   // 32-column blocks of dK and of dV
+    constexpr int DBM = DBK > DBV ? DBK : DBV;
+    constexpr int QPK = DK + 8, QPV = DV + 8;     // LDS row pitches of the Q and dO tiles
+    constexpr int CHK = BR * DK / 8 / 256, CHV = BR * DV / 8 / 256;
+    constexpr int TILES_B = 2 * BR * (QPK + QPV) * 2;       // Q and dO, double-buffered
+    constexpr int RED_B = 2 * (DBK + DBV) * 16 * 64 * 4;   // dK/dV partials of two wavefronts
     constexpr int ARENA = TILES_B > RED_B ? TILES_B : RED_B;
     __shared__ __align__(16) unsigned char arena[ARENA];
     __shared__ __align__(16) float lse_s[2][BR];
     __shared__ __align__(16) float dlt_s[2][BR];
     __shared__ int tl_s[2][BR];          // sequence-local token position of each row
     __shared__ int tok_s[2048];          // token of each entry of the piece (<= 2048 / G entries)
-    typedef uint16_t Tile[BR * QP];
-    Tile* Qs = reinterpret_cast<Tile*>(arena);
-    Tile* dOs = reinterpret_cast<Tile*>(arena + 2 * BR * QP * 2);
+    typedef uint16_t TileQ[BR * QPK];
+    typedef uint16_t TileO[BR * QPV];
+    TileQ* Qs = reinterpret_cast<TileQ*>(arena);
+    TileO* dOs = reinterpret_cast<TileO*>(arena + 2 * BR * QPK * 2);
 
     const int piece = blockIdx.x;
     if (piece >= p.pstart[p.N2 * p.NB]) return;
@@ -326,18 +330,20 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
 
     const int myk = 32 * kw + c;
     const bool col_ok = myk < nkeys;
-    u32x4 kreg[KS], vreg[KS];
+    u32x4 kreg[KSK], vreg[KSV];
     const uint16_t* kp = p.k.p + h2 * p.k.sh + (int64_t)(key_row0 + myk) * p.k.ss;
     const uint16_t* vp = p.v.p + h2 * p.v.sh + (int64_t)(key_row0 + myk) * p.v.ss;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KSM; ++s) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        kreg[s] = col_ok ? ld16(kp + 16 * s + 8 * g) : z;
-        vreg[s] = col_ok ? ld16(vp + 16 * s + 8 * g) : z;
+        if (s < KSK) kreg[s] = col_ok ? ld16(kp + 16 * s + 8 * g) : z;
+        if (s < KSV) vreg[s] = col_ok ? ld16(vp + 16 * s + 8 * g) : z;
     }
-    f32x16 dva[DB], dka[DB];
+    f32x16 dva[DBV], dka[DBK];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
+    for (int db = 0; db < DBV; ++db) dva[db] = zero16();
+#pragma unroll
+    for (int db = 0; db < DBK; ++db) dka[db] = zero16();
 
     const int E = max(1, BR / p.G);             // entries per step
     const int n_steps = (ee - eb + E - 1) / E;
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     // unconditional: padding rows re-read the piece's last entry and are
     // given LSE = +inf when stored, so their P is exactly zero; nothing loaded
     // is used before store_tile.
-    u32x4 pq[CH], pdo[CH];
+    u32x4 pq[CHK], pdo[CHV];
     float pl = INFINITY, pd = 0.f;
     int ptl = 0;
     bool pok = false;
@@ -364,14 +370,25 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     const int qss = (int)p.q.ss, qsh = (int)p.q.sh, dss = (int)p.dout.ss, dsh = (int)p.dout.sh;
     auto load_tile = [&](int st) {
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
             const int rq = div_g(r);
             const int t = tok_s[min(st * E + rq, n_e - 1)];
             const int h = h2 * p.G + r - rq * p.G;
             pq[x] = ld16(p.q.p + ((int64_t)t * qss + (int64_t)h * qsh + cc));
-            pdo[x] = ld16(p.dout.p + ((int64_t)t * dss + (int64_t)h * dsh + cc));
+            if constexpr (DK == DV) pdo[x] = ld16(p.dout.p + ((int64_t)t * dss + (int64_t)h * dsh + cc));
+        }
+        if constexpr (DK != DV) {
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) {
+                const int e = tid + 256 * x;
+                const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+                const int rq = div_g(r);
+                const int t = tok_s[min(st * E + rq, n_e - 1)];
+                const int h = h2 * p.G + r - rq * p.G;
+                pdo[x] = ld16(p.dout.p + ((int64_t)t * dss + (int64_t)h * dsh + cc));
+            }
         }
         {
             const int r = tid & (BR - 1);
@@ -387,11 +404,16 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Qs[buf][r * QP + cc], pq[x]);
-            st16(&dOs[buf][r * QP + cc], pdo[x]);
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+            st16(&Qs[buf][r * QPK + cc], pq[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+            st16(&dOs[buf][r * QPV + cc], pdo[x]);
         }
         if (tid < BR) {
             lse_s[buf][tid] = pok ? pl : INFINITY;
@@ -429,9 +451,9 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
                 for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
             }
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                sa = T::mma(ld16(&Qb[(r0 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
-                pa = T::mma(ld16(&dOb[(r0 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+            for (int s = 0; s < KSM; ++s) {
+                if (s < KSK) sa = T::mma(ld16(&Qb[(r0 + c) * QPK + 16 * s + 8 * g]), kreg[s], sa);
+                if (s < KSV) pa = T::mma(ld16(&dOb[(r0 + c) * QPV + 16 * s + 8 * g]), vreg[s], pa);
             }
             auto grad = [&](auto masked_tag) {
                 constexpr bool MK = decltype(masked_tag)::value;
@@ -460,9 +482,9 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
                 const u32x4 bP = acc_to_operand<T>(sa, hh);
                 const u32x4 bS = acc_to_operand<T>(pa, hh);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dva[db] = T::mma(ld_tr<true>(dOb, QP, r0 + 16 * hh, db * 32, lane), bP, dva[db]);
-                    dka[db] = T::mma(ld_tr<true>(Qb, QP, r0 + 16 * hh, db * 32, lane), bS, dka[db]);
+                for (int db = 0; db < DBM; ++db) {
+                    if (db < DBV) dva[db] = T::mma(ld_tr<true>(dOb, QPV, r0 + 16 * hh, db * 32, lane), bP, dva[db]);
+                    if (db < DBK) dka[db] = T::mma(ld_tr<true>(Qb, QPK, r0 + 16 * hh, db * 32, lane), bS, dka[db]);
                 }
             }
         }
@@ -471,25 +493,26 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
 
     // row halves -> one sum (through LDS, reusing the Q/dO tiles)
     float* red = reinterpret_cast<float*>(arena);
+    constexpr int NA = DBV + DBK;            // dV blocks, then dK blocks
     if (rh == 1) {
 #pragma unroll
-        for (int a = 0; a < 2 * DB; ++a) {
-            const f32x16& v = a < DB ? dva[a] : dka[a - DB];
+        for (int a = 0; a < NA; ++a) {
+            const f32x16& v = a < DBV ? dva[a] : dka[a - DBV];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 f32x4 x = {v[4 * r4 + 0], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]};
-                *reinterpret_cast<f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]) = x;
+                *reinterpret_cast<f32x4*>(&red[(((kw * NA + a) * 4 + r4) * 64 + lane) * 4]) = x;
             }
         }
     }
     __syncthreads();
     if (rh == 1 || !col_ok) return;
 #pragma unroll
-    for (int a = 0; a < 2 * DB; ++a) {
-        f32x16& v = a < DB ? dva[a] : dka[a - DB];
+    for (int a = 0; a < NA; ++a) {
+        f32x16& v = a < DBV ? dva[a] : dka[a - DBV];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&red[(((kw * 2 * DB + a) * 4 + r4) * 64 + lane) * 4]);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&red[(((kw * NA + a) * 4 + r4) * 64 + lane) * 4]);
             v[4 * r4 + 0] += x[0]; v[4 * r4 + 1] += x[1]; v[4 * r4 + 2] += x[2]; v[4 * r4 + 3] += x[3];
         }
     }
@@ -498,27 +521,35 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
         const int64_t dko = h2 * p.dk.sh + (int64_t)(key_row0 + myk) * p.dk.ss;
         const int64_t dvo = h2 * p.dv.sh + (int64_t)(key_row0 + myk) * p.dv.ss;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBM; ++db)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int e = db * 32 + 8 * q + 4 * g;
-                st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
-                            dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-                st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
-                            dva[db][4 * q + 3]);
+                if (db < DBK)
+                    st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale,
+                                dka[db][4 * q + 1] * p.scale, dka[db][4 * q + 2] * p.scale,
+                                dka[db][4 * q + 3] * p.scale);
+                if (db < DBV)
+                    st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1],
+                                dva[db][4 * q + 2], dva[db][4 * q + 3]);
             }
     } else {
-        // fp32 partial [piece][half][key][d] for dK, then the same for dV
-        float* pk = p.partial + (((int64_t)piece * p.halves + half) * 2 * 64 + myk) * D;
-        float* pv = pk + 64 * D;
+        // fp32 partials of a (piece, half): dK [64][DK], then dV [64][DV]
+        float* const base = p.partial + ((int64_t)piece * p.halves + half) * 64 * (DK + DV);
+        float* pk = base + myk * DK;
+        float* pv = base + 64 * DK + myk * DV;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DBM; ++db)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                f32x4 a = {dka[db][4 * q + 0], dka[db][4 * q + 1], dka[db][4 * q + 2], dka[db][4 * q + 3]};
-                f32x4 v = {dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2], dva[db][4 * q + 3]};
-                *reinterpret_cast<f32x4*>(pk + db * 32 + 8 * q + 4 * g) = a;
-                *reinterpret_cast<f32x4*>(pv + db * 32 + 8 * q + 4 * g) = v;
+                if (db < DBK) {
+                    f32x4 a = {dka[db][4 * q + 0], dka[db][4 * q + 1], dka[db][4 * q + 2], dka[db][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(pk + db * 32 + 8 * q + 4 * g) = a;
+                }
+                if (db < DBV) {
+                    f32x4 v = {dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2], dva[db][4 * q + 3]};
+                    *reinterpret_cast<f32x4*>(pv + db * 32 + 8 * q + 4 * g) = v;
+                }
             }
     }
 }
@@ -526,15 +557,22 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
 // Sum the partials of blocks split into several pieces, in piece order; a
 // block no token chose (no piece) gets zeros, and a block with one piece was
 // written by the dK/dV kernel itself.  Grid:
-// (bucket, 64-key half, key group); one (key, 8 values) item per thread,
-// 256 / (D/8) keys per workgroup; the pieces' partials are read four at a
-// time so that their loads are in flight together.
-template <int D>
-constexpr int reduce_key_groups() { return 64 / (256 / (D / 8)); }
+// (bucket, 64-key half, key group); one (key, 8 columns) item per thread: the
+// item's dK columns when they exist (d0 < DK) and its dV columns when those
+// do (d0 < DV); LPR threads per key, LPR the power of two that covers the
+// wider head.  The pieces' partials are read four at a time so that their
+// loads are in flight together.
+template <int DK, int DV>
+constexpr int reduce_lanes() {
+    constexpr int w = (DK > DV ? DK : DV) / 8;
+    return w <= 8 ? 8 : w <= 16 ? 16 : 32;
+}
+template <int DK, int DV>
+constexpr int reduce_key_groups() { return 64 / (256 / reduce_lanes<DK, DV>()); }
 
-template <class T, int D>
+template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
-    constexpr int LPR = D / 8;                  // threads per key row, 8 values each
+    constexpr int LPR = reduce_lanes<DK, DV>();   // threads per key row, 8 columns each
     const int bucket = blockIdx.x, half = blockIdx.y;
     const int h2 = bucket / p.NB, blk = bucket % p.NB;
     const int kb0 = half * 64;
@@ -543,20 +581,27 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
     if (np == 1) return;
     const int nkeys = min(64, p.bs - kb0);
     const int key = blockIdx.z * (256 / LPR) + threadIdx.x / LPR, d0 = (threadIdx.x % LPR) * 8;
-    if (key >= nkeys) return;
+    const bool has_k = d0 < DK, has_v = d0 < DV;
+    if (key >= nkeys || !(has_k || has_v)) return;
     float ak[8], av[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
-    const float* base = p.partial + ((int64_t)ps * p.halves + half) * 2 * 64 * D + key * D + d0;
-    const int64_t pstride = (int64_t)p.halves * 2 * 64 * D;   // between consecutive pieces
-    auto add = [&](const float* pk) {
-        const float* pv = pk + 64 * D;
-        const f32x4 k0 = *reinterpret_cast<const f32x4*>(pk), k1 = *reinterpret_cast<const f32x4*>(pk + 4);
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(pv), v1 = *reinterpret_cast<const f32x4*>(pv + 4);
+    // partials of a (piece, half): dK [64][DK], then dV [64][DV]
+    const float* base = p.partial + ((int64_t)ps * p.halves + half) * 64 * (DK + DV);
+    const int kofs = key * DK + d0, vofs = 64 * DK + key * DV + d0;
+    const int64_t pstride = (int64_t)p.halves * 64 * (DK + DV);   // between consecutive pieces
+    auto add = [&](const float* pp) {
+        if (has_k) {
+            const f32x4 k0 = *reinterpret_cast<const f32x4*>(pp + kofs);
+            const f32x4 k1 = *reinterpret_cast<const f32x4*>(pp + kofs + 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ak[i] += k0[i]; ak[4 + i] += k1[i];
-            av[i] += v0[i]; av[4 + i] += v1[i];
+            for (int i = 0; i < 4; ++i) { ak[i] += k0[i]; ak[4 + i] += k1[i]; }
+        }
+        if (has_v) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(pp + vofs);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(pp + vofs + 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { av[i] += v0[i]; av[4 + i] += v1[i]; }
         }
     };
     int x = 0;
@@ -568,8 +613,8 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) ak[i] *= p.scale;
     const int64_t row = (int64_t)blk * p.bs + kb0 + key;
-    st_grad8<T>(p.dk.p, h2 * p.dk.sh + row * p.dk.ss + d0, p.grad_f32, ak);
-    st_grad8<T>(p.dv.p, h2 * p.dv.sh + row * p.dv.ss + d0, p.grad_f32, av);
+    if (has_k) st_grad8<T>(p.dk.p, h2 * p.dk.sh + row * p.dk.ss + d0, p.grad_f32, ak);
+    if (has_v) st_grad8<T>(p.dv.p, h2 * p.dv.sh + row * p.dv.ss + d0, p.grad_f32, av);
 }
 
 // ---------------------------------------------------------------------------
@@ -584,15 +629,16 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
 // K^T dS^T uses the two 16-key tiles of a wavefront as one 32-deep operand.
 // The four wavefronts' partial dQ^T are summed through LDS at the end.
 
-template <class T, int D>
+template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     constexpr int BK = 128;
-    constexpr int KP = D + 8;
-    constexpr int KS = D / 32;       // k-steps of 16x16x32 over the head dimension
-    constexpr int DB = D / 16;       // 16-row blocks of dQ^T
-    constexpr int CH = BK * D / 8 / 256;
-    __shared__ __align__(16) uint16_t Ks[BK * KP];
-    __shared__ __align__(16) uint16_t Vs[BK * KP];
+    constexpr int KPK = DK + 8, KPV = DV + 8;     // LDS row pitches of the K and V chunks
+    constexpr int KSK = DK / 32, KSV = DV / 32;   // k-steps of 16x16x32: S over DK, dP over DV
+    constexpr int KSM = KSK > KSV ? KSK : KSV;
+    constexpr int DB = DK / 16;                   // 16-row blocks of dQ^T
+    constexpr int CHK = BK * DK / 8 / 256, CHV = BK * DV / 8 / 256;
+    __shared__ __align__(16) uint16_t Ks[BK * KPK];
+    __shared__ __align__(16) uint16_t Vs[BK * KPV];
     __shared__ int kpos_s[BK];
     __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
 
@@ -610,14 +656,14 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     const bool head_ok = gh < p.G;
     const int h = h2 * p.G + (head_ok ? gh : 0);
 
-    u32x4 qreg[KS], doreg[KS];
+    u32x4 qreg[KSK], doreg[KSV];
     const uint16_t* qp = p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh;
     const uint16_t* dop = p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KSM; ++s) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        qreg[s] = head_ok ? ld16(qp + 32 * s + 8 * G16) : z;
-        doreg[s] = head_ok ? ld16(dop + 32 * s + 8 * G16) : z;
+        if (s < KSK) qreg[s] = head_ok ? ld16(qp + 32 * s + 8 * G16) : z;
+        if (s < KSV) doreg[s] = head_ok ? ld16(dop + 32 * s + 8 * G16) : z;
     }
     const float l2 = head_ok ? p.lse2[(int64_t)t * p.Hq + h] : INFINITY;
     const float dl = head_ok ? p.delta[(int64_t)t * p.Hq + h] : 0.f;
@@ -639,38 +685,63 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
         blk_s[i] = (blk >= 0 && blk < nblk) ? blk : -1;
     }
     __syncthreads();
-    u32x4 kv[CH], vv[CH];
+    u32x4 kv[CHK], vv[CHV];
     int kpos_r = 0x7fffffff;
     // slot and row-in-block of gathered key n: when block_size divides the
     // chunk, chunk c0 starts at slot c0 / block_size and a row's part of that
     // is fixed, so the divisions are done once
     const bool bs_divides = BK % p.bs == 0;
-    int rq[CH], rr[CH];
+    int rq[CHK], rr[CHK], rqv[CHV], rrv[CHV];
 #pragma unroll
-    for (int x = 0; x < CH; ++x) {
-        const int r = (tid + 256 * x) / (D / 8);
+    for (int x = 0; x < CHK; ++x) {
+        const int r = (tid + 256 * x) / (DK / 8);
         rq[x] = r / p.bs;
         rr[x] = r % p.bs;
+    }
+#pragma unroll
+    for (int x = 0; x < CHV; ++x) {
+        if constexpr (DK == DV) {
+            rqv[x] = rq[x];
+            rrv[x] = rr[x];
+        } else {
+            const int r = (tid + 256 * x) / (DV / 8);
+            rqv[x] = r / p.bs;
+            rrv[x] = r % p.bs;
+        }
     }
     const int rq_k = (tid & (BK - 1)) / p.bs, rr_k = (tid & (BK - 1)) % p.bs;
     // row strides are below 2^23 elements: 32 x 32 -> 64-bit row offsets
     const int kss = (int)p.k.ss, vss = (int)p.v.ss;
     const uint16_t* const kh = p.k.p + (int64_t)h2 * p.k.sh;
     const uint16_t* const vh = p.v.p + (int64_t)h2 * p.v.sh;
+    // packed key row of gathered key c0 + r (row krow0, masked, for an
+    // ignored choice or past the gathered keys)
+    auto key_row = [&](int c0, int cs, int r, int q, int rm) {
+        int slot, rb;
+        if (bs_divides) { slot = cs + q; rb = rm; }
+        else { const int n = c0 + r; slot = n / p.bs; rb = n % p.bs; }
+        const int blk = blk_s[min(slot, p.count - 1)];
+        const bool ok = c0 + r < nk && blk >= 0;
+        return krow0 + (ok ? blk * p.bs + rb : 0);
+    };
     auto load_chunk = [&](int c0) {
         const int cs = bs_divides ? c0 / p.bs : 0;
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            int slot, rb;
-            if (bs_divides) { slot = cs + rq[x]; rb = rr[x]; }
-            else { const int n = c0 + r; slot = n / p.bs; rb = n % p.bs; }
-            const int blk = blk_s[min(slot, p.count - 1)];
-            const bool ok = c0 + r < nk && blk >= 0;
-            const int row = krow0 + (ok ? blk * p.bs + rb : 0);
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+            const int row = key_row(c0, cs, r, rq[x], rr[x]);
             kv[x] = ld16(kh + (int64_t)row * kss + cc);
-            vv[x] = ld16(vh + (int64_t)row * vss + cc);
+            if constexpr (DK == DV) vv[x] = ld16(vh + (int64_t)row * vss + cc);
+        }
+        if constexpr (DK != DV) {
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) {
+                const int e = tid + 256 * x;
+                const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+                const int row = key_row(c0, cs, r, rqv[x], rrv[x]);
+                vv[x] = ld16(vh + (int64_t)row * vss + cc);
+            }
         }
         const int n = c0 + (tid & (BK - 1));
         int slot, rb;
@@ -683,11 +754,16 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     for (int c0 = 0; c0 < nk; c0 += BK) {
         __syncthreads();
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Ks[r * KP + cc], kv[x]);
-            st16(&Vs[r * KP + cc], vv[x]);
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+            st16(&Ks[r * KPK + cc], kv[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+            st16(&Vs[r * KPV + cc], vv[x]);
         }
         if (tid < BK) kpos_s[tid] = kpos_r;
         // whether any key of the chunk is masked for this token
@@ -701,9 +777,9 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
             dp[x][0] = dp[x][1] = dp[x][2] = dp[x][3] = -dl;   // dP^T accumulates onto -Delta
             const int kr = 32 * w + 16 * x + col;       // A rows: keys
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                s[x] = T::mma16(ld16(&Ks[kr * KP + 32 * ks + 8 * G16]), qreg[ks], s[x]);
-                dp[x] = T::mma16(ld16(&Vs[kr * KP + 32 * ks + 8 * G16]), doreg[ks], dp[x]);
+            for (int ks = 0; ks < KSM; ++ks) {
+                if (ks < KSK) s[x] = T::mma16(ld16(&Ks[kr * KPK + 32 * ks + 8 * G16]), qreg[ks], s[x]);
+                if (ks < KSV) dp[x] = T::mma16(ld16(&Vs[kr * KPV + 32 * ks + 8 * G16]), doreg[ks], dp[x]);
             }
             if (masked) {
 #pragma unroll
@@ -727,7 +803,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
         bS[3] = T::pack_op(dp[1][2], dp[1][3]);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            dq[db] = T::mma16(ld_tr16x16_acc(Ks, KP, 32 * w, 16 * db, lane), bS, dq[db]);
+            dq[db] = T::mma16(ld_tr16x16_acc(Ks, KPK, 32 * w, 16 * db, lane), bS, dq[db]);
     }
 
     // sum the four wavefronts' partials (through LDS, reusing Ks)
@@ -769,15 +845,15 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 // against the 16 heads (S^T = K Q^T, so each lane holds one head column) and
 // keeps a running max and sum per head and an O^T partial; the four partials
 // are merged at the end.
-template <class T, int D>
+template <class T, int DK, int DV>
 __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
     constexpr int BK = 128;
-    constexpr int KP = D + 8;
-    constexpr int KS = D / 32;       // k-steps of 16x16x32 over the head dimension
-    constexpr int DB = D / 16;       // 16-row blocks of O^T
-    constexpr int CH = BK * D / 8 / 256;
-    __shared__ __align__(16) uint16_t Ks[BK * KP];
-    __shared__ __align__(16) uint16_t Vs[BK * KP];
+    constexpr int KPK = DK + 8, KPV = DV + 8;     // LDS row pitches of the K and V chunks
+    constexpr int KS = DK / 32;      // k-steps of 16x16x32 over the query/key head dimension
+    constexpr int DB = DV / 16;      // 16-row blocks of O^T
+    constexpr int CHK = BK * DK / 8 / 256, CHV = BK * DV / 8 / 256;
+    __shared__ __align__(16) uint16_t Ks[BK * KPK];
+    __shared__ __align__(16) uint16_t Vs[BK * KPV];
     __shared__ int kpos_s[BK];
     __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
 
@@ -817,19 +893,31 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
     __syncthreads();
     // chunk loads as in the dQ kernel: unconditional, an ignored choice or a
     // row past the gathered keys re-reads key row krow0 and is masked
-    u32x4 kv[CH], vv[CH];
+    u32x4 kv[CHK], vv[CHV];
     int kpos_r = 0x7fffffff;
+    // packed key row of gathered key n (row krow0, masked, if there is none)
+    auto key_row = [&](int n) {
+        const int blk = blk_s[min(n / p.bs, p.count - 1)];
+        const bool ok = n < nk && blk >= 0;
+        return (int64_t)krow0 + (ok ? (int64_t)blk * p.bs + n % p.bs : 0);
+    };
     auto load_chunk = [&](int c0) {
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            const int n = c0 + r;
-            const int blk = blk_s[min(n / p.bs, p.count - 1)];
-            const bool ok = n < nk && blk >= 0;
-            const int64_t row = (int64_t)krow0 + (ok ? (int64_t)blk * p.bs + n % p.bs : 0);
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+            const int64_t row = key_row(c0 + r);
             kv[x] = ld16(p.k.p + row * p.k.ss + (int64_t)h2 * p.k.sh + cc);
-            vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+            if constexpr (DK == DV) vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+        }
+        if constexpr (DK != DV) {
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) {
+                const int e = tid + 256 * x;
+                const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+                const int64_t row = key_row(c0 + r);
+                vv[x] = ld16(p.v.p + row * p.v.ss + (int64_t)h2 * p.v.sh + cc);
+            }
         }
         const int n = c0 + (tid & (BK - 1));
         const int blk = blk_s[min(n / p.bs, p.count - 1)];
@@ -839,11 +927,16 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
     for (int c0 = 0; c0 < nk; c0 += BK) {
         __syncthreads();
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
+        for (int x = 0; x < CHK; ++x) {
             const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Ks[r * KP + cc], kv[x]);
-            st16(&Vs[r * KP + cc], vv[x]);
+            const int r = e / (DK / 8), cc = (e % (DK / 8)) * 8;
+            st16(&Ks[r * KPK + cc], kv[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+            st16(&Vs[r * KPV + cc], vv[x]);
         }
         if (tid < BK) kpos_s[tid] = kpos_r;
         __syncthreads();
@@ -857,7 +950,7 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
             const int kr = 32 * w + 16 * x + col;       // A rows: keys
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                sc[x] = T::mma16(ld16(&Ks[kr * KP + 32 * ks + 8 * G16]), qreg[ks], sc[x]);
+                sc[x] = T::mma16(ld16(&Ks[kr * KPK + 32 * ks + 8 * G16]), qreg[ks], sc[x]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int kpos = kpos_s[32 * w + 16 * x + 4 * G16 + r];
@@ -893,7 +986,7 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             o[db][0] *= alpha; o[db][1] *= alpha; o[db][2] *= alpha; o[db][3] *= alpha;
-            o[db] = T::mma16(ld_tr16x16_acc(Vs, KP, 32 * w, 16 * db, lane), bP, o[db]);
+            o[db] = T::mma16(ld_tr16x16_acc(Vs, KPV, 32 * w, 16 * db, lane), bP, o[db]);
         }
     }
 
@@ -959,23 +1052,41 @@ static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T, int DK, int DV>
 static hipError_t launch_nsa_fwd_t(const NsaParams& p, hipStream_t st) {
-    PROF_LAUNCH(KID_FWD, st, (nsa_fwd_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_FWD, st, (nsa_fwd_kernel<T, DK, DV>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T>
+static hipError_t launch_nsa_fwd_dims(const NsaParams& p, int D, int Dv, hipStream_t st) {
+    if (D == 64) return launch_nsa_fwd_t<T, 64, 64>(p, st);
+    if (D == 128) return launch_nsa_fwd_t<T, 128, 128>(p, st);
+    (void)Dv;   // (192, 128): the only other pair the host accepts
+    return launch_nsa_fwd_t<T, 192, 128>(p, st);
+}
+
+// DK: head dim of Q and K, DV: of V, O and dO (the row pass reduces dO o O)
+template <class T, int DK, int DV>
 static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStream_t st) {
     hipError_t e = launch_index(p, st);
     if (e != hipSuccess) return e;
-    e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, D, false, st);
+    e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, DV, false, st);
     if (e != hipSuccess) return e;
-    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, D>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
-    PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, D>), dim3(p.N2 * p.NB, p.halves, reduce_key_groups<D>()),
-                dim3(256), 0, st, p);
-    PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, D>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, DK, DV>),
+                dim3(p.N2 * p.NB, p.halves, reduce_key_groups<DK, DV>()), dim3(256), 0, st, p);
+    PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st,
+                p);
     return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_nsa_dims(const NsaParams& p, const BwdParams& bp, int D, int Dv, hipStream_t st) {
+    if (D == 64) return launch_nsa_t<T, 64, 64>(p, bp, st);
+    if (D == 128) return launch_nsa_t<T, 128, 128>(p, bp, st);
+    (void)Dv;   // (192, 128): the only other pair the host accepts
+    return launch_nsa_t<T, 192, 128>(p, bp, st);
 }
 
 }  // namespace sdpa
@@ -1012,13 +1123,19 @@ int read_seqs(int64_t batch, const int64_t* cuq, const int64_t* cuk, Seqs& S) {
     return SDPA_OK;
 }
 
+// Head dims (Q/K D, V Dv) with kernels: equal 64 or 128, and D = 192 with
+// Dv = 128 (the Ascend page: D is 192 or 128, unequal for K and V allowed).
+bool nsa_dims_ok(int64_t D, int64_t Dv) {
+    return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 192 && Dv == 128);
+}
+
 // Validation shared by the size query, the backward and the index build
 // (Ascend page, "Constraints"): block_size <= 128 and a multiple of 16,
 // 1 <= block_count <= 128, count * size < 8192, every KV length a multiple of
 // block_size and >= count * size; sparse_mode 2 needs equal lengths.
 int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_t Hq, int64_t Hkv,
-                   int64_t D, int64_t bs, int64_t count, int sparse_mode, Seqs& S) {
-    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+                   int64_t D, int64_t Dv, int64_t bs, int64_t count, int sparse_mode, Seqs& S) {
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (Hq / Hkv > 32) return SDPA_ERR_INVALID;
     if (bs < 16 || bs > 128 || bs % 16) return SDPA_ERR_INVALID;
     if (count < 1 || count > 128 || count * bs >= 8192) return SDPA_ERR_INVALID;
@@ -1029,14 +1146,14 @@ int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_
         if (S.lk[b] < count * bs) return SDPA_ERR_INVALID;
         if (sparse_mode == 2 && S.lq[b] != S.lk[b]) return SDPA_ERR_INVALID;
     }
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!nsa_dims_ok(D, Dv)) return SDPA_ERR_UNSUPPORTED;
     if (batch > sdpa::kMaxSeqArgs) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq * Hkv * count >= ((int64_t)1 << 31) || S.Tk >= ((int64_t)1 << 31)) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq > 2147483647 || Hkv * ((Hq / Hkv + 15) / 16) > 65535) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
 }
 
-NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t bs, int64_t count) {
+NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv, int64_t bs, int64_t count) {
     NsaLayout L;
     L.NB = S.Tk / bs;
     L.nbk = Hkv * L.NB;
@@ -1053,7 +1170,7 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.pieces = o; o = up(o + L.max_pieces * 3 * 4);
     L.lse2 = o; o = up(o + S.Tq * Hq * 4);
     L.delta = o; o = up(o + S.Tq * Hq * 4);
-    L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 2 * 64 * D * 4);
+    L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
     L.total = o;
     return L;
 }
@@ -1104,16 +1221,16 @@ extern "C" {
 
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
-                                     int64_t D, int64_t block_size, int64_t block_count,
+                                     int64_t D, int64_t Dv, int64_t block_size, int64_t block_count,
                                      int deterministic, size_t* bytes) {
     if (!bytes || !cu_seqlens_q_host || !cu_seqlens_kv_host) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (deterministic < 0 || deterministic > 2) return SDPA_ERR_INVALID;
     Seqs S;
-    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, Dv, block_size,
                                block_count, 0, S))
         return s;
-    *bytes = nsa_layout(S, Hq, Hkv, D, block_size, block_count).total;
+    *bytes = nsa_layout(S, Hq, Hkv, D, Dv, block_size, block_count).total;
     return SDPA_OK;
 }
 
@@ -1137,7 +1254,7 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
 }
 
 int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
@@ -1150,7 +1267,7 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     Seqs S;
-    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, Dv, block_size,
                                block_count, sparse_mode, S))
         return s;
     for (const sdpa_tensor3* t : {q, k, v, o_out})
@@ -1173,15 +1290,15 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == SDPA_F16)
-        e = D == 64 ? sdpa::launch_nsa_fwd_t<sdpa::F16, 64>(p, st) : sdpa::launch_nsa_fwd_t<sdpa::F16, 128>(p, st);
+        e = sdpa::launch_nsa_fwd_dims<sdpa::F16>(p, (int)D, (int)Dv, st);
     else
-        e = D == 64 ? sdpa::launch_nsa_fwd_t<sdpa::BF16, 64>(p, st) : sdpa::launch_nsa_fwd_t<sdpa::BF16, 128>(p, st);
+        e = sdpa::launch_nsa_fwd_dims<sdpa::BF16>(p, (int)D, (int)Dv, st);
     if (e != hipSuccess) return hip_fail(e, "selected forward launch");
     return SDPA_OK;
 }
 
 int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                       double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       int deterministic, int grad_dtype,
@@ -1202,13 +1319,13 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (deterministic < 0 || deterministic > 2) return SDPA_ERR_INVALID;
     if (stats->kind != SDPA_STATS_LSE && stats->kind != SDPA_STATS_MAX_SUM) return SDPA_ERR_INVALID;
     Seqs S;
-    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, block_size,
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, Dv, block_size,
                                block_count, sparse_mode, S))
         return s;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = t3_ok(t)) return s;
     if (!sdpa::row_stride_ok(stats->stride_s)) return SDPA_ERR_UNSUPPORTED;
-    const NsaLayout L = nsa_layout(S, Hq, Hkv, D, block_size, block_count);
+    const NsaLayout L = nsa_layout(S, Hq, Hkv, D, Dv, block_size, block_count);
     if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
     if (int s = device_ok()) return s;
     if (S.Tk == 0) return SDPA_OK;
@@ -1240,9 +1357,9 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (dtype == SDPA_F16)
-        e = D == 64 ? sdpa::launch_nsa_t<sdpa::F16, 64>(p, bp, st) : sdpa::launch_nsa_t<sdpa::F16, 128>(p, bp, st);
+        e = sdpa::launch_nsa_dims<sdpa::F16>(p, bp, (int)D, (int)Dv, st);
     else
-        e = D == 64 ? sdpa::launch_nsa_t<sdpa::BF16, 64>(p, bp, st) : sdpa::launch_nsa_t<sdpa::BF16, 128>(p, bp, st);
+        e = sdpa::launch_nsa_dims<sdpa::BF16>(p, bp, (int)D, (int)Dv, st);
     if (e != hipSuccess) return hip_fail(e, "selected launch");
     return SDPA_OK;
 }
@@ -1256,10 +1373,10 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
     if (!cu_seqlens_q_host || !cu_seqlens_kv_host || !topk || !offsets_out || !entries_out || !workspace)
         return SDPA_ERR_NULLPTR;
     Seqs S;
-    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hkv, Hkv, 128, block_size,
+    if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hkv, Hkv, 128, 128, block_size,
                                block_count, 0, S))
         return s;
-    const NsaLayout L = nsa_layout(S, Hkv, Hkv, 128, block_size, block_count);
+    const NsaLayout L = nsa_layout(S, Hkv, Hkv, 128, 128, block_size, block_count);
     if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
     if (int s = device_ok()) return s;
     if (L.nbk == 0) return SDPA_OK;

@@ -22,7 +22,7 @@ Conventions
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -156,6 +156,11 @@ class Workload:
     block_count: int = 0
     stats_source: str = "oracle"   # who produces O and the stats
     extra: dict = field(default_factory=dict)
+    Dv_: int = 0              # head dim of V, O and dO when it differs from D
+
+    @property
+    def Dv(self) -> int:
+        return self.Dv_ or self.D
 
     # -- dense helpers -------------------------------------------------------
     def dense_physical_shape(self, heads: int) -> tuple:
@@ -176,7 +181,9 @@ class Workload:
         return int(np.sum(self.lengths)) if self.lengths is not None else self.B * self.S
 
     def packed_bits(self, tensor_id: int, heads: int) -> np.ndarray:
-        return normal_bits((self.T, heads, self.D), self.dtype, self.config_id, tensor_id)
+        """(T, heads, dim): Q and K take D, V and dO take Dv."""
+        dim = self.Dv if tensor_id in (TID_V, TID_DO) else self.D
+        return normal_bits((self.T, heads, dim), self.dtype, self.config_id, tensor_id)
 
     def cu_seqlens(self) -> np.ndarray:
         return inclusive_offsets(self.lengths)
@@ -195,7 +202,8 @@ class Workload:
             f = sum(5 * 2.0 * int(L) * int(L) * self.D * self.Hq for L in self.lengths)
             return f / 2 if self.causal else f
         if self.kind == "selected":
-            return 5 * 2.0 * self.T * self.Hq * self.block_count * self.block_size * self.D
+            # S, dQ and dK contract or produce D columns, dP and dV Dv columns
+            return 2.0 * self.T * self.Hq * self.block_count * self.block_size * (3 * self.D + 2 * self.Dv)
         raise ValueError(self.kind)
 
 
@@ -222,6 +230,13 @@ def workload(config_id: int) -> Workload:
                         lengths=np.array([4096], dtype=np.int64), block_size=64,
                         block_count=16, stats_source="oracle")
     raise ValueError(f"no workload {config_id}")
+
+
+def with_head_dims(wl: Workload, D: int, Dv: int) -> Workload:
+    """The same workload with query/key head dim D and value head dim Dv (the
+    NSA page allows D of 192 or 128, unequal for K and V); scale 1/sqrt(D)."""
+    return replace(wl, name=f"{wl.name} with Dqk{D} Dv{Dv}", D=D, Dv_=0 if Dv == D else Dv,
+                   scale=1.0 / math.sqrt(D))
 
 
 ALL_CONFIGS = (1, 2, 3, 4, 5)

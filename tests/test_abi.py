@@ -197,9 +197,10 @@ def test_fwd_varlen_valid_without_device():
 def fwd_selected_call(**kw):
     a = dict(dtype=1, cu=[512], Hq=16, Hkv=1, D=128, bs=64, count=4, mode=2, m=FAKE, l=FAKE)
     a.update(kw)
+    a.setdefault("Dv", a["D"])
     cu = (ctypes.c_int64 * len(a["cu"]))(*a["cu"])
     ts = [t3() for _ in range(4)]
-    return lib().sdpa_fwd_selected(a["dtype"], len(a["cu"]), cu, cu, a["Hq"], a["Hkv"], a["D"], 0.088,
+    return lib().sdpa_fwd_selected(a["dtype"], len(a["cu"]), cu, cu, a["Hq"], a["Hkv"], a["D"], a["Dv"], 0.088,
                                    a["mode"], FAKE, 4 * a["count"], a["count"], 1, a["bs"], a["count"],
                                    *[ctypes.byref(t) for t in ts], a["m"], a["l"], 16, 1, None)
 
@@ -216,17 +217,17 @@ def test_fwd_selected_validation():
     cu = (ctypes.c_int64 * 1)(512)
     ts = [t3() for _ in range(4)]
     ts[1] = big
-    assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 0.088, 2, FAKE, 64, 16, 1, 64, 4,
+    assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 128, 0.088, 2, FAKE, 64, 16, 1, 64, 4,
                                    *[ctypes.byref(t) for t in ts], FAKE, FAKE, 16, 1, None) == UNSUPPORTED
 
 
 def bwd_selected_call(**kw):
-    a = dict(dtype=1, grad=1, det=0)
+    a = dict(dtype=1, grad=1, det=0, D=128, Dv=128)
     a.update(kw)
     cu = (ctypes.c_int64 * 1)(512)
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 16)
     ts = [t3() for _ in range(8)]
-    return lib().sdpa_bwd_selected(a["dtype"], 1, cu, cu, 16, 1, 128, 0.088, 2, FAKE, 16, 4, 1, 64, 4,
+    return lib().sdpa_bwd_selected(a["dtype"], 1, cu, cu, 16, 1, a["D"], a["Dv"], 0.088, 2, FAKE, 16, 4, 1, 64, 4,
                                    a["det"], a["grad"], *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
                                    *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None)
 
@@ -235,14 +236,26 @@ def test_bwd_selected_validation():
     assert bwd_selected_call(grad=0) == INVALID       # bf16 inputs, fp16 gradients
     assert bwd_selected_call(grad=7) == INVALID
     assert bwd_selected_call(det=3) == INVALID
+    assert bwd_selected_call(Dv=0) == INVALID
+    assert bwd_selected_call(D=192, Dv=192) == UNSUPPORTED    # kernels: (64,64), (128,128), (192,128)
+    assert bwd_selected_call(D=128, Dv=64) == UNSUPPORTED
+    n = ctypes.c_size_t(0)
+    cu = (ctypes.c_int64 * 1)(512)
+    assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 192, 128, 64, 4, 0, ctypes.byref(n)) == OK
+    m = ctypes.c_size_t(0)
+    assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 128, 128, 64, 4, 0, ctypes.byref(m)) == OK
+    assert n.value > m.value                             # wider dK partials
+    assert fwd_selected_call(D=192) == UNSUPPORTED       # (192, 192): no kernel
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_bwd_selected_valid_without_device():
     assert bwd_selected_call() == HIP
     assert bwd_selected_call(grad=2) == HIP           # fp32 gradients
+    assert bwd_selected_call(D=192, Dv=128) == HIP    # unequal head dims
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_fwd_selected_valid_without_device():
     assert fwd_selected_call() == HIP
+    assert fwd_selected_call(D=192, Dv=128) == HIP

@@ -37,7 +37,7 @@ def _check_stats(m_got, l_got, f, what):
 
 
 def _run_forward(t, topk_dev, cu, bs, scale, mode):
-    o = torch.full_like(t["q"], float("nan"))
+    o = torch.full_like(t["do"], float("nan"))      # O has the value head dim
     m = torch.full(t["q"].shape[:2], float("nan"), dtype=torch.float32, device="cuda")
     l = torch.full_like(m, float("nan"))
     sb.fwd_selected(t["q"], t["k"], t["v"], topk_dev, cu, cu, bs, scale, mode, o=o, m=m, l=l)
@@ -60,9 +60,10 @@ def _case(x, t, topk, cu, bs, scale, mode, dtype, backward=True):
         assert_rel(to_f64(got), ref, dtype, f"{name} from the GPU forward")
 
 
-def _random_inputs(T, Hq, N2, D, dtype, rng):
+def _random_inputs(T, Hq, N2, D, dtype, rng, Dv=None):
+    Dv = D if Dv is None else Dv
     bits = {n: synth.encode(rng.standard_normal(shape), dtype)
-            for n, shape in (("q", (T, Hq, D)), ("k", (T, N2, D)), ("v", (T, N2, D)), ("do", (T, Hq, D)))}
+            for n, shape in (("q", (T, Hq, D)), ("k", (T, N2, D)), ("v", (T, N2, Dv)), ("do", (T, Hq, Dv)))}
     return ({n: synth.decode(b, dtype) for n, b in bits.items()},
             {n: to_device(b, dtype) for n, b in bits.items()})
 
@@ -80,7 +81,7 @@ def test_config5_forward():
     _case(x, t, wl.topk(), cu, wl.block_size, wl.scale, 2, wl.dtype)
 
 
-@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128)])
 @pytest.mark.parametrize("mode", [0, 2])
 @pytest.mark.parametrize("lengths,G,N2,bs,count", [
     ((256, 128), 2, 2, 64, 2),
@@ -88,7 +89,7 @@ def test_config5_forward():
     ((384, 192), 16, 1, 64, 3),
     ((96, 192), 20, 1, 48, 2),     # 20 heads: two 16-head tiles, the second partly empty
 ])
-def test_forward_small(dtype, D, mode, lengths, G, N2, bs, count):
+def test_forward_small(dtype, D, Dv, mode, lengths, G, N2, bs, count):
     rng = np.random.default_rng(len(lengths) * 100 + G * 10 + bs + D + mode + 7)
     lengths = np.array(lengths)
     cu = np.cumsum(lengths)
@@ -98,7 +99,7 @@ def test_forward_small(dtype, D, mode, lengths, G, N2, bs, count):
         starts = np.concatenate([[0], cu[:-1]])
         for s0, s1 in zip(starts, cu):
             topk[s0:s1] = rng.integers(0, (s1 - s0) // bs, size=topk[s0:s1].shape)
-    x, t = _random_inputs(T, G * N2, N2, D, dtype, rng)
+    x, t = _random_inputs(T, G * N2, N2, D, dtype, rng, Dv)
     _case(x, t, topk, cu, bs, 1 / math.sqrt(D), mode, dtype)
 
 

@@ -107,9 +107,9 @@ def test_packed(D):
         _compare(g32, g16, g, dtype, det == 0 or D == 64, f"det={det}")
 
 
-@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128)])
 @pytest.mark.parametrize("lengths,G,bs,count", [((256, 128), 2, 64, 2), ((96, 160, 80), 16, 16, 5)])
-def test_selected(dtype, D, lengths, G, bs, count):
+def test_selected(dtype, D, Dv, lengths, G, bs, count):
     """One-piece blocks (written by the dK/dV kernel) and split blocks (summed
     by the reduction) both store through the fp32 path."""
     rng = np.random.default_rng(G + bs + D)
@@ -117,7 +117,7 @@ def test_selected(dtype, D, lengths, G, bs, count):
     cu = np.cumsum(lengths)
     T = int(cu[-1])
     topk = synth.draw_topk(lengths, 1, bs, count, config_id=44)
-    x, t = _inputs({"q": (T, G, D), "k": (T, 1, D), "v": (T, 1, D), "do": (T, G, D)}, dtype, rng)
+    x, t = _inputs({"q": (T, G, D), "k": (T, 1, D), "v": (T, 1, Dv), "do": (T, G, Dv)}, dtype, rng)
     scale = 1 / math.sqrt(D)
     f = oracle.selected_forward(x["q"], x["k"], x["v"], topk, cu, cu, bs, scale, 2)
     g = oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], topk, cu, cu, bs, scale, 2)

@@ -86,7 +86,7 @@ def test_config5_nsa_selected():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype,D", [("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128), ("f16", 192, 128)])
 @pytest.mark.parametrize("mode", [0, 2])
 @pytest.mark.parametrize("lengths,G,N2,bs,count", [
     ((256, 128), 2, 2, 64, 2),
@@ -95,7 +95,9 @@ def test_config5_nsa_selected():
     ((384, 192), 16, 1, 64, 3),
     ((96, 192), 2, 1, 48, 2),      # block size that does not divide a 128-key chunk
 ])
-def test_selected_small(dtype, D, mode, lengths, G, N2, bs, count):
+def test_selected_small(dtype, D, Dv, mode, lengths, G, N2, bs, count):
+    """D: head dim of Q and K, Dv: of V and dO (192/128: the page's unequal
+    head dims)."""
     rng = np.random.default_rng(len(lengths) * 100 + G * 10 + bs + D + mode)
     lengths = np.array(lengths)
     cu = np.cumsum(lengths)
@@ -108,7 +110,7 @@ def test_selected_small(dtype, D, mode, lengths, G, N2, bs, count):
             topk[s0:s1] = rng.integers(0, nb, size=topk[s0:s1].shape)
     Hq = G * N2
     bits = {n: synth.encode(rng.standard_normal(shape), dtype)
-            for n, shape in (("q", (T, Hq, D)), ("k", (T, N2, D)), ("v", (T, N2, D)), ("do", (T, Hq, D)))}
+            for n, shape in (("q", (T, Hq, D)), ("k", (T, N2, D)), ("v", (T, N2, Dv)), ("do", (T, Hq, Dv)))}
     x = {n: synth.decode(b, dtype) for n, b in bits.items()}
     t = {n: to_device(b, dtype) for n, b in bits.items()}
     scale = 1 / math.sqrt(D)
@@ -117,5 +119,30 @@ def test_selected_small(dtype, D, mode, lengths, G, N2, bs, count):
     o = to_device(synth.encode(f["O"], dtype), dtype)
     lse = torch.tensor(f["lse"], dtype=torch.float32, device="cuda")
     dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o, t["do"], lse, topk, cu, bs, scale, mode)
+    for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
+        assert_rel(to_f64(got), ref, dtype, name)
+
+
+def test_unequal_head_dims_long_sequence():
+    """Dqk = 192, Dv = 128 bf16 at the NSA workload's head grouping (16 query
+    heads per KV head, 16 blocks of 64 keys, causal) on a 2048-token sequence:
+    early blocks are chosen by many tokens and split into several pieces, so
+    the partial reduction runs with the two widths."""
+    rng = np.random.default_rng(192)
+    lengths = np.array([2048])
+    cu = np.cumsum(lengths)
+    T, G, D, Dv, bs, count, dtype = 2048, 16, 192, 128, 64, 16, "bf16"
+    topk = synth.draw_topk(lengths, 1, bs, count, config_id=5)
+    bits = {n: synth.encode(rng.standard_normal(shape), dtype)
+            for n, shape in (("q", (T, G, D)), ("k", (T, 1, D)), ("v", (T, 1, Dv)), ("do", (T, G, Dv)))}
+    x = {n: synth.decode(b, dtype) for n, b in bits.items()}
+    t = {n: to_device(b, dtype) for n, b in bits.items()}
+    scale = 1 / math.sqrt(D)
+    f = oracle.selected_forward(x["q"], x["k"], x["v"], topk, cu, cu, bs, scale, 2)
+    g = oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], topk, cu, cu, bs, scale, 2)
+    o = to_device(synth.encode(f["O"], dtype), dtype)
+    stats = (torch.tensor(f["m"], dtype=torch.float32, device="cuda"),
+             torch.tensor(f["l"], dtype=torch.float32, device="cuda"))
+    dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o, t["do"], stats, topk, cu, bs, scale, 2)
     for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
         assert_rel(to_f64(got), ref, dtype, name)

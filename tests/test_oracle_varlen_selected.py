@@ -131,20 +131,24 @@ def _torch_biased(q, k, v, do, bias, scale):
     return o.detach().numpy(), [x.numpy() for x in g]
 
 
-def _tiny_selected(lengths=(32,), N2=1, G=2, D=4, bs=4, count=3, seed=0):
+def _tiny_selected(lengths=(32,), N2=1, G=2, D=4, bs=4, count=3, seed=0, Dv=None):
     lengths = np.array(lengths)
     cu = np.cumsum(lengths)
     T = int(cu[-1])
+    Dv = D if Dv is None else Dv
     rng = np.random.default_rng(seed)
-    q, do = rng.standard_normal((T, N2 * G, D)), rng.standard_normal((T, N2 * G, D))
-    k, v = rng.standard_normal((T, N2, D)), rng.standard_normal((T, N2, D))
+    q, do = rng.standard_normal((T, N2 * G, D)), rng.standard_normal((T, N2 * G, Dv))
+    k, v = rng.standard_normal((T, N2, D)), rng.standard_normal((T, N2, Dv))
     topk = synth.draw_topk(lengths, N2, bs, count, config_id=77)
     return q, k, v, do, topk, cu
 
 
 @pytest.mark.parametrize("sparse_mode", [0, 2])
-def test_selected_equals_biased_dense(sparse_mode):
-    q, k, v, do, topk, cu = _tiny_selected(lengths=(24, 16), N2=2, G=2, count=3)
+@pytest.mark.parametrize("D,Dv", [(4, 4), (6, 3)])
+def test_selected_equals_biased_dense(sparse_mode, D, Dv):
+    """Also with a value head dim unlike the query/key one (the Ascend page
+    supports unequal D for K and V)."""
+    q, k, v, do, topk, cu = _tiny_selected(lengths=(24, 16), N2=2, G=2, count=3, D=D, Dv=Dv)
     # inject duplicates and out-of-order entries on some rows
     topk[5, 0] = [1, 1, 0]
     topk[30, 1] = [2, 0, 2]
@@ -160,7 +164,7 @@ def test_selected_equals_biased_dense(sparse_mode):
 
 
 def test_selected_finite_differences_with_duplicates():
-    q, k, v, do, topk, cu = _tiny_selected(lengths=(32,), N2=1, G=2, D=3, bs=4, count=3, seed=3)
+    q, k, v, do, topk, cu = _tiny_selected(lengths=(32,), N2=1, G=2, D=3, bs=4, count=3, seed=3, Dv=2)
     topk[20, 0] = [2, 2, 5]
     bs, scale, mode = 4, 0.6, 2
     g = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, mode)
@@ -174,7 +178,7 @@ def test_selected_finite_differences_with_duplicates():
         x = base[j]
         # a sample of coordinates keeps the test quick
         for idx in [(20, 0, 1), (9, 0, 2), (21, 0, 0), (3, 0, 1), (31, 0, 2)]:
-            idx = idx if x.shape[1] > idx[1] else (idx[0], 0, idx[2])
+            idx = (idx[0], min(idx[1], x.shape[1] - 1), min(idx[2], x.shape[2] - 1))
             args = [a.copy() for a in base]
             args[j][idx] += h
             lp = loss(*args)
