@@ -4,7 +4,10 @@
 // block_size rows that topk[t, h2, :] names, gathered with repetition (the
 // operator page's Gather over 0 <= i < selectedBlockCount, "Formula" section);
 // the gradients are the page's dV = P^T dY, dQ = dS K / sqrt(d),
-// dK = dS^T Q / sqrt(d) over those keys.
+// dK = dS^T Q / sqrt(d) over those keys.  Q and K have head dim DK, V, O and
+// dY head dim DV (the page: 192 or 128, unequal allowed); S, dQ and dK
+// contract or produce DK columns, dP, dV and O DV columns.  Gradients are
+// stored in the input type or fp32.
 //
 // Kernels, all on the caller's stream:
 //   nsa_index_kernel<false>  per (KV head, KV block): how many (token, slot)
@@ -21,6 +24,8 @@
 //                            order (deterministic); zero-fills unselected blocks
 //   nsa_dq_kernel            per (token, KV head, 16-head tile): dQ over the
 //                            gathered keys, without atomics
+//   nsa_fwd_kernel           the forward: O and (max, sum) per (token, head)
+//                            over the gathered keys, same tiling as nsa_dq
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
