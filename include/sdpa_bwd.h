@@ -29,7 +29,7 @@
  *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
  *   keep every row 16-byte aligned.  The row stride (S or T) of every tensor
  *   and of the statistics must lie in [0, 2^23) elements.  D is 64 or 128
- *   (the selected backward also takes D = 192 with a value head dim of 128).
+ *   (the selected calls also take D = 192, with a value head dim of 192 or 128).
  *   Any other layout returns SDPA_ERR_UNSUPPORTED.
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library allocates no device memory, keeps no per-call state and never
@@ -228,7 +228,8 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   grad_dtype: `dtype` or SDPA_F32, as for sdpa_bwd.
  *   D: head dim of q, k, dq, dk; Dv: of v, o, dout, dv (the page: D is 192
  *   or 128, and K and V may differ).  Kernels exist for (D, Dv) = (64, 64),
- *   (128, 128) and (192, 128); other valid pairs return SDPA_ERR_UNSUPPORTED.
+ *   (128, 128), (192, 192) and (192, 128); other valid pairs return
+ *   SDPA_ERR_UNSUPPORTED.
  */
 int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                      const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,

@@ -78,15 +78,21 @@ __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
 // Preprocess
 // ---------------------------------------------------------------------------
 
-// Grid, D/16 lanes per row (16 elements each): dense, x = chunks of rows of
-// one (batch, head) = y; packed, x = chunks of the (token, head) rows in
-// memory order (the heads of a token are adjacent in the packed layout).
+// Grid, LPR lanes per row (a power of two; 16 elements per lane at D=64 and
+// 128, 24 at D=192): dense, x = chunks of rows of one (batch, head) = y;
+// packed, x = chunks of the (token, head) rows in memory order (the heads of
+// a token are adjacent in the packed layout).
 template <int D>
-constexpr int pre_rows_per_block() { return 256 / (D / 16); }
+constexpr int pre_lanes() { return D == 64 ? 4 : 8; }
+template <int D>
+constexpr int pre_rows_per_block() { return 256 / pre_lanes<D>(); }
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) {
-    constexpr int LPR = D / 16;
+    constexpr int LPR = pre_lanes<D>();
+    constexpr int EPL = D / LPR;                 // elements per lane
+    constexpr int NC = EPL / 8;                  // 16-byte chunks per lane
+    static_assert(EPL % 8 == 0 && (LPR & (LPR - 1)) == 0, "row split");
     constexpr int RPB = pre_rows_per_block<D>();
     const int part = threadIdx.x % LPR;
     int64_t R;
@@ -104,14 +110,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
         R = (int64_t)y * p.Sq + i;
         L = RowLoc{y / p.Hq, y % p.Hq, min(i, p.Sq - 1)};
     }
-    const uint16_t* op = p.o.p + toff(p.o, L) + part * 16;
-    const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * 16;
-    const u32x4 o0 = ld16(op), o1 = ld16(op + 8);
-    const u32x4 d0 = ld16(dp), d1 = ld16(dp + 8);
+    const uint16_t* op = p.o.p + toff(p.o, L) + part * EPL;
+    const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * EPL;
+    u32x4 oc[NC], dc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        oc[c] = ld16(op + 8 * c);
+        dc[c] = ld16(dp + 8 * c);
+    }
     const int64_t so = L.b * p.st_sb + L.h * p.st_sh + L.i * p.st_ss;
     const float sa = p.st_a[so];
     const float sb = p.stats_kind ? p.st_b[so] : 0.f;
-    float acc = dot8<T>(d1, o1, dot8<T>(d0, o0));
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc = dot8<T>(dc[c], oc[c], acc);
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (!ok) return;
@@ -121,11 +133,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) 
     }
     if (zero_dq) {
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 16);
-        dst[0] = z;
-        dst[1] = z;
-        dst[2] = z;
-        dst[3] = z;
+        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * EPL);
+#pragma unroll
+        for (int c = 0; c < EPL / 4; ++c) dst[c] = z;
     }
 }
 
@@ -1059,7 +1069,11 @@ static hipError_t launch_pre_t(const BwdParams& p, bool zero_dq, hipStream_t st)
 }
 
 hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st) {
-    if (dtype == 0) return D == 64 ? launch_pre_t<F16, 64>(p, zero_dq, st) : launch_pre_t<F16, 128>(p, zero_dq, st);
+    if (dtype == 0) {
+        if (D == 192) return launch_pre_t<F16, 192>(p, zero_dq, st);
+        return D == 64 ? launch_pre_t<F16, 64>(p, zero_dq, st) : launch_pre_t<F16, 128>(p, zero_dq, st);
+    }
+    if (D == 192) return launch_pre_t<BF16, 192>(p, zero_dq, st);
     return D == 64 ? launch_pre_t<BF16, 64>(p, zero_dq, st) : launch_pre_t<BF16, 128>(p, zero_dq, st);
 }
 

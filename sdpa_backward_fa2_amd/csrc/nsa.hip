@@ -1067,8 +1067,8 @@ template <class T>
 static hipError_t launch_nsa_fwd_dims(const NsaParams& p, int D, int Dv, hipStream_t st) {
     if (D == 64) return launch_nsa_fwd_t<T, 64, 64>(p, st);
     if (D == 128) return launch_nsa_fwd_t<T, 128, 128>(p, st);
-    (void)Dv;   // (192, 128): the only other pair the host accepts
-    return launch_nsa_fwd_t<T, 192, 128>(p, st);
+    if (Dv == 192) return launch_nsa_fwd_t<T, 192, 192>(p, st);
+    return launch_nsa_fwd_t<T, 192, 128>(p, st);      // the other pair the host accepts
 }
 
 // DK: head dim of Q and K, DV: of V, O and dO (the row pass reduces dO o O)
@@ -1090,8 +1090,8 @@ template <class T>
 static hipError_t launch_nsa_dims(const NsaParams& p, const BwdParams& bp, int D, int Dv, hipStream_t st) {
     if (D == 64) return launch_nsa_t<T, 64, 64>(p, bp, st);
     if (D == 128) return launch_nsa_t<T, 128, 128>(p, bp, st);
-    (void)Dv;   // (192, 128): the only other pair the host accepts
-    return launch_nsa_t<T, 192, 128>(p, bp, st);
+    if (Dv == 192) return launch_nsa_t<T, 192, 192>(p, bp, st);
+    return launch_nsa_t<T, 192, 128>(p, bp, st);      // the other pair the host accepts
 }
 
 }  // namespace sdpa
@@ -1128,10 +1128,10 @@ int read_seqs(int64_t batch, const int64_t* cuq, const int64_t* cuk, Seqs& S) {
     return SDPA_OK;
 }
 
-// Head dims (Q/K D, V Dv) with kernels: equal 64 or 128, and D = 192 with
-// Dv = 128 (the Ascend page: D is 192 or 128, unequal for K and V allowed).
+// Head dims (Q/K D, V Dv) with kernels: equal 64, 128 or 192, and D = 192
+// with Dv = 128 (the Ascend page: D is 192 or 128, unequal for K and V allowed).
 bool nsa_dims_ok(int64_t D, int64_t Dv) {
-    return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 192 && Dv == 128);
+    return (D == Dv && (D == 64 || D == 128 || D == 192)) || (D == 192 && Dv == 128);
 }
 
 // Validation shared by the size query, the backward and the index build

@@ -235,7 +235,7 @@ def workload(config_id: int) -> Workload:
 def with_head_dims(wl: Workload, D: int, Dv: int) -> Workload:
     """The same workload with query/key head dim D and value head dim Dv (the
     NSA page allows D of 192 or 128, unequal for K and V); scale 1/sqrt(D)."""
-    return replace(wl, name=f"{wl.name} with Dqk{D} Dv{Dv}", D=D, Dv_=0 if Dv == D else Dv,
+    return replace(wl, name=wl.name.replace(f"D{wl.D}", f"Dqk{D} Dv{Dv}"), D=D, Dv_=0 if Dv == D else Dv,
                    scale=1.0 / math.sqrt(D))
 
 

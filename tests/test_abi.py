@@ -237,7 +237,7 @@ def test_bwd_selected_validation():
     assert bwd_selected_call(grad=7) == INVALID
     assert bwd_selected_call(det=3) == INVALID
     assert bwd_selected_call(Dv=0) == INVALID
-    assert bwd_selected_call(D=192, Dv=192) == UNSUPPORTED    # kernels: (64,64), (128,128), (192,128)
+    assert bwd_selected_call(D=64, Dv=128) == UNSUPPORTED     # kernels: equal 64/128/192, and (192,128)
     assert bwd_selected_call(D=128, Dv=64) == UNSUPPORTED
     n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 1)(512)
@@ -245,7 +245,7 @@ def test_bwd_selected_validation():
     m = ctypes.c_size_t(0)
     assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 128, 128, 64, 4, 0, ctypes.byref(m)) == OK
     assert n.value > m.value                             # wider dK partials
-    assert fwd_selected_call(D=192) == UNSUPPORTED       # (192, 192): no kernel
+    assert fwd_selected_call(D=128, Dv=192) == UNSUPPORTED
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
@@ -253,6 +253,7 @@ def test_bwd_selected_valid_without_device():
     assert bwd_selected_call() == HIP
     assert bwd_selected_call(grad=2) == HIP           # fp32 gradients
     assert bwd_selected_call(D=192, Dv=128) == HIP    # unequal head dims
+    assert bwd_selected_call(D=192, Dv=192) == HIP
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")

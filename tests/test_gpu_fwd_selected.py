@@ -81,7 +81,7 @@ def test_config5_forward():
     _case(x, t, wl.topk(), cu, wl.block_size, wl.scale, 2, wl.dtype)
 
 
-@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128), ("f16", 192, 192)])
 @pytest.mark.parametrize("mode", [0, 2])
 @pytest.mark.parametrize("lengths,G,N2,bs,count", [
     ((256, 128), 2, 2, 64, 2),

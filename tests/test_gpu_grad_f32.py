@@ -107,7 +107,7 @@ def test_packed(D):
         _compare(g32, g16, g, dtype, det == 0 or D == 64, f"det={det}")
 
 
-@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128), ("bf16", 192, 192)])
 @pytest.mark.parametrize("lengths,G,bs,count", [((256, 128), 2, 64, 2), ((96, 160, 80), 16, 16, 5)])
 def test_selected(dtype, D, Dv, lengths, G, bs, count):
     """One-piece blocks (written by the dK/dV kernel) and split blocks (summed

@@ -86,7 +86,8 @@ def test_config5_nsa_selected():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128), ("f16", 192, 128)])
+@pytest.mark.parametrize("dtype,D,Dv", [("f16", 64, 64), ("bf16", 128, 128), ("bf16", 192, 128), ("f16", 192, 128),
+                                        ("bf16", 192, 192)])
 @pytest.mark.parametrize("mode", [0, 2])
 @pytest.mark.parametrize("lengths,G,N2,bs,count", [
     ((256, 128), 2, 2, 64, 2),
