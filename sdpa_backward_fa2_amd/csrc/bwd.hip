@@ -5,11 +5,12 @@
 //                      log2-domain LSE, and (D=128 atomic mode) the fp32 dQ
 //                      accumulator row cleared.                   [HBM-bound]
 //   bwd_fused8_kernel  D=64: one launch of four-wavefront workgroups, two per
-//                      CU; the first ones run the key-tile outer body (dK, dV
-//                      of 64 keys over every query tile of every query head
-//                      of the group), the rest the query-tile outer body (dQ
-//                      of 64 rows over the key tiles they see).  No atomics.
-//                                                                       [MFMA]
+//                      CU, running work items of two kinds: the key-tile
+//                      outer body (dK, dV of 64 keys over every query tile of
+//                      every query head of the group) and a query-tile outer
+//                      body (dQ of 64 rows, or of 128 rows in the wide form
+//                      for large causal problems, over the key tiles they
+//                      see).  No atomics.                                [MFMA]
 //   bwd_main_kernel    D=128: one four-wavefront workgroup per (sequence, KV
 //                      head, 128-key tile); dK and dV accumulate in registers
 //                      across every query tile of every query head of the
@@ -998,6 +999,208 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
                         dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
 }
 
+// ---------------------------------------------------------------------------
+// Wide query-tile body of the D=64 kernel: dQ of 128 query rows
+// ---------------------------------------------------------------------------
+//
+// Wavefront w owns rows 32w .. +31 of the tile against all 64 keys of each
+// step, so there are no key-slice partials to sum at the end: per step, S^T
+// and dP^T of the two 32-key halves (v_mfma_f32_32x32x16; dP^T accumulates
+// onto -Delta), P and dS, then dQ^T += K^T dS^T.  K and V tiles are double
+// buffered in LDS and the next one is loaded into registers during the step.
+// With twice the rows of the 64-row body an item covers twice the work, so
+// the per-item costs (first loads, dispatch, epilogue) are paid half as
+// often.  On a causal diagonal, a wavefront whose rows all precede the step's
+// keys skips the step's products (its P is zero there).
+
+template <int D>
+struct DqwLds {
+    static constexpr int BK = 64, KP = D + 8;
+    static constexpr int TILE_B = BK * KP * 2;
+    static constexpr int BYTES = 4 * TILE_B;   // K and V, two buffers each
+};
+
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    static_assert(D == 64, "wide dQ body: D=64");
+    constexpr int BQ = 128;                 // query rows per workgroup
+    constexpr int BK = DqwLds<D>::BK;       // keys per step
+    constexpr int KS = D / 16;              // k-steps over the head dimension (32x32x16)
+    constexpr int DB = D / 32;              // 32-row blocks of dQ^T
+    constexpr int KP = DqwLds<D>::KP;       // row stride of the K and V tiles  [key][d]
+    constexpr int TILE = BK * KP;           // elements of one tile
+    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per tile
+    uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena);
+    uint16_t* Vs0 = Ks0 + 2 * TILE;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    const int b = by / p.Hq, h = by % p.Hq;
+    const int hk = h / (p.Hq / p.Hkv);
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
+    const int i0 = bx * BQ;
+    if (i0 >= lq) return;
+
+    const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
+    const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
+    const uint16_t* kb = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;   // tile being loaded
+    const uint16_t* vb = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
+    const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
+
+    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
+    const int n_steps = (kend + BK - 1) / BK;
+
+    // byte offsets of this thread's chunks within a key tile
+    const uint32_t kss = 2u * (uint32_t)p.k.ss, vss = 2u * (uint32_t)p.v.ss;
+    uint32_t koff[CH], voff[CH];
+    int crow[CH], ccol[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + kThreads * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        ccol[x] = cc;
+        koff[x] = r * kss + 2 * cc;
+        voff[x] = r * vss + 2 * cc;
+    }
+    // Unconditional loads: keys past the end of the sequence re-read its last
+    // key and are masked out (P = 0); nothing loaded is used before the tile
+    // is stored after the step's products.
+    u32x4 pk[CH], pv[CH];
+    auto load_tile = [&](int st) {
+        const int j0 = st * BK;
+        uint32_t ok_[CH], ov_[CH];
+        if (j0 + BK <= lk) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
+        } else {
+            const int last = lk - 1 - j0;
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                const uint32_t r = min(crow[x], last);
+                ok_[x] = r * kss + 2 * ccol[x];
+                ov_[x] = r * vss + 2 * ccol[x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            pk[x] = ld16_at(kb, ok_[x]);
+            pv[x] = ld16_at(vb, ov_[x]);
+        }
+        kb += k_step;
+        vb += v_step;
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* Kd = Ks0 + buf * TILE;
+        uint16_t* Vd = Vs0 + buf * TILE;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
+            st16(&Vd[crow[x] * KP + ccol[x]], pv[x]);
+        }
+    };
+
+    // Prologue: the first key tile and this lane's query row are requested
+    // before anything waits for memory.
+    if (n_steps > 0) load_tile(0);
+    const int my_i = i0 + 32 * w + c;
+    const bool row_ok = my_i < lq;
+    // a row past the end of the sequence re-reads its last row; its LSE is
+    // +inf (P = 0) and its dQ is not stored
+    const int my_ic = min(my_i, lq - 1);
+    u32x4 qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
+        doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
+    }
+    // this row's log2-domain LSE and Delta from the row pass
+    const int64_t ws = p.varlen ? (int64_t)(q0 + my_ic) * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq + my_ic;
+    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
+    const float dl = p.delta[ws];
+
+    f32x16 dq[DB], ndl16;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
+
+    if (n_steps > 0) store_tile(0);
+    wait_all_memory();
+    __syncthreads();
+
+    // last key this lane's row keeps, relative to the 8q+4g part of a tile row
+    const int t_row = min(lk - 1, CAUSAL ? my_i : INT_MAX) - 4 * g;
+    const int w_row0 = i0 + 32 * w;   // the wavefront's first row
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const int j0 = st * BK;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+        const uint16_t* Kb = Ks0 + buf * TILE;
+        const uint16_t* Vb = Vs0 + buf * TILE;
+        // every key of the step after every row of this wavefront: P = 0
+        const bool dead = CAUSAL && j0 > w_row0 + 31;
+
+        f32x16 ds[2];
+        if (!dead) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    s = T::mma(ld16(&Kb[(32 * kh + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
+                    dp = T::mma(ld16(&Vb[(32 * kh + c) * KP + 16 * ks + 8 * g]), doreg[ks], dp);
+                }
+                // element rg: key j0 + 32kh + 8(rg/4) + 4g + rg%4, query my_i
+                const int jh = j0 + 32 * kh;
+                const bool masked = (CAUSAL && jh + 31 > w_row0) || (jh + 32 > lk);
+                if (masked) {
+                    const int t = t_row - jh;
+#pragma unroll
+                    for (int rg = 0; rg < 16; ++rg) {
+                        float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                        pvv = (8 * (rg >> 2) + (rg & 3) <= t) ? pvv : 0.f;
+                        dp[rg] = pvv * dp[rg];
+                    }
+                } else {
+#pragma unroll
+                    for (int rg = 0; rg < 16; ++rg)
+                        dp[rg] = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2)) * dp[rg];
+                }
+                ds[kh] = dp;
+            }
+        }
+        if (has_next) store_tile(buf ^ 1);
+        if (!dead) {
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x4 bS = acc_to_operand<T>(ds[kh], hh);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kh + 16 * hh, db * 32, lane), bS, dq[db]);
+                }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        __syncthreads();
+    }
+
+    if (!row_ok) return;
+    const int64_t dqo = b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            st_grad4<T>(p.dq.p, dqo + db * 32 + 8 * q + 4 * g, p.grad_f32, dq[db][4 * q + 0] * p.scale,
+                        dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
+}
+
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
     __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
@@ -1011,33 +1214,74 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
     bwd_dq8_body<T, D, CAUSAL>(p, arena, gridDim.x - 1 - item, unit);
 }
 
-// dK/dV and dQ in one launch: the first n_main workgroups run the key-tile
-// outer kernel (key tiles in ascending order, so the longest causal ranges
-// start first), the rest the query-tile outer dQ kernel (query tiles in
-// descending order).  The dQ workgroups fill the CUs the long dK/dV
-// workgroups leave idle near the end.
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, int main_x, int main_y, int dq_x, int dq_y,
-                                                                   int alternate) {
-    constexpr int A = Main8Lds<D>::BYTES > Dq8Lds<D>::BYTES ? Main8Lds<D>::BYTES : Dq8Lds<D>::BYTES;
+// dK/dV and dQ in one launch: key-tile items (the key-tile outer body, dK and
+// dV of 64 keys) and query-tile items, dQ of 64 rows or, causal with more
+// items than the GPU has workgroup slots, of 128 rows with the wide body
+// (half the items, so half the per-item costs; with fewer items the time is
+// the longest item's, and non-causal the wide step's lower efficiency is not
+// paid back: measured).  Item order, longest first so the dQ items fill the
+// CUs that the long dK/dV items leave idle near the end: causal with one
+// query head per KV head and equal lengths, key tile k has n_k - k steps and
+// query tile m has m + 1 (64 rows) or 2m + 2 (128 rows), so segments of two
+// items (key tile k, query tile n_q - 1 - k) or of three (key tiles 2j and
+// 2j + 1 around query tile n_q - 1 - j), each over every (sequence, head), go
+// out in decreasing length; otherwise the key tiles, then the query tiles in
+// descending order.
+// The two forms are separate instantiations (WIDE): one kernel holding both
+// query-tile bodies spilled registers.
+struct Fused8Map {
+    int main_x, main_y, dq_x, dq_y;
+    int alternate;   // the two- or three-item segment order
+};
+
+template <class T, int D, bool CAUSAL, bool WIDE>
+__device__ __forceinline__ void fused8_dq(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    if constexpr (WIDE) bwd_dqw_body<T, D, CAUSAL>(p, arena, bx, by);
+    else bwd_dq8_body<T, D, CAUSAL>(p, arena, bx, by);
+}
+
+template <class T, int D, bool CAUSAL, bool WIDE>
+__global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, Fused8Map m) {
+    constexpr int A = Main8Lds<D>::BYTES > (WIDE ? DqwLds<D>::BYTES : Dq8Lds<D>::BYTES)
+                          ? Main8Lds<D>::BYTES : (WIDE ? DqwLds<D>::BYTES : Dq8Lds<D>::BYTES);
     __shared__ __align__(16) unsigned char arena[A];
     const int id = blockIdx.x;
-    if (alternate) {
-        // main_x == dq_y and main_y == dq_x: segment 2k is key tile k (k+1-th
-        // longest causal range), segment 2k+1 the query tile with as many key
-        // steps, so work items are dispatched roughly longest first
-        const int seg = id / main_x, within = id % main_x;
-        if (!(seg & 1)) bwd_main8_body<T, D, CAUSAL>(p, arena, within, seg >> 1);
-        else bwd_dq8_body<T, D, CAUSAL>(p, arena, dq_x - 1 - (seg >> 1), within);
+    constexpr bool wide = WIDE;
+    if (m.alternate) {
+        // main_x == dq_y; main_y == dq_x (64-row items) or 2 * dq_x (wide)
+        const int seg = id / m.main_x, within = id % m.main_x;
+        if constexpr (wide) {
+            const int j = seg / 3, r = seg % 3;
+            if (r == 1) bwd_dqw_body<T, D, CAUSAL>(p, arena, m.dq_x - 1 - j, within);
+            else bwd_main8_body<T, D, CAUSAL>(p, arena, within, 2 * j + (r >> 1));
+        } else {
+            if (!(seg & 1)) bwd_main8_body<T, D, CAUSAL>(p, arena, within, seg >> 1);
+            else bwd_dq8_body<T, D, CAUSAL>(p, arena, m.dq_x - 1 - (seg >> 1), within);
+        }
         return;
     }
-    const int n_main = main_x * main_y;
+    const int n_main = m.main_x * m.main_y;
     if (id < n_main) {
-        bwd_main8_body<T, D, CAUSAL>(p, arena, id % main_x, id / main_x);
+        bwd_main8_body<T, D, CAUSAL>(p, arena, id % m.main_x, id / m.main_x);
     } else {
         const int r = id - n_main;
-        bwd_dq8_body<T, D, CAUSAL>(p, arena, dq_x - 1 - r / dq_y, r % dq_y);
+        fused8_dq<T, D, CAUSAL, WIDE>(p, arena, m.dq_x - 1 - r / m.dq_y, r % m.dq_y);
     }
+}
+
+// Workgroup slots of the D=64 fused kernel on the current device: two per
+// compute unit (0 if the count is unknown).
+static int fused8_slots() {
+    constexpr int kMaxDev = 64;
+    static int cached[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) return 0;
+        cached[dev] = 2 * cu;
+    }
+    return cached[dev];
 }
 
 // ---------------------------------------------------------------------------
@@ -1052,17 +1296,19 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
         if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
         const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
         static_assert(32 * kKeySlices == 64, "key tile of the fused kernel");
-        const int qx = L.max_q_tiles64, qy = L.n_seq * p.Hq;
-        const int n = mx * my + qx * qy;
-        if (n > 0)
-        {
-            // Causal with one query head per KV head: main key tile k has as many
-            // steps as query tile n-1-k has key steps, so the two kinds alternate
-            // in decreasing length; otherwise the key-tile items (the longer
-            // ones) go first.
-            const int alternate = (CAUSAL && mx == qy && my == qx) ? 1 : 0;
-            PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL>), dim3(n), dim3(kThreads), 0, st, p, mx, my,
-                        qx, qy, alternate);
+        const int qy = L.n_seq * p.Hq;
+        // 128-row dQ items, causal, when the 64-row form has more items than slots
+        const int slots = fused8_slots();
+        const long n64 = (long)mx * my + (long)L.max_q_tiles64 * qy;
+        const bool wide = CAUSAL && slots > 0 && n64 > slots;
+        Fused8Map m{mx, my, wide ? L.max_q_tiles128 : L.max_q_tiles64, qy, 0};
+        const int n = mx * my + m.dq_x * qy;
+        if (n > 0) {
+            m.alternate = (CAUSAL && mx == qy && my == (wide ? 2 : 1) * m.dq_x) ? 1 : 0;
+            if (wide)
+                PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL, true>), dim3(n), dim3(kThreads), 0, st, p, m);
+            else
+                PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL, false>), dim3(n), dim3(kThreads), 0, st, p, m);
         }
         return hipGetLastError();
     } else {
