@@ -90,10 +90,11 @@ def test_gqa_causal():
     _dense(4, 16, 4, 1024, 1024, "f16", True, [(0, 1), (3, 3)], seed=33)
 
 
-def test_rectangular_causal():
-    """Sq=1000 < Sk=1200, causal top-left: the last 200 keys are seen by no
-    query (zero dK, dV)."""
-    _dense(4, 8, 8, 1000, 1200, "f16", True, [(0, 2), (3, 4)], seed=34)
+@pytest.mark.parametrize("Sq,Sk", [(1000, 1200), (1200, 1000)])
+def test_rectangular_causal(Sq, Sk):
+    """Causal, top-left aligned: with Sq < Sk the last keys are seen by no
+    query (zero dK, dV); with Sq > Sk the rows past Sk see every key."""
+    _dense(4, 8, 8, Sq, Sk, "f16", True, [(0, 2), (3, 4)], seed=34)
 
 
 def test_packed_ragged_sequences():
