@@ -444,22 +444,33 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
         // a bucket's entries are sorted by token, so row 0 holds the step's
         // first token: when it sees the whole half block, no element is masked
         const bool masked = nkeys < 64 || (p.sparse_mode == 2 && last_kpos > tl_s[buf][0]);
+        // S^T and dP^T of every 32-row block of the step first, then each
+        // block's softmax gradient and dV/dK products, so that (one wavefront
+        // per SIMD) the matrix cores work through the next block's products
+        // while the vector ALUs run this block's softmax.  dP^T accumulates
+        // onto the rows' -Delta: pa ends as dP - Delta.
+        f32x16 sab[NSB], pab[NSB];
 #pragma unroll
         for (int sb = 0; sb < NSB; ++sb) {
             const int r0 = (BR / 2) * rh + 32 * sb;     // first row of this 32-row block
-            // dP^T accumulates onto the rows' -Delta: pa ends as dP - Delta
-            f32x16 sa = zero16(), pa;
+            sab[sb] = zero16();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][r0 + 8 * q + 4 * g]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+                for (int r = 0; r < 4; ++r) pab[sb][4 * q + r] = nd[r];
             }
 #pragma unroll
             for (int s = 0; s < KSM; ++s) {
-                if (s < KSK) sa = T::mma(ld16(&Qb[(r0 + c) * QPK + 16 * s + 8 * g]), kreg[s], sa);
-                if (s < KSV) pa = T::mma(ld16(&dOb[(r0 + c) * QPV + 16 * s + 8 * g]), vreg[s], pa);
+                if (s < KSK) sab[sb] = T::mma(ld16(&Qb[(r0 + c) * QPK + 16 * s + 8 * g]), kreg[s], sab[sb]);
+                if (s < KSV) pab[sb] = T::mma(ld16(&dOb[(r0 + c) * QPV + 16 * s + 8 * g]), vreg[s], pab[sb]);
             }
+        }
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+            const int r0 = (BR / 2) * rh + 32 * sb;
+            f32x16& sa = sab[sb];
+            f32x16& pa = pab[sb];
             auto grad = [&](auto masked_tag) {
                 constexpr bool MK = decltype(masked_tag)::value;
 #pragma unroll
