@@ -370,46 +370,80 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         const uint16_t* Qb = Qs[buf];
         const uint16_t* dOb = dOs[buf];
         const bool masked = (CAUSAL && i0 < j0 + BC) || !full_cols;
-        // S^T and dP^T of both 32-row halves of the query tile first, then each
-        // half's softmax gradient and dV/dK products: the matrix cores work
-        // through the second half's S and dP while the vector ALUs run the first
-        // half's softmax, and the first half's dV/dK products while they run the
-        // second's.  With one wavefront per SIMD this overlap has to come from
-        // within the wavefront.  dP^T accumulates onto the rows' -Delta: pa ends
-        // as dP - Delta.
-        f32x16 sa[MB], pa[MB];
+        if constexpr (!DQ_ATOMIC) {
+            // S^T and dP^T of both 32-row halves of the query tile first, then
+            // each half's softmax gradient and dV/dK products: the matrix
+            // cores work through the second half's S and dP while the vector
+            // ALUs run the first half's softmax, and the first half's dV/dK
+            // products while they run the second's.  With one wavefront per
+            // SIMD this overlap has to come from within the wavefront.  dP^T
+            // accumulates onto the rows' -Delta: pa ends as dP - Delta.
+            f32x16 sa[MB], pa[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            sa[mb] = zero16();
+            for (int mb = 0; mb < MB; ++mb) {
+                sa[mb] = zero16();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) pa[mb][4 * q + r] = nd[r];
-            }
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                sa[mb] = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa[mb]);
-                pa[mb] = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa[mb]);
-            }
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            if (masked)
-                softmax_grad_tile_nd<true>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
-            else
-                softmax_grad_tile_nd<false>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, 0);
-            if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const u32x4 bP = acc_to_operand<T>(sa[mb], hh);
-                const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                    dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                    for (int r = 0; r < 4; ++r) pa[mb][4 * q + r] = nd[r];
                 }
-                if (DQ_ATOMIC) {
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    sa[mb] = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa[mb]);
+                    pa[mb] = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa[mb]);
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                if (masked)
+                    softmax_grad_tile_nd<true>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
+                else
+                    softmax_grad_tile_nd<false>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, 0);
+                if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x4 bP = acc_to_operand<T>(sa[mb], hh);
+                    const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                    }
+                }
+            }
+        } else {
+            // Atomic mode, which also stages dS^T for its dQ product: one 32-row
+            // half at a time (S and dP of both halves first was 6 % slower
+            // here on the packed workload).
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                f32x16 sa = zero16(), pa;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+                }
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    sa = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
+                    pa = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+                }
+                if (masked)
+                    softmax_grad_tile_nd<true>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
+                else
+                    softmax_grad_tile_nd<false>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, 0);
+                if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const u32x4 bP = acc_to_operand<T>(sa, hh);
+                    const u32x4 bS = acc_to_operand<T>(pa, hh);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                    }
                     // dS^T rows j = 32w + c; bS holds query rows 16hh + 4g + 0..3 and
                     // 16hh + 8 + 4g + 0..3 of this half tile, packed in pairs
                     u32x2 lo, hi;
