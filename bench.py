@@ -39,7 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def kernel_sources(kernel: str) -> list:
     """The files a kernel's code comes from: its sources (NSA kernels also use
     the dense preprocess) and the build script, which holds the compiler flags."""
-    files = ("common.h", "bwd.hip", "nsa.hip") if kernel.startswith("nsa") else ("common.h", "bwd.hip")
+    base = ("common.h", "bwd_shared.h", "bwd.hip", "bwd128.hip")
+    files = base + ("nsa.hip",) if kernel.startswith("nsa") else base
     return [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f) for f in files] + [
         os.path.join(ROOT, "sdpa_backward_fa2_amd", "build.py")]
 

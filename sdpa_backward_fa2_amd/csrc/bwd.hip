@@ -1,4 +1,6 @@
-// SDPA backward, FlashAttention-2 style, for gfx950.
+// SDPA backward, FlashAttention-2 style, for gfx950: the row pass and the D=64
+// kernel.  (The D=128 kernels are in bwd128.hip; the helpers both use in
+// bwd_shared.h.)
 //
 // Kernels (all on the caller's stream):
 //   bwd_pre_kernel     per row: Delta = sum_d dO*O, the statistics as
@@ -11,69 +13,17 @@
 //                      body (dQ of 64 rows, or of 128 rows in the wide form
 //                      for large causal problems, over the key tiles they
 //                      see).  No atomics.                                [MFMA]
-//   bwd_main_kernel    D=128: one four-wavefront workgroup per (sequence, KV
-//                      head, 128-key tile); dK and dV accumulate in registers
-//                      across every query tile of every query head of the
-//                      group; per 64-row query tile S, dP, dV, dK and, in
-//                      atomic mode, dQ += dS K through fp32 atomics.     [MFMA]
-//   bwd_dq_convert     D=128 atomic mode: dQ = scale * accumulator, rounded.
-//   bwd_dq8_kernel     D=128 deterministic mode: the query-tile outer dQ body
-//                      as its own launch.                                [MFMA]
 //
 // The formulas: dV = P^T dO, dQ = s dS K, dK = s dS^T Q (Ascend
 // aclnnNsaSelectedAttentionGrad page, "Formula" section), with
 // dS = P o (dP - Delta), Delta_i = sum_j P_ij dP_ij = sum_d dO_id O_id, the
 // softmax gradient written with the forward output instead of P.
+#include "bwd_shared.h"
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
 
 namespace sdpa {
-
-// ---------------------------------------------------------------------------
-// Row location helpers
-// ---------------------------------------------------------------------------
-
-struct RowLoc {
-    int64_t b, h, i;   // dense: batch, head, row; packed: b = 0, i = token
-};
-
-__device__ __forceinline__ RowLoc row_of(const BwdParams& p, int64_t R) {
-    RowLoc L;
-    if (p.varlen) {
-        L.b = 0; L.h = R % p.Hq; L.i = R / p.Hq;
-    } else {
-        L.i = R % p.Sq;
-        const int64_t bh = R / p.Sq;
-        L.h = bh % p.Hq; L.b = bh / p.Hq;
-    }
-    return L;
-}
-
-// log2-domain LSE of one row from the caller's statistics (a = LSE, or a = row
-// max and b = row sum): LSE*log2e, or m*log2e + log2(l); +inf for a row
-// without keys, so that its P is exactly zero.
-__device__ __forceinline__ float stats_to_lse2(int kind, float a, float b) {
-    if (kind == 0) return (a == -INFINITY) ? INFINITY : a * kLog2e;
-    return (b > 0.f) ? a * kLog2e + log2f(b) : INFINITY;
-}
-
-template <class T>
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc = 0.f) {
-    acc = T::dot2(a[0], b[0], acc);
-    acc = T::dot2(a[1], b[1], acc);
-    acc = T::dot2(a[2], b[2], acc);
-    return T::dot2(a[3], b[3], acc);
-}
-
-// dQ accumulator row of statistics row R (head-major; see BwdParams)
-__device__ __forceinline__ int64_t acc_row(const BwdParams& p, const RowLoc& L, int64_t R) {
-    return p.varlen ? L.h * p.Sq + L.i : R;
-}
-
-__device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
-    return L.b * t.sb + L.h * t.sh + L.i * t.ss;
-}
 
 // ---------------------------------------------------------------------------
 // Preprocess
@@ -150,365 +100,6 @@ static void launch_pre(const BwdParams& p, int zero_dq, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// Main backward kernel (KV-tile outer)
-// ---------------------------------------------------------------------------
-//
-// Per step (one 64-row query tile of one query head) each wavefront, owning 32
-// of the workgroup's 128 keys, computes S and dP (32 x 32 per half tile), P and
-// dS, then dV^T += dO^T P and dK^T += Q^T dS.  Q and dO tiles sit row-major in
-// LDS; the transposed operands of the dV/dK products come from
-// ds_read_b64_tr_b16.  The next tile's Q/dO rows are loaded into registers
-// while the current one is consumed and written to the other half of a double
-// buffer.  In atomic mode dS^T goes to LDS and the four wavefronts split
-// dQ_tile = dS K (64 x D) between them, adding it to the fp32 accumulator with
-// global atomics.  Masks are evaluated only on tiles that need them (the
-// causal diagonal, a ragged last key tile); ragged query rows carry LSE = +inf
-// and so contribute P = 0 without a mask.
-
-// P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - Delta) for one 32x32
-// C tile held as (sa, pa), whose dP accumulator started from -Delta (pa
-// already holds dP - Delta); rows 8q + 4g + r of the tile, this lane's key.  Element (q, r) is kept when 8q + r >= t, with t the first
-// kept row offset of this lane's key (INT_MAX for a key past the end).
-template <bool MASKED>
-__device__ __forceinline__ void softmax_grad_tile_nd(f32x16& sa, f32x16& pa, const float* lse_row,
-                                                     float scale_log2, int g, int t) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rg = 4 * q + r;
-            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
-            if (MASKED) pv = (8 * q + r >= t) ? pv : 0.f;
-            sa[rg] = pv;
-            pa[rg] = pv * pa[rg];
-        }
-    }
-}
-
-// Dispatch places consecutive workgroups (x fastest) on consecutive XCDs of
-// the eight.  For a grid of n_unit units (heads, whose workgroups share their
-// tensors) of n_item items each, linear slot L is mapped so that XCD L % 8
-// runs the items of one unit after another: its concurrently running
-// workgroups then share a unit's data in that XCD's L2, instead of every XCD
-// reading every unit.  Needs n_unit % 8 == 0 (else the plain mapping).  A
-// bijection on [0, n_unit * n_item).
-__device__ __forceinline__ void xcd_unit_order(int n_unit, int n_item, int L, int& unit, int& item) {
-    if (n_unit & 7) {
-        unit = L % n_unit;
-        item = L / n_unit;
-        return;
-    }
-    const int xcd = L & 7, slot = L >> 3;
-    unit = (slot / n_item) * 8 + xcd;
-    item = slot % n_item;
-}
-
-template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
-    constexpr int BC = 128;          // keys per workgroup: 4 wavefronts x 32
-    constexpr int BR = 64;           // query rows per step
-    constexpr int NW = 4;
-    constexpr int KS = D / 16;       // k-steps over the head dimension
-    constexpr int MB = BR / 32;      // 32-row blocks of the query tile
-    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int QP = D + 8;        // row stride of Qs, dOs, Ks  [row][d]
-    constexpr int SP = BR + 8;       // row stride of dST          [j][i]
-    constexpr int CH = BR * D / 8 / 256;     // 16-byte chunks per thread per tile
-    constexpr int NBLK = MB * DB / NW;       // dQ 32x32 blocks per wavefront
-    static_assert(CH >= 1 && NBLK >= 1, "tile shape");
-    __shared__ __align__(16) uint16_t Qs[2][BR * QP];
-    __shared__ __align__(16) uint16_t dOs[2][BR * QP];
-    __shared__ __align__(16) uint16_t Ks[DQ_ATOMIC ? BC * QP : 8];
-    __shared__ __align__(16) uint16_t dST[DQ_ATOMIC ? BC * SP : 8];
-    __shared__ __align__(16) float lse_s[2][BR];
-    __shared__ __align__(16) float dlt_s[2][BR];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 5, c = lane & 31;
-    // Grid (sequence x KV head, key tile): the key tiles go out longest causal
-    // range first, and with gridDim.x a multiple of 8 each (sequence, KV head)
-    // stays on one XCD, whose L2 its workgroups share.  (Ordering one unit's
-    // tiles together instead, as the dQ kernel does, was measured 7-9 % slower
-    // here: this kernel runs one workgroup per CU and needs the longest-first
-    // order more than the locality.)
-    const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
-    const int G = p.Hq / p.Hkv;
-    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
-    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int j0 = blockIdx.y * BC;
-    if (j0 >= lk) return;
-    const bool full_cols = j0 + BC <= lk;
-
-    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
-    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
-
-    const int my_j = j0 + 32 * w + c;
-    const bool col_ok = my_j < lk;
-    u32x4 kreg[KS], vreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
-        vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
-        if (DQ_ATOMIC) st16(&Ks[(32 * w + c) * QP + 16 * s + 8 * g], kreg[s]);
-    }
-
-    f32x16 dva[DB], dka[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
-
-    // steps: query heads of the group outer, query tiles from the causal start inner
-    const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
-    const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
-    const int n_steps = G * per_head;
-
-    // per-thread byte offsets of its 16-byte chunks inside a tile (row r,
-    // column cc); row strides are below 2^23 elements, so they fit 32 bits
-    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
-    const int64_t ws_ss = p.varlen ? p.Hq : 1;      // row stride of lse2 / delta
-    const uint32_t wss = 4u * (uint32_t)ws_ss;
-    uint32_t qoff[CH], dooff[CH];
-    int crow[CH], ccol[CH];
-#pragma unroll
-    for (int x = 0; x < CH; ++x) {
-        const int e = tid + 256 * x;
-        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-        crow[x] = r;
-        ccol[x] = cc;
-        qoff[x] = r * qss + 2 * cc;
-        dooff[x] = r * doss + 2 * cc;
-    }
-
-    // Cursor of the tile to load next (head ld_h, rows from ld_i0): the query
-    // rows of one head from i_begin to the end, then the next head of the
-    // group; pointers advance in scalar registers.
-    int ld_h = hk * G, ld_i0 = i_begin;
-    const uint16_t *ld_q, *ld_do;
-    const float *ld_l, *ld_d;
-    auto seek = [&]() {
-        ld_q = p.q.p + b * p.q.sb + ld_h * p.q.sh + (int64_t)(q0 + ld_i0) * p.q.ss;
-        ld_do = p.dout.p + b * p.dout.sb + ld_h * p.dout.sh + (int64_t)(q0 + ld_i0) * p.dout.ss;
-        const int64_t ws = p.varlen ? (int64_t)(q0 + ld_i0) * p.Hq + ld_h : ((int64_t)b * p.Hq + ld_h) * p.Sq + ld_i0;
-        ld_l = p.lse2 + ws;
-        ld_d = p.delta + ws;
-    };
-    seek();
-
-    // Tile loads are unconditional (rows past the end re-read the last row),
-    // and nothing loaded is used before store_tile, so the prefetch of the next
-    // tile is not waited for until the current step's products are issued.
-    u32x4 pq[CH], pdo[CH];
-    float pl = INFINITY, pd = 0.f;
-    int pi0 = 0;
-    auto load_tile = [&]() {
-        uint32_t oq[CH], odo[CH];
-        uint32_t so = (uint32_t)(tid & (BR - 1)) * wss;
-        if (ld_i0 + BR <= lq) {
-#pragma unroll
-            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
-        } else {
-            const int last = lq - 1 - ld_i0;
-#pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                const uint32_t r = min(crow[x], last);
-                oq[x] = r * qss + 2 * ccol[x];
-                odo[x] = r * doss + 2 * ccol[x];
-            }
-            so = (uint32_t)min(tid & (BR - 1), last) * wss;
-        }
-#pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            pq[x] = ld16_at(ld_q, oq[x]);
-            pdo[x] = ld16_at(ld_do, odo[x]);
-        }
-        pl = ldf_at(ld_l, so);
-        pd = ldf_at(ld_d, so);
-        pi0 = ld_i0;
-        ld_i0 += BR;
-        if (ld_i0 >= lq) {
-            ld_i0 = i_begin;
-            ++ld_h;
-            seek();
-        } else {
-            ld_q += BR * p.q.ss; ld_do += BR * p.dout.ss; ld_l += BR * ws_ss; ld_d += BR * ws_ss;
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Qs[buf][r * QP + cc], pq[x]);
-            st16(&dOs[buf][r * QP + cc], pdo[x]);
-        }
-        if (tid < BR) {
-            const bool ok = pi0 + tid < lq;     // a row past the end has P = 0
-            lse_s[buf][tid] = ok ? pl : INFINITY;
-            dlt_s[buf][tid] = ok ? -pd : 0.f;       // stored negated: it seeds dP - Delta
-        }
-    };
-
-    if (n_steps > 0) {
-        load_tile();
-        store_tile(0);
-    }
-    wait_all_memory();
-    __syncthreads();
-
-    // first kept row offset of this lane's key within a 32-row half, before
-    // the 8q+4g part: key my_j needs row >= my_j; a key past the end keeps nothing
-    const int t_key = col_ok ? (CAUSAL ? my_j - 4 * g : INT_MIN / 2) : INT_MAX / 2;
-
-    int h = hk * G, i0 = i_begin;          // the step's tile
-    for (int st = 0; st < n_steps; ++st) {
-        const int buf = st & 1;
-        const bool has_next = st + 1 < n_steps;
-        if (has_next) load_tile();
-
-        const uint16_t* Qb = Qs[buf];
-        const uint16_t* dOb = dOs[buf];
-        const bool masked = (CAUSAL && i0 < j0 + BC) || !full_cols;
-        if constexpr (!DQ_ATOMIC) {
-            // S^T and dP^T of both 32-row halves of the query tile first, then
-            // each half's softmax gradient and dV/dK products: the matrix
-            // cores work through the second half's S and dP while the vector
-            // ALUs run the first half's softmax, and the first half's dV/dK
-            // products while they run the second's.  With one wavefront per
-            // SIMD this overlap has to come from within the wavefront.  dP^T
-            // accumulates onto the rows' -Delta: pa ends as dP - Delta.
-            f32x16 sa[MB], pa[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                sa[mb] = zero16();
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pa[mb][4 * q + r] = nd[r];
-                }
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    sa[mb] = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa[mb]);
-                    pa[mb] = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa[mb]);
-                }
-            }
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                if (masked)
-                    softmax_grad_tile_nd<true>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
-                else
-                    softmax_grad_tile_nd<false>(sa[mb], pa[mb], &lse_s[buf][mb * 32], p.scale_log2, g, 0);
-                if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const u32x4 bP = acc_to_operand<T>(sa[mb], hh);
-                    const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
-                    }
-                }
-            }
-        } else {
-            // Atomic mode, which also stages dS^T for its dQ product: one 32-row
-            // half at a time (S and dP of both halves first was 6 % slower
-            // here on the packed workload).
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                f32x16 sa = zero16(), pa;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf][mb * 32 + 8 * q + 4 * g]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
-                }
-#pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    sa = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
-                    pa = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
-                }
-                if (masked)
-                    softmax_grad_tile_nd<true>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
-                else
-                    softmax_grad_tile_nd<false>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, 0);
-                if (mb == MB - 1 && has_next) store_tile(buf ^ 1);
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const u32x4 bP = acc_to_operand<T>(sa, hh);
-                    const u32x4 bS = acc_to_operand<T>(pa, hh);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
-                    }
-                    // dS^T rows j = 32w + c; bS holds query rows 16hh + 4g + 0..3 and
-                    // 16hh + 8 + 4g + 0..3 of this half tile, packed in pairs
-                    u32x2 lo, hi;
-                    lo[0] = bS[0]; lo[1] = bS[1]; hi[0] = bS[2]; hi[1] = bS[3];
-                    st8(&dST[(32 * w + c) * SP + mb * 32 + 16 * hh + 4 * g], lo);
-                    st8(&dST[(32 * w + c) * SP + mb * 32 + 16 * hh + 8 + 4 * g], hi);
-                }
-            }
-        }
-
-        if (DQ_ATOMIC) {
-            __syncthreads();
-            f32x16 acc[NBLK];
-#pragma unroll
-            for (int x = 0; x < NBLK; ++x) acc[x] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < BC / 16; ++ks)
-#pragma unroll
-                for (int x = 0; x < NBLK; ++x) {
-                    const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
-                    acc[x] = T::mma(ld_tr<false>(dST, SP, 16 * ks, ib * 32, lane),
-                                    ld_tr<false>(Ks, QP, 16 * ks, db * 32, lane), acc[x]);
-                }
-            // accumulator rows of this (sequence, head): head-major, row stride D floats
-            const int64_t arow0 = p.varlen ? ((int64_t)h * p.Sq + q0) : (((int64_t)b * p.Hq + h) * p.Sq);
-            float* dqa = p.dqacc + (arow0 + i0) * D + c;
-            const bool full_rows = i0 + BR <= lq;
-#pragma unroll
-            for (int x = 0; x < NBLK; ++x) {
-                const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
-                float* base = dqa + (ib * 32 + 4 * g) * D + db * 32;
-                if (full_rows) {
-#pragma unroll
-                    for (int rg = 0; rg < 16; ++rg)
-                        atomicAdd(base + (8 * (rg >> 2) + (rg & 3)) * D, acc[x][rg]);
-                } else {
-#pragma unroll
-                    for (int rg = 0; rg < 16; ++rg) {
-                        const int i = i0 + ib * 32 + 8 * (rg >> 2) + 4 * g + (rg & 3);
-                        if (i < lq) atomicAdd(base + (8 * (rg >> 2) + (rg & 3)) * D, acc[x][rg]);
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        i0 += BR;
-        if (i0 >= lq) { i0 = i_begin; ++h; }
-    }
-
-    if (!col_ok) return;
-    const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
-    const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = db * 32 + 8 * q + 4 * g;
-            st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
-                        dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-            st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
-                        dva[db][4 * q + 3]);
-        }
-}
-
-// ---------------------------------------------------------------------------
 // dK/dV body, four wavefronts (two workgroups per CU), software-pipelined
 // ---------------------------------------------------------------------------
 //
@@ -525,14 +116,6 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 // its rows' log2-domain LSE and negated Delta from the row pass.  The two row
 // halves' dK/dV partials are summed through LDS at the end.  dQ is left to
 // the query-outer body.
-
-// Wavefronts per workgroup of the D=64 kernel and the dQ body: two row halves
-// of kKeySlices key slices.  Four wavefronts let two workgroups share a CU (two
-// wavefronts per SIMD), so one workgroup's memory waits and barriers overlap
-// the other's arithmetic.
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kKeySlices = kWaves / 2;
 
 template <int D>
 struct Main8Lds {
@@ -804,245 +387,6 @@ __device__ __forceinline__ void bwd_main8_body(const BwdParams& p, unsigned char
 }
 
 // ---------------------------------------------------------------------------
-// dQ finalisation (atomic mode)
-// ---------------------------------------------------------------------------
-
-template <class T, int D>
-__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
-    constexpr int LPR = D / 8;
-    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t R = gt / LPR;
-    const int part = (int)(gt % LPR);
-    if (R >= p.rows) return;
-    const RowLoc L = row_of(p, R);
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * 8);
-    const f32x4 a = src[0], c = src[1];
-    const float x[8] = {a[0] * p.scale, a[1] * p.scale, a[2] * p.scale, a[3] * p.scale,
-                        c[0] * p.scale, c[1] * p.scale, c[2] * p.scale, c[3] * p.scale};
-    st_grad8<T>(p.dq.p, toff(p.dq, L) + part * 8, p.grad_f32, x);
-}
-
-// ---------------------------------------------------------------------------
-// dQ pass without atomics, four wavefronts (query-tile outer)
-// ---------------------------------------------------------------------------
-//
-// One workgroup per (sequence, query head, 64-row query tile); it walks the
-// 64-key tiles the tile can see.  Wavefront w = kw + 2*rh owns query rows
-// 32*rh .. +31 and keys 32*kw .. +31 of every key tile.  Scores are computed
-// transposed, S^T = K Q^T and dP^T = V dO^T, so that each lane holds one query
-// column: its LSE and Delta are lane-uniform, and dS^T feeds
-// dQ^T += K^T dS^T directly as the B operand.  Q and dO stay in registers for
-// the whole kernel; key tiles stream through a double-buffered LDS copy whose
-// next tile is loaded into registers while the current one is used.  Each
-// wavefront accumulates dQ^T over its key slice; the two slices' partials are
-// summed through LDS at the end and dQ is written once, scaled and rounded.
-
-template <int D>
-struct Dq8Lds {
-    static constexpr int BK = 32 * kKeySlices, KP = D + 8, DB = D / 32;
-    static constexpr int TILE_B = BK * KP * 2;
-    static constexpr int LOOP_B = 4 * TILE_B;
-    static constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;
-    static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
-};
-
-template <class T, int D, bool CAUSAL>
-__device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
-    constexpr int BQ = 64;           // query rows per workgroup
-    constexpr int BK = 32 * kKeySlices;   // keys per step
-    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
-    constexpr int DB = D / 32;       // 32-row blocks of dQ^T
-    constexpr int KP = D + 8;        // row stride of Ks, Vs  [key][d]
-    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per key tile
-    constexpr int TILE_B = BK * KP * 2;
-    constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
-    constexpr int LOOP_B = 4 * TILE_B;
-    constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;   // key slices 1.. of both row halves
-    static_assert(Dq8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
-    uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
-    uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
-    const int kw = w % kKeySlices, rh = w / kKeySlices;
-    const int g = lane >> 5, c = lane & 31;
-    const int b = by / p.Hq, h = by % p.Hq;
-    const int hk = h / (p.Hq / p.Hkv);
-    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
-    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int i0 = bx * BQ;
-    if (i0 >= lq) return;
-
-    const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
-    const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
-    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
-    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
-
-    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
-    const int n_steps = (kend + BK - 1) / BK;
-
-    // byte offsets of this thread's chunks within a key tile
-    const uint32_t kss = 2u * (uint32_t)p.k.ss, vss = 2u * (uint32_t)p.v.ss;
-    uint32_t koff[CH], voff[CH];
-    int crow[CH], ccol[CH];
-#pragma unroll
-    for (int x = 0; x < CH; ++x) {
-        const int e = tid + kThreads * x;
-        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-        crow[x] = r;
-        ccol[x] = cc;
-        koff[x] = r * kss + 2 * cc;
-        voff[x] = r * vss + 2 * cc;
-    }
-    // Unconditional loads: keys past the end of the sequence re-read its last
-    // key and are masked out (P = 0), so nothing is waited for before the tile
-    // is stored after the step's products.
-    u32x4 pk[CH], pv[CH];
-    const uint16_t* kb = kbase;          // key tile being loaded, advanced per step
-    const uint16_t* vb = vbase;
-    const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
-    auto load_tile = [&](int st) {
-        const int j0 = st * BK;
-        uint32_t ok_[CH], ov_[CH];
-        if (j0 + BK <= lk) {
-#pragma unroll
-            for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
-        } else {
-            const int last = lk - 1 - j0;
-#pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                const uint32_t r = min(crow[x], last);
-                ok_[x] = r * kss + 2 * ccol[x];
-                ov_[x] = r * vss + 2 * ccol[x];
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            pk[x] = ld16_at(kb, ok_[x]);
-            pv[x] = ld16_at(vb, ov_[x]);
-        }
-        kb += k_step;
-        vb += v_step;
-    };
-    auto store_tile = [&](int buf) {
-        uint16_t* Kd = Ks0 + buf * (BK * KP);
-        uint16_t* Vd = Vs0 + buf * (BK * KP);
-#pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
-            st16(&Vd[crow[x] * KP + ccol[x]], pv[x]);
-        }
-    };
-
-    // Prologue: the first key tile and this lane's query row are requested
-    // before anything waits for memory.
-    if (n_steps > 0) load_tile(0);
-    const int my_i = i0 + 32 * rh + c;
-    const bool row_ok = my_i < lq;
-    // a row past the end of the sequence re-reads its last row; its LSE is
-    // +inf (P = 0) and its dQ is not stored
-    const int my_ic = min(my_i, lq - 1);
-    u32x4 qreg[KS], doreg[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
-        doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
-    }
-    // this row's log2-domain LSE and Delta from the row pass
-    const int64_t ws = p.varlen ? (int64_t)(q0 + my_ic) * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq + my_ic;
-    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
-    const float dl = p.delta[ws];
-
-    f32x16 dq[DB], ndl16;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) dq[db] = zero16();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
-
-    if (n_steps > 0) store_tile(0);
-    wait_all_memory();
-    __syncthreads();
-
-    // last key this lane's row keeps, relative to the 8q+4g part of a tile row
-    const int t_row = min(lk - 1, CAUSAL ? my_i : INT_MAX) - 32 * kw - 4 * g;
-
-    for (int st = 0; st < n_steps; ++st) {
-        const int buf = st & 1;
-        const int j0 = st * BK;
-        const bool has_next = st + 1 < n_steps;
-        if (has_next) load_tile(st + 1);
-        const uint16_t* Kb = Ks0 + buf * (BK * KP);
-        const uint16_t* Vb = Vs0 + buf * (BK * KP);
-
-        f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
-            dp = T::mma(ld16(&Vb[(32 * kw + c) * KP + 16 * ks + 8 * g]), doreg[ks], dp);
-        }
-        // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
-        const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);
-        if (masked) {
-            const int t = t_row - j0;
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-                float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
-                pvv = (8 * (rg >> 2) + (rg & 3) <= t) ? pvv : 0.f;
-                dp[rg] = pvv * dp[rg];
-            }
-        } else {
-#pragma unroll
-            for (int rg = 0; rg < 16; ++rg) {
-                const float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
-                dp[rg] = pvv * dp[rg];
-            }
-        }
-        if (has_next) store_tile(buf ^ 1);
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const u32x4 bS = acc_to_operand<T>(dp, hh);
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-                dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane), bS, dq[db]);
-        }
-        __builtin_amdgcn_s_setprio(0);
-        __syncthreads();
-    }
-
-    // sum the key slices through LDS (slices 1..3 write, slice 0 adds)
-    float* red = reinterpret_cast<float*>(arena);
-    if (kw != 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                f32x4 x = {dq[db][4 * r4 + 0], dq[db][4 * r4 + 1], dq[db][4 * r4 + 2], dq[db][4 * r4 + 3]};
-                *reinterpret_cast<f32x4*>(&red[(((((kw - 1) * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]) = x;
-            }
-    }
-    __syncthreads();
-    if (kw != 0 || !row_ok) return;
-#pragma unroll
-    for (int sl = 0; sl < kKeySlices - 1; ++sl)
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&red[((((sl * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]);
-                dq[db][4 * r4 + 0] += x[0]; dq[db][4 * r4 + 1] += x[1];
-                dq[db][4 * r4 + 2] += x[2]; dq[db][4 * r4 + 3] += x[3];
-            }
-    const int64_t dqo = b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            st_grad4<T>(p.dq.p, dqo + db * 32 + 8 * q + 4 * g, p.grad_f32, dq[db][4 * q + 0] * p.scale,
-                        dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
-}
-
-// ---------------------------------------------------------------------------
 // Wide query-tile body of the D=64 kernel: dQ of 128 query rows
 // ---------------------------------------------------------------------------
 //
@@ -1244,18 +588,6 @@ __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* 
                         dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
 }
 
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
-    __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
-    // units: (sequence, query head), sharing K and V; items: query tiles,
-    // the longest causal range (the last tile) first.  With the plain grid
-    // each XCD took every eighth query tile of every head and so read every
-    // head's K and V; per-unit order took the S=4096, D=128 dQ pass from 325
-    // to 236 us.
-    int unit, item;
-    xcd_unit_order(gridDim.y, gridDim.x, blockIdx.y * gridDim.x + blockIdx.x, unit, item);
-    bwd_dq8_body<T, D, CAUSAL>(p, arena, gridDim.x - 1 - item, unit);
-}
 
 // dK/dV and dQ in one launch: key-tile items (the key-tile outer body, dK and
 // dV of 64 keys) and query-tile items, dQ of 64 rows or, causal with more
@@ -1333,7 +665,8 @@ static int fused8_slots() {
 
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    if constexpr (D == 64) {
+    static_assert(D == 64, "the D=64 launch");
+    {
         // The row pass, then one launch of both bodies; dQ is computed without
         // atomics, so the result is deterministic whatever the caller asked for.
         if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
@@ -1352,26 +685,6 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
                 PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL, true>), dim3(n), dim3(kThreads), 0, st, p, m);
             else
                 PROF_LAUNCH(KID_BWD_FUSED, st, (bwd_fused8_kernel<T, D, CAUSAL, false>), dim3(n), dim3(kThreads), 0, st, p, m);
-        }
-        return hipGetLastError();
-    } else {
-        const int64_t row_threads = p.rows * (D / 8);
-        const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
-        const bool have_rows = p.rows > 0;
-        if ((L.phase & BwdLaunch::kFirst) && have_rows) launch_pre<T, D>(p, L.deterministic ? 0 : 1, st);
-        const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
-        const bool have_main = main_grid.x > 0 && main_grid.y > 0;
-        if (L.deterministic) {
-            if (have_main)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
-            const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
-            if (dq_grid.x > 0 && dq_grid.y > 0)
-                PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
-        } else {
-            if (have_main)
-                PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
-            if ((L.phase & BwdLaunch::kLast) && have_rows)
-                PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
         }
         return hipGetLastError();
     }
@@ -1398,9 +711,8 @@ hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hi
 }
 
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    if (L.dtype == 0)
-        return L.D == 64 ? launch_bwd_d<F16, 64>(p, L, st) : launch_bwd_d<F16, 128>(p, L, st);
-    return L.D == 64 ? launch_bwd_d<BF16, 64>(p, L, st) : launch_bwd_d<BF16, 128>(p, L, st);
+    if (L.D != 64) return launch_bwd_d128(p, L, st);
+    return L.dtype == 0 ? launch_bwd_d<F16, 64>(p, L, st) : launch_bwd_d<BF16, 64>(p, L, st);
 }
 
 }  // namespace sdpa

@@ -1,0 +1,303 @@
+// Device helpers shared by the D=64 and D=128 backward kernels: statistics
+// row locations, the softmax gradient of one 32x32 tile, the workgroup shape
+// of the four-wavefront bodies and the 64-row query-tile dQ body.
+#pragma once
+#include "common.h"
+
+namespace sdpa {
+
+// ---------------------------------------------------------------------------
+// Row location helpers
+// ---------------------------------------------------------------------------
+
+struct RowLoc {
+    int64_t b, h, i;   // dense: batch, head, row; packed: b = 0, i = token
+};
+
+__device__ __forceinline__ RowLoc row_of(const BwdParams& p, int64_t R) {
+    RowLoc L;
+    if (p.varlen) {
+        L.b = 0; L.h = R % p.Hq; L.i = R / p.Hq;
+    } else {
+        L.i = R % p.Sq;
+        const int64_t bh = R / p.Sq;
+        L.h = bh % p.Hq; L.b = bh / p.Hq;
+    }
+    return L;
+}
+
+// log2-domain LSE of one row from the caller's statistics (a = LSE, or a = row
+// max and b = row sum): LSE*log2e, or m*log2e + log2(l); +inf for a row
+// without keys, so that its P is exactly zero.
+__device__ __forceinline__ float stats_to_lse2(int kind, float a, float b) {
+    if (kind == 0) return (a == -INFINITY) ? INFINITY : a * kLog2e;
+    return (b > 0.f) ? a * kLog2e + log2f(b) : INFINITY;
+}
+
+template <class T>
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc = 0.f) {
+    acc = T::dot2(a[0], b[0], acc);
+    acc = T::dot2(a[1], b[1], acc);
+    acc = T::dot2(a[2], b[2], acc);
+    return T::dot2(a[3], b[3], acc);
+}
+
+// dQ accumulator row of statistics row R (head-major; see BwdParams)
+__device__ __forceinline__ int64_t acc_row(const BwdParams& p, const RowLoc& L, int64_t R) {
+    return p.varlen ? L.h * p.Sq + L.i : R;
+}
+
+__device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
+    return L.b * t.sb + L.h * t.sh + L.i * t.ss;
+}
+
+// P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - Delta) for one 32x32
+// C tile held as (sa, pa), whose dP accumulator started from -Delta (pa
+// already holds dP - Delta); rows 8q + 4g + r of the tile, this lane's key.  Element (q, r) is kept when 8q + r >= t, with t the first
+// kept row offset of this lane's key (INT_MAX for a key past the end).
+template <bool MASKED>
+__device__ __forceinline__ void softmax_grad_tile_nd(f32x16& sa, f32x16& pa, const float* lse_row,
+                                                     float scale_log2, int g, int t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rg = 4 * q + r;
+            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
+            if (MASKED) pv = (8 * q + r >= t) ? pv : 0.f;
+            sa[rg] = pv;
+            pa[rg] = pv * pa[rg];
+        }
+    }
+}
+
+// Wavefronts per workgroup of the D=64 kernel and the dQ body: two row halves
+// of kKeySlices key slices.  Four wavefronts let two workgroups share a CU (two
+// wavefronts per SIMD), so one workgroup's memory waits and barriers overlap
+// the other's arithmetic.
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeySlices = kWaves / 2;
+
+// ---------------------------------------------------------------------------
+// dQ pass without atomics, four wavefronts (query-tile outer)
+// ---------------------------------------------------------------------------
+//
+// One workgroup per (sequence, query head, 64-row query tile); it walks the
+// 64-key tiles the tile can see.  Wavefront w = kw + 2*rh owns query rows
+// 32*rh .. +31 and keys 32*kw .. +31 of every key tile.  Scores are computed
+// transposed, S^T = K Q^T and dP^T = V dO^T, so that each lane holds one query
+// column: its LSE and Delta are lane-uniform, and dS^T feeds
+// dQ^T += K^T dS^T directly as the B operand.  Q and dO stay in registers for
+// the whole kernel; key tiles stream through a double-buffered LDS copy whose
+// next tile is loaded into registers while the current one is used.  Each
+// wavefront accumulates dQ^T over its key slice; the two slices' partials are
+// summed through LDS at the end and dQ is written once, scaled and rounded.
+
+template <int D>
+struct Dq8Lds {
+    static constexpr int BK = 32 * kKeySlices, KP = D + 8, DB = D / 32;
+    static constexpr int TILE_B = BK * KP * 2;
+    static constexpr int LOOP_B = 4 * TILE_B;
+    static constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;
+    static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
+};
+
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    constexpr int BQ = 64;           // query rows per workgroup
+    constexpr int BK = 32 * kKeySlices;   // keys per step
+    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
+    constexpr int DB = D / 32;       // 32-row blocks of dQ^T
+    constexpr int KP = D + 8;        // row stride of Ks, Vs  [key][d]
+    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per key tile
+    constexpr int TILE_B = BK * KP * 2;
+    constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
+    constexpr int LOOP_B = 4 * TILE_B;
+    constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;   // key slices 1.. of both row halves
+    static_assert(Dq8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
+    uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
+    uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int kw = w % kKeySlices, rh = w / kKeySlices;
+    const int g = lane >> 5, c = lane & 31;
+    const int b = by / p.Hq, h = by % p.Hq;
+    const int hk = h / (p.Hq / p.Hkv);
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
+    const int i0 = bx * BQ;
+    if (i0 >= lq) return;
+
+    const uint16_t* qbase = p.q.p + b * p.q.sb + h * p.q.sh + (int64_t)q0 * p.q.ss;
+    const uint16_t* dobase = p.dout.p + b * p.dout.sb + h * p.dout.sh + (int64_t)q0 * p.dout.ss;
+    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
+    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
+
+    const int kend = CAUSAL ? min(lk, i0 + BQ) : lk;
+    const int n_steps = (kend + BK - 1) / BK;
+
+    // byte offsets of this thread's chunks within a key tile
+    const uint32_t kss = 2u * (uint32_t)p.k.ss, vss = 2u * (uint32_t)p.v.ss;
+    uint32_t koff[CH], voff[CH];
+    int crow[CH], ccol[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + kThreads * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        ccol[x] = cc;
+        koff[x] = r * kss + 2 * cc;
+        voff[x] = r * vss + 2 * cc;
+    }
+    // Unconditional loads: keys past the end of the sequence re-read its last
+    // key and are masked out (P = 0), so nothing is waited for before the tile
+    // is stored after the step's products.
+    u32x4 pk[CH], pv[CH];
+    const uint16_t* kb = kbase;          // key tile being loaded, advanced per step
+    const uint16_t* vb = vbase;
+    const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
+    auto load_tile = [&](int st) {
+        const int j0 = st * BK;
+        uint32_t ok_[CH], ov_[CH];
+        if (j0 + BK <= lk) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
+        } else {
+            const int last = lk - 1 - j0;
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                const uint32_t r = min(crow[x], last);
+                ok_[x] = r * kss + 2 * ccol[x];
+                ov_[x] = r * vss + 2 * ccol[x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            pk[x] = ld16_at(kb, ok_[x]);
+            pv[x] = ld16_at(vb, ov_[x]);
+        }
+        kb += k_step;
+        vb += v_step;
+    };
+    auto store_tile = [&](int buf) {
+        uint16_t* Kd = Ks0 + buf * (BK * KP);
+        uint16_t* Vd = Vs0 + buf * (BK * KP);
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
+            st16(&Vd[crow[x] * KP + ccol[x]], pv[x]);
+        }
+    };
+
+    // Prologue: the first key tile and this lane's query row are requested
+    // before anything waits for memory.
+    if (n_steps > 0) load_tile(0);
+    const int my_i = i0 + 32 * rh + c;
+    const bool row_ok = my_i < lq;
+    // a row past the end of the sequence re-reads its last row; its LSE is
+    // +inf (P = 0) and its dQ is not stored
+    const int my_ic = min(my_i, lq - 1);
+    u32x4 qreg[KS], doreg[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
+        doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
+    }
+    // this row's log2-domain LSE and Delta from the row pass
+    const int64_t ws = p.varlen ? (int64_t)(q0 + my_ic) * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq + my_ic;
+    const float l2 = row_ok ? p.lse2[ws] : INFINITY;
+    const float dl = p.delta[ws];
+
+    f32x16 dq[DB], ndl16;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
+
+    if (n_steps > 0) store_tile(0);
+    wait_all_memory();
+    __syncthreads();
+
+    // last key this lane's row keeps, relative to the 8q+4g part of a tile row
+    const int t_row = min(lk - 1, CAUSAL ? my_i : INT_MAX) - 32 * kw - 4 * g;
+
+    for (int st = 0; st < n_steps; ++st) {
+        const int buf = st & 1;
+        const int j0 = st * BK;
+        const bool has_next = st + 1 < n_steps;
+        if (has_next) load_tile(st + 1);
+        const uint16_t* Kb = Ks0 + buf * (BK * KP);
+        const uint16_t* Vb = Vs0 + buf * (BK * KP);
+
+        f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
+            dp = T::mma(ld16(&Vb[(32 * kw + c) * KP + 16 * ks + 8 * g]), doreg[ks], dp);
+        }
+        // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
+        const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);
+        if (masked) {
+            const int t = t_row - j0;
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                pvv = (8 * (rg >> 2) + (rg & 3) <= t) ? pvv : 0.f;
+                dp[rg] = pvv * dp[rg];
+            }
+        } else {
+#pragma unroll
+            for (int rg = 0; rg < 16; ++rg) {
+                const float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                dp[rg] = pvv * dp[rg];
+            }
+        }
+        if (has_next) store_tile(buf ^ 1);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const u32x4 bS = acc_to_operand<T>(dp, hh);
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane), bS, dq[db]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __syncthreads();
+    }
+
+    // sum the key slices through LDS (slices 1..3 write, slice 0 adds)
+    float* red = reinterpret_cast<float*>(arena);
+    if (kw != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                f32x4 x = {dq[db][4 * r4 + 0], dq[db][4 * r4 + 1], dq[db][4 * r4 + 2], dq[db][4 * r4 + 3]};
+                *reinterpret_cast<f32x4*>(&red[(((((kw - 1) * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]) = x;
+            }
+    }
+    __syncthreads();
+    if (kw != 0 || !row_ok) return;
+#pragma unroll
+    for (int sl = 0; sl < kKeySlices - 1; ++sl)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&red[((((sl * 2 + rh) * DB + db) * 4 + r4) * 64 + lane) * 4]);
+                dq[db][4 * r4 + 0] += x[0]; dq[db][4 * r4 + 1] += x[1];
+                dq[db][4 * r4 + 2] += x[2]; dq[db][4 * r4 + 3] += x[3];
+            }
+    const int64_t dqo = b * p.dq.sb + h * p.dq.sh + (int64_t)(q0 + my_i) * p.dq.ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            st_grad4<T>(p.dq.p, dqo + db * 32 + 8 * q + 4 * g, p.grad_f32, dq[db][4 * q + 0] * p.scale,
+                        dq[db][4 * q + 1] * p.scale, dq[db][4 * q + 2] * p.scale, dq[db][4 * q + 3] * p.scale);
+}
+
+}  // namespace sdpa

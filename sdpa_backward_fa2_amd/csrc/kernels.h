@@ -31,6 +31,8 @@ struct BwdLaunch {
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
+// The D=128 backward (bwd128.hip); launch_bwd hands D=128 calls to it.
+hipError_t launch_bwd_d128(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // Delta and log2-LSE per statistics row (and the dQ accumulator clear).
 hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st);
 // Sets the text sdpa_last_error() returns on this thread.
