@@ -12,8 +12,12 @@ Prints ONE JSON line:
   value       counted TFLOP/s of the whole step: 5 matmuls of 2*Sq*Sk*D per
               head, halved for causal, divided by the measured step time;
   roofline    the main kernel's counted FLOP per launch over its average
-              duration (HIP events around each launch on its stream), against
-              the MI355X dense fp16/bf16 MFMA peak of 2516.6 TFLOP/s;
+              duration, against the MI355X dense fp16/bf16 MFMA peak of
+              2516.6 TFLOP/s.  The duration comes from HIP events that the
+              runtime fills with the kernel's own dispatch-packet begin and end
+              timestamps (hipExtLaunchKernelGGL on the launch stream), over the
+              same K steps run again; a kernel time longer than the whole step
+              cannot be right and is reported as null;
   cpu_baseline the fp64 CPU oracle on the same inputs, timed on this host.
 
     python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--dq-mode 0|1|2]
@@ -148,10 +152,18 @@ def cpu_baseline(wl, host) -> dict:
     import oracle
     import synth
     try:
+        host_cores = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        host_cores = os.cpu_count() or 1
+    blas, threads = "unknown", host_cores
+    try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if pools:
+            blas = ",".join(sorted({str(i.get("internal_api")) for i in pools}))
+            threads = max(int(i.get("num_threads", 1)) for i in pools)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
     x = {k: synth.decode(v, wl.dtype) if wl.kind != "dense" else v
          for k, v in host.items() if k in ("q", "k", "v", "do")}
     if wl.kind == "dense":
@@ -200,6 +212,7 @@ def cpu_baseline(wl, host) -> dict:
     t = statistics.median(times)
     flops = wl.counted_flops() * share(units[:n])
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cores": int(host_cores), "blas": blas, "blas_threads": int(threads),
             "sample": f"{n} of {len(units)} {what} of the same problem, fp64 numpy oracle, "
                       f"median of {reps} run(s), {t:.2f} s per run"}
 
@@ -270,7 +283,8 @@ def main():
     flops = wl.counted_flops()
     value = flops / (ms * 1e-3) / 1e12
 
-    # per-kernel durations: the same K steps again with HIP events around every launch
+    # per-kernel durations: the same K steps again, each launch carrying an event
+    # pair filled with its dispatch packet's begin and end timestamps
     with sb.KernelTimer() as kt:
         for _ in range(args.steps):
             call()
@@ -282,11 +296,13 @@ def main():
     share = KERNEL_FLOP_SHARE.get((main_name, not atomic), 0.0)
     main_us = kernels[main_name]["avg_us"]
     per_launch = flops * share * args.steps / kernels[main_name]["launches"]
-    achieved = per_launch / (main_us * 1e-6) / 1e12
+    # a kernel of the step cannot take longer than the step
+    sane = main_us * 1e-3 <= ms * 1.001
+    achieved = per_launch / (main_us * 1e-6) / 1e12 if sane else None
     workload_name = f"config{args.config}" + (f"_d{wl.D}_dv{wl.Dv}" if head_dims else "")
     roofline = {"bound": "mfma", "kernel": main_name, "achieved": achieved,
                 "peak": PEAK_MFMA_16BIT_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_16BIT_TFLOPS,
+                "frac": achieved / PEAK_MFMA_16BIT_TFLOPS if sane else None,
                 "traffic": traffic_for(main_name, workload_name)}
     if wl.kind == "dense":
         cfg = {"workload": wl.name, "B": wl.B, "H": wl.Hq, "S": wl.S, "D": wl.D, "causal": wl.causal,

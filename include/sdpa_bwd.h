@@ -165,8 +165,7 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  *     1: guaranteed bitwise reproducible: the atomic-free query-outer pass;
  *     2: fp32 atomic accumulation inside the key-outer kernel and a final
  *        conversion (FlashAttention-2's method; run-to-run rounding
- *        differences possible); D=128 only, D=64 has no atomic kernel and
- *        runs mode 1.
+ *        differences possible), at D=64 and D=128.
  *     Any other value: SDPA_ERR_INVALID.  The workspace size depends on it.
  *   grad_dtype: element type of dq, dk and dv: `dtype`, or SDPA_F32 for fp32
  *     gradients (same layout rules, strides in fp32 elements); anything else
@@ -286,11 +285,14 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
 /*
  * Kernel timing for measurement tools (not needed for computing anything).
  * Between sdpa_profile_begin() and sdpa_profile_end() every kernel launch of
- * this library is bracketed by a pair of HIP events recorded on its launch
- * stream.  sdpa_profile_end() waits for the last recorded event, writes for
+ * this library carries a pair of HIP events that the runtime fills with the
+ * kernel's own begin and end timestamps (hipExtLaunchKernelGGL), so the
+ * elapsed time is the kernel's execution alone, without launch gaps.
+ * sdpa_profile_end() waits for the last event, writes for
  * each kernel id k < n_kernels the summed elapsed milliseconds total_ms[k]
  * and the number of launches launches[k], and disables timing.  Kernel ids:
- * 0 forward, 1 backward preprocess, 2 backward main (D=128), 3 dQ convert,
+ * 0 forward, 1 backward preprocess, 2 backward key-tile kernel (D=128; D=64
+ * in dQ mode 2), 3 dQ convert,
  * 4 deterministic dQ (D=128), 5 NSA index build (three launches), 6 NSA dK/dV,
  * 7 NSA dQ, 8 fused dK/dV and dQ (D=64), 9 NSA dK/dV partial reduction;
  * sdpa_kernel_name(id) gives the kernel's symbol name stem.  Not thread-safe

@@ -97,10 +97,9 @@ Carve carve_bwd(int64_t rows, int64_t D, bool deterministic) {
 
 // dQ mode of the dense and packed entry points: 0 = the library's fastest
 // method, 1 = bitwise reproducible, 2 = fp32 atomic accumulation (FA2's
-// method; D=128 only, other head sizes have no atomic kernel and run mode 1).
-// Every method the library picks today is the atomic-free one.
+// method).  The fastest method is the atomic-free one at every head size.
 bool dq_mode_ok(int mode) { return mode >= 0 && mode <= 2; }
-bool dq_atomic(int mode, int64_t D) { return mode == 2 && D == 128; }
+bool dq_atomic(int mode, int64_t D) { (void)D; return mode == 2; }
 
 int check_stats(const sdpa_stats* s) {
     if (!s->lse_or_max) return SDPA_ERR_NULLPTR;
@@ -411,7 +410,10 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;
     if (int s = check_stats_stride(stats)) return s;
-    if (P.max_lk / 128 + 1 > kMaxGridY || Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
+    // the D=128 dQ launch puts (sequence, query head) of a chunk of up to
+    // kMaxSeqArgs sequences in grid y, the D=128 key-tile launch the key tiles
+    if (P.max_lk / 128 + 1 > kMaxGridY || std::min<int64_t>(batch, sdpa::kMaxSeqArgs) * Hq > kMaxGridY)
+        return SDPA_ERR_UNSUPPORTED;
     const bool det = !dq_atomic(deterministic, D);
     const int64_t rows = P.Tq * Hq;
     const Carve cv = carve_bwd(rows, D, det);

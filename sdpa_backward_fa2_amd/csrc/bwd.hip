@@ -666,9 +666,10 @@ static int fused8_slots() {
 template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     static_assert(D == 64, "the D=64 launch");
+    if (!L.deterministic) return launch_bwd_d64_atomic(p, L, st);   // dQ mode 2: fp32 atomics
     {
         // The row pass, then one launch of both bodies; dQ is computed without
-        // atomics, so the result is deterministic whatever the caller asked for.
+        // atomics, so the result is deterministic (dQ modes 0 and 1).
         if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
         const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
         static_assert(32 * kKeySlices == 64, "key tile of the fused kernel");

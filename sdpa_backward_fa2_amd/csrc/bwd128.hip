@@ -4,7 +4,8 @@
 //
 // Kernels (all on the caller's stream; the row pass is bwd.hip's):
 //   bwd_main_kernel    one four-wavefront workgroup per (sequence, KV head,
-//                      128-key tile); dK and dV accumulate in registers
+//                      128-key tile); D=128 in every dQ mode, D=64 in the
+//                      atomic mode; dK and dV accumulate in registers
 //                      across every query tile of every query head of the
 //                      group; per 64-row query tile S, dP, dV, dK and, in
 //                      atomic mode, dQ += dS K through fp32 atomics.     [MFMA]
@@ -392,29 +393,38 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq8_kernel(BwdParams p) {
 // Launch
 // ---------------------------------------------------------------------------
 
+// FA2's dQ method: the key-tile kernel adds dS K to a zeroed fp32
+// accumulator with atomics, then a row pass scales and rounds it into dQ.
 template <class T, int D, bool CAUSAL>
-static hipError_t launch_bwd128_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
+static hipError_t launch_bwd_atomic_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     const int64_t row_threads = p.rows * (D / 8);
     const dim3 row_grid((unsigned)((row_threads + 255) / 256));   // dQ conversion: 8 elements per thread
     const bool have_rows = p.rows > 0;
     if ((L.phase & BwdLaunch::kFirst) && have_rows) {
-        const hipError_t e = launch_bwd_pre(p, L.dtype, D, !L.deterministic, st);
+        const hipError_t e = launch_bwd_pre(p, L.dtype, D, true, st);
         if (e != hipSuccess) return e;
     }
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
-    const bool have_main = main_grid.x > 0 && main_grid.y > 0;
-    if (L.deterministic) {
-        if (have_main)
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
-        const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
-        if (dq_grid.x > 0 && dq_grid.y > 0)
-            PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
-    } else {
-        if (have_main)
-            PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
-        if ((L.phase & BwdLaunch::kLast) && have_rows)
-            PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
+    if (main_grid.x > 0 && main_grid.y > 0)
+        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
+    if ((L.phase & BwdLaunch::kLast) && have_rows)
+        PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+template <class T, int D, bool CAUSAL>
+static hipError_t launch_bwd128_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
+    if (!L.deterministic) return launch_bwd_atomic_t<T, D, CAUSAL>(p, L, st);
+    if ((L.phase & BwdLaunch::kFirst) && p.rows > 0) {
+        const hipError_t e = launch_bwd_pre(p, L.dtype, D, false, st);
+        if (e != hipSuccess) return e;
     }
+    const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
+    if (main_grid.x > 0 && main_grid.y > 0)
+        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
+    const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
+    if (dq_grid.x > 0 && dq_grid.y > 0)
+        PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
@@ -422,6 +432,12 @@ hipError_t launch_bwd_d128(const BwdParams& p, const BwdLaunch& L, hipStream_t s
     if (L.dtype == 0)
         return L.causal ? launch_bwd128_t<F16, 128, true>(p, L, st) : launch_bwd128_t<F16, 128, false>(p, L, st);
     return L.causal ? launch_bwd128_t<BF16, 128, true>(p, L, st) : launch_bwd128_t<BF16, 128, false>(p, L, st);
+}
+
+hipError_t launch_bwd_d64_atomic(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
+    if (L.dtype == 0)
+        return L.causal ? launch_bwd_atomic_t<F16, 64, true>(p, L, st) : launch_bwd_atomic_t<F16, 64, false>(p, L, st);
+    return L.causal ? launch_bwd_atomic_t<BF16, 64, true>(p, L, st) : launch_bwd_atomic_t<BF16, 64, false>(p, L, st);
 }
 
 }  // namespace sdpa

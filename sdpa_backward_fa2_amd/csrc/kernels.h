@@ -33,6 +33,9 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool cau
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // The D=128 backward (bwd128.hip); launch_bwd hands D=128 calls to it.
 hipError_t launch_bwd_d128(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
+// The D=64 backward with FA2's fp32-atomic dQ accumulation (bwd128.hip's
+// key-tile kernel at D=64 and the dQ conversion).
+hipError_t launch_bwd_d64_atomic(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // Delta and log2-LSE per statistics row (and the dQ accumulator clear).
 hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hipStream_t st);
 // Sets the text sdpa_last_error() returns on this thread.

@@ -1092,8 +1092,11 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
     PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, DK, DV>),
                 dim3(p.N2 * p.NB, p.halves, reduce_key_groups<DK, DV>()), dim3(256), 0, st, p);
-    PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0, st,
-                p);
+    // with no query token (every query length 0) dK and dV are the reduction's
+    // zeros and there is no dQ row to write
+    if (p.Tq > 0)
+        PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0,
+                    st, p);
     return hipGetLastError();
 }
 

@@ -1,4 +1,5 @@
-// Per-kernel HIP-event timing (sdpa_profile_begin / sdpa_profile_end).
+// Per-kernel timing (sdpa_profile_begin / sdpa_profile_end): event pairs that
+// the runtime fills with each kernel's own dispatch timestamps.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -33,26 +34,22 @@ ProfState& state() {
 
 bool prof_enabled() { return state().on.load(std::memory_order_relaxed); }
 
-void prof_mark(int kid, hipStream_t st, bool start) {
+void prof_events(int kid, hipEvent_t* start, hipEvent_t* stop) {
     ProfState& s = state();
     std::lock_guard<std::mutex> lk(s.mu);
-    if (start) {
-        if (s.used == s.pool.size()) {
-            Mark m;
-            if (hipEventCreate(&m.start) != hipSuccess || hipEventCreate(&m.stop) != hipSuccess) {
-                s.error = true;
-                return;
-            }
-            s.pool.push_back(m);
+    *start = *stop = nullptr;
+    if (s.used == s.pool.size()) {
+        Mark m;
+        if (hipEventCreate(&m.start) != hipSuccess || hipEventCreate(&m.stop) != hipSuccess) {
+            s.error = true;
+            return;
         }
-        Mark& m = s.pool[s.used];
-        m.kid = kid;
-        if (hipEventRecord(m.start, st) != hipSuccess) s.error = true;
-    } else {
-        if (s.used >= s.pool.size()) return;
-        if (hipEventRecord(s.pool[s.used].stop, st) != hipSuccess) s.error = true;
-        ++s.used;
+        s.pool.push_back(m);
     }
+    Mark& m = s.pool[s.used++];
+    m.kid = kid;
+    *start = m.start;
+    *stop = m.stop;
 }
 
 }  // namespace sdpa

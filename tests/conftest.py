@@ -27,3 +27,18 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """After a GPU run, write every parity comparison's error and bound to
+    gpurun_out/parity_margins.txt (worst ratio first), when that folder
+    exists: the margin under the bound, not only pass or fail."""
+    gu = sys.modules.get("gpu_util")
+    out_dir = os.path.join(ROOT, "gpurun_out")
+    if gu is None or not getattr(gu, "MARGINS", None) or not os.path.isdir(out_dir):
+        return
+    rows = sorted(gu.MARGINS, key=lambda r: -r[3] / r[4])
+    with open(os.path.join(out_dir, "parity_margins.txt"), "w") as fh:
+        fh.write("# err/bound  err  bound  dtype  what  test\n")
+        for test, what, dtype, e, tol in rows:
+            fh.write(f"{e / tol:.3f} {e:.3e} {tol:.0e} {dtype} {what} {test}\n")

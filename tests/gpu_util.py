@@ -1,5 +1,7 @@
 """Helpers shared by the GPU parity tests: moving synth's bit patterns onto the
 device and measuring errors against the oracle.  No attention arithmetic."""
+import os
+
 import numpy as np
 import torch
 
@@ -40,8 +42,16 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     return float(np.max(np.abs(got - ref))) / (denom if denom > 0 else 1.0)
 
 
+# (test id, what, dtype, error, bound) of every assert_rel in this session;
+# conftest writes them out at the end of a GPU run so the margin under each
+# bound is on record, not only pass or fail
+MARGINS = []
+
+
 def assert_rel(got, ref, dtype: str, what: str):
     e = rel_err(got, ref)
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    MARGINS.append((test, what, dtype, e, REL_TOL[dtype]))
     assert e <= REL_TOL[dtype], f"{what}: max|err|/max|ref| = {e:.3e} > {REL_TOL[dtype]:.0e}"
     return e
 

@@ -94,12 +94,11 @@ def test_workspace_size_query():
         n = ctypes.c_size_t(0)
         assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, D, mode, ctypes.byref(n)) == OK
         return n.value
-    # atomic-free modes: LSE and Delta rows; the atomic mode (D=128 only) adds
-    # the fp32 dQ accumulator
+    # atomic-free modes: LSE and Delta rows; the atomic mode adds the fp32 dQ
+    # accumulator
     for D in (64, 128):
         assert size(D, 0) == size(D, 1) >= rows * 8
-    assert size(64, 2) == size(64, 1)
-    assert size(128, 2) >= size(128, 1) + rows * 128 * 4
+        assert size(D, 2) >= size(D, 1) + rows * D * 4
     m = ctypes.c_size_t(0)
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 3, ctypes.byref(m)) == INVALID
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 0, ctypes.byref(m)) == UNSUPPORTED

@@ -194,7 +194,7 @@ def test_oracle_stats_max_sum_form():
 @pytest.mark.parametrize("cid", [2, 3])
 def test_dq_modes(cid):
     """Mode 1 is bitwise stable; mode 0 (fastest) is today the same atomic-free
-    pass, so bitwise equal to it; mode 2 (fp32 atomics, D=128) agrees within
+    pass, so bitwise equal to it; mode 2 (fp32 atomics, D=64 and D=128) agrees within
     the tolerance."""
     wl, (q, k, v, do, o, lse), _ = _gpu_stats_config(cid)
     a = _run_bwd(q, k, v, o, do, lse, wl.scale, wl.causal, 1)
