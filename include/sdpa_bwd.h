@@ -183,6 +183,30 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * sdpa_bwd_noalloc: sdpa_bwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, results and error codes
+ * are those of sdpa_bwd, and it runs the same kernels.  The per-row scratch
+ * (log2-LSE and Delta, plus the fp32 dQ accumulator in dQ mode 2) lives in a
+ * fixed 16 MiB array inside the library, one per GPU, kept until the process
+ * ends; a problem whose sdpa_bwd_workspace_size exceeds 16 MiB
+ * (16777216 bytes) returns SDPA_ERR_WORKSPACE, with the needed size in
+ * sdpa_last_error(), before any HIP call.  Modes 0 and 1 need 8 bytes per
+ * query row and head (about 2 million rows); mode 2 adds 4*D bytes per row.
+ * The call allocates nothing (no hipMalloc, no library allocation); the first
+ * call on a GPU looks up that GPU's array address once.  Every call on one
+ * GPU shares that GPU's array and leaves its contents behind: the kernels
+ * rewrite (and in mode 2 clear) what they read, but calls that overlap in
+ * time on one GPU (different streams or threads) race on it and must be
+ * serialised by the caller.
+ */
+int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                     double scale, int causal, int deterministic, int grad_dtype,
+                     const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
+                     const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv, void* stream);
+
+/*
  * sdpa_bwd_varlen_workspace_size / sdpa_bwd_varlen: packed variable-length
  * backward (TND).  `batch` sequences; cu_seqlens_q_host / cu_seqlens_kv_host
  * are HOST arrays of `batch` int64 inclusive end offsets with no leading zero

@@ -18,7 +18,7 @@ import re
 import torch
 
 __all__ = [
-    "SdpaError", "load", "library_path", "fwd_stats", "bwd", "bwd_varlen", "bwd_selected",
+    "SdpaError", "load", "library_path", "fwd_stats", "bwd", "bwd_noalloc", "bwd_varlen", "bwd_selected",
     "selected_build_index", "bwd_workspace_size", "bwd_varlen_workspace_size",
     "bwd_selected_workspace_size", "STATUS",
 ]
@@ -79,6 +79,8 @@ _SIGS = {
                                         ctypes.POINTER(c_size)]),
     "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                          P4, P4, P4, P4, P4, PS, P4, P4, P4, c_vp, c_size, c_vp]),
+    "sdpa_bwd_noalloc": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
+                                 P4, P4, P4, P4, P4, PS, P4, P4, P4, c_vp]),
     "sdpa_bwd_varlen_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_int,
                                                ctypes.POINTER(c_size)]),
     "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
@@ -271,7 +273,7 @@ def fwd_stats_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, o=None, l
 # dQ modes (the `deterministic` argument of the backward entry points)
 DQ_FASTEST = 0          # the library's fastest method (atomic-free today)
 DQ_DETERMINISTIC = 1    # bitwise reproducible
-DQ_ATOMIC = 2           # fp32 atomic accumulation (D=128; D=64 runs mode 1)
+DQ_ATOMIC = 2           # fp32 atomic accumulation (FA2's method)
 
 
 def bwd_workspace_size(dtype: int, B, Hq, Hkv, Sq, Sk, D, deterministic: int) -> int:
@@ -337,6 +339,24 @@ def bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int 
                              workspace, grad_dtype)
     call()
     return outs
+
+
+def bwd_noalloc(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
+                dq=None, dk=None, dv=None, grad_dtype=None):
+    """The dense backward through sdpa_bwd_noalloc: no workspace, the library's
+    fixed per-GPU scratch instead (16 MiB; larger problems raise
+    SDPA_ERR_WORKSPACE).  Outputs as bwd; given dq, dk, dv are written in place."""
+    lib = load()
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
+    sa = _stats_arg(stats, packed=False)
+    structs = [_t4(x) for x in (q, k, v, o, dout, dq, dk, dv)]
+    _check(lib.sdpa_bwd_noalloc(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal),
+                                int(deterministic), gdt, *[ctypes.byref(x) for x in structs[:5]],
+                                ctypes.byref(sa), *[ctypes.byref(x) for x in structs[5:]],
+                                _stream_ptr(q.device)), "sdpa_bwd_noalloc")
+    return dq, dk, dv
 
 
 # ----------------------------------------------------------------------------

@@ -9,12 +9,17 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/sdpa_bwd.h"
 #include "common.h"
 #include "kernels.h"
+
+// Scratch of sdpa_bwd_noalloc (16 MiB per GPU; see scratch_address below).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -145,6 +150,35 @@ int read_packed(int64_t batch, const int64_t* cuq, const int64_t* cuk, Packed& P
     }
     P.Tq = pq; P.Tk = pk;
     if (P.Tq >= ((int64_t)1 << 31) || P.Tk >= ((int64_t)1 << 31)) return SDPA_ERR_UNSUPPORTED;
+    return SDPA_OK;
+}
+
+// Scratch of sdpa_bwd_noalloc: the per-row log2-LSE and Delta (and, in dQ
+// mode 2, the fp32 dQ accumulator) live in this fixed array instead of a
+// caller workspace.  Each GPU the library runs on holds its own copy, at its
+// own address, until the process ends.  In host code the name `scratch` only
+// stands in for the symbol; kernels get the device address that
+// hipGetSymbolAddress returns, fetched once per device.
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array.
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxScratchDevices) return set_err(SDPA_ERR_UNSUPPORTED, "device ordinal above 63");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return set_err(SDPA_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return SDPA_OK;
 }
 
@@ -316,17 +350,20 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
     return SDPA_OK;
 }
 
-int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
-             double scale, int causal, int deterministic, int grad_dtype,
-             const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
-             const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
-             const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
-             void* workspace, size_t workspace_bytes, void* stream) {
+// The dense backward behind both entry points: `workspace` is the caller's
+// buffer (sdpa_bwd), or null for the library's own scratch array
+// (sdpa_bwd_noalloc), which is fetched only once the arguments are valid.
+static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                     double scale, int causal, int deterministic, int grad_dtype,
+                     const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
+                     const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
+                     void* workspace, size_t workspace_bytes, bool scratch, void* stream) {
     if (!q || !k || !v || !o || !dout || !stats || !dq || !dk || !dv) return SDPA_ERR_NULLPTR;
     for (const sdpa_tensor4* t : {q, k, v, o, dout, dq, dk, dv})
         if (!t->data) return SDPA_ERR_NULLPTR;
     if (int s = check_stats(stats)) return s;
-    if (!workspace) return SDPA_ERR_NULLPTR;
+    if (!scratch && !workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
@@ -343,9 +380,18 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     const bool det = !dq_atomic(deterministic, D);
     const int64_t rows = B * Hq * Sq;
     const Carve cv = carve_bwd(rows, D, det);
-    if (workspace_bytes < cv.total) return SDPA_ERR_WORKSPACE;
+    if (scratch && cv.total > kScratchBytes) {
+        g_last_error = "sdpa_bwd_noalloc: the problem needs " + std::to_string(cv.total) +
+                       " bytes of scratch, above the library's fixed " + std::to_string(kScratchBytes) +
+                       " bytes; call sdpa_bwd with a workspace";
+        return SDPA_ERR_WORKSPACE;
+    }
+    if (!scratch && workspace_bytes < cv.total) return SDPA_ERR_WORKSPACE;
     if (int s = check_device()) return s;
     if (B == 0) return SDPA_OK;
+    if (scratch) {
+        if (int s = scratch_address(&workspace)) return s;
+    }
 
     char* ws = static_cast<char*>(workspace);
     sdpa::BwdParams p{};
@@ -361,10 +407,29 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
     if (log_enabled())
-        std::fprintf(stderr, "[sdpa_bwd] bwd dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld causal=%d det=%d main_grid=(%lld,%lld)\n",
-                     dtype, (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq, (long long)Sk,
-                     (long long)D, causal, (int)det, (long long)(B * Hkv), (long long)((Sk + 127) / 128));
+        std::fprintf(stderr, "[sdpa_bwd] bwd%s dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld causal=%d det=%d main_grid=(%lld,%lld)\n",
+                     scratch ? "_noalloc" : "", dtype, (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq,
+                     (long long)Sk, (long long)D, causal, (int)det, (long long)(B * Hkv), (long long)((Sk + 127) / 128));
     return run_bwd(dtype, p, D, causal != 0, det, nullptr, B, Sq, Sk, static_cast<hipStream_t>(stream));
+}
+
+int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+             double scale, int causal, int deterministic, int grad_dtype,
+             const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+             const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
+             const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
+                     stats, dq, dk, dv, workspace, workspace_bytes, false, stream);
+}
+
+int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                     double scale, int causal, int deterministic, int grad_dtype,
+                     const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
+                     const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
+                     const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv, void* stream) {
+    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
+                     stats, dq, dk, dv, nullptr, 0, true, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -105,6 +105,37 @@ def test_workspace_size_query():
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, None) == NULLPTR
 
 
+def noalloc_call(**kw):
+    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, scale=0.125, causal=0, det=0,
+             stats=sb.Stats(0, FAKE, None, 256, 128, 1))
+    a.update(kw)
+    ts = [t4() for _ in range(8)]
+    return lib().sdpa_bwd_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"],
+                                  a["causal"], a["det"], a["dtype"], *[ctypes.byref(t) for t in ts[:5]],
+                                  ctypes.byref(a["stats"]), *[ctypes.byref(t) for t in ts[5:]], None)
+
+
+def test_noalloc_validation():
+    """sdpa_bwd_noalloc validates like sdpa_bwd and refuses, before any HIP
+    call, a problem whose scratch exceeds its fixed 16 MiB."""
+    assert noalloc_call(stats=sb.Stats(1, FAKE, None, 256, 128, 1)) == NULLPTR
+    assert noalloc_call(dtype=7) == INVALID
+    assert noalloc_call(D=96) == UNSUPPORTED
+    rows_limit = (16 << 20) // 8
+    assert noalloc_call(Hq=64, Hkv=64, Sq=rows_limit // 64 + 64) == WORKSPACE    # 8 B per row, modes 0/1
+    assert b"16777216" in lib().sdpa_last_error()
+    assert noalloc_call(Hq=16, Hkv=16, Sq=4096, det=2) == WORKSPACE                # + 4*D B per row, mode 2
+    n = ctypes.c_size_t(0)
+    assert lib().sdpa_bwd_workspace_size(0, 1, 16, 16, 4096, 4096, 64, 2, ctypes.byref(n)) == OK
+    assert n.value > (16 << 20)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_noalloc_valid_without_device():
+    assert noalloc_call() == HIP
+    assert noalloc_call(Hq=12, Hkv=12, Sq=1024, Sk=1024, det=2) == HIP   # 12.6 MB of scratch fits
+
+
 def t3(ptr=FAKE, strides=(32 * 128, 128, 1)):
     return sb.Tensor3(ptr, *strides)
 
@@ -135,6 +166,8 @@ def test_varlen_validation():
     assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 2, ctypes.byref(n)) == OK
     assert n.value >= 300 * 32 * (8 + 128 * 4)         # plus the fp32 dQ accumulator
     assert varlen_call([100, 300], [100, 300], det=5) == INVALID
+    # (sequence, query head) of a chunk of sequences must fit grid y (65535)
+    assert varlen_call([100, 300], [100, 300], Hq=40000, Hkv=40000) == UNSUPPORTED
     big = sb.Tensor3(FAKE, 1 << 23, 128, 1)                          # token stride 2^23
     cu = (ctypes.c_int64 * 2)(100, 300)
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
