@@ -244,34 +244,46 @@ def selected_block_lists(topk, cu_q, cu_kv, block_size: int):
     return offsets, entries
 
 
-def _selected_token_rows(q, k, v, topk, cu_q, cu_kv, block_size, scale, sparse_mode):
+def _selected_token_rows(q, k, v, topk, cu_q, cu_kv, block_size, scale, sparse_mode, atten_mask=None):
     """Yields, per token t and KV head h2: the token, its query-head range, the
-    absolute gathered positions and the admissible set over them."""
+    absolute gathered positions and the admissible set over them.
+
+    atten_mask: optional 2-D boolean array indexed by (sequence-local query
+    position, sequence-local key position), True where the score is masked
+    out, the same for every sequence and head (the Ascend page's
+    attenMaskOptional, "Parameters" table: BOOL/UINT8, two dimensions; the page
+    does not say more, so this reads it as the usual keep-out mask over the
+    score matrix, combined with sparse_mode's causal rule)."""
     Tq, Hq, _ = q.shape
     _, Hkv, _ = k.shape
     G = Hq // Hkv
     pos_local = selected_key_positions(topk, block_size)
+    mask = None if atten_mask is None else np.asarray(atten_mask).astype(bool)
     for s0, s1, k0 in zip(_starts(cu_q), cu_q, _starts(cu_kv)):
         for t in range(int(s0), int(s1)):
             t_local = t - int(s0)
             for h2 in range(Hkv):
                 p = pos_local[t, h2]
                 allowed = (p <= t_local) if sparse_mode == 2 else np.ones(p.shape, bool)
+                if mask is not None:
+                    allowed = allowed & ~mask[t_local, p]
                 yield t, slice(h2 * G, (h2 + 1) * G), h2, int(k0) + p, allowed
 
 
 def selected_forward(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float,
-                     sparse_mode: int) -> dict:
+                     sparse_mode: int, atten_mask=None) -> dict:
     """Attention of every query token over its gathered keys.  sparse_mode 0: no
     mask; 2: causal, key position <= query position within the sequence (the
     page allows "0 or 2" without defining them; this is the plain reading).
+    atten_mask: see _selected_token_rows.  A row left with no admissible key
+    has P = 0, O = 0, m = -inf and l = 0.
     Returns O (T, Hq, Dv), lse, m, l (T, Hq)."""
     Tq, Hq, _ = q.shape
     Dv = v.shape[2]
     O = np.zeros((Tq, Hq, Dv))
     lse, m, l = (np.zeros((Tq, Hq)) for _ in range(3))
     for t, hs, h2, pos, allowed in _selected_token_rows(q, k, v, topk, cu_q, cu_kv,
-                                                        block_size, scale, sparse_mode):
+                                                        block_size, scale, sparse_mode, atten_mask):
         f = head_forward(q[t, hs], k[pos, h2], v[pos, h2], scale,
                          np.broadcast_to(allowed, (hs.stop - hs.start, pos.size)))
         O[t, hs], lse[t, hs], m[t, hs], l[t, hs] = f["O"], f["lse"], f["m"], f["l"]
@@ -279,13 +291,14 @@ def selected_forward(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float,
 
 
 def selected_backward(q, k, v, do, topk, cu_q, cu_kv, block_size: int, scale: float,
-                      sparse_mode: int) -> dict:
+                      sparse_mode: int, atten_mask=None) -> dict:
     """Exact gradients of the gathered attention: per token, the dense head
     backward over the gathered keys, then dK/dV scattered back to the gathered
-    positions with duplicates accumulating."""
+    positions with duplicates accumulating.  atten_mask: see
+    _selected_token_rows."""
     dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     for t, hs, h2, pos, allowed in _selected_token_rows(q, k, v, topk, cu_q, cu_kv,
-                                                        block_size, scale, sparse_mode):
+                                                        block_size, scale, sparse_mode, atten_mask):
         g = head_backward(q[t, hs], k[pos, h2], v[pos, h2], do[t, hs], scale,
                           np.broadcast_to(allowed, (hs.stop - hs.start, pos.size)))
         dq[t, hs] = g["dq"]

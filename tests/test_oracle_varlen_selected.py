@@ -96,9 +96,10 @@ def test_varlen_finite_differences():
 # selected (NSA)
 # ----------------------------------------------------------------------------
 
-def _multiplicity_bias(topk, cu_q, cu_kv, bs, sparse_mode, Tk):
+def _multiplicity_bias(topk, cu_q, cu_kv, bs, sparse_mode, Tk, mask=None):
     """Dense additive bias per (token, kv head, key): ln(number of slots that
-    name the key's block), -inf if none or if causally excluded."""
+    name the key's block), -inf if none, if causally excluded or if the user
+    mask (sequence-local query, key) excludes it."""
     T, N2, count = topk.shape
     bias = np.full((T, N2, Tk), -np.inf)
     starts_q = np.concatenate([[0], cu_q[:-1]])
@@ -109,6 +110,8 @@ def _multiplicity_bias(topk, cu_q, cu_kv, bs, sparse_mode, Tk):
                 mult = np.bincount(topk[t, h2], minlength=(k1 - k0) // bs)
                 for j in range(k1 - k0):
                     if sparse_mode == 2 and j > t - s0:
+                        continue
+                    if mask is not None and mask[t - s0, j]:
                         continue
                     if mult[j // bs]:
                         bias[t, h2, k0 + j] = math.log(mult[j // bs])
@@ -161,6 +164,86 @@ def test_selected_equals_biased_dense(sparse_mode, D, Dv):
     np.testing.assert_allclose(g["dq"], dq_t, atol=1e-12)
     np.testing.assert_allclose(g["dk"], dk_t, atol=1e-12)
     np.testing.assert_allclose(g["dv"], dv_t, atol=1e-12)
+
+
+def _random_keep_out(sq, sk, seed, p=0.3):
+    """A user attention mask (True = masked out) of the given shape."""
+    return np.random.default_rng(seed).random((sq, sk)) < p
+
+
+@pytest.mark.parametrize("sparse_mode", [0, 2])
+def test_selected_user_mask_equals_biased_dense(sparse_mode):
+    """The user mask (Ascend attenMaskOptional, read as True = masked out over
+    sequence-local (query, key) positions, shared by sequences and heads) is
+    the dense biased attention with -inf where the mask is set: pinned against
+    torch fp64 autograd on a mask built independently of the oracle."""
+    q, k, v, do, topk, cu = _tiny_selected(lengths=(24, 16), N2=2, G=2, count=3, D=5, Dv=3, seed=9)
+    topk[5, 0] = [1, 1, 0]
+    bs, scale = 4, 0.45
+    mask = _random_keep_out(24, 24, seed=4)
+    bias = _multiplicity_bias(topk, cu, cu, bs, sparse_mode, k.shape[0], mask)
+    # rows the mask leaves without any key are tested separately
+    live = np.isfinite(bias).any(axis=2).all(axis=1)
+    f = oracle.selected_forward(q, k, v, topk, cu, cu, bs, scale, sparse_mode, atten_mask=mask)
+    g = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, sparse_mode, atten_mask=mask)
+    do_live = do * live[:, None, None]
+    g_live = oracle.selected_backward(q, k, v, do_live, topk, cu, cu, bs, scale, sparse_mode, atten_mask=mask)
+    bias_live = np.where(live[:, None, None], bias, 0.0)    # dead rows: any finite bias, zero dO
+    o_t, (dq_t, dk_t, dv_t) = _torch_biased(q, k, v, do_live, bias_live, scale)
+    np.testing.assert_allclose(f["O"][live], o_t[live], atol=1e-12)
+    np.testing.assert_allclose(g_live["dq"][live], dq_t[live], atol=1e-12)
+    np.testing.assert_allclose(g_live["dk"], dk_t, atol=1e-12)
+    np.testing.assert_allclose(g_live["dv"], dv_t, atol=1e-12)
+    # a token whose every gathered key is masked: O = 0, m = -inf, l = 0 and
+    # no gradient flows through it
+    for t in np.flatnonzero(~live):
+        for h in range(q.shape[1]):
+            h2 = h // 2
+            if not np.isfinite(bias[t, h2]).any():
+                assert np.all(f["O"][t, h] == 0) and f["m"][t, h] == -np.inf and f["l"][t, h] == 0
+                assert np.all(g["dq"][t, h] == 0)
+
+
+def test_selected_user_mask_special_cases():
+    """An all-False mask changes nothing (bitwise); a mask that is the causal
+    pattern under sparse_mode 0 is sparse_mode 2 without a mask (bitwise)."""
+    q, k, v, do, topk, cu = _tiny_selected(lengths=(20, 12), N2=1, G=3, count=3, D=4, seed=2)
+    bs, scale = 4, 0.5
+    none = np.zeros((20, 20), bool)
+    a = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, 2)
+    b = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, 2, atten_mask=none)
+    causal_keep_out = np.arange(20)[None, :] > np.arange(20)[:, None]
+    c = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, 0, atten_mask=causal_keep_out)
+    for key in ("dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key])
+        assert np.array_equal(a[key], c[key])
+
+
+def test_selected_user_mask_finite_differences():
+    q, k, v, do, topk, cu = _tiny_selected(lengths=(32,), N2=1, G=2, D=3, bs=4, count=3, seed=6, Dv=2)
+    bs, scale, mode = 4, 0.6, 0
+    mask = _random_keep_out(32, 32, seed=8, p=0.4)
+    mask[:, 0] = False                          # every token keeps key 0 when block 0 is chosen
+    topk[:, 0, 0] = 0
+    g = oracle.selected_backward(q, k, v, do, topk, cu, cu, bs, scale, mode, atten_mask=mask)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(do * oracle.selected_forward(q_, k_, v_, topk, cu, cu, bs, scale, mode,
+                                                          atten_mask=mask)["O"]))
+
+    h = 1e-6
+    for j, ref in enumerate((g["dq"], g["dk"], g["dv"])):
+        base = [q, k, v]
+        x = base[j]
+        for idx in [(20, 0, 1), (9, 0, 2), (0, 0, 0), (3, 0, 1), (31, 0, 2), (14, 0, 0)]:
+            idx = (idx[0], min(idx[1], x.shape[1] - 1), min(idx[2], x.shape[2] - 1))
+            args = [a.copy() for a in base]
+            args[j][idx] += h
+            lp = loss(*args)
+            args[j][idx] -= 2 * h
+            lm = loss(*args)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - ref[idx]) <= 1e-7 * max(1.0, np.max(np.abs(ref))), (j, idx, fd, ref[idx])
 
 
 def test_selected_finite_differences_with_duplicates():
