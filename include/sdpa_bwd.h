@@ -239,6 +239,17 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  * indices are relative to the token's sequence start in K/V.
  *   sparse_mode 0: no mask; 2: causal, key position <= query position within
  *   the sequence (the page supports "0 or 2" without defining them).
+ *   atten_mask: optional DEVICE byte array (the page's attenMaskOptional,
+ *   BOOL/UINT8, two dimensions, "Parameters" table), or NULL for none.  Byte
+ *   atten_mask[i * atten_mask_stride + j] nonzero masks out key position j
+ *   for query position i, both counted from the start of their sequence; the
+ *   same mask applies to every sequence and head, on top of sparse_mode's
+ *   causal rule (the page gives no formula for it; this is the usual
+ *   keep-out reading).  It needs a row for every query position of the
+ *   longest query sequence and atten_mask_stride >= the longest KV sequence
+ *   (else SDPA_ERR_INVALID); base and stride must be 16-byte multiples, with
+ *   the stride below 2^31 (else SDPA_ERR_UNSUPPORTED).  A query left with no
+ *   admissible key gets P = 0 (forward: O = 0, max = -inf, sum = 0).
  *   Constraints (Ascend page, "Constraints"): block_size <= 128 and a multiple
  *   of 16; 1 <= block_count <= 128; block_count * block_size < 8192; every KV
  *   sequence length a multiple of block_size and >= block_count * block_size;
@@ -260,7 +271,8 @@ int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu
                                      int deterministic, size_t* bytes);
 int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
-                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      double scale, int sparse_mode, const uint8_t* atten_mask, int64_t atten_mask_stride,
+                      const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       int deterministic, int grad_dtype,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
@@ -273,8 +285,8 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
  * producing O and the softmaxMax / softmaxSum statistics that
  * sdpa_bwd_selected consumes (Ascend page, "Formula": P is the softmax of the
  * scaled scores over the gathered blocks; "Parameters": softmaxMax,
- * softmaxSum).  Arguments, topk, sparse_mode, head dims (D, Dv) and
- * constraints as sdpa_bwd_selected; o_out: (Tq, Hq, Dv) written.
+ * softmaxSum).  Arguments, topk, sparse_mode, atten_mask, head dims (D, Dv)
+ * and constraints as sdpa_bwd_selected; o_out: (Tq, Hq, Dv) written.
  *   max_out[t*stats_stride_s + h*stats_stride_h]: max over the admissible
  *   gathered keys of the scaled score (natural units); sum_out at the same
  *   offset: sum of exp(score - max).  A token with no admissible key gets
@@ -283,7 +295,8 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
  */
 int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
-                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      double scale, int sparse_mode, const uint8_t* atten_mask,
+                      int64_t atten_mask_stride, const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                       const sdpa_tensor3* o_out, float* max_out, float* sum_out,

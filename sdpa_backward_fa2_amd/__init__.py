@@ -88,10 +88,10 @@ _SIGS = {
     "sdpa_bwd_selected_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64,
                                                  c_i64, c_i64, c_int, ctypes.POINTER(c_size)]),
     "sdpa_bwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
-                                  c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int, c_int,
+                                  c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_int, c_int,
                                   P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
     "sdpa_fwd_selected": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
-                                  c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                  c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
                                   P3, P3, P3, P3, c_vp, c_vp, c_i64, c_i64, c_vp]),
     "sdpa_profile_begin": (c_int, []),
     "sdpa_profile_end": (c_int, [c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)]),
@@ -436,11 +436,21 @@ def bwd_selected_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, block_size, bloc
     return out.value
 
 
+def _mask_arg(atten_mask):
+    """(pointer, row stride) of an optional 2-D bool/uint8 device mask."""
+    if atten_mask is None:
+        return None, 0
+    if atten_mask.dim() != 2 or atten_mask.dtype not in (torch.bool, torch.uint8) or atten_mask.stride(1) != 1:
+        raise ValueError("atten_mask: a 2-D bool or uint8 device tensor with unit column stride")
+    return atten_mask.data_ptr(), atten_mask.stride(0)
+
+
 def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
                      sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
-                     workspace=None, grad_dtype=None):
+                     workspace=None, grad_dtype=None, atten_mask=None):
     """Marshal one NSA selected-attention backward once; returns (call, (dq, dk, dv)).
-    topk: int32 (T, Hkv, count) on the device."""
+    topk: int32 (T, Hkv, count) on the device; atten_mask: optional (Sq, Sk)
+    bool/uint8 device tensor, True = masked out (sequence-local positions)."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
     Hkv, Dv = k.shape[1], v.shape[2]
@@ -453,12 +463,13 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
     structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(sparse_mode),
+    mp, ms = _mask_arg(atten_mask)
+    args = (dt, n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(sparse_mode), mp, ms,
             topk.data_ptr(), *topk.stride(), block_size, count, int(deterministic), gdt,
             *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
     fn = lib.sdpa_bwd_selected
-    keep = (structs, sa, ws, stats, topk, aq, ak)
+    keep = (structs, sa, ws, stats, topk, aq, ak, atten_mask)
 
     def call():
         _check(fn(*args), "sdpa_bwd_selected")
@@ -469,17 +480,18 @@ def prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int
 
 def bwd_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size: int, scale: float,
                  sparse_mode: int, deterministic: int = DQ_FASTEST, dq=None, dk=None, dv=None,
-                 workspace=None, grad_dtype=None):
+                 workspace=None, grad_dtype=None, atten_mask=None):
     """NSA selected-attention backward; topk: int32 (T, Hkv, count) on the device;
-    gradients in q's dtype or float32 (grad_dtype, or the given tensors')."""
+    gradients in q's dtype or float32 (grad_dtype, or the given tensors');
+    atten_mask as prepare_selected."""
     call, outs = prepare_selected(q, k, v, o, dout, stats, topk, cu_q, cu_kv, block_size, scale,
-                                  sparse_mode, deterministic, dq, dk, dv, workspace, grad_dtype)
+                                  sparse_mode, deterministic, dq, dk, dv, workspace, grad_dtype, atten_mask)
     call()
     return outs
 
 
 def fwd_selected(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float, sparse_mode: int,
-                 o=None, m=None, l=None):
+                 o=None, m=None, l=None, atten_mask=None):
     """NSA selected-attention forward: O and the (max, sum) statistics (T, Hq)
     fp32 over each token's gathered keys; topk: int32 (T, Hkv, count) on the device.
     O has v's head dim."""
@@ -496,8 +508,9 @@ def fwd_selected(q, k, v, topk, cu_q, cu_kv, block_size: int, scale: float, spar
     assert m.stride() == l.stride()
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
+    mp, ms = _mask_arg(atten_mask)
     st = lib.sdpa_fwd_selected(_dtype_code(q), n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(sparse_mode),
-                               topk.data_ptr(), *topk.stride(), int(block_size), count,
+                               mp, ms, topk.data_ptr(), *topk.stride(), int(block_size), count,
                                _t3(q), _t3(k), _t3(v), _t3(o), m.data_ptr(), l.data_ptr(),
                                m.stride(0), m.stride(1), _stream_ptr(q.device))
     _check(st, "sdpa_fwd_selected")

@@ -65,6 +65,11 @@ struct NsaParams {
     float* partial;       // [max_pieces][halves][64][D] for dK then dV
     int halves;           // ceil(bs / 64)
     int sparse_mode;
+    // optional user mask over (sequence-local query, sequence-local key)
+    // positions, nonzero = masked out; rows mask_ss bytes apart, 16-byte
+    // aligned, shared by every sequence and head (null: none)
+    const uint8_t* mask;
+    int64_t mask_ss;
     int Tq;
     int grad_f32;         // dQ, dK, dV are fp32 (else the input dtype)
     float scale, scale_log2;
@@ -74,6 +79,21 @@ struct NsaParams {
     float* l_out;         // sum of exp(score - max)
     int64_t st_ss, st_sh; // token and head strides of m_out / l_out
 };
+
+// Bit i of the result is set when byte i of the 16 is nonzero.
+__device__ __forceinline__ uint32_t mask_bits16(u32x4 v) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t t = v[i] | (v[i] >> 4);
+        t |= t >> 2;
+        t |= t >> 1;
+        // bit 0 of each byte is now "byte != 0"; the multiply gathers the
+        // four into bits 24..27 (no two partial products meet below 2^32)
+        r |= (((t & 0x01010101u) * 0x01020408u) >> 24 & 0xFu) << (4 * i);
+    }
+    return r;
+}
 
 __device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) {
     int r = -1;
@@ -288,7 +308,9 @@ __global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
 // P and dS on the vector ALU, dV^T += dO^T P and dK^T += Q^T dS with the
 // transposed operands read by ds_read_b64_tr_b16.
 
-template <class T, int DK, int DV>
+// UM: with a user attention mask (a separate instance, so that the mask's
+// staging registers do not weigh on the unmasked kernel).
+template <class T, int DK, int DV, bool UM>
 __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     // DK: head dim of Q and K; DV: of V, O and dO.  Rows per step: 128 at
     // DK = DV = 128 (each wavefront takes two 32-row blocks of its 64-row
@@ -309,6 +331,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     __shared__ __align__(16) float lse_s[2][BR];
     __shared__ __align__(16) float dlt_s[2][BR];
     __shared__ int tl_s[2][BR];          // sequence-local token position of each row
+    __shared__ uint64_t mbits_s[UM ? 2 : 1][UM ? BR : 1];  // user mask: bit j = key j of this half masked
     __shared__ int tok_s[2048];          // token of each entry of the piece (<= 2048 / G entries)
     typedef uint16_t TileQ[BR * QPK];
     typedef uint16_t TileO[BR * QPV];
@@ -365,6 +388,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     // given LSE = +inf when stored, so their P is exactly zero; nothing loaded
     // is used before store_tile.
     u32x4 pq[CHK], pdo[CHV];
+    u32x4 pm[UM ? 4 : 1];                       // user mask bytes of the row's 64 keys
     float pl = INFINITY, pd = 0.f;
     int ptl = 0;
     bool pok = false;
@@ -405,6 +429,18 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             pd = p.delta[(int64_t)t * p.Hq + h];
             ptl = t - q0s;
             pok = r < E * p.G && li < n_e;
+            if constexpr (UM) {
+              if (tid < BR) {
+                // 16-byte pieces of the row's mask bytes for this half's keys
+                // (kpos0 and the row stride are multiples of 16; nkeys is too)
+                const u32x4* mp = reinterpret_cast<const u32x4*>(p.mask + (int64_t)ptl * p.mask_ss + kpos0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    pm[j] = 16 * j < nkeys ? mp[j] : z;
+                }
+              }
+            }
         }
     };
     auto store_tile = [&](int buf) {
@@ -424,6 +460,9 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             lse_s[buf][tid] = pok ? pl : INFINITY;
             dlt_s[buf][tid] = pok ? -pd : 0.f;      // stored negated: it seeds dP - Delta
             tl_s[buf][tid] = ptl;
+            if constexpr (UM)
+                mbits_s[buf][tid] = (uint64_t)(mask_bits16(pm[0]) | (mask_bits16(pm[1]) << 16)) |
+                                    ((uint64_t)(mask_bits16(pm[2]) | (mask_bits16(pm[3]) << 16)) << 32);
         }
     };
 
@@ -471,8 +510,9 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             const int r0 = (BR / 2) * rh + 32 * sb;
             f32x16& sa = sab[sb];
             f32x16& pa = pab[sb];
-            auto grad = [&](auto masked_tag) {
+            auto grad = [&](auto masked_tag, auto user_tag) {
                 constexpr bool MK = decltype(masked_tag)::value;
+                constexpr bool UMK = decltype(user_tag)::value;   // user mask: MK as well
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int rb = r0 + 8 * q + 4 * g;
@@ -482,7 +522,8 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
                         const int rg = 4 * q + r;
                         float pv = fast_exp2(__builtin_fmaf(sa[rg], p.scale_log2, -Lr[r]));
                         if (MK) {
-                            const bool off = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
+                            bool off = !col_ok || (p.sparse_mode == 2 && my_kpos > tl_s[buf][rb + r]);
+                            if constexpr (UMK) off = off || ((mbits_s[buf][rb + r] >> myk) & 1);
                             pv = off ? 0.f : pv;
                         }
                         sa[rg] = pv;
@@ -490,8 +531,9 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
                     }
                 }
             };
-            if (masked) grad(std::true_type{});
-            else grad(std::false_type{});
+            if constexpr (UM) grad(std::true_type{}, std::true_type{});
+            else if (masked) grad(std::true_type{}, std::false_type{});
+            else grad(std::false_type{}, std::false_type{});
             if (sb == NSB - 1 && has_next) store_tile(buf ^ 1);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -726,6 +768,9 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
         }
     }
     const int rq_k = (tid & (BK - 1)) / p.bs, rr_k = (tid & (BK - 1)) % p.bs;
+    // the user mask's row of this token (a masked key is treated as absent)
+    const uint8_t* mrow = p.mask ? p.mask + (int64_t)t_local * p.mask_ss : nullptr;
+    uint32_t mbyte = 0;
     // row strides are below 2^23 elements: 32 x 32 -> 64-bit row offsets
     const int kss = (int)p.k.ss, vss = (int)p.v.ss;
     const uint16_t* const kh = p.k.p + (int64_t)h2 * p.k.sh;
@@ -765,9 +810,12 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
         else { slot = n / p.bs; rb = n % p.bs; }
         const int blk = blk_s[min(slot, p.count - 1)];
         kpos_r = (n < nk && blk >= 0) ? blk * p.bs + rb : 0x7fffffff;   // masked: no key there
+        if (mrow && kpos_r != 0x7fffffff) mbyte = mrow[kpos_r];
     };
     load_chunk(0);
     for (int c0 = 0; c0 < nk; c0 += BK) {
+        if (mrow && mbyte) kpos_r = 0x7fffffff;
+        mbyte = 0;
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < CHK; ++x) {
@@ -911,6 +959,9 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
     // row past the gathered keys re-reads key row krow0 and is masked
     u32x4 kv[CHK], vv[CHV];
     int kpos_r = 0x7fffffff;
+    // the user mask's row of this token (a masked key is treated as absent)
+    const uint8_t* mrow = p.mask ? p.mask + (int64_t)t_local * p.mask_ss : nullptr;
+    uint32_t mbyte = 0;
     // packed key row of gathered key n (row krow0, masked, if there is none)
     auto key_row = [&](int n) {
         const int blk = blk_s[min(n / p.bs, p.count - 1)];
@@ -938,9 +989,12 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
         const int n = c0 + (tid & (BK - 1));
         const int blk = blk_s[min(n / p.bs, p.count - 1)];
         kpos_r = (n < nk && blk >= 0) ? blk * p.bs + n % p.bs : 0x7fffffff;
+        if (mrow && kpos_r != 0x7fffffff) mbyte = mrow[kpos_r];
     };
     load_chunk(0);
     for (int c0 = 0; c0 < nk; c0 += BK) {
+        if (mrow && mbyte) kpos_r = 0x7fffffff;
+        mbyte = 0;
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < CHK; ++x) {
@@ -1089,7 +1143,12 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     if (e != hipSuccess) return e;
     e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, DV, false, st);
     if (e != hipSuccess) return e;
-    PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV>), dim3(p.max_pieces, p.halves), dim3(256), 0, st, p);
+    if (p.mask)
+        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, true>), dim3(p.max_pieces, p.halves), dim3(256), 0,
+                    st, p);
+    else
+        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
+                    st, p);
     PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, DK, DV>),
                 dim3(p.N2 * p.NB, p.halves, reduce_key_groups<DK, DV>()), dim3(256), 0, st, p);
     // with no query token (every query length 0) dK and dV are the reduction's
@@ -1153,19 +1212,26 @@ bool nsa_dims_ok(int64_t D, int64_t Dv) {
 // 1 <= block_count <= 128, count * size < 8192, every KV length a multiple of
 // block_size and >= count * size; sparse_mode 2 needs equal lengths.
 int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_t Hq, int64_t Hkv,
-                   int64_t D, int64_t Dv, int64_t bs, int64_t count, int sparse_mode, Seqs& S) {
+                   int64_t D, int64_t Dv, int64_t bs, int64_t count, int sparse_mode, Seqs& S,
+                   const uint8_t* mask = nullptr, int64_t mask_stride = 0) {
     if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (Hq / Hkv > 32) return SDPA_ERR_INVALID;
     if (bs < 16 || bs > 128 || bs % 16) return SDPA_ERR_INVALID;
     if (count < 1 || count > 128 || count * bs >= 8192) return SDPA_ERR_INVALID;
     if (sparse_mode != 0 && sparse_mode != 2) return SDPA_ERR_INVALID;
     if (int s = read_seqs(batch, cuq, cuk, S)) return s;
+    int64_t max_lk = 0;
     for (size_t b = 0; b < S.lk.size(); ++b) {
         if (S.lk[b] % bs) return SDPA_ERR_INVALID;
         if (S.lk[b] < count * bs) return SDPA_ERR_INVALID;
         if (sparse_mode == 2 && S.lq[b] != S.lk[b]) return SDPA_ERR_INVALID;
+        max_lk = std::max(max_lk, S.lk[b]);
     }
+    // a user mask row covers every key position of the longest sequence
+    if (mask && mask_stride < max_lk) return SDPA_ERR_INVALID;
     if (!nsa_dims_ok(D, Dv)) return SDPA_ERR_UNSUPPORTED;
+    if (mask && ((reinterpret_cast<uintptr_t>(mask) & 15u) || (mask_stride % 16) || mask_stride >= ((int64_t)1 << 31)))
+        return SDPA_ERR_UNSUPPORTED;
     if (batch > sdpa::kMaxSeqArgs) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq * Hkv * count >= ((int64_t)1 << 31) || S.Tk >= ((int64_t)1 << 31)) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq > 2147483647 || Hkv * ((Hq / Hkv + 15) / 16) > 65535) return SDPA_ERR_UNSUPPORTED;
@@ -1274,7 +1340,8 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
 
 int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
-                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      double scale, int sparse_mode, const uint8_t* atten_mask, int64_t atten_mask_stride,
+                      const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                       const sdpa_tensor3* o_out, float* max_out, float* sum_out,
@@ -1287,7 +1354,7 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     Seqs S;
     if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, Dv, block_size,
-                               block_count, sparse_mode, S))
+                               block_count, sparse_mode, S, atten_mask, atten_mask_stride))
         return s;
     for (const sdpa_tensor3* t : {q, k, v, o_out})
         if (int s = t3_ok(t)) return s;
@@ -1304,6 +1371,7 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     p.m_out = max_out; p.l_out = sum_out;
     p.st_ss = stats_stride_s; p.st_sh = stats_stride_h;
     p.sparse_mode = sparse_mode;
+    p.mask = atten_mask; p.mask_ss = atten_mask_stride;
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -1318,7 +1386,8 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
 
 int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                       const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
-                      double scale, int sparse_mode, const int32_t* topk, int64_t tk_st,
+                      double scale, int sparse_mode, const uint8_t* atten_mask, int64_t atten_mask_stride,
+                      const int32_t* topk, int64_t tk_st,
                       int64_t tk_sn, int64_t tk_sk, int64_t block_size, int64_t block_count,
                       int deterministic, int grad_dtype,
                       const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
@@ -1339,7 +1408,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     if (stats->kind != SDPA_STATS_LSE && stats->kind != SDPA_STATS_MAX_SUM) return SDPA_ERR_INVALID;
     Seqs S;
     if (int s = check_selected(batch, cu_seqlens_q_host, cu_seqlens_kv_host, Hq, Hkv, D, Dv, block_size,
-                               block_count, sparse_mode, S))
+                               block_count, sparse_mode, S, atten_mask, atten_mask_stride))
         return s;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = t3_ok(t)) return s;
@@ -1359,6 +1428,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     p.delta = reinterpret_cast<float*>(ws + L.delta);
     p.partial = reinterpret_cast<float*>(ws + L.partial);
     p.sparse_mode = sparse_mode;
+    p.mask = atten_mask; p.mask_ss = atten_mask_stride;
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
 

@@ -227,13 +227,15 @@ def test_fwd_varlen_valid_without_device():
 
 
 def fwd_selected_call(**kw):
-    a = dict(dtype=1, cu=[512], Hq=16, Hkv=1, D=128, bs=64, count=4, mode=2, m=FAKE, l=FAKE)
+    a = dict(dtype=1, cu=[512], Hq=16, Hkv=1, D=128, bs=64, count=4, mode=2, m=FAKE, l=FAKE,
+             mask=None, mask_stride=0)
     a.update(kw)
     a.setdefault("Dv", a["D"])
     cu = (ctypes.c_int64 * len(a["cu"]))(*a["cu"])
     ts = [t3() for _ in range(4)]
     return lib().sdpa_fwd_selected(a["dtype"], len(a["cu"]), cu, cu, a["Hq"], a["Hkv"], a["D"], a["Dv"], 0.088,
-                                   a["mode"], FAKE, 4 * a["count"], a["count"], 1, a["bs"], a["count"],
+                                   a["mode"], a["mask"], a["mask_stride"],
+                                   FAKE, 4 * a["count"], a["count"], 1, a["bs"], a["count"],
                                    *[ctypes.byref(t) for t in ts], a["m"], a["l"], 16, 1, None)
 
 
@@ -249,17 +251,24 @@ def test_fwd_selected_validation():
     cu = (ctypes.c_int64 * 1)(512)
     ts = [t3() for _ in range(4)]
     ts[1] = big
-    assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 128, 0.088, 2, FAKE, 64, 16, 1, 64, 4,
+    assert lib().sdpa_fwd_selected(1, 1, cu, cu, 16, 1, 128, 128, 0.088, 2, None, 0, FAKE, 64, 16, 1, 64, 4,
                                    *[ctypes.byref(t) for t in ts], FAKE, FAKE, 16, 1, None) == UNSUPPORTED
+    # user attention mask: a row must cover the longest KV sequence (INVALID),
+    # base and stride 16-byte multiples (UNSUPPORTED)
+    assert fwd_selected_call(mask=FAKE, mask_stride=496) == INVALID
+    assert fwd_selected_call(mask=FAKE, mask_stride=520) == UNSUPPORTED
+    assert fwd_selected_call(mask=FAKE + 8, mask_stride=512) == UNSUPPORTED
+    assert fwd_selected_call(mask=FAKE, mask_stride=496, D=96) == INVALID     # INVALID before UNSUPPORTED
 
 
 def bwd_selected_call(**kw):
-    a = dict(dtype=1, grad=1, det=0, D=128, Dv=128)
+    a = dict(dtype=1, grad=1, det=0, D=128, Dv=128, mask=None, mask_stride=0)
     a.update(kw)
     cu = (ctypes.c_int64 * 1)(512)
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 16)
     ts = [t3() for _ in range(8)]
-    return lib().sdpa_bwd_selected(a["dtype"], 1, cu, cu, 16, 1, a["D"], a["Dv"], 0.088, 2, FAKE, 16, 4, 1, 64, 4,
+    return lib().sdpa_bwd_selected(a["dtype"], 1, cu, cu, 16, 1, a["D"], a["Dv"], 0.088, 2,
+                                   a["mask"], a["mask_stride"], FAKE, 16, 4, 1, 64, 4,
                                    a["det"], a["grad"], *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
                                    *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None)
 
@@ -271,6 +280,8 @@ def test_bwd_selected_validation():
     assert bwd_selected_call(Dv=0) == INVALID
     assert bwd_selected_call(D=64, Dv=128) == UNSUPPORTED     # kernels: equal 64/128/192, and (192,128)
     assert bwd_selected_call(D=128, Dv=64) == UNSUPPORTED
+    assert bwd_selected_call(mask=FAKE, mask_stride=256) == INVALID     # row shorter than the KV length
+    assert bwd_selected_call(mask=FAKE, mask_stride=1 << 31) == UNSUPPORTED
     n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 1)(512)
     assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 192, 128, 64, 4, 0, ctypes.byref(n)) == OK
@@ -286,6 +297,7 @@ def test_bwd_selected_valid_without_device():
     assert bwd_selected_call(grad=2) == HIP           # fp32 gradients
     assert bwd_selected_call(D=192, Dv=128) == HIP    # unequal head dims
     assert bwd_selected_call(D=192, Dv=192) == HIP
+    assert bwd_selected_call(mask=FAKE, mask_stride=512) == HIP   # with a user mask
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
