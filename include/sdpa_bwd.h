@@ -253,7 +253,8 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   Constraints (Ascend page, "Constraints"): block_size <= 128 and a multiple
  *   of 16; 1 <= block_count <= 128; block_count * block_size < 8192; every KV
  *   sequence length a multiple of block_size and >= block_count * block_size;
- *   Hq a multiple of Hkv with Hq / Hkv <= 32; at most 64 sequences; token
+ *   Hq a multiple of Hkv with Hq / Hkv <= 32; any number of sequences (more
+ *   than 64 take a table of 16 bytes per sequence in the workspace); token
  *   and head strides of every tensor below 2^23 elements.  Topk
  *   values outside the sequence's blocks select nothing (those slots are
  *   ignored); the statistics must then describe the same reduced key set.

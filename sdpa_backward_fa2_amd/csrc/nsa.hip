@@ -65,6 +65,7 @@ struct NsaParams {
     float* partial;       // [max_pieces][halves][64][D] for dK then dV
     int halves;           // ceil(bs / 64)
     int sparse_mode;
+    int t_base;           // forward: first token of this launch (grid x counts from it)
     // optional user mask over (sequence-local query, sequence-local key)
     // positions, nonzero = masked out; rows mask_ss bytes apart, 16-byte
     // aligned, shared by every sequence and head (null: none)
@@ -95,18 +96,55 @@ __device__ __forceinline__ uint32_t mask_bits16(u32x4 v) {
     return r;
 }
 
-__device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) {
+// Sequence table access.  Up to kMaxSeqArgs sequences travel in the kernel
+// arguments; more live in the workspace as int4 (q0, k0, lq, lk) rows, filled
+// by nsa_seqtab_kernel at the start of the call.
+struct SeqRow {
+    int q0, k0, lq, lk;
+};
+
+__device__ __forceinline__ SeqRow seq_row(const SeqTable& s, int i) {
+    if (s.dev) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(s.dev + 4 * i);
+        return SeqRow{v[0], v[1], v[2], v[3]};
+    }
+    return SeqRow{s.q0[i], s.k0[i], s.lq[i], s.lk[i]};
+}
+
+// The sequence holding position x of the packed query (F = 0) or key (F = 1)
+// rows, or -1.  Starts are non-decreasing and each sequence ends where the
+// next starts, so it is the last sequence starting at or before x, provided x
+// lies before its end.
+template <int F>
+__device__ __forceinline__ int seq_of(const SeqTable& s, int x) {
+    if (s.dev) {
+        int lo = 0, hi = s.n - 1, r = -1;
+        while (lo <= hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s.dev[4 * mid + F] <= x) { r = mid; lo = mid + 1; }
+            else hi = mid - 1;
+        }
+        if (r >= 0 && x >= s.dev[4 * r + F] + s.dev[4 * r + 2 + F]) r = -1;
+        return r;
+    }
     int r = -1;
-    for (int i = 0; i < s.n; ++i)
-        if (key_row >= s.k0[i] && key_row < s.k0[i] + s.lk[i]) r = i;
+    for (int i = 0; i < s.n; ++i) {
+        const int a = F ? s.k0[i] : s.q0[i], n = F ? s.lk[i] : s.lq[i];
+        if (x >= a && x < a + n) r = i;
+    }
     return r;
 }
 
-__device__ __forceinline__ int seq_of_token(const SeqTable& s, int t) {
-    int r = -1;
-    for (int i = 0; i < s.n; ++i)
-        if (t >= s.q0[i] && t < s.q0[i] + s.lq[i]) r = i;
-    return r;
+__device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) { return seq_of<1>(s, key_row); }
+__device__ __forceinline__ int seq_of_token(const SeqTable& s, int t) { return seq_of<0>(s, t); }
+
+// Writes rows first .. first + chunk.n - 1 of the workspace sequence table.
+__global__ __launch_bounds__(64) void nsa_seqtab_kernel(SeqTable chunk, int32_t* table, int first) {
+    const int i = threadIdx.x;
+    if (i >= chunk.n) return;
+    i32x4 v;
+    v[0] = chunk.q0[i]; v[1] = chunk.k0[i]; v[2] = chunk.lq[i]; v[3] = chunk.lk[i];
+    *reinterpret_cast<i32x4*>(table + 4 * (first + i)) = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -130,9 +168,10 @@ __global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
         if (!FILL && tid == 0) p.counts[bucket] = 0;
         return;
     }
-    const int gl = g - p.seqs.k0[s] / p.bs;      // block index within its sequence
-    const int64_t e0 = (int64_t)p.seqs.q0[s] * p.count;
-    const int64_t e1 = (int64_t)(p.seqs.q0[s] + p.seqs.lq[s]) * p.count;
+    const SeqRow sr = seq_row(p.seqs, s);
+    const int gl = g - sr.k0 / p.bs;             // block index within its sequence
+    const int64_t e0 = (int64_t)sr.q0 * p.count;
+    const int64_t e1 = (int64_t)(sr.q0 + sr.lq) * p.count;
     const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
     const unsigned long long below = (1ull << lane) - 1ull;
     if (p.tk_vec4) {
@@ -352,7 +391,8 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
     if (kb0 >= p.bs) return;
     const int nkeys = min(64, p.bs - kb0);
     const int s_idx = seq_of_block(p.seqs, blk * p.bs);
-    const int blk_local = blk - p.seqs.k0[s_idx] / p.bs;
+    const SeqRow srow_info = seq_row(p.seqs, s_idx);
+    const int blk_local = blk - srow_info.k0 / p.bs;
     const int key_row0 = blk * p.bs + kb0;      // packed KV row of key 0 of this half
     const int kpos0 = blk_local * p.bs + kb0;   // its sequence-local position
 
@@ -375,7 +415,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
 
     const int E = max(1, BR / p.G);             // entries per step
     const int n_steps = (ee - eb + E - 1) / E;
-    const int q0s = p.seqs.q0[s_idx];
+    const int q0s = srow_info.q0;
 
     // The tokens of the piece's entries go to LDS once, so that a step's
     // row addresses need no dependent global load.
@@ -707,9 +747,10 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     const int col = lane & 15, G16 = lane >> 4;
     const int s_idx = seq_of_token(p.seqs, t);
     if (s_idx < 0) return;
-    const int t_local = t - p.seqs.q0[s_idx];
-    const int krow0 = p.seqs.k0[s_idx];
-    const int nblk = p.seqs.lk[s_idx] / p.bs;   // blocks of this sequence
+    const SeqRow sq = seq_row(p.seqs, s_idx);
+    const int t_local = t - sq.q0;
+    const int krow0 = sq.k0;
+    const int nblk = sq.lk / p.bs;              // blocks of this sequence
     const int gh = ht * 16 + col;               // head within the group
     const bool head_ok = gh < p.G;
     const int h = h2 * p.G + (head_ok ? gh : 0);
@@ -921,16 +962,17 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
     __shared__ int kpos_s[BK];
     __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
 
-    const int t = blockIdx.x;
+    const int t = p.t_base + blockIdx.x;
     const int h2 = blockIdx.y / ((p.G + 15) / 16);
     const int ht = blockIdx.y % ((p.G + 15) / 16);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 15, G16 = lane >> 4;
     const int s_idx = seq_of_token(p.seqs, t);
     if (s_idx < 0) return;
-    const int t_local = t - p.seqs.q0[s_idx];
-    const int krow0 = p.seqs.k0[s_idx];
-    const int nblk = p.seqs.lk[s_idx] / p.bs;
+    const SeqRow sq = seq_row(p.seqs, s_idx);
+    const int t_local = t - sq.q0;
+    const int krow0 = sq.k0;
+    const int nblk = sq.lk / p.bs;
     const int gh = ht * 16 + col;
     const bool head_ok = gh < p.G;
     const int h = h2 * p.G + (head_ok ? gh : 0);
@@ -1181,7 +1223,7 @@ size_t up(size_t x) { return (x + kAlignN - 1) / kAlignN * kAlignN; }
 struct NsaLayout {
     int64_t NB = 0, nbk = 0, E = 0, chunk = 1, max_pieces = 0, halves = 1;
     size_t counts = 0, offsets = 0, entries = 0, pstart = 0, pieces = 0, lse2 = 0, delta = 0,
-           partial = 0, total = 0;
+           partial = 0, seqtab = 0, total = 0;
 };
 
 struct Seqs {
@@ -1232,7 +1274,6 @@ int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_
     if (!nsa_dims_ok(D, Dv)) return SDPA_ERR_UNSUPPORTED;
     if (mask && ((reinterpret_cast<uintptr_t>(mask) & 15u) || (mask_stride % 16) || mask_stride >= ((int64_t)1 << 31)))
         return SDPA_ERR_UNSUPPORTED;
-    if (batch > sdpa::kMaxSeqArgs) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq * Hkv * count >= ((int64_t)1 << 31) || S.Tk >= ((int64_t)1 << 31)) return SDPA_ERR_UNSUPPORTED;
     if (S.Tq > 2147483647 || Hkv * ((Hq / Hkv + 15) / 16) > 65535) return SDPA_ERR_UNSUPPORTED;
     return SDPA_OK;
@@ -1256,17 +1297,46 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.lse2 = o; o = up(o + S.Tq * Hq * 4);
     L.delta = o; o = up(o + S.Tq * Hq * 4);
     L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
+    // more sequences than the kernel arguments carry: a table in the workspace
+    const int64_t n = (int64_t)S.q0.size();
+    L.seqtab = o; o = up(o + (n > sdpa::kMaxSeqArgs ? (size_t)n * 16 : 0));
     L.total = o;
     return L;
 }
 
-void fill_seq_table(sdpa::SeqTable& t, const Seqs& S) {
-    t.n = (int)S.q0.size();
+// Sequences [first, first + n) of S into an argument table.
+void fill_seq_chunk(sdpa::SeqTable& t, const Seqs& S, int64_t first, int n) {
+    t.n = n;
     t.dev = nullptr;
-    for (int i = 0; i < t.n; ++i) {
-        t.q0[i] = (int32_t)S.q0[i]; t.k0[i] = (int32_t)S.k0[i];
-        t.lq[i] = (int32_t)S.lq[i]; t.lk[i] = (int32_t)S.lk[i];
+    for (int i = 0; i < n; ++i) {
+        t.q0[i] = (int32_t)S.q0[first + i]; t.k0[i] = (int32_t)S.k0[first + i];
+        t.lq[i] = (int32_t)S.lq[first + i]; t.lk[i] = (int32_t)S.lk[first + i];
     }
+}
+
+// The kernels' sequence table: in the arguments for up to kMaxSeqArgs
+// sequences, else the workspace table at `table` (filled by launch_seqtab).
+void fill_seq_table(sdpa::SeqTable& t, const Seqs& S, int32_t* table) {
+    const int64_t n = (int64_t)S.q0.size();
+    if (n <= sdpa::kMaxSeqArgs) {
+        fill_seq_chunk(t, S, 0, (int)n);
+        return;
+    }
+    t.n = (int)n;
+    t.dev = table;
+}
+
+// Fills the workspace sequence table, kMaxSeqArgs rows per launch (kernels,
+// no copies, so the call stays capturable in a graph).
+hipError_t launch_seqtab(const Seqs& S, int32_t* table, hipStream_t st) {
+    const int64_t n = (int64_t)S.q0.size();
+    if (n <= sdpa::kMaxSeqArgs) return hipSuccess;
+    for (int64_t c = 0; c < n; c += sdpa::kMaxSeqArgs) {
+        sdpa::SeqTable chunk{};
+        fill_seq_chunk(chunk, S, c, (int)std::min<int64_t>(sdpa::kMaxSeqArgs, n - c));
+        hipLaunchKernelGGL(sdpa::nsa_seqtab_kernel, dim3(1), dim3(64), 0, st, chunk, table, (int)c);
+    }
+    return hipGetLastError();
 }
 
 thread_local std::string g_nsa_err;
@@ -1328,7 +1398,7 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
     p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
     p.g_mul = (65536 + p.G - 1) / p.G;
     p.chunk = (int)L.chunk; p.max_pieces = (int)L.max_pieces;
-    fill_seq_table(p.seqs, S);
+    fill_seq_table(p.seqs, S, reinterpret_cast<int32_t*>(ws + L.seqtab));
     p.counts = reinterpret_cast<int32_t*>(ws + L.counts);
     p.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
     p.entries = reinterpret_cast<int32_t*>(ws + L.entries);
@@ -1365,7 +1435,6 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     p.topk = topk; p.tk_st = tk_st; p.tk_sn = tk_sn; p.tk_sk = tk_sk;
     p.count = (int)block_count; p.bs = (int)block_size; p.N2 = (int)Hkv;
     p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
-    fill_seq_table(p.seqs, S);
     p.Tq = (int)S.Tq;
     p.q = arg(q); p.k = arg(k); p.v = arg(v); p.o = arg(o_out);
     p.m_out = max_out; p.l_out = sum_out;
@@ -1375,12 +1444,22 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (dtype == SDPA_F16)
-        e = sdpa::launch_nsa_fwd_dims<sdpa::F16>(p, (int)D, (int)Dv, st);
-    else
-        e = sdpa::launch_nsa_fwd_dims<sdpa::BF16>(p, (int)D, (int)Dv, st);
-    if (e != hipSuccess) return hip_fail(e, "selected forward launch");
+    // one launch per kMaxSeqArgs sequences (the forward has no workspace for
+    // a sequence table), over those sequences' tokens
+    const int64_t n = (int64_t)S.q0.size();
+    for (int64_t c = 0; c < n; c += sdpa::kMaxSeqArgs) {
+        const int m = (int)std::min<int64_t>(sdpa::kMaxSeqArgs, n - c);
+        fill_seq_chunk(p.seqs, S, c, m);
+        p.t_base = (int)S.q0[c];
+        p.Tq = (int)(S.q0[c + m - 1] + S.lq[c + m - 1] - S.q0[c]);   // tokens of this launch
+        if (p.Tq == 0) continue;
+        hipError_t e;
+        if (dtype == SDPA_F16)
+            e = sdpa::launch_nsa_fwd_dims<sdpa::F16>(p, (int)D, (int)Dv, st);
+        else
+            e = sdpa::launch_nsa_fwd_dims<sdpa::BF16>(p, (int)D, (int)Dv, st);
+        if (e != hipSuccess) return hip_fail(e, "selected forward launch");
+    }
     return SDPA_OK;
 }
 
@@ -1444,7 +1523,8 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     bp.rows = S.Tq * Hq;
     bp.varlen = 1;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    hipError_t e = launch_seqtab(S, reinterpret_cast<int32_t*>(ws + L.seqtab), st);
+    if (e != hipSuccess) return hip_fail(e, "sequence table launch");
     if (dtype == SDPA_F16)
         e = sdpa::launch_nsa_dims<sdpa::F16>(p, bp, (int)D, (int)Dv, st);
     else
@@ -1474,7 +1554,9 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
     fill_index_params(p, S, L, ws, topk, tk_st, tk_sn, tk_sk, Hkv, Hkv, block_size, block_count);
     p.offsets = offsets_out;
     p.entries = entries_out;
-    hipError_t e = sdpa::launch_index(p, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_seqtab(S, reinterpret_cast<int32_t*>(ws + L.seqtab), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sequence table launch");
+    e = sdpa::launch_index(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "index launch");
     return SDPA_OK;
 }

@@ -303,4 +303,5 @@ def test_bwd_selected_valid_without_device():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_fwd_selected_valid_without_device():
     assert fwd_selected_call() == HIP
+    assert fwd_selected_call(cu=[256 * (i + 1) for i in range(70)]) == HIP   # 70 sequences
     assert fwd_selected_call(D=192, Dv=128) == HIP

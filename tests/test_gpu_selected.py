@@ -48,6 +48,24 @@ def test_index_small_exact(lengths, N2, bs, count):
     _check_index(topk, cu, cu, bs)
 
 
+def test_index_many_sequences_exact():
+    """70 sequences: more than the 64 the kernel arguments carry, so the
+    sequence table goes through the workspace."""
+    rng = np.random.default_rng(70)
+    lengths = rng.integers(2, 7, size=70) * 32
+    topk = synth.draw_topk(lengths, 2, 32, 2, config_id=70)
+    cu = np.cumsum(lengths)
+    _check_index(topk, cu, cu, 32)
+
+
+def test_index_long_sequence_exact():
+    """T = 32768 with the NSA workload's recipe (16 blocks of 64 keys)."""
+    lengths = np.array([32768])
+    topk = synth.draw_topk(lengths, 1, 64, 16, config_id=5)
+    cu = np.cumsum(lengths)
+    _check_index(topk, cu, cu, 64)
+
+
 def _run_selected(q, k, v, o, do, stats, topk, cu, bs, scale, mode, det=False):
     dq = torch.full_like(q, float("nan"))
     dk = torch.full_like(k, float("nan"))
@@ -147,3 +165,36 @@ def test_unequal_head_dims_long_sequence():
     dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o, t["do"], stats, topk, cu, bs, scale, 2)
     for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
         assert_rel(to_f64(got), ref, dtype, name)
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_many_sequences(mode):
+    """70 packed sequences (lengths 32..192, some below block_count blocks of
+    keys) through the forward and the backward: more sequences than the kernel
+    arguments hold."""
+    rng = np.random.default_rng(700 + mode)
+    lengths = rng.integers(2, 7, size=70) * 32
+    cu = np.cumsum(lengths)
+    T, G, N2, D, bs, count, dtype = int(cu[-1]), 2, 1, 64, 32, 2, "f16"
+    topk = synth.draw_topk(lengths, N2, bs, count, config_id=71)
+    if mode == 0:
+        starts = np.concatenate([[0], cu[:-1]])
+        for s0, s1 in zip(starts, cu):
+            topk[s0:s1] = rng.integers(0, (s1 - s0) // bs, size=topk[s0:s1].shape)
+    bits = {n: synth.encode(rng.standard_normal(shape), dtype)
+            for n, shape in (("q", (T, G, D)), ("k", (T, N2, D)), ("v", (T, N2, D)), ("do", (T, G, D)))}
+    x = {n: synth.decode(b, dtype) for n, b in bits.items()}
+    t = {n: to_device(b, dtype) for n, b in bits.items()}
+    scale = 1 / math.sqrt(D)
+    f = oracle.selected_forward(x["q"], x["k"], x["v"], topk, cu, cu, bs, scale, mode)
+    g = oracle.selected_backward(x["q"], x["k"], x["v"], x["do"], topk, cu, cu, bs, scale, mode)
+    o, m, l = sb.fwd_selected(t["q"], t["k"], t["v"], _topk_dev(topk), cu, cu, bs, scale, mode)
+    torch.cuda.synchronize()
+    assert_rel(to_f64(o), f["O"], dtype, "O, 70 sequences")
+    assert float(np.max(np.abs(to_f64(m) - f["m"]))) <= 1e-4
+    o_ref = to_device(synth.encode(f["O"], dtype), dtype)
+    stats = (torch.tensor(f["m"], dtype=torch.float32, device="cuda"),
+             torch.tensor(f["l"], dtype=torch.float32, device="cuda"))
+    dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o_ref, t["do"], stats, topk, cu, bs, scale, mode)
+    for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
+        assert_rel(to_f64(got), ref, dtype, f"{name}, 70 sequences")
