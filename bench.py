@@ -224,7 +224,7 @@ def cpu_baseline(wl, host) -> dict:
 # keyed by (kernel, dQ formed without atomics); recomputed S and dP in the
 # query-outer dQ kernels are not counted.
 KERNEL_FLOP_SHARE = {
-    ("bwd_fused8_kernel", True): 1.0,
+    ("bwd_fused8_kernel", True): 1.0, ("bwd_fused2_kernel", True): 1.0,
     ("bwd_main_kernel", False): 1.0, ("bwd_main_kernel", True): 0.8, ("bwd_dq8_kernel", True): 0.2,
     ("nsa_kv_kernel", True): 0.8, ("nsa_dq_kernel", True): 0.2,
 }

@@ -101,7 +101,7 @@ _SIGS = {
 }
 
 
-N_KERNEL_IDS = 10
+N_KERNEL_IDS = 11
 
 
 class KernelTimer:

@@ -407,16 +407,19 @@ struct DqwLds {
     static constexpr int BYTES = 4 * TILE_B;   // K and V, two buffers each
 };
 
-template <class T, int D, bool CAUSAL>
+// NW: wavefronts of the workgroup (4, or 2 in the two-wavefront form); each
+// owns 32 rows, so a workgroup covers 32 * NW rows.
+template <class T, int D, bool CAUSAL, int NW = 4>
 __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     static_assert(D == 64, "wide dQ body: D=64");
-    constexpr int BQ = 128;                 // query rows per workgroup
+    constexpr int NT = 64 * NW;             // threads
+    constexpr int BQ = 32 * NW;             // query rows per workgroup
     constexpr int BK = DqwLds<D>::BK;       // keys per step
     constexpr int KS = D / 16;              // k-steps over the head dimension (32x32x16)
     constexpr int DB = D / 32;              // 32-row blocks of dQ^T
     constexpr int KP = DqwLds<D>::KP;       // row stride of the K and V tiles  [key][d]
     constexpr int TILE = BK * KP;           // elements of one tile
-    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per tile
+    constexpr int CH = BK * D / 8 / NT;   // 16-byte chunks per thread per tile
     uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena);
     uint16_t* Vs0 = Ks0 + 2 * TILE;
 
@@ -445,7 +448,7 @@ __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* 
     int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
-        const int e = tid + kThreads * x;
+        const int e = tid + NT * x;
         const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
         crow[x] = r;
         ccol[x] = cc;
@@ -644,6 +647,282 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, Fu
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two-wavefront form of the D=64 kernel
+// ---------------------------------------------------------------------------
+//
+// Workgroups of two wavefronts, four per CU (still two wavefronts per SIMD).
+// Key-tile item: 64 keys; wavefront kw owns keys 32*kw .. +31 against every
+// 32-row query tile, so each wavefront holds the whole dK/dV of its keys and
+// stores them itself: no cross-wavefront reduction at the end, and the
+// per-step barrier joins two wavefronts instead of four.  Query-tile item: 64
+// rows, wavefront rh owns rows 32*rh .. +31 against 64-key tiles (the wide
+// body with two wavefronts), again with nothing to reduce.  A key-tile
+// wavefront's step (32 keys x 32 rows: S, dP, softmax gradient, dV, dK) is
+// that of the four-wavefront form; an item runs on two SIMDs instead of four,
+// so it takes twice as long, and the form pays only when there are enough
+// items to fill the CUs (see the launch).
+constexpr int k2Threads = 128;
+
+template <int D>
+struct Key2Lds {
+    static constexpr int BR = 32, QP = D + 8, NBUF = 3;
+    static constexpr int TILE_B = BR * QP * 2;
+    static constexpr int OFF_STAT = 2 * NBUF * TILE_B;
+    static constexpr int BYTES = OFF_STAT + 2 * NBUF * BR * 4;
+};
+
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    using L = Key2Lds<D>;
+    constexpr int BC = 64;           // keys per workgroup
+    constexpr int BR = L::BR;        // query rows per step
+    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
+    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
+    constexpr int QP = L::QP;        // row stride of the Q and dO tiles  [row][d]
+    constexpr int TILE = BR * QP;
+    constexpr int CH = BR * D / 8 / k2Threads;   // 16-byte chunks per thread per tile
+    static_assert(CH >= 1, "tile shape");
+    uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena);
+    uint16_t* dOs0 = Qs0 + L::NBUF * TILE;
+    float* lse_s = reinterpret_cast<float*>(arena + L::OFF_STAT);
+    float* dlt_s = lse_s + L::NBUF * BR;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, kw = tid >> 6;
+    const int g = lane >> 5, c = lane & 31;
+    const int b = bx / p.Hkv, hk = bx % p.Hkv;
+    const int G = p.Hq / p.Hkv;
+    int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
+    if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
+    const int j0 = by * BC;
+    if (j0 >= lk) return;
+    const bool full_cols = j0 + BC <= lk;
+
+    const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
+    const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
+    const int my_j = j0 + 32 * kw + c;
+    const bool col_ok = my_j < lk;
+
+    f32x16 dva[DB], dka[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
+
+    // causal: the first query tile holding a row >= j0
+    const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
+    const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
+    const int n_steps = G * per_head;
+
+    const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
+    uint32_t qoff[CH], dooff[CH];
+    int crow[CH], ccol[CH];
+#pragma unroll
+    for (int x = 0; x < CH; ++x) {
+        const int e = tid + k2Threads * x;
+        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+        crow[x] = r;
+        ccol[x] = cc;
+        qoff[x] = r * qss + 2 * cc;
+        dooff[x] = r * doss + 2 * cc;
+    }
+    const uint16_t* const q_seq = p.q.p + b * p.q.sb + (int64_t)q0 * p.q.ss;
+    const uint16_t* const do_seq = p.dout.p + b * p.dout.sb + (int64_t)q0 * p.dout.ss;
+    const int64_t ws_ss = p.varlen ? p.Hq : 1;
+    const int64_t q_step = BR * p.q.ss, do_step = BR * p.dout.ss, st_step = BR * ws_ss;
+    int ld_h = hk * G, ld_i0 = i_begin;
+    const uint16_t *ld_q, *ld_do;
+    const float *ld_sa, *ld_sb;
+    auto seek = [&]() {
+        ld_q = q_seq + ld_h * p.q.sh + (int64_t)ld_i0 * p.q.ss;
+        ld_do = do_seq + ld_h * p.dout.sh + (int64_t)ld_i0 * p.dout.ss;
+        const int64_t ws = p.varlen ? (int64_t)(q0 + ld_i0) * p.Hq + ld_h
+                                    : ((int64_t)b * p.Hq + ld_h) * p.Sq + ld_i0;
+        ld_sa = p.lse2 + ws;
+        ld_sb = p.delta + ws;
+    };
+    auto advance = [&]() {
+        ld_i0 += BR;
+        if (ld_i0 >= lq) {
+            ld_i0 = i_begin;
+            ++ld_h;
+            seek();
+        } else {
+            ld_q += q_step; ld_do += do_step; ld_sa += st_step; ld_sb += st_step;
+        }
+    };
+    seek();
+
+    // Unconditional tile loads, as in the four-wavefront body: rows past the
+    // end re-read the last row and get LSE = +inf when stored.
+    struct TileRegs { u32x4 q[CH], d[CH]; float sa, sb; };
+    const int srow = tid & (BR - 1);
+    const uint32_t sss = 4u * (uint32_t)ws_ss;
+    const uint32_t srow_off = srow * sss;
+    auto load_tile = [&](TileRegs& t) {
+        uint32_t oq[CH], odo[CH], so = srow_off;
+        if (ld_i0 + BR <= lq) {
+#pragma unroll
+            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
+        } else {
+            const int last = lq - 1 - ld_i0;
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                const uint32_t r = min(crow[x], last);
+                oq[x] = r * qss + 2 * ccol[x];
+                odo[x] = r * doss + 2 * ccol[x];
+            }
+            so = (uint32_t)min(srow, last) * sss;
+        }
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            t.q[x] = ld16_at(ld_q, oq[x]);
+            t.d[x] = ld16_at(ld_do, odo[x]);
+        }
+        t.sa = ldf_at(ld_sa, so);
+        t.sb = ldf_at(ld_sb, so);
+    };
+    auto store_tile = [&](const TileRegs& t, int buf, int i0) {
+        uint16_t* Qd = Qs0 + buf * TILE;
+        uint16_t* dOd = dOs0 + buf * TILE;
+#pragma unroll
+        for (int x = 0; x < CH; ++x) {
+            st16(&Qd[crow[x] * QP + ccol[x]], t.q[x]);
+            st16(&dOd[crow[x] * QP + ccol[x]], t.d[x]);
+        }
+        if (tid < BR) {
+            const bool ok = i0 + tid < lq;
+            lse_s[buf * BR + tid] = ok ? t.sa : INFINITY;
+            dlt_s[buf * BR + tid] = ok ? -t.sb : 0.f;
+        }
+    };
+    u32x4 kreg[KS], vreg[KS];
+    auto s_dp = [&](int buf, f32x16& sa, f32x16& pa) {
+        const uint16_t* Qb = Qs0 + buf * TILE;
+        const uint16_t* dOb = dOs0 + buf * TILE;
+        sa = zero16();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf * BR + 8 * q + 4 * g]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sa = T::mma(ld16(&Qb[c * QP + 16 * s + 8 * g]), kreg[s], sa);
+            pa = T::mma(ld16(&dOb[c * QP + 16 * s + 8 * g]), vreg[s], pa);
+        }
+    };
+
+    int i0_k = i_begin, i0_k1 = i_begin;
+    TileRegs tr0, tr1;
+    if (n_steps > 0) { load_tile(tr0); i0_k = ld_i0; advance(); }
+    if (n_steps > 1) { load_tile(tr1); i0_k1 = ld_i0; advance(); }
+    {
+        const int jr = min(my_j, lk - 1);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kreg[s] = ld16(kbase + (int64_t)jr * p.k.ss + 16 * s + 8 * g);
+            vreg[s] = ld16(vbase + (int64_t)jr * p.v.ss + 16 * s + 8 * g);
+        }
+    }
+    if (n_steps > 0) store_tile(tr0, 0, i0_k);
+    if (n_steps > 1) store_tile(tr1, 1, i0_k1);
+    wait_all_memory();
+    __syncthreads();
+
+    // first kept row offset of this lane's key, relative to 8q+4g of a tile
+    const int t_key = col_ok ? (CAUSAL ? my_j - 4 * g : INT_MIN / 2) : INT_MAX / 2;
+    // a wavefront whose keys all follow every row of a tile has P = 0 there
+    const int w_key0 = j0 + 32 * kw;
+
+    f32x16 sa, pa;
+    if (n_steps > 0) s_dp(0, sa, pa);
+    int bk = 0, bk1 = 1, bk2 = 2;
+    for (int k = 0; k < n_steps; ++k) {
+        const bool has2 = k + 2 < n_steps;
+        int i0_k2 = i0_k1;
+        TileRegs trn;
+        if (has2) { load_tile(trn); i0_k2 = ld_i0; advance(); }
+
+        const bool dead = CAUSAL && i0_k + BR <= w_key0;
+        const bool masked = (CAUSAL && i0_k < j0 + BC) || !full_cols;
+        u32x4 bP[2], bS[2];
+        if (masked) {
+            softmax_grad_tile_nd<true>(sa, pa, &lse_s[bk * BR], p.scale_log2, g, t_key - i0_k);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
+            s_dp(bk1, sa, pa);
+        } else {
+            softmax_grad_tile_nd<false>(sa, pa, &lse_s[bk * BR], p.scale_log2, g, 0);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
+            s_dp(bk1, sa, pa);
+        }
+
+        const uint16_t* Qb = Qs0 + bk * TILE;
+        const uint16_t* dOb = dOs0 + bk * TILE;
+        if (!dead) {
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dva[db] = T::mma(ld_tr<true>(dOb, QP, 16 * hh, db * 32, lane), bP[hh], dva[db]);
+                    dka[db] = T::mma(ld_tr<true>(Qb, QP, 16 * hh, db * 32, lane), bS[hh], dka[db]);
+                }
+            __builtin_amdgcn_s_setprio(0);
+        }
+        if (has2) store_tile(trn, bk2, i0_k2);
+        __syncthreads();
+        const int t = bk; bk = bk1; bk1 = bk2; bk2 = t;
+        i0_k = i0_k1;
+        i0_k1 = i0_k2;
+    }
+
+    if (!col_ok) return;
+    const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
+    const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = db * 32 + 8 * q + 4 * g;
+            st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
+                        dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+            st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
+                        dva[db][4 * q + 3]);
+        }
+}
+
+// Query-tile items of the two-wavefront form: the wide body with two
+// wavefronts, 64 rows against 64-key tiles.
+template <class T, int D, bool CAUSAL>
+__device__ __forceinline__ void fused2_dq(const BwdParams& p, unsigned char* arena, int bx, int by) {
+    bwd_dqw_body<T, D, CAUSAL, 2>(p, arena, bx, by);
+}
+
+// The two-wavefront launch: key-tile items and 64-row query-tile items in one
+// grid, ordered as the four-wavefront kernel orders its 64-row form.
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(k2Threads, 2) void bwd_fused2_kernel(BwdParams p, Fused8Map m) {
+    constexpr int A = Key2Lds<D>::BYTES > DqwLds<D>::BYTES ? Key2Lds<D>::BYTES : DqwLds<D>::BYTES;
+    __shared__ __align__(16) unsigned char arena[A];
+    const int id = blockIdx.x;
+    if (m.alternate) {
+        const int seg = id / m.main_x, within = id % m.main_x;
+        if (!(seg & 1)) bwd_key2_body<T, D, CAUSAL>(p, arena, within, seg >> 1);
+        else fused2_dq<T, D, CAUSAL>(p, arena, m.dq_x - 1 - (seg >> 1), within);
+        return;
+    }
+    const int n_main = m.main_x * m.main_y;
+    if (id < n_main) {
+        bwd_key2_body<T, D, CAUSAL>(p, arena, id % m.main_x, id / m.main_x);
+    } else {
+        const int r = id - n_main;
+        fused2_dq<T, D, CAUSAL>(p, arena, m.dq_x - 1 - r / m.dq_y, r % m.dq_y);
+    }
+}
+
 // Workgroup slots of the D=64 fused kernel on the current device: two per
 // compute unit (0 if the count is unknown).
 static int fused8_slots() {
@@ -667,6 +946,27 @@ template <class T, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
     static_assert(D == 64, "the D=64 launch");
     if (!L.deterministic) return launch_bwd_d64_atomic(p, L, st);   // dQ mode 2: fp32 atomics
+    if (CAUSAL) {
+        // Two-wavefront form for causal problems of at most 1536 keys with at
+        // least 1.5 items per workgroup slot (four per CU).  Measured against
+        // the four-wavefront form (D=64, fp16, same box): B4 H12 S1024
+        // 43.6 -> 41.7 us, B8 H12 S1024 77.5 -> 75.9 us, B4 H16 S1536
+        // 100.4 -> 98.4 us; B2 H16 S2048 even; longer keys (B4 H12 S2048
+        // +2.5 %, B1 H16 S4096 +6 %) and fewer items (B2 H12 S1024 +28 %)
+        // lose, since an item then runs on two SIMDs instead of four.
+        const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
+        const int qy = L.n_seq * p.Hq;
+        const int slots2 = 2 * fused8_slots();
+        const long n2 = (long)mx * my + (long)L.max_q_tiles64 * qy;
+        if (slots2 > 0 && my <= 24 && 2 * n2 >= 3L * slots2) {
+            if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
+            Fused8Map m{mx, my, L.max_q_tiles64, qy, 0};
+            m.alternate = (mx == qy && my == m.dq_x) ? 1 : 0;
+            PROF_LAUNCH(KID_BWD_FUSED2, st, (bwd_fused2_kernel<T, D, CAUSAL>), dim3((unsigned)n2), dim3(k2Threads), 0,
+                        st, p, m);
+            return hipGetLastError();
+        }
+    }
     {
         // The row pass, then one launch of both bodies; dQ is computed without
         // atomics, so the result is deterministic (dQ modes 0 and 1).

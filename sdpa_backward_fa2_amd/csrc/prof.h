@@ -25,7 +25,8 @@ enum KernelId {
     KID_NSA_DQ = 7,
     KID_BWD_FUSED = 8,
     KID_NSA_KV_REDUCE = 9,
-    KID_COUNT = 10
+    KID_BWD_FUSED2 = 10,
+    KID_COUNT = 11
 };
 
 bool prof_enabled();

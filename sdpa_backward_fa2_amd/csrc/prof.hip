@@ -91,7 +91,7 @@ const char* sdpa_kernel_name(int kernel_id) {
     static const char* names[sdpa::KID_COUNT] = {
         "fwd_kernel", "bwd_pre_kernel", "bwd_main_kernel", "bwd_dq_convert_kernel",
         "bwd_dq8_kernel", "nsa_index_kernels", "nsa_kv_kernel", "nsa_dq_kernel",
-        "bwd_fused8_kernel", "nsa_kv_reduce_kernel"};
+        "bwd_fused8_kernel", "nsa_kv_reduce_kernel", "bwd_fused2_kernel"};
     if (kernel_id < 0 || kernel_id >= sdpa::KID_COUNT) return "";
     return names[kernel_id];
 }
