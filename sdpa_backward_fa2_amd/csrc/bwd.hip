@@ -659,14 +659,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_fused8_kernel(BwdParams p, Fu
 // rows, wavefront rh owns rows 32*rh .. +31 against 64-key tiles (the wide
 // body with two wavefronts), again with nothing to reduce.  A key-tile
 // wavefront's step (32 keys x 32 rows: S, dP, softmax gradient, dV, dK) is
-// that of the four-wavefront form; an item runs on two SIMDs instead of four,
-// so it takes twice as long, and the form pays only when there are enough
-// items to fill the CUs (see the launch).
+// twice that of the four-wavefront form per wavefront; an item runs on two
+// SIMDs instead of four, so it takes twice as long, and the form pays only
+// when there are enough items to fill the CUs (see the launch).
 constexpr int k2Threads = 128;
 
+// Key-tile item of the two-wavefront form: 64 keys, wavefront kw owns keys
+// 32*kw .. +31 against every 64-row query tile, as two 32-row blocks per step
+// (S and dP of both, then each block's softmax gradient and dV/dK products,
+// so the matrix cores work on one block while the vector ALUs run the other's
+// softmax).  Q/dO tiles are double-buffered in LDS; the next tile is loaded
+// into registers during the step.  Against 32-row steps with the next tile's
+// S and dP computed during this tile's softmax: GPT-2 shape 41.4 -> 40.1 us.
 template <int D>
 struct Key2Lds {
-    static constexpr int BR = 32, QP = D + 8, NBUF = 3;
+    static constexpr int BR = 64, QP = D + 8, NBUF = 2;
     static constexpr int TILE_B = BR * QP * 2;
     static constexpr int OFF_STAT = 2 * NBUF * TILE_B;
     static constexpr int BYTES = OFF_STAT + 2 * NBUF * BR * 4;
@@ -675,14 +682,8 @@ struct Key2Lds {
 template <class T, int D, bool CAUSAL>
 __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     using L = Key2Lds<D>;
-    constexpr int BC = 64;           // keys per workgroup
-    constexpr int BR = L::BR;        // query rows per step
-    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
-    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int QP = L::QP;        // row stride of the Q and dO tiles  [row][d]
-    constexpr int TILE = BR * QP;
-    constexpr int CH = BR * D / 8 / k2Threads;   // 16-byte chunks per thread per tile
-    static_assert(CH >= 1, "tile shape");
+    constexpr int BC = 64, BR = L::BR, KS = D / 16, DB = D / 32, QP = L::QP, TILE = BR * QP;
+    constexpr int CH = BR * D / 8 / k2Threads;
     uint16_t* Qs0 = reinterpret_cast<uint16_t*>(arena);
     uint16_t* dOs0 = Qs0 + L::NBUF * TILE;
     float* lse_s = reinterpret_cast<float*>(arena + L::OFF_STAT);
@@ -698,7 +699,6 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
     const int j0 = by * BC;
     if (j0 >= lk) return;
     const bool full_cols = j0 + BC <= lk;
-
     const uint16_t* kbase = p.k.p + b * p.k.sb + hk * p.k.sh + (int64_t)k0 * p.k.ss;
     const uint16_t* vbase = p.v.p + b * p.v.sb + hk * p.v.sh + (int64_t)k0 * p.v.ss;
     const int my_j = j0 + 32 * kw + c;
@@ -708,22 +708,17 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
 
-    // causal: the first query tile holding a row >= j0
-    const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
+    const int i_begin = CAUSAL ? j0 : 0;     // j0 is a multiple of the 64-row tile
     const int per_head = lq > i_begin ? (lq - i_begin + BR - 1) / BR : 0;
     const int n_steps = G * per_head;
 
     const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
-    uint32_t qoff[CH], dooff[CH];
     int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
         const int e = tid + k2Threads * x;
-        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-        crow[x] = r;
-        ccol[x] = cc;
-        qoff[x] = r * qss + 2 * cc;
-        dooff[x] = r * doss + 2 * cc;
+        crow[x] = e / (D / 8);
+        ccol[x] = (e % (D / 8)) * 8;
     }
     const uint16_t* const q_seq = p.q.p + b * p.q.sb + (int64_t)q0 * p.q.ss;
     const uint16_t* const do_seq = p.dout.p + b * p.dout.sb + (int64_t)q0 * p.dout.ss;
@@ -752,32 +747,18 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
     };
     seek();
 
-    // Unconditional tile loads, as in the four-wavefront body: rows past the
-    // end re-read the last row and get LSE = +inf when stored.
     struct TileRegs { u32x4 q[CH], d[CH]; float sa, sb; };
     const int srow = tid & (BR - 1);
     const uint32_t sss = 4u * (uint32_t)ws_ss;
-    const uint32_t srow_off = srow * sss;
     auto load_tile = [&](TileRegs& t) {
-        uint32_t oq[CH], odo[CH], so = srow_off;
-        if (ld_i0 + BR <= lq) {
-#pragma unroll
-            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
-        } else {
-            const int last = lq - 1 - ld_i0;
-#pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                const uint32_t r = min(crow[x], last);
-                oq[x] = r * qss + 2 * ccol[x];
-                odo[x] = r * doss + 2 * ccol[x];
-            }
-            so = (uint32_t)min(srow, last) * sss;
-        }
+        const int last = lq - 1 - ld_i0;     // rows past the end re-read the last row
 #pragma unroll
         for (int x = 0; x < CH; ++x) {
-            t.q[x] = ld16_at(ld_q, oq[x]);
-            t.d[x] = ld16_at(ld_do, odo[x]);
+            const uint32_t r = min(crow[x], last);
+            t.q[x] = ld16_at(ld_q, r * qss + 2 * ccol[x]);
+            t.d[x] = ld16_at(ld_do, r * doss + 2 * ccol[x]);
         }
+        const uint32_t so = (uint32_t)min(srow, last) * sss;
         t.sa = ldf_at(ld_sa, so);
         t.sb = ldf_at(ld_sb, so);
     };
@@ -796,87 +777,72 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
         }
     };
     u32x4 kreg[KS], vreg[KS];
-    auto s_dp = [&](int buf, f32x16& sa, f32x16& pa) {
-        const uint16_t* Qb = Qs0 + buf * TILE;
-        const uint16_t* dOb = dOs0 + buf * TILE;
-        sa = zero16();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf * BR + 8 * q + 4 * g]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            sa = T::mma(ld16(&Qb[c * QP + 16 * s + 8 * g]), kreg[s], sa);
-            pa = T::mma(ld16(&dOb[c * QP + 16 * s + 8 * g]), vreg[s], pa);
-        }
-    };
 
-    int i0_k = i_begin, i0_k1 = i_begin;
-    TileRegs tr0, tr1;
-    if (n_steps > 0) { load_tile(tr0); i0_k = ld_i0; advance(); }
-    if (n_steps > 1) { load_tile(tr1); i0_k1 = ld_i0; advance(); }
+    int i0_k = i_begin;
     {
+        TileRegs tr0;
+        if (n_steps > 0) { load_tile(tr0); i0_k = ld_i0; advance(); }
         const int jr = min(my_j, lk - 1);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             kreg[s] = ld16(kbase + (int64_t)jr * p.k.ss + 16 * s + 8 * g);
             vreg[s] = ld16(vbase + (int64_t)jr * p.v.ss + 16 * s + 8 * g);
         }
+        if (n_steps > 0) store_tile(tr0, 0, i0_k);
     }
-    if (n_steps > 0) store_tile(tr0, 0, i0_k);
-    if (n_steps > 1) store_tile(tr1, 1, i0_k1);
     wait_all_memory();
     __syncthreads();
 
-    // first kept row offset of this lane's key, relative to 8q+4g of a tile
     const int t_key = col_ok ? (CAUSAL ? my_j - 4 * g : INT_MIN / 2) : INT_MAX / 2;
-    // a wavefront whose keys all follow every row of a tile has P = 0 there
-    const int w_key0 = j0 + 32 * kw;
-
-    f32x16 sa, pa;
-    if (n_steps > 0) s_dp(0, sa, pa);
-    int bk = 0, bk1 = 1, bk2 = 2;
     for (int k = 0; k < n_steps; ++k) {
-        const bool has2 = k + 2 < n_steps;
-        int i0_k2 = i0_k1;
+        const int buf = k & 1;
+        const bool has1 = k + 1 < n_steps;
+        int i0_k1 = i0_k;
         TileRegs trn;
-        if (has2) { load_tile(trn); i0_k2 = ld_i0; advance(); }
-
-        const bool dead = CAUSAL && i0_k + BR <= w_key0;
-        const bool masked = (CAUSAL && i0_k < j0 + BC) || !full_cols;
-        u32x4 bP[2], bS[2];
-        if (masked) {
-            softmax_grad_tile_nd<true>(sa, pa, &lse_s[bk * BR], p.scale_log2, g, t_key - i0_k);
+        if (has1) { load_tile(trn); i0_k1 = ld_i0; advance(); }
+        const uint16_t* Qb = Qs0 + buf * TILE;
+        const uint16_t* dOb = dOs0 + buf * TILE;
+        // S^T and dP^T - Delta of both 32-row blocks
+        f32x16 sab[2], pab[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
-            s_dp(bk1, sa, pa);
-        } else {
-            softmax_grad_tile_nd<false>(sa, pa, &lse_s[bk * BR], p.scale_log2, g, 0);
+        for (int rb = 0; rb < 2; ++rb) {
+            sab[rb] = zero16();
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) { bP[hh] = acc_to_operand<T>(sa, hh); bS[hh] = acc_to_operand<T>(pa, hh); }
-            s_dp(bk1, sa, pa);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 nd = *reinterpret_cast<const f32x4*>(&dlt_s[buf * BR + 32 * rb + 8 * q + 4 * g]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pab[rb][4 * q + r] = nd[r];
+            }
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                sab[rb] = T::mma(ld16(&Qb[(32 * rb + c) * QP + 16 * s + 8 * g]), kreg[s], sab[rb]);
+                pab[rb] = T::mma(ld16(&dOb[(32 * rb + c) * QP + 16 * s + 8 * g]), vreg[s], pab[rb]);
+            }
         }
-
-        const uint16_t* Qb = Qs0 + bk * TILE;
-        const uint16_t* dOb = dOs0 + bk * TILE;
-        if (!dead) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            const int r0 = i0_k + 32 * rb;
+            const bool masked = (CAUSAL && r0 < j0 + BC) || !full_cols;
+            if (masked)
+                softmax_grad_tile_nd<true>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, t_key - r0);
+            else
+                softmax_grad_tile_nd<false>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, 0);
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+            for (int hh = 0; hh < 2; ++hh) {
+                const u32x4 bP = acc_to_operand<T>(sab[rb], hh);
+                const u32x4 bS = acc_to_operand<T>(pab[rb], hh);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    dva[db] = T::mma(ld_tr<true>(dOb, QP, 16 * hh, db * 32, lane), bP[hh], dva[db]);
-                    dka[db] = T::mma(ld_tr<true>(Qb, QP, 16 * hh, db * 32, lane), bS[hh], dka[db]);
+                    dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rb + 16 * hh, db * 32, lane), bP, dva[db]);
+                    dka[db] = T::mma(ld_tr<true>(Qb, QP, 32 * rb + 16 * hh, db * 32, lane), bS, dka[db]);
                 }
+            }
             __builtin_amdgcn_s_setprio(0);
         }
-        if (has2) store_tile(trn, bk2, i0_k2);
+        if (has1) store_tile(trn, buf ^ 1, i0_k1);
         __syncthreads();
-        const int t = bk; bk = bk1; bk1 = bk2; bk2 = t;
         i0_k = i0_k1;
-        i0_k1 = i0_k2;
     }
 
     if (!col_ok) return;
@@ -947,18 +913,19 @@ static hipError_t launch_bwd_t(const BwdParams& p, const BwdLaunch& L, hipStream
     static_assert(D == 64, "the D=64 launch");
     if (!L.deterministic) return launch_bwd_d64_atomic(p, L, st);   // dQ mode 2: fp32 atomics
     if (CAUSAL) {
-        // Two-wavefront form for causal problems of at most 1536 keys with at
-        // least 1.5 items per workgroup slot (four per CU).  Measured against
+        // Two-wavefront form for causal problems of at most 2048 keys with at
+        // least one item per workgroup slot (four per CU).  Measured against
         // the four-wavefront form (D=64, fp16, same box): B4 H12 S1024
-        // 43.6 -> 41.7 us, B8 H12 S1024 77.5 -> 75.9 us, B4 H16 S1536
-        // 100.4 -> 98.4 us; B2 H16 S2048 even; longer keys (B4 H12 S2048
-        // +2.5 %, B1 H16 S4096 +6 %) and fewer items (B2 H12 S1024 +28 %)
-        // lose, since an item then runs on two SIMDs instead of four.
+        // 43.8 -> 40.6 us, B2 H16 S2048 84.0 -> 80.9, B4 H12 S2048
+        // 124.3 -> 121.8, B8 H8 S512 23.6 -> 22.8; B1 H16 S4096 even (+1 %);
+        // with fewer items it loses (B2 H12 S1024 +17 %, B1 H12 S1024 +30 %,
+        // B2 H8 S512 +23 %, B1 H2 S8192 +50 %): an item runs on two SIMDs
+        // instead of four, so the longest items set the time.
         const int mx = L.n_seq * p.Hkv, my = L.max_kv_tiles64;
         const int qy = L.n_seq * p.Hq;
         const int slots2 = 2 * fused8_slots();
         const long n2 = (long)mx * my + (long)L.max_q_tiles64 * qy;
-        if (slots2 > 0 && my <= 24 && 2 * n2 >= 3L * slots2) {
+        if (slots2 > 0 && my <= 32 && n2 >= slots2) {
             if (L.phase & BwdLaunch::kFirst) launch_pre<T, D>(p, 0, st);
             Fused8Map m{mx, my, L.max_q_tiles64, qy, 0};
             m.alternate = (mx == qy && my == m.dq_x) ? 1 : 0;
