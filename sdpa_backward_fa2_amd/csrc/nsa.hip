@@ -10,11 +10,15 @@
 // stored in the input type or fp32.
 //
 // Kernels, all on the caller's stream:
-//   nsa_index_kernel<false>  per (KV head, KV block): how many (token, slot)
-//                            choices name the block (ballot counts, no atomics)
-//   nsa_scan_kernel          CSR offsets of those lists and a table of work
+//   nsa_rank_kernel          per (token tile, KV head): each (token, slot)
+//                            entry's rank within its tile and block, and the
+//                            tile's per-block totals (LDS counters, no atomics)
+//   nsa_hist_scan_kernel     per (KV block, KV head): prefixes of those totals
+//                            over the tiles, and the block's entry count
+//   nsa_scan_kernel          CSR offsets of the lists and a table of work
 //                            pieces (at most `chunk` entries of one block each)
-//   nsa_index_kernel<true>   fills each block's list in (token, slot) order
+//   nsa_scatter_kernel       stores each entry in its block's list, which so
+//                            comes out in (token, slot) order
 //   bwd_pre_kernel           Delta and log2-LSE per (token, head)  [bwd.hip]
 //   nsa_kv_kernel            per piece and 64-key half of its block: dK, dV
 //                            over the piece's tokens (G heads per token form
@@ -47,7 +51,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct NsaParams {
     const int32_t* topk;
     int64_t tk_st, tk_sn, tk_sk;
-    int tk_vec4;          // slots contiguous, count % 4 == 0, 16-byte aligned rows
     int count, bs, N2, NB, G, Hq;
     int g_mul;            // ceil(2^16 / G): r / G == (r * g_mul) >> 16 for 0 <= r < 256
     int chunk;            // entries per work piece
@@ -58,6 +61,9 @@ struct NsaParams {
     int32_t* entries;     // [Tq*N2*count]
     int32_t* pstart;      // [N2*NB + 1] first piece of each bucket
     int32_t* pieces;      // [max_pieces][3]: bucket, first entry, end entry
+    int tt, n_tiles;      // index build: tokens per tile, tiles (ceil(Tq / tt))
+    int32_t* hist;        // [N2][NB][n_tiles] per-tile block totals, then their prefixes
+    int32_t* rank;        // [N2][Tq * count] entry ranks within their tile and block
     // backward
     TensorArg q, k, v, dout, dq, dk, dv;
     const float* lse2;
@@ -148,133 +154,142 @@ __global__ __launch_bounds__(64) void nsa_seqtab_kernel(SeqTable chunk, int32_t*
 }
 
 // ---------------------------------------------------------------------------
-// Inverse index
+// Inverse index: a stable counting sort of the (token, slot) entries by block
 // ---------------------------------------------------------------------------
+//
+// The entries e = t * count + slot of KV head h2 are cut into tiles of p.tt
+// consecutive tokens.  nsa_rank_kernel (one wavefront per tile and head)
+// walks its tile in entry order, 64 entries a step, with one LDS counter per
+// block: each entry's rank among the tile's earlier entries naming the same
+// block is the counter plus the number of lower lanes of its step that name
+// it (a match mask built from one ballot per bit of the block number).  It
+// writes the ranks and the tile's per-block totals hist[h2][g][tile].
+// nsa_hist_scan_kernel turns each block's row of tile totals into exclusive
+// prefixes and the block's count; nsa_scan_kernel makes the CSR offsets and
+// the work pieces; nsa_scatter_kernel stores each entry at offset + tile
+// prefix + rank.  Every list comes out in (token, slot) order without
+// atomics, in work linear in the entries plus blocks x tiles.
 
-// One workgroup of 16 wavefronts per (KV block, KV head).  The sequence's
-// (token, slot) entries are split into 16 contiguous spans, one per wavefront;
-// a wavefront walks its span 64 entries at a time with coalesced loads and a
-// ballot.  The counting pass writes the block's total; the filling pass
-// counts again, takes the wavefronts' exclusive prefix and writes each match
-// at its rank, so every list comes out in (token, slot) order without atomics.
-template <bool FILL>
-__global__ __launch_bounds__(1024) void nsa_index_kernel(NsaParams p) {
-    __shared__ int wave_n[16];
-    const int g = blockIdx.x, h2 = blockIdx.y;
-    const int bucket = h2 * p.NB + g;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int s = seq_of_block(p.seqs, g * p.bs);
-    if (s < 0) {
-        if (!FILL && tid == 0) p.counts[bucket] = 0;
-        return;
+constexpr int kIdxWin = 4096;   // block counters per pass of the rank kernel
+
+// The global block named by entry c + lane of a tile step (e_end: the tile's
+// end), or -1 past the tile's end or when the value is not a block of the
+// token's sequence.  s_cur (uniform) is moved past the sequences that end at
+// or before the step's first token; sequences partition the packed tokens.
+__device__ __forceinline__ int step_block(const NsaParams& p, const int32_t* tk, int c, int e_end, int lane,
+                                          int& s_cur) {
+    const int e = min(c + lane, e_end - 1);
+    const int t = (int)((uint32_t)e / (uint32_t)p.count);
+    const int slot = e - t * p.count;
+    const int v = tk[(int64_t)t * p.tk_st + (int64_t)slot * p.tk_sk];
+    const int t_first = (int)((uint32_t)c / (uint32_t)p.count);
+    const int t_last = (int)((uint32_t)min(c + 63, e_end - 1) / (uint32_t)p.count);
+    while (s_cur + 1 < p.seqs.n) {
+        const SeqRow r = seq_row(p.seqs, s_cur);
+        if (r.q0 + r.lq > t_first) break;
+        ++s_cur;
     }
-    const SeqRow sr = seq_row(p.seqs, s);
-    const int gl = g - sr.k0 / p.bs;             // block index within its sequence
-    const int64_t e0 = (int64_t)sr.q0 * p.count;
-    const int64_t e1 = (int64_t)(sr.q0 + sr.lq) * p.count;
+    int g = -1;
+    for (int s = s_cur; s < p.seqs.n; ++s) {
+        const SeqRow r = seq_row(p.seqs, s);
+        if (r.q0 > t_last) break;
+        if (t >= r.q0 && t < r.q0 + r.lq && v >= 0 && v < r.lk / p.bs) g = r.k0 / p.bs + v;
+    }
+    return c + lane < e_end ? g : -1;
+}
+
+__global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
+    __shared__ int cnt[kIdxWin];
+    const int tile = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
+    const int t0 = tile * p.tt, t1 = min(p.Tq, t0 + p.tt);
+    const int e_begin = t0 * p.count, e_end = t1 * p.count;
+    const int sa = seq_of_token(p.seqs, t0), sb = seq_of_token(p.seqs, t1 - 1);
+    // the blocks of the sequences the tile touches
+    const int gA = seq_row(p.seqs, sa).k0 / p.bs;
+    const SeqRow rb = seq_row(p.seqs, sb);
+    const int gB = (rb.k0 + rb.lk) / p.bs;
     const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
+    int32_t* rank = p.rank + (int64_t)h2 * p.Tq * p.count;
+    int32_t* hist = p.hist + (int64_t)h2 * p.NB * p.n_tiles;
     const unsigned long long below = (1ull << lane) - 1ull;
-    if (p.tk_vec4) {
-        // Four consecutive slots of one token per lane and 16-byte load (the
-        // slots of a token are contiguous and count is a multiple of 4); a
-        // wavefront's span is a multiple of 256 entries.
-        const int64_t span = ((e1 - e0 + 15) / 16 + 255) / 256 * 256;
-        const int64_t a = e0 + w * span;
-        const int64_t b = min(a + span, e1);
-        const int cnt4 = p.count / 4;
-        auto hits = [&](int64_t c) -> int {   // match bits of entries c .. c+3
-            if (c >= b) return 0;
-            const int64_t t = (int64_t)((uint32_t)(c >> 2) / (uint32_t)cnt4);
-            const int slot = (int)(c - t * p.count);
-            const i32x4 v = *reinterpret_cast<const i32x4*>(tk + t * p.tk_st + slot);
-            return (v[0] == gl) | ((v[1] == gl) << 1) | ((v[2] == gl) << 2) | ((v[3] == gl) << 3);
-        };
-        int n = 0;
-        for (int64_t c = a; c < b; c += 1024) {
-            int m[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) m[u] = hits(c + 256 * u + 4 * lane);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) n += __popc(m[u]);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o);
-        if (lane == 0) wave_n[w] = n;
-        __syncthreads();
-        if (!FILL) {
-            if (tid == 0) {
-                int tot = 0;
-                for (int i = 0; i < 16; ++i) tot += wave_n[i];
-                p.counts[bucket] = tot;
+    for (int w0 = gA; w0 < gB; w0 += kIdxWin) {
+        const int nw = min(gB - w0, kIdxWin);
+        int bits = 0;
+        while ((1 << bits) < nw) ++bits;
+        for (int i = lane; i < nw; i += 64) cnt[i] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        int s_cur = sa;
+        for (int c = e_begin; c < e_end; c += 64) {
+            const int g = step_block(p, tk, c, e_end, lane, s_cur);
+            const int key = g - w0;
+            const bool mine = g >= w0 && key < nw;
+            unsigned long long m = __ballot(mine);
+            for (int b = 0; b < bits; ++b) {
+                const bool on = (key >> b) & 1;
+                const unsigned long long hb = __ballot(mine && on);
+                m &= on ? hb : ~hb;
             }
-            return;
-        }
-        int base = p.offsets[bucket];
-        for (int i = 0; i < w; ++i) base += wave_n[i];
-        for (int64_t c = a; c < b; c += 1024) {
-            int m[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) m[u] = hits(c + 256 * u + 4 * lane);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                // exclusive prefix of the lanes' match counts from the bits of
-                // their 3-bit counts
-                const int k = __popc(m[u]);
-                const unsigned long long b0 = __ballot(k & 1), b1 = __ballot(k & 2), b2 = __ballot(k & 4);
-                int r = base + __popcll(b0 & below) + 2 * __popcll(b1 & below) + 4 * __popcll(b2 & below);
-                const int64_t e = c + 256 * u + 4 * lane;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (m[u] & (1 << q)) p.entries[r++] = (int32_t)(e + q);
-                base += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+            // one wavefront: its LDS reads and writes take effect in program order
+            if (mine) {
+                const int old = cnt[key];
+                const int before = __popcll(m & below);
+                if (before == 0) cnt[key] = old + __popcll(m);
+                rank[c + lane] = old + before;
             }
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         }
+        for (int i = lane; i < nw; i += 64) hist[(int64_t)(w0 + i) * p.n_tiles + tile] = cnt[i];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+}
+
+// One wavefront per (block, KV head): exclusive prefixes over the tiles of the
+// block's sequence, in place, and the block's entry count.
+__global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
+    const int g = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
+    const int bucket = h2 * p.NB + g;
+    const int s = seq_of_block(p.seqs, g * p.bs);
+    const SeqRow r = seq_row(p.seqs, s < 0 ? 0 : s);
+    if (s < 0 || r.lq == 0) {
+        if (lane == 0) p.counts[bucket] = 0;
         return;
     }
-    // General strides: one entry per lane, eight chunks in flight.
-    const int64_t span = ((e1 - e0 + 15) / 16 + 63) / 64 * 64;
-    const int64_t a = e0 + w * span;
-    const int64_t b = min(a + span, e1);
-    const double inv_count = 1.0 / p.count;
-    auto match = [&](int64_t e) -> bool {
-        if (e >= b) return false;
-        // t = e / count through a double reciprocal, corrected to the exact quotient
-        int64_t t = (int64_t)((double)e * inv_count);
-        t += (t + 1) * p.count <= e;
-        t -= t * p.count > e;
-        const int64_t slot = e - t * p.count;
-        return tk[t * p.tk_st + slot * p.tk_sk] == gl;
-    };
-    int n = 0;
-    for (int64_t c = a; c < b; c += 512) {
-        bool m[8];
+    const int ta = r.q0 / p.tt, tb = (r.q0 + r.lq - 1) / p.tt + 1;
+    int32_t* h = p.hist + (int64_t)bucket * p.n_tiles;
+    // each lane takes a run of consecutive tiles
+    const int per = (tb - ta + 63) / 64;
+    const int a = min(tb, ta + lane * per), b = min(tb, a + per);
+    int sum = 0;
+    for (int i = a; i < b; ++i) sum += h[i];
+    int x = sum;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) m[u] = match(c + 64 * u + lane);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) n += __popcll(__ballot(m[u]));
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
     }
-    if (lane == 0) wave_n[w] = n;
-    __syncthreads();
-    if (!FILL) {
-        if (tid == 0) {
-            int tot = 0;
-            for (int i = 0; i < 16; ++i) tot += wave_n[i];
-            p.counts[bucket] = tot;
-        }
-        return;
+    int run = x - sum;
+    for (int i = a; i < b; ++i) {
+        const int v = h[i];
+        h[i] = run;
+        run += v;
     }
-    int base = p.offsets[bucket];
-    for (int i = 0; i < w; ++i) base += wave_n[i];
-    for (int64_t c = a; c < b; c += 512) {
-        bool m[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) m[u] = match(c + 64 * u + lane);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const unsigned long long bal = __ballot(m[u]);
-            if (m[u]) p.entries[base + __popcll(bal & below)] = (int32_t)(c + 64 * u + lane);
-            base += __popcll(bal);
-        }
+    if (lane == 63) p.counts[bucket] = x;
+}
+
+// One wavefront per (tile, KV head): entry e goes to offset + tile prefix +
+// rank of its block's list.
+__global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
+    const int tile = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
+    const int t0 = tile * p.tt, t1 = min(p.Tq, t0 + p.tt);
+    const int e_begin = t0 * p.count, e_end = t1 * p.count;
+    const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
+    const int32_t* rank = p.rank + (int64_t)h2 * p.Tq * p.count;
+    const int32_t* hist = p.hist + (int64_t)h2 * p.NB * p.n_tiles;
+    const int32_t* off = p.offsets + h2 * p.NB;
+    int s_cur = seq_of_token(p.seqs, t0);
+    for (int c = e_begin; c < e_end; c += 64) {
+        const int g = step_block(p, tk, c, e_end, lane, s_cur);
+        if (g >= 0) p.entries[off[g] + hist[(int64_t)g * p.n_tiles + tile] + rank[c + lane]] = c + lane;
     }
 }
 
@@ -1157,10 +1172,12 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
 // ---------------------------------------------------------------------------
 
 static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
-    const dim3 grid(p.NB, p.N2);
-    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<false>), grid, dim3(1024), 0, st, p);
+    if (p.n_tiles > 0)
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_rank_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+    PROF_LAUNCH(KID_NSA_INDEX, st, nsa_hist_scan_kernel, dim3(p.NB, p.N2), dim3(64), 0, st, p);
     PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
-    PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_index_kernel<true>), grid, dim3(1024), 0, st, p);
+    if (p.n_tiles > 0)
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1221,8 +1238,8 @@ constexpr size_t kAlignN = 256;
 size_t up(size_t x) { return (x + kAlignN - 1) / kAlignN * kAlignN; }
 
 struct NsaLayout {
-    int64_t NB = 0, nbk = 0, E = 0, chunk = 1, max_pieces = 0, halves = 1;
-    size_t counts = 0, offsets = 0, entries = 0, pstart = 0, pieces = 0, lse2 = 0, delta = 0,
+    int64_t NB = 0, nbk = 0, E = 0, chunk = 1, max_pieces = 0, halves = 1, tt = 16, n_tiles = 0;
+    size_t counts = 0, offsets = 0, entries = 0, pstart = 0, pieces = 0, hist = 0, rank = 0, lse2 = 0, delta = 0,
            partial = 0, seqtab = 0, total = 0;
 };
 
@@ -1288,12 +1305,18 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.chunk = std::max<int64_t>(1, 2048 / G);
     L.max_pieces = L.nbk + (L.E + L.chunk - 1) / L.chunk;
     L.halves = (bs + 63) / 64;
+    // index tiles: 16 tokens, doubled until blocks x tiles is at most 2^22
+    // (the per-tile totals stay within 16 MiB per KV head)
+    while (L.NB * ((S.Tq + L.tt - 1) / L.tt) > ((int64_t)1 << 22)) L.tt *= 2;
+    L.n_tiles = (S.Tq + L.tt - 1) / L.tt;
     size_t o = 0;
     L.counts = o; o = up(o + L.nbk * 4);
     L.offsets = o; o = up(o + (L.nbk + 1) * 4);
     L.entries = o; o = up(o + std::max<int64_t>(L.E, 1) * 4);
     L.pstart = o; o = up(o + (L.nbk + 1) * 4);
     L.pieces = o; o = up(o + L.max_pieces * 3 * 4);
+    L.hist = o; o = up(o + (size_t)Hkv * L.NB * L.n_tiles * 4);
+    L.rank = o; o = up(o + std::max<int64_t>(L.E, 1) * 4);
     L.lse2 = o; o = up(o + S.Tq * Hq * 4);
     L.delta = o; o = up(o + S.Tq * Hq * 4);
     L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
@@ -1392,8 +1415,6 @@ int sdpa_bwd_selected_workspace_size(int dtype, int64_t batch, const int64_t* cu
 static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout& L, char* ws, const int32_t* topk,
                               int64_t st, int64_t sn, int64_t sk, int64_t Hq, int64_t Hkv, int64_t bs, int64_t count) {
     p.topk = topk; p.tk_st = st; p.tk_sn = sn; p.tk_sk = sk;
-    p.tk_vec4 = (sk == 1 && count % 4 == 0 && st % 4 == 0 && sn % 4 == 0 &&
-                 reinterpret_cast<uintptr_t>(topk) % 16 == 0 && S.Tq * count < (int64_t(1) << 33)) ? 1 : 0;
     p.count = (int)count; p.bs = (int)bs; p.N2 = (int)Hkv; p.NB = (int)L.NB;
     p.G = (int)(Hq / Hkv); p.Hq = (int)Hq;
     p.g_mul = (65536 + p.G - 1) / p.G;
@@ -1404,6 +1425,9 @@ static void fill_index_params(sdpa::NsaParams& p, const Seqs& S, const NsaLayout
     p.entries = reinterpret_cast<int32_t*>(ws + L.entries);
     p.pstart = reinterpret_cast<int32_t*>(ws + L.pstart);
     p.pieces = reinterpret_cast<int32_t*>(ws + L.pieces);
+    p.tt = (int)L.tt; p.n_tiles = (int)L.n_tiles;
+    p.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+    p.rank = reinterpret_cast<int32_t*>(ws + L.rank);
     p.halves = (int)L.halves;
     p.Tq = (int)S.Tq;
 }

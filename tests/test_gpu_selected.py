@@ -66,6 +66,30 @@ def test_index_long_sequence_exact():
     _check_index(topk, cu, cu, 64)
 
 
+def _random_topk(lq, lk, N2, bs, count, seed):
+    """Blocks drawn uniformly (repeats allowed) from each token's own sequence."""
+    rng = np.random.default_rng(seed)
+    rows = [rng.integers(0, k // bs, size=(q, N2, count)) for q, k in zip(lq, lk)]
+    return np.concatenate(rows).astype(np.int32)
+
+
+def test_index_short_and_empty_query_sequences():
+    """Query lengths 0 to 33 (several sequences share a 16-token tile of the
+    index build) against longer key sequences."""
+    lq = np.array([5, 0, 7, 33, 1, 0, 20, 2, 0])
+    lk = np.array([64, 96, 64, 128, 64, 64, 96, 64, 64])
+    topk = _random_topk(lq, lk, 2, 32, 2, seed=9)
+    _check_index(topk, np.cumsum(lq), np.cumsum(lk), 32)
+
+
+def test_index_many_blocks():
+    """4097 key blocks (more than one pass of the rank kernel's block
+    counters) and blocks x tiles above 2^22 (the tile doubles to 32 tokens)."""
+    lq, lk = np.array([20000]), np.array([4097 * 16])
+    topk = _random_topk(lq, lk, 2, 16, 2, seed=4097)
+    _check_index(topk, np.cumsum(lq), np.cumsum(lk), 16)
+
+
 def _run_selected(q, k, v, o, do, stats, topk, cu, bs, scale, mode, det=False):
     dq = torch.full_like(q, float("nan"))
     dk = torch.full_like(k, float("nan"))
