@@ -167,21 +167,28 @@ __global__ __launch_bounds__(64) void nsa_seqtab_kernel(SeqTable chunk, int32_t*
 // nsa_hist_scan_kernel turns each block's row of tile totals into exclusive
 // prefixes and the block's count; nsa_scan_kernel makes the CSR offsets and
 // the work pieces; nsa_scatter_kernel stores each entry at offset + tile
-// prefix + rank.  Every list comes out in (token, slot) order without
-// atomics, in work linear in the entries plus blocks x tiles.
+// prefix + rank.  Every list comes out in (token, slot) order
+// without atomics, in work linear in the entries plus blocks x tiles.
 
 constexpr int kIdxWin = 4096;   // block counters per pass of the rank kernel
+constexpr int kIdxBatch = 4;    // tile steps whose top-k values are loaded together
 
-// The global block named by entry c + lane of a tile step (e_end: the tile's
-// end), or -1 past the tile's end or when the value is not a block of the
-// token's sequence.  s_cur (uniform) is moved past the sequences that end at
-// or before the step's first token; sequences partition the packed tokens.
-__device__ __forceinline__ int step_block(const NsaParams& p, const int32_t* tk, int c, int e_end, int lane,
-                                          int& s_cur) {
+// The top-k value of entry c + lane of a tile step (e_end: the tile's end;
+// lanes past it read the tile's last entry).
+__device__ __forceinline__ int step_choice(const NsaParams& p, const int32_t* tk, int c, int e_end, int lane) {
     const int e = min(c + lane, e_end - 1);
     const int t = (int)((uint32_t)e / (uint32_t)p.count);
     const int slot = e - t * p.count;
-    const int v = tk[(int64_t)t * p.tk_st + (int64_t)slot * p.tk_sk];
+    return tk[(int64_t)t * p.tk_st + (int64_t)slot * p.tk_sk];
+}
+
+// The global block that value v of entry c + lane names, or -1 past the
+// tile's end or when v is not a block of the token's sequence.  s_cur
+// (uniform) is moved past the sequences that end at or before the step's
+// first token; sequences partition the packed tokens.
+__device__ __forceinline__ int step_block(const NsaParams& p, int v, int c, int e_end, int lane, int& s_cur) {
+    const int e = min(c + lane, e_end - 1);
+    const int t = (int)((uint32_t)e / (uint32_t)p.count);
     const int t_first = (int)((uint32_t)c / (uint32_t)p.count);
     const int t_last = (int)((uint32_t)min(c + 63, e_end - 1) / (uint32_t)p.count);
     while (s_cur + 1 < p.seqs.n) {
@@ -219,41 +226,46 @@ __global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
         for (int i = lane; i < nw; i += 64) cnt[i] = 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         int s_cur = sa;
-        for (int c = e_begin; c < e_end; c += 64) {
-            const int g = step_block(p, tk, c, e_end, lane, s_cur);
-            const int key = g - w0;
-            const bool mine = g >= w0 && key < nw;
-            unsigned long long m = __ballot(mine);
-            for (int b = 0; b < bits; ++b) {
-                const bool on = (key >> b) & 1;
-                const unsigned long long hb = __ballot(mine && on);
-                m &= on ? hb : ~hb;
+        for (int cb = e_begin; cb < e_end; cb += 64 * kIdxBatch) {
+            int v[kIdxBatch];
+#pragma unroll
+            for (int u = 0; u < kIdxBatch; ++u) v[u] = step_choice(p, tk, min(cb + 64 * u, e_end - 1), e_end, lane);
+#pragma unroll
+            for (int u = 0; u < kIdxBatch; ++u) {
+                const int c = cb + 64 * u;
+                if (c >= e_end) break;
+                const int g = step_block(p, v[u], c, e_end, lane, s_cur);
+                const int key = g - w0;
+                const bool mine = g >= w0 && key < nw;
+                unsigned long long m = __ballot(mine);
+                for (int b = 0; b < bits; ++b) {
+                    const bool on = (key >> b) & 1;
+                    const unsigned long long hb = __ballot(mine && on);
+                    m &= on ? hb : ~hb;
+                }
+                // one wavefront: its LDS reads and writes take effect in program order
+                if (mine) {
+                    const int old = cnt[key];
+                    const int before = __popcll(m & below);
+                    if (before == 0) cnt[key] = old + __popcll(m);
+                    rank[c + lane] = old + before;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
             }
-            // one wavefront: its LDS reads and writes take effect in program order
-            if (mine) {
-                const int old = cnt[key];
-                const int before = __popcll(m & below);
-                if (before == 0) cnt[key] = old + __popcll(m);
-                rank[c + lane] = old + before;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         }
         for (int i = lane; i < nw; i += 64) hist[(int64_t)(w0 + i) * p.n_tiles + tile] = cnt[i];
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
 }
 
-// One wavefront per (block, KV head): exclusive prefixes over the tiles of the
-// block's sequence, in place, and the block's entry count.
-__global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
-    const int g = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
-    const int bucket = h2 * p.NB + g;
+// One wavefront, one (block, KV head) = bucket: exclusive prefixes over the
+// tiles of the block's sequence, in place; returns the block's entry count
+// (in every lane).
+__device__ __forceinline__ int hist_scan_bucket(const NsaParams& p, int bucket, int lane) {
+    const int g = bucket % p.NB;
     const int s = seq_of_block(p.seqs, g * p.bs);
     const SeqRow r = seq_row(p.seqs, s < 0 ? 0 : s);
-    if (s < 0 || r.lq == 0) {
-        if (lane == 0) p.counts[bucket] = 0;
-        return;
-    }
+    if (s < 0 || r.lq == 0) return 0;
     const int ta = r.q0 / p.tt, tb = (r.q0 + r.lq - 1) / p.tt + 1;
     int32_t* h = p.hist + (int64_t)bucket * p.n_tiles;
     // each lane takes a run of consecutive tiles
@@ -273,7 +285,13 @@ __global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
         h[i] = run;
         run += v;
     }
-    if (lane == 63) p.counts[bucket] = x;
+    return __shfl(x, 63);
+}
+
+__global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
+    const int bucket = blockIdx.y * p.NB + blockIdx.x;
+    const int n = hist_scan_bucket(p, bucket, threadIdx.x);
+    if (threadIdx.x == 0) p.counts[bucket] = n;
 }
 
 // One wavefront per (tile, KV head): entry e goes to offset + tile prefix +
@@ -287,9 +305,23 @@ __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
     const int32_t* hist = p.hist + (int64_t)h2 * p.NB * p.n_tiles;
     const int32_t* off = p.offsets + h2 * p.NB;
     int s_cur = seq_of_token(p.seqs, t0);
-    for (int c = e_begin; c < e_end; c += 64) {
-        const int g = step_block(p, tk, c, e_end, lane, s_cur);
-        if (g >= 0) p.entries[off[g] + hist[(int64_t)g * p.n_tiles + tile] + rank[c + lane]] = c + lane;
+    for (int cb = e_begin; cb < e_end; cb += 64 * kIdxBatch) {
+        int v[kIdxBatch], rk[kIdxBatch], g[kIdxBatch], pos[kIdxBatch];
+#pragma unroll
+        for (int u = 0; u < kIdxBatch; ++u) {
+            const int c = min(cb + 64 * u, e_end - 1);
+            v[u] = step_choice(p, tk, c, e_end, lane);
+            rk[u] = rank[min(c + lane, e_end - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kIdxBatch; ++u)
+            g[u] = cb + 64 * u < e_end ? step_block(p, v[u], cb + 64 * u, e_end, lane, s_cur) : -1;
+#pragma unroll
+        for (int u = 0; u < kIdxBatch; ++u)
+            pos[u] = g[u] >= 0 ? off[g[u]] + hist[(int64_t)g[u] * p.n_tiles + tile] + rk[u] : -1;
+#pragma unroll
+        for (int u = 0; u < kIdxBatch; ++u)
+            if (g[u] >= 0) p.entries[pos[u]] = cb + 64 * u + lane;
     }
 }
 
@@ -953,6 +985,218 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dQ at Dqk = 192: wavefronts on their own
+// ---------------------------------------------------------------------------
+//
+// Workgroup (four wavefronts) per (token, KV head, tile of 16 query heads).
+// The token's gathered keys go in steps of 32; wavefront w takes steps w,
+// w + 4, ... on its own: it loads the step's K and V rows from global memory
+// straight into registers in the A-operand layout of v_mfma_f32_16x16x32
+// (S^T = K Q^T and dP^T = V dO^T, 16 keys x 16 heads per tile, so the heads
+// are the MFMA columns and each lane's LSE and Delta are one value), the next
+// step's rows in flight meanwhile, and stages only K in an LDS tile of its
+// own for the transposed operand of dQ^T += K^T dS^T (the two 16-key tiles of
+// the step as one 32-deep operand).  No LDS is shared during the loop, so
+// there is no barrier; the four partial dQ^T are summed through LDS at the
+// end, in wavefront order.  (A 16-key group lies within one block: block
+// sizes are multiples of 16.)  At Dqk = 192 the shared-chunk kernel above
+// needs 86 KB of LDS and 320 registers, one workgroup per CU; this form fits
+// two wavefronts per SIMD: 519 -> 300 us at (192, 128) and 467 -> 356 us at
+// (192, 192) on the NSA workload shape.  At Dqk = 128, where both run two
+// wavefronts per SIMD, the shared-chunk kernel is faster (190 against 241
+// us): its loads read whole rows, four per instruction, where a wavefront's
+// own MFMA-layout loads touch 16 rows each.
+
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(256, 2) void nsa_dq_wave_kernel(NsaParams p) {
+    constexpr int KPK = DK + 8;                   // LDS row pitch of a wavefront's K tile
+    constexpr int KSK = DK / 32, KSV = DV / 32;   // k-steps of 16x16x32: S over DK, dP over DV
+    constexpr int KSM = KSK > KSV ? KSK : KSV;
+    constexpr int DB = DK / 16;                   // 16-row blocks of dQ^T
+    constexpr bool PF = DK <= 128 && DV <= 128;   // two register sets of K/V rows fit
+    constexpr int TILE = 32 * KPK;
+    __shared__ __align__(16) uint16_t Kt[4 * TILE];
+    __shared__ int blk_s[128];          // the token's chosen blocks (block_count <= 128)
+    static_assert(sizeof(Kt) >= 3 * DB * 64 * 16, "reduction space");
+
+    const int t = blockIdx.x;
+    const int h2 = blockIdx.y / ((p.G + 15) / 16);
+    const int ht = blockIdx.y % ((p.G + 15) / 16);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: the step loop and its block lookups stay scalar
+    const int col = lane & 15, G16 = lane >> 4;
+    const int s_idx = seq_of_token(p.seqs, t);
+    if (s_idx < 0) return;
+    const SeqRow sq = seq_row(p.seqs, s_idx);
+    const int t_local = t - sq.q0;
+    const int krow0 = sq.k0;
+    const int nblk = sq.lk / p.bs;              // blocks of this sequence
+    const int gh = ht * 16 + col;               // head within the group
+    const bool head_ok = gh < p.G;
+    const int h = h2 * p.G + (head_ok ? gh : 0);
+
+    u32x4 qreg[KSK], doreg[KSV];
+    const uint16_t* qp = p.q.p + (int64_t)t * p.q.ss + (int64_t)h * p.q.sh;
+    const uint16_t* dop = p.dout.p + (int64_t)t * p.dout.ss + (int64_t)h * p.dout.sh;
+#pragma unroll
+    for (int s = 0; s < KSM; ++s) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        if (s < KSK) qreg[s] = head_ok ? ld16(qp + 32 * s + 8 * G16) : z;
+        if (s < KSV) doreg[s] = head_ok ? ld16(dop + 32 * s + 8 * G16) : z;
+    }
+    const float l2 = head_ok ? p.lse2[(int64_t)t * p.Hq + h] : INFINITY;
+    const float dl = head_ok ? p.delta[(int64_t)t * p.Hq + h] : 0.f;
+
+    f32x4 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero4();
+
+    // the token's chosen blocks (-1 for a choice outside the sequence)
+    const int32_t* tk = p.topk + (int64_t)t * p.tk_st + (int64_t)h2 * p.tk_sn;
+    for (int i = tid; i < p.count; i += 256) {
+        const int blk = tk[(int64_t)i * p.tk_sk];
+        blk_s[i] = (blk >= 0 && blk < nblk) ? blk : -1;
+    }
+    __syncthreads();
+
+    const int nk = p.count * p.bs;              // gathered keys, a multiple of 16
+    const int n_steps = (nk + 31) / 32;
+    // row strides are below 2^23 elements: 32 x 32 -> 64-bit row offsets
+    const int kss = (int)p.k.ss, vss = (int)p.v.ss;
+    const uint16_t* const kh = p.k.p + (int64_t)h2 * p.k.sh;
+    const uint16_t* const vh = p.v.p + (int64_t)h2 * p.v.sh;
+    // the user mask's row of this token (a masked key is treated as absent)
+    const uint8_t* mrow = p.mask ? p.mask + (int64_t)t_local * p.mask_ss : nullptr;
+    uint16_t* const Kw = Kt + w * TILE;
+
+    // Rows of one step: K and V of this lane's key in the two 16-key groups.
+    // Loads are unconditional: a group past the gathered keys or of an
+    // ignored choice re-reads key row krow0 and is masked.
+    struct Rows {
+        u32x4 k[2][KSK], v[2][KSV];
+    };
+    // group x of step st: its sequence-local key position base (-1: absent)
+    auto group_pos = [&](int st, int x) {
+        const int n16 = st * 32 + 16 * x;
+        const int blk = blk_s[min(n16 / p.bs, p.count - 1)];
+        return (n16 < nk && blk >= 0) ? blk * p.bs + n16 % p.bs : -1;
+    };
+    auto load = [&](Rows& r, int st) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int pos = group_pos(st, x);
+            const int row = krow0 + (pos >= 0 ? pos + col : 0);
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) r.k[x][ks] = ld16(kh + (int64_t)row * kss + 32 * ks + 8 * G16);
+#pragma unroll
+            for (int ks = 0; ks < KSV; ++ks) r.v[x][ks] = ld16(vh + (int64_t)row * vss + 32 * ks + 8 * G16);
+        }
+    };
+    auto step = [&](const Rows& r, int st) {
+        const int pos0 = group_pos(st, 0), pos1 = group_pos(st, 1);
+        // user-mask bytes of the four keys of each group this lane's C
+        // elements cover
+        uint32_t mb[2] = {0u, 0u};
+        if (mrow) {
+            if (pos0 >= 0) mb[0] = *reinterpret_cast<const uint32_t*>(mrow + pos0 + 4 * G16);
+            if (pos1 >= 0) mb[1] = *reinterpret_cast<const uint32_t*>(mrow + pos1 + 4 * G16);
+        }
+        // K rows into this wavefront's tile for the transposed dQ operand
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int ks = 0; ks < KSK; ++ks) st16(&Kw[(16 * x + col) * KPK + 32 * ks + 8 * G16], r.k[x][ks]);
+        f32x4 s[2], dp[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            s[x] = zero4();
+            dp[x][0] = dp[x][1] = dp[x][2] = dp[x][3] = -dl;   // dP^T accumulates onto -Delta
+#pragma unroll
+            for (int ks = 0; ks < KSM; ++ks) {
+                if (ks < KSK) s[x] = T::mma16(r.k[x][ks], qreg[ks], s[x]);
+                if (ks < KSV) dp[x] = T::mma16(r.v[x][ks], doreg[ks], dp[x]);
+            }
+        }
+        // element (x, e): key position pos_x + 4*G16 + e of the sequence
+        const bool whole = pos0 >= 0 && pos1 >= 0 && !mrow &&
+                           (p.sparse_mode != 2 || max(pos0, pos1) + 15 <= t_local);
+        if (whole) {
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dp[x][e] = fast_exp2(__builtin_fmaf(s[x][e], p.scale_log2, -l2)) * dp[x][e];
+        } else {
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int pos = x ? pos1 : pos0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kp = pos + 4 * G16 + e;
+                    const bool off = pos < 0 || (p.sparse_mode == 2 && kp > t_local) || ((mb[x] >> (8 * e)) & 0xffu);
+                    const float pv = fast_exp2(__builtin_fmaf(s[x][e], p.scale_log2, -l2));
+                    dp[x][e] = off ? 0.f : pv * dp[x][e];
+                }
+            }
+        }
+        u32x4 bS;
+        bS[0] = T::pack_op(dp[0][0], dp[0][1]);
+        bS[1] = T::pack_op(dp[0][2], dp[0][3]);
+        bS[2] = T::pack_op(dp[1][0], dp[1][1]);
+        bS[3] = T::pack_op(dp[1][2], dp[1][3]);
+        // one wavefront writes and reads its tile: LDS keeps the order
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            dq[db] = T::mma16(ld_tr16x16_acc(Kw, KPK, 0, 16 * db, lane), bS, dq[db]);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+
+    if constexpr (PF) {
+        Rows ra, rb;
+        if (w < n_steps) load(ra, w);
+        for (int st = w; st < n_steps; st += 8) {
+            const bool b_ok = st + 4 < n_steps;
+            if (b_ok) load(rb, st + 4);
+            step(ra, st);
+            if (!b_ok) break;
+            if (st + 8 < n_steps) load(ra, st + 8);
+            step(rb, st + 4);
+        }
+    } else {
+        Rows ra;
+        for (int st = w; st < n_steps; st += 4) {
+            load(ra, st);
+            step(ra, st);
+        }
+    }
+
+    // sum the four wavefronts' partials (through LDS, reusing the K tiles)
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(Kt);
+    if (w != 0) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<f32x4*>(&red[((((w - 1) * DB) + db) * 64 + lane) * 4]) = dq[db];
+    }
+    __syncthreads();
+    if (w != 0 || !head_ok) return;
+#pragma unroll
+    for (int x = 0; x < 3; ++x)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&red[(((x * DB) + db) * 64 + lane) * 4]);
+            dq[db][0] += v[0]; dq[db][1] += v[1]; dq[db][2] += v[2]; dq[db][3] += v[3];
+        }
+    // dQ^T tile: lane holds head `col`, head dims 16*db + 4*G16 + r
+    const int64_t dqo = (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+        st_grad4<T>(p.dq.p, dqo + 16 * db + 4 * G16, p.grad_f32, dq[db][0] * p.scale, dq[db][1] * p.scale,
+                    dq[db][2] * p.scale, dq[db][3] * p.scale);
+}
+
+// ---------------------------------------------------------------------------
 // Forward: O and the (max, sum) statistics over each token's gathered keys
 // ---------------------------------------------------------------------------
 //
@@ -1212,9 +1456,13 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
                 dim3(p.N2 * p.NB, p.halves, reduce_key_groups<DK, DV>()), dim3(256), 0, st, p);
     // with no query token (every query length 0) dK and dV are the reduction's
     // zeros and there is no dQ row to write
-    if (p.Tq > 0)
-        PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), dim3(p.Tq, p.N2 * ((p.G + 15) / 16)), dim3(256), 0,
-                    st, p);
+    if (p.Tq > 0) {
+        const dim3 grid(p.Tq, p.N2 * ((p.G + 15) / 16));
+        if constexpr (DK > 128)
+            PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_wave_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
+        else
+            PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
