@@ -28,8 +28,9 @@
  *   (T, N, D) ("TND", the Ascend page's only layout).  The last (D) stride must
  *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
  *   keep every row 16-byte aligned.  The row stride (S or T) of every tensor
- *   and of the statistics must lie in [0, 2^23) elements.  D is 64 or 128
- *   (the selected calls also take D = 192, with a value head dim of 192 or 128).
+ *   and of the statistics must lie in [0, 2^23) elements.  D is 64, 128 or
+ *   192, the same for Q/K and V (the selected calls also take D = 192 with a
+ *   value head dim of 128).
  *   Any other layout returns SDPA_ERR_UNSUPPORTED.
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library allocates no device memory, keeps no per-call state and never
@@ -165,7 +166,9 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  *     1: guaranteed bitwise reproducible: the atomic-free query-outer pass;
  *     2: fp32 atomic accumulation inside the key-outer kernel and a final
  *        conversion (FlashAttention-2's method; run-to-run rounding
- *        differences possible), at D=64 and D=128.
+ *        differences possible), at D=64 and D=128; at D=192 the key-outer
+ *        kernel's tiles leave no LDS for it and the value returns
+ *        SDPA_ERR_UNSUPPORTED.
  *     Any other value: SDPA_ERR_INVALID.  The workspace size depends on it.
  *   grad_dtype: element type of dq, dk and dv: `dtype`, or SDPA_F32 for fp32
  *     gradients (same layout rules, strides in fp32 elements); anything else

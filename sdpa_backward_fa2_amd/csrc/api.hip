@@ -106,6 +106,12 @@ Carve carve_bwd(int64_t rows, int64_t D, bool deterministic) {
 bool dq_mode_ok(int mode) { return mode >= 0 && mode <= 2; }
 bool dq_atomic(int mode, int64_t D) { (void)D; return mode == 2; }
 
+// Head dims of the dense and packed paths (equal for Q/K and V).  At D = 192
+// the key-tile kernel's tiles take 102 KB of LDS, which leaves no room for
+// the K and dS^T tiles of the atomic dQ form: dQ mode 2 is not offered there.
+bool dense_dim_ok(int64_t D) { return D == 64 || D == 128 || D == 192; }
+bool dense_mode_ok(int mode, int64_t D) { return !(D == 192 && mode == 2); }
+
 int check_stats(const sdpa_stats* s) {
     if (!s->lse_or_max) return SDPA_ERR_NULLPTR;
     if (s->kind == SDPA_STATS_MAX_SUM && !s->sum) return SDPA_ERR_NULLPTR;
@@ -218,7 +224,7 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o_out})
         if (int s = tensor4_ok(t)) return s;
     if (Sq >= kMaxLen || Sk >= kMaxLen || B * Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
@@ -253,7 +259,7 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o_out})
         if (int s = tensor3_ok(t)) return s;
     if (std::min<int64_t>(batch, sdpa::kMaxSeqArgs) * Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
@@ -299,7 +305,7 @@ int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
     *bytes = carve_bwd(B * Hq * Sq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
@@ -371,7 +377,7 @@ static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor4_ok(t)) return s;
     if (int s = check_stats_stride(stats)) return s;
@@ -445,7 +451,7 @@ int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_s
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
     *bytes = carve_bwd(P.Tq * Hq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
@@ -471,7 +477,7 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (int s = check_stats_kind(stats)) return s;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
-    if (D != 64 && D != 128) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;
     if (int s = check_stats_stride(stats)) return s;

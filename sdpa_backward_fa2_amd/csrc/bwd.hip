@@ -979,6 +979,7 @@ hipError_t launch_bwd_pre(const BwdParams& p, int dtype, int D, bool zero_dq, hi
 }
 
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
+    if (L.D == 192) return launch_bwd_d192(p, L, st);
     if (L.D != 64) return launch_bwd_d128(p, L, st);
     return L.dtype == 0 ? launch_bwd_d<F16, 64>(p, L, st) : launch_bwd_d<BF16, 64>(p, L, st);
 }

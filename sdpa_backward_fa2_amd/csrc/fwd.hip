@@ -152,10 +152,15 @@ static hipError_t launch_fwd_t(const FwdParams& p, int max_lq, bool causal, hipS
     return hipGetLastError();
 }
 
+template <class T>
+static hipError_t launch_fwd_dt(const FwdParams& p, int D, int max_lq, bool causal, hipStream_t st) {
+    if (D == 64) return launch_fwd_t<T, 64>(p, max_lq, causal, st);
+    if (D == 128) return launch_fwd_t<T, 128>(p, max_lq, causal, st);
+    return launch_fwd_t<T, 192>(p, max_lq, causal, st);
+}
+
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st) {
-    if (dtype == 0)
-        return D == 64 ? launch_fwd_t<F16, 64>(p, max_lq, causal, st) : launch_fwd_t<F16, 128>(p, max_lq, causal, st);
-    return D == 64 ? launch_fwd_t<BF16, 64>(p, max_lq, causal, st) : launch_fwd_t<BF16, 128>(p, max_lq, causal, st);
+    return dtype == 0 ? launch_fwd_dt<F16>(p, D, max_lq, causal, st) : launch_fwd_dt<BF16>(p, D, max_lq, causal, st);
 }
 
 }  // namespace sdpa

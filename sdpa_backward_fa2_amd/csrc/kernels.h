@@ -15,7 +15,7 @@ inline bool row_stride_ok(int64_t s) { return s >= 0 && s < kMaxRowStride; }
 
 struct BwdLaunch {
     int dtype;            // 0 fp16, 1 bf16
-    int D;                // 64 or 128
+    int D;                // 64, 128 or 192
     bool causal;
     bool deterministic;
     int n_seq;            // batch (dense) or number of packed sequences
@@ -31,8 +31,10 @@ struct BwdLaunch {
 
 hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
-// The D=128 backward (bwd128.hip); launch_bwd hands D=128 calls to it.
+// The D=128 backward (bwd128.hip) and the D=192 backward (bwd192.hip);
+// launch_bwd hands those calls to them.
 hipError_t launch_bwd_d128(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
+hipError_t launch_bwd_d192(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // The D=64 backward with FA2's fp32-atomic dQ accumulation (bwd128.hip's
 // key-tile kernel at D=64 and the dQ conversion).
 hipError_t launch_bwd_d64_atomic(const BwdParams& p, const BwdLaunch& L, hipStream_t st);

@@ -84,7 +84,8 @@ int main(void) {
         EXPECT(sdpa_bwd_varlen_workspace_size(SDPA_BF16, 3, cu, cu, 32, 32, 128, 0, &n), SDPA_OK);
         EXPECT(varlen(3, cu, 32, 128, 0, n), SDPA_ERR_HIP);
         EXPECT(varlen(3, bad, 32, 128, 0, n), SDPA_ERR_INVALID);
-        EXPECT(varlen(3, cu, 32, 192, 0, n), SDPA_ERR_UNSUPPORTED);
+        EXPECT(varlen(3, cu, 32, 96, 0, n), SDPA_ERR_UNSUPPORTED);
+        EXPECT(varlen(3, cu, 32, 192, 2, n), SDPA_ERR_UNSUPPORTED);   /* no atomic dQ at D=192 */
         EXPECT(varlen(3, cu, 32, 128, 0, 8), SDPA_ERR_WORKSPACE);
         EXPECT(varlen(3, cu, 40000, 128, 0, (size_t)1 << 40), SDPA_ERR_UNSUPPORTED);
         EXPECT(varlen(0, cu, 32, 128, 0, n), SDPA_ERR_INVALID);

@@ -99,7 +99,11 @@ def test_workspace_size_query():
     for D in (64, 128):
         assert size(D, 0) == size(D, 1) >= rows * 8
         assert size(D, 2) >= size(D, 1) + rows * D * 4
+    # D=192: the atomic-free modes only
+    assert size(192, 0) == size(192, 1) >= rows * 8
     m = ctypes.c_size_t(0)
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 192, 2, ctypes.byref(m)) == UNSUPPORTED
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 256, 0, ctypes.byref(m)) == UNSUPPORTED
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 3, ctypes.byref(m)) == INVALID
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 0, ctypes.byref(m)) == UNSUPPORTED
     assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, None) == NULLPTR
@@ -157,7 +161,8 @@ def test_varlen_validation():
     assert varlen_call([100, 50], [100, 50]) == INVALID           # non-monotone
     assert varlen_call([100, 300], [100, 300], grad=0) == INVALID  # bf16 inputs, fp16 gradients
     assert varlen_call([100, 300], [100, 300], Hq=3, Hkv=2) == INVALID
-    assert varlen_call([100, 300], [100, 300], D=192) == UNSUPPORTED
+    assert varlen_call([100, 300], [100, 300], D=96) == UNSUPPORTED
+    assert varlen_call([100, 300], [100, 300], D=192, det=2) == UNSUPPORTED   # no atomic dQ at D=192
     assert varlen_call([100, 300], [100, 300], ws_bytes=8) == WORKSPACE
     n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 2)(100, 300)

@@ -60,10 +60,15 @@ def _check_case(B, Hq, Hkv, Sq, Sk, D, dtype, causal, layout, seed=0, stats="gpu
         o = to_device(synth.encode(f["O"], dtype), dtype)
         lse = torch.tensor(f["lse"], dtype=torch.float32, device="cuda")
     g = oracle.dense_backward(qx, kx, vx, dox, scale, causal)
-    for det in (0, 1, 2):
+    for det in _modes(D):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, scale, causal, det)
         for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
             assert_rel(to_f64(got), ref, dtype, f"{name} det={det}")
+
+
+def _modes(D):
+    """dQ modes offered at head dim D (no fp32-atomic form at D=192)."""
+    return (0, 1) if D == 192 else (0, 1, 2)
 
 
 # ----------------------------------------------------------------------------
@@ -146,7 +151,7 @@ def test_config3_long_context_sampled_heads():
 # ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 192])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("S", [1, 37, 128, 200, 385])
 def test_sweep_square(dtype, D, causal, S):
@@ -158,7 +163,7 @@ def test_sweep_rectangular_noncausal(Sq, Sk):
     _check_case(1, 3, 3, Sq, Sk, 64, "f16", False, "bhsd", seed=Sq * Sk)
 
 
-@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16")])
+@pytest.mark.parametrize("D,dtype", [(64, "f16"), (128, "bf16"), (192, "f16")])
 @pytest.mark.parametrize("Sq,Sk", [(64, 300), (257, 129), (5, 1), (1, 77), (200, 64), (130, 131)])
 def test_sweep_rectangular_causal(Sq, Sk, D, dtype):
     """Causal with Sq != Sk, top-left aligned: keys past the last query get
@@ -170,7 +175,7 @@ def test_rectangular_causal_gqa():
     _check_case(2, 4, 2, 96, 230, 128, "f16", True, "bhsd", seed=77)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 192])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_gqa(Hq, Hkv, causal, D):
@@ -207,3 +212,18 @@ def test_dq_modes(cid):
     for x, y in zip(a, c):
         e = float((x.float() - y.float()).abs().max() / x.float().abs().max())
         assert e <= REL_TOL[wl.dtype]
+
+
+def test_d192_longer_causal_from_gpu_forward():
+    """D=192 over several 128-key tiles and 64-row query tiles with a ragged
+    tail, O and LSE from the library's own forward."""
+    _check_case(2, 4, 2, 700, 700, 192, "bf16", True, "bshd", seed=192)
+
+
+def test_d192_atomic_mode_is_unsupported():
+    case = _random_case(1, 2, 2, 64, 64, 192, "f16", "bhsd", 1)
+    q, k, v, do = (case[n][0] for n in ("q", "k", "v", "do"))
+    o, lse = sb.fwd_stats(q, k, v, 0.1, True)
+    with pytest.raises(sb.SdpaError) as e:
+        sb.bwd(q, k, v, o, do, lse, 0.1, True, deterministic=2)
+    assert e.value.status == 3   # SDPA_ERR_UNSUPPORTED

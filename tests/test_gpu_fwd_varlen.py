@@ -57,7 +57,7 @@ def _fwd_case(lq, lk, Hq, Hkv, D, dtype, causal, seed, backward=True):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 192])
 def test_ragged_causal(dtype, D):
     lengths = [1, 200, 0, 129, 64, 300]
     _fwd_case(lengths, lengths, 2, 2, D, dtype, True, seed=20 + D)
@@ -68,7 +68,7 @@ def test_noncausal_unequal_and_empty_key_sequence():
     _fwd_case([100, 7, 250], [37, 0, 129], 3, 3, 64, "f16", False, seed=21, backward=False)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [64, 128, 192])
 def test_causal_unequal_lengths(D):
     # top-left causal per sequence; the third sequence has no keys
     _fwd_case([100, 7, 64, 250], [37, 300, 0, 129], 2, 2, D, "f16", True, seed=25 + D)
