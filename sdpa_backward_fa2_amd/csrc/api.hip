@@ -328,19 +328,28 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
         return SDPA_OK;
     }
     // Packed: launch per chunk of up to kMaxSeqArgs sequences; the row-wise
-    // kernels cover all rows on the first chunk only.
+    // kernels cover all rows on the first chunk only.  Sequences go longest
+    // (most key rows, then query rows) first: every sequence carries its own
+    // row offsets, so the order is free, and the kernels take their units in
+    // table order.
     p.varlen = 1;
     const int64_t n = (int64_t)packed->q0.size();
+    std::vector<int64_t> order((size_t)n);
+    for (int64_t b = 0; b < n; ++b) order[(size_t)b] = b;
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t c) {
+        return packed->lk[a] != packed->lk[c] ? packed->lk[a] > packed->lk[c] : packed->lq[a] > packed->lq[c];
+    });
     for (int64_t c0 = 0; c0 < n; c0 += sdpa::kMaxSeqArgs) {
         const int64_t c1 = std::min<int64_t>(n, c0 + sdpa::kMaxSeqArgs);
         int64_t mlq = 0, mlk = 0;
         p.seqs.n = (int)(c1 - c0);
         p.seqs.dev = nullptr;
-        for (int64_t b = c0; b < c1; ++b) {
-            p.seqs.q0[b - c0] = (int32_t)packed->q0[b];
-            p.seqs.k0[b - c0] = (int32_t)packed->k0[b];
-            p.seqs.lq[b - c0] = (int32_t)packed->lq[b];
-            p.seqs.lk[b - c0] = (int32_t)packed->lk[b];
+        for (int64_t i = c0; i < c1; ++i) {
+            const size_t b = (size_t)order[(size_t)i];
+            p.seqs.q0[i - c0] = (int32_t)packed->q0[b];
+            p.seqs.k0[i - c0] = (int32_t)packed->k0[b];
+            p.seqs.lq[i - c0] = (int32_t)packed->lq[b];
+            p.seqs.lk[i - c0] = (int32_t)packed->lk[b];
             mlq = std::max(mlq, packed->lq[b]);
             mlk = std::max(mlk, packed->lk[b]);
         }

@@ -57,6 +57,34 @@ __device__ __forceinline__ void xcd_unit_order(int n_unit, int n_item, int L, in
     item = slot % n_item;
 }
 
+// The key-tile kernel's order.  Units (sequence, KV head) share Q and dO;
+// items are a unit's key tiles, longest causal range first.  With n_unit a
+// multiple of 8, unit u runs on XCD u % 8, and each XCD takes its units in
+// groups of kXcdGroup: all items of a group, item-major across its units,
+// before the next group, so that the workgroups an XCD runs at once read few
+// units' rows from its L2.  Packed sequences come sorted by decreasing length
+// (the host sorts them), so the longest units go first.  Plain order (units
+// fastest) otherwise.  A bijection on [0, n_unit * n_item).  With four units
+// per XCD (B2 H16 S4096) a group is the whole XCD share and the order is the
+// plain one.  On 8 packed sequences x 32 heads (32 units per XCD) it cut the
+// kernel's HBM reads from 1121 to 336 MB per launch (FETCH_SIZE); the time
+// stayed 387-391 us, which the one-wavefront-per-SIMD kernel spends on
+// latency, not bandwidth.  Groups of 2 were slower (401 us), of 8 the same.
+constexpr int kXcdGroup = 4;
+__device__ __forceinline__ void xcd_group_order(int n_unit, int n_item, int L, int& unit, int& item) {
+    if (n_unit & 7) {
+        unit = L % n_unit;
+        item = L / n_unit;
+        return;
+    }
+    const int xcd = L & 7, slot = L >> 3;
+    const int per_xcd = n_unit >> 3;
+    const int gi = slot / (kXcdGroup * n_item), s = slot % (kXcdGroup * n_item);
+    const int gu = min(kXcdGroup, per_xcd - gi * kXcdGroup);   // units in this group
+    item = s / gu;
+    unit = (gi * kXcdGroup + s % gu) * 8 + xcd;
+}
+
 template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
     constexpr int BC = 128;          // keys per workgroup: 4 wavefronts x 32
@@ -80,17 +108,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int g = lane >> 5, c = lane & 31;
-    // Grid (sequence x KV head, key tile): the key tiles go out longest causal
-    // range first, and with gridDim.x a multiple of 8 each (sequence, KV head)
-    // stays on one XCD, whose L2 its workgroups share.  (Ordering one unit's
-    // tiles together instead, as the dQ kernel does, was measured 7-9 % slower
-    // here: this kernel runs one workgroup per CU and needs the longest-first
-    // order more than the locality.)
-    const int b = blockIdx.x / p.Hkv, hk = blockIdx.x % p.Hkv;
+    // Grid (sequence x KV head, key tile), taken in XCD groups: each XCD runs
+    // the key tiles of kXcdGroup of its units at a time, longest causal range
+    // first (see xcd_group_order).
+    int unit, tile;
+    xcd_group_order(gridDim.x, gridDim.y, blockIdx.y * gridDim.x + blockIdx.x, unit, tile);
+    const int b = unit / p.Hkv, hk = unit % p.Hkv;
     const int G = p.Hq / p.Hkv;
     int q0 = 0, k0 = 0, lq = p.Sq, lk = p.Sk;
     if (p.varlen) seq_get(p.seqs, b, q0, k0, lq, lk);
-    const int j0 = blockIdx.y * BC;
+    const int j0 = tile * BC;
     if (j0 >= lk) return;
     const bool full_cols = j0 + BC <= lk;
 
