@@ -93,7 +93,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     constexpr int KS = D / 16;       // k-steps over the head dimension
     constexpr int MB = BR / 32;      // 32-row blocks of the query tile
     constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    constexpr int QP = D + 8;        // row stride of Qs, dOs, Ks  [row][d]
+    // row stride of Qs, dOs, Ks [row][d]: D=128 tiles are unpadded and
+    // chunk-swizzled (swz128), the others padded by 8 columns
+    constexpr bool SWZ = D == 128;
+    constexpr int QP = SWZ ? D : D + 8;
     constexpr int SP = BR + 8;       // row stride of dST          [j][i]
     constexpr int CH = BR * D / 8 / 256;     // 16-byte chunks per thread per tile
     constexpr int NBLK = MB * DB / NW;       // dQ 32x32 blocks per wavefront
@@ -104,6 +107,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     __shared__ __align__(16) uint16_t dST[DQ_ATOMIC ? BC * SP : 8];
     __shared__ __align__(16) float lse_s[2][BR];
     __shared__ __align__(16) float dlt_s[2][BR];
+    // column position of (row, col) in a tile, and the transposed operand read
+    auto tcol = [](int row, int col) { return SWZ ? swz128_col(row, col) : col; };
+    auto ldt_acc = [&](const uint16_t* X, int k0, int n0, int ln) {
+        if constexpr (SWZ) return ld_tr_swz128<true>(X, k0, n0, ln);
+        else return ld_tr<true>(X, QP, k0, n0, ln);
+    };
+    auto ldt_row = [&](const uint16_t* X, int k0, int n0, int ln) {
+        if constexpr (SWZ) return ld_tr_swz128<false>(X, k0, n0, ln);
+        else return ld_tr<false>(X, QP, k0, n0, ln);
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -132,7 +145,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         u32x4 z = {0u, 0u, 0u, 0u};
         kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
         vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
-        if (DQ_ATOMIC) st16(&Ks[(32 * w + c) * QP + 16 * s + 8 * g], kreg[s]);
+        if (DQ_ATOMIC) st16(&Ks[(32 * w + c) * QP + tcol(32 * w + c, 16 * s + 8 * g)], kreg[s]);
     }
 
     f32x16 dva[DB], dka[DB];
@@ -220,8 +233,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
         for (int x = 0; x < CH; ++x) {
             const int e = tid + 256 * x;
             const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Qs[buf][r * QP + cc], pq[x]);
-            st16(&dOs[buf][r * QP + cc], pdo[x]);
+            st16(&Qs[buf][r * QP + tcol(r, cc)], pq[x]);
+            st16(&dOs[buf][r * QP + tcol(r, cc)], pdo[x]);
         }
         if (tid < BR) {
             const bool ok = pi0 + tid < lq;     // a row past the end has P = 0
@@ -270,8 +283,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                 }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    sa[mb] = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa[mb]);
-                    pa[mb] = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa[mb]);
+                    const int o = (mb * 32 + c) * QP + tcol(mb * 32 + c, 16 * s + 8 * g);
+                    sa[mb] = T::mma(ld16(&Qb[o]), kreg[s], sa[mb]);
+                    pa[mb] = T::mma(ld16(&dOb[o]), vreg[s], pa[mb]);
                 }
             }
 #pragma unroll
@@ -287,8 +301,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                        dva[db] = T::mma(ldt_acc(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        dka[db] = T::mma(ldt_acc(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
                     }
                 }
             }
@@ -307,8 +321,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                 }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    sa = T::mma(ld16(&Qb[(mb * 32 + c) * QP + 16 * s + 8 * g]), kreg[s], sa);
-                    pa = T::mma(ld16(&dOb[(mb * 32 + c) * QP + 16 * s + 8 * g]), vreg[s], pa);
+                    const int o = (mb * 32 + c) * QP + tcol(mb * 32 + c, 16 * s + 8 * g);
+                    sa = T::mma(ld16(&Qb[o]), kreg[s], sa);
+                    pa = T::mma(ld16(&dOb[o]), vreg[s], pa);
                 }
                 if (masked)
                     softmax_grad_tile_nd<true>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
@@ -321,8 +336,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     const u32x4 bS = acc_to_operand<T>(pa, hh);
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ld_tr<true>(dOb, QP, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ld_tr<true>(Qb, QP, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                        dva[db] = T::mma(ldt_acc(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        dka[db] = T::mma(ldt_acc(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
                     }
                     // dS^T rows j = 32w + c; bS holds query rows 16hh + 4g + 0..3 and
                     // 16hh + 8 + 4g + 0..3 of this half tile, packed in pairs
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                 for (int x = 0; x < NBLK; ++x) {
                     const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
                     acc[x] = T::mma(ld_tr<false>(dST, SP, 16 * ks, ib * 32, lane),
-                                    ld_tr<false>(Ks, QP, 16 * ks, db * 32, lane), acc[x]);
+                                    ldt_row(Ks, 16 * ks, db * 32, lane), acc[x]);
                 }
             // accumulator rows of this (sequence, head): head-major, row stride D floats
             const int64_t arow0 = p.varlen ? ((int64_t)h * p.Sq + q0) : (((int64_t)b * p.Hq + h) * p.Sq);

@@ -213,6 +213,36 @@ __device__ __forceinline__ u32x4 ld_tr(const uint16_t* X, int ld, int k0, int n0
     return r;
 }
 
+// Tiles of 128 16-bit columns (256-byte rows, no padding) store 16-byte chunk
+// j of row r at chunk j ^ swz128(r).  A 16-byte read of rows r0 .. r0+15 at
+// one chunk (the MFMA A operand, one row per lane) then meets 16 distinct
+// chunks, and a transposed read of 4 consecutive rows (from a multiple of 4)
+// over 4 chunks of one aligned group meets 4 distinct groups: both fill the
+// 64 banks without conflict, where a padded row pitch serves only one of them.
+// In the D=128 key-tile kernel: 343 -> 306 us on B2 H16 S4096 bf16 causal,
+// 390 -> 355 us on 8 packed sequences x 32 heads.  (A 160-column pitch with
+// the swap confined to each group of four chunks, whose addresses stay
+// immediate offsets, gave 330 us; in the dQ pass, at 252 of 256 registers,
+// either form spills.)
+__device__ __forceinline__ int swz128(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz128_col(int r, int col) { return (((col >> 3) ^ swz128(r)) << 3) | (col & 7); }
+
+// ld_tr on a swizzled 128-column tile.
+template <bool ACC>
+__device__ __forceinline__ u32x4 ld_tr_swz128(const uint16_t* X, int k0, int n0, int lane) {
+    const int p = lane & 15, grp = lane >> 4;
+    const int g = grp >> 1, cb = (grp & 1) * 16;
+    const int kr0 = (ACC ? (k0 + 4 * g) : (k0 + 8 * g)) + (p >> 2);
+    const int kr1 = (ACC ? (k0 + 8 + 4 * g) : (k0 + 8 * g + 4)) + (p >> 2);
+    const int col = n0 + cb + 4 * (p & 3);
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + kr0 * 128 + swz128_col(kr0, col)));
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(X + kr1 * 128 + swz128_col(kr1, col)));
+    const u32x2 a = __builtin_bit_cast(u32x2, v0), b = __builtin_bit_cast(u32x2, v1);
+    u32x4 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    return r;
+}
+
 // The same for v_mfma_f32_16x16x32 operands: 16-lane group G = lane / 16 holds
 // k = k0 + 8*G + t (t = 0..7) of column n0 + lane % 16.  (16x16 C tiles: lane
 // holds column lane % 16, rows 4*G + r in register r.)
