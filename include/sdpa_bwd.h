@@ -28,9 +28,12 @@
  *   (T, N, D) ("TND", the Ascend page's only layout).  The last (D) stride must
  *   be 1 and every base pointer 16-byte aligned; the S/T and H/N strides must
  *   keep every row 16-byte aligned.  The row stride (S or T) of every tensor
- *   and of the statistics must lie in [0, 2^23) elements.  D is 64, 128 or
- *   192, the same for Q/K and V (the selected calls also take D = 192 with a
- *   value head dim of 128).
+ *   and of the statistics must lie in [0, 2^23) elements.  Head dims: D of
+ *   Q, K, dQ and dK, Dv of V, O, dO and dV; (D, Dv) is (64, 64), (128, 128),
+ *   (192, 192) or (192, 128), the unequal pair that the Ascend page's head
+ *   dim constraint allows ("Constraints": D is 192 or 128, K and V may
+ *   differ).  Any other pair returns SDPA_ERR_UNSUPPORTED; D or Dv below 1
+ *   is SDPA_ERR_INVALID.
  *   Any other layout returns SDPA_ERR_UNSUPPORTED.
  * - Ownership: the caller owns every buffer, including the workspace.  The
  *   library allocates no device memory, keeps no per-call state and never
@@ -120,7 +123,8 @@ const char* sdpa_last_error(void);
  * sdpa_fwd_stats: attention forward in training mode, producing O and the LSE
  * statistics that the backward consumes (the cuDNN sample's forward graph with
  * is_inference=False: outputs o and stats; forward-graph cell).
- *   q: (B, Hq, Sq, D); k, v: (B, Hkv, Sk, D); o_out: (B, Hq, Sq, D) written;
+ *   q: (B, Hq, Sq, D); k: (B, Hkv, Sk, D); v: (B, Hkv, Sk, Dv);
+ *   o_out: (B, Hq, Sq, Dv) written;
  *   lse_out: (B, Hq, Sq) written, natural-log LSE of the scaled scores.
  *   Hq must be a multiple of Hkv; query head h reads KV head h / (Hq/Hkv).
  *   causal: key j visible to query i iff j <= i, for any Sq and Sk (aligned
@@ -129,7 +133,7 @@ const char* sdpa_last_error(void);
  * Needs no workspace.
  */
 int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
-                   int64_t D, double scale, int causal,
+                   int64_t D, int64_t Dv, double scale, int causal,
                    const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
                    const sdpa_tensor4* o_out, const sdpa_stats_out* lse_out, void* stream);
 
@@ -140,7 +144,8 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
  * the equivalent LSE = max + ln(sum)).
  *   cu_seqlens_q_host, cu_seqlens_kv_host: host arrays of `batch` inclusive
  *   end offsets (no leading zero), non-decreasing; read during the call only.
- *   q: (Tq, Hq, D); k, v: (Tk, Hkv, D); o_out: (Tq, Hq, D) written.
+ *   q: (Tq, Hq, D); k: (Tk, Hkv, D); v: (Tk, Hkv, Dv); o_out: (Tq, Hq, Dv)
+ *   written.
  *   lse_out: natural-log LSE of token t, head n at t*stride_s + n*stride_h
  *   (stride_b unused), written for every query token.
  *   causal: per sequence, key j visible to query i iff j <= i in local
@@ -149,7 +154,7 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
  * Needs no workspace; errors as sdpa_fwd_stats.
  */
 int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                           double scale, int causal, const sdpa_tensor3* q, const sdpa_tensor3* k,
                           const sdpa_tensor3* v, const sdpa_tensor3* o_out, const sdpa_stats_out* lse_out,
                           void* stream);
@@ -158,7 +163,7 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  * sdpa_bwd_workspace_size / sdpa_bwd: dense SDPA backward (the cuDNN sample's
  * sdpa_backward node: inputs q, k, v, o, dO, stats, attn_scale,
  * use_causal_mask; outputs dQ, dK, dV; backward-graph cell).
- *   Shapes as sdpa_fwd_stats; dout, dq like q; dk, dv like k.
+ *   Shapes as sdpa_fwd_stats; dq like q, dk like k; dout like o, dv like v.
  *   deterministic selects how dQ is formed (the Ascend page's deterministic
  *     option, "Constraints", extended):
  *     0: the library's fastest method; today that is the atomic-free query-
@@ -166,9 +171,9 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  *     1: guaranteed bitwise reproducible: the atomic-free query-outer pass;
  *     2: fp32 atomic accumulation inside the key-outer kernel and a final
  *        conversion (FlashAttention-2's method; run-to-run rounding
- *        differences possible), at D=64 and D=128; at D=192 the key-outer
- *        kernel's tiles leave no LDS for it and the value returns
- *        SDPA_ERR_UNSUPPORTED.
+ *        differences possible), at (D, Dv) = (64, 64) and (128, 128); at
+ *        D=192 the key-outer kernel's tiles leave no LDS for it and the
+ *        value returns SDPA_ERR_UNSUPPORTED.
  *     Any other value: SDPA_ERR_INVALID.  The workspace size depends on it.
  *   grad_dtype: element type of dq, dk and dv: `dtype`, or SDPA_F32 for fp32
  *     gradients (same layout rules, strides in fp32 elements); anything else
@@ -177,8 +182,8 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
  *     contents on entry, 256-byte aligned.
  */
 int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                            int64_t Sk, int64_t D, int deterministic, size_t* bytes);
-int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                            int64_t Sk, int64_t D, int64_t Dv, int deterministic, size_t* bytes);
+int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
              double scale, int causal, int deterministic, int grad_dtype,
              const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
              const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
@@ -203,7 +208,7 @@ int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t 
  * time on one GPU (different streams or threads) race on it and must be
  * serialised by the caller.
  */
-int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
                      double scale, int causal, int deterministic, int grad_dtype,
                      const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
                      const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
@@ -218,14 +223,15 @@ int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
  * and {1024} for one sequence).  Sequence b owns rows [cu[b-1], cu[b]) with
  * cu[-1] = 0.  Causal masking uses positions local to each sequence (j <= i,
  * top-left aligned when the query and key lengths differ).
- *   q, o, dout, dq: (Tq, Hq, D); k, v, dk, dv: (Tk, Hkv, D); stats per (t, h).
+ *   q, dq: (Tq, Hq, D); o, dout: (Tq, Hq, Dv); k, dk: (Tk, Hkv, D);
+ *   v, dv: (Tk, Hkv, Dv); stats per (t, h).
  *   deterministic, grad_dtype: as for sdpa_bwd.
  */
 int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
-                                   int64_t D, int deterministic, size_t* bytes);
+                                   int64_t D, int64_t Dv, int deterministic, size_t* bytes);
 int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                     double scale, int causal, int deterministic, int grad_dtype,
                     const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                     const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,

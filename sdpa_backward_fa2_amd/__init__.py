@@ -71,19 +71,19 @@ PI64 = ctypes.POINTER(c_i64)
 _SIGS = {
     "sdpa_status_string": (ctypes.c_char_p, [c_int]),
     "sdpa_last_error": (ctypes.c_char_p, []),
-    "sdpa_fwd_stats": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
+    "sdpa_fwd_stats": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                P4, P4, P4, P4, ctypes.POINTER(StatsOut), c_vp]),
-    "sdpa_fwd_stats_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int,
+    "sdpa_fwd_stats_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int,
                                       P3, P3, P3, P3, ctypes.POINTER(StatsOut), c_vp]),
-    "sdpa_bwd_workspace_size": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
+    "sdpa_bwd_workspace_size": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_int,
                                         ctypes.POINTER(c_size)]),
-    "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
+    "sdpa_bwd": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                          P4, P4, P4, P4, P4, PS, P4, P4, P4, c_vp, c_size, c_vp]),
-    "sdpa_bwd_noalloc": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
+    "sdpa_bwd_noalloc": (c_int, [c_int, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                                  P4, P4, P4, P4, P4, PS, P4, P4, P4, c_vp]),
-    "sdpa_bwd_varlen_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_int,
+    "sdpa_bwd_varlen_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_int,
                                                ctypes.POINTER(c_size)]),
-    "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
+    "sdpa_bwd_varlen": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64, c_dbl, c_int, c_int, c_int,
                                 P3, P3, P3, P3, P3, PS, P3, P3, P3, c_vp, c_size, c_vp]),
     "sdpa_bwd_selected_workspace_size": (c_int, [c_int, c_i64, PI64, PI64, c_i64, c_i64, c_i64, c_i64,
                                                  c_i64, c_i64, c_int, ctypes.POINTER(c_size)]),
@@ -231,17 +231,18 @@ def _workspace(nbytes: int, device, workspace: torch.Tensor | None) -> torch.Ten
 # ----------------------------------------------------------------------------
 
 def fwd_stats(q, k, v, scale: float, causal: bool, o=None, lse=None):
-    """O and the natural-log LSE (B, Hq, Sq) fp32 for dense (B, H, S, D) inputs."""
+    """O and the natural-log LSE (B, Hq, Sq) fp32 for dense (B, H, S, D) inputs
+    (v and O may have their own head dim Dv)."""
     lib = load()
     B, Hq, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
+    Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty_like(q) if Dv == D else q.new_empty((B, Hq, Sq, Dv))
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     l3 = _squeeze_stats(lse)
     so = StatsOut(l3.data_ptr(), *l3.stride())
-    st = lib.sdpa_fwd_stats(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal),
+    st = lib.sdpa_fwd_stats(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, Dv, float(scale), int(causal),
                             _t4(q), _t4(k), _t4(v), _t4(o), ctypes.byref(so), _stream_ptr(q.device))
     _check(st, "sdpa_fwd_stats")
     return o, lse
@@ -252,15 +253,15 @@ def fwd_stats_varlen(q, k, v, cu_q, cu_kv, scale: float, causal: bool, o=None, l
     cu_q / cu_kv: host sequences of inclusive end offsets."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
-    Hkv = k.shape[1]
+    Hkv, Dv = k.shape[1], v.shape[2]
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty_like(q) if Dv == D else q.new_empty((q.shape[0], Hq, Dv))
     if lse is None:
         lse = torch.empty((q.shape[0], Hq), dtype=torch.float32, device=q.device)
     so = StatsOut(lse.data_ptr(), 0, lse.stride(1), lse.stride(0))
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
-    st = lib.sdpa_fwd_stats_varlen(_dtype_code(q), n, aq, ak, Hq, Hkv, D, float(scale), int(causal),
+    st = lib.sdpa_fwd_stats_varlen(_dtype_code(q), n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(causal),
                                    _t3(q), _t3(k), _t3(v), _t3(o), ctypes.byref(so), _stream_ptr(q.device))
     _check(st, "sdpa_fwd_stats_varlen")
     return o, lse
@@ -276,9 +277,9 @@ DQ_DETERMINISTIC = 1    # bitwise reproducible
 DQ_ATOMIC = 2           # fp32 atomic accumulation (FA2's method)
 
 
-def bwd_workspace_size(dtype: int, B, Hq, Hkv, Sq, Sk, D, deterministic: int) -> int:
+def bwd_workspace_size(dtype: int, B, Hq, Hkv, Sq, Sk, D, deterministic: int, Dv=None) -> int:
     n = c_size(0)
-    _check(load().sdpa_bwd_workspace_size(dtype, B, Hq, Hkv, Sq, Sk, D, int(deterministic),
+    _check(load().sdpa_bwd_workspace_size(dtype, B, Hq, Hkv, Sq, Sk, D, D if Dv is None else Dv, int(deterministic),
                                           ctypes.byref(n)), "sdpa_bwd_workspace_size")
     return n.value
 
@@ -308,14 +309,14 @@ def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, determinist
     float32 (given tensors, else grad_dtype)."""
     lib = load()
     B, Hq, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
+    Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
     dt = _dtype_code(q)
     dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
-    nbytes = bwd_workspace_size(dt, B, Hq, Hkv, Sq, Sk, D, deterministic)
+    nbytes = bwd_workspace_size(dt, B, Hq, Hkv, Sq, Sk, D, deterministic, Dv)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=False)
     structs = [_t4(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal), int(deterministic), gdt,
+    args = (dt, B, Hq, Hkv, Sq, Sk, D, Dv, float(scale), int(causal), int(deterministic), gdt,
             *[ctypes.byref(x) for x in structs[:5]], ctypes.byref(sa),
             *[ctypes.byref(x) for x in structs[5:]], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
@@ -348,11 +349,11 @@ def bwd_noalloc(q, k, v, o, dout, stats, scale: float, causal: bool, determinist
     SDPA_ERR_WORKSPACE).  Outputs as bwd; given dq, dk, dv are written in place."""
     lib = load()
     B, Hq, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
+    Hkv, Sk, Dv = k.shape[1], k.shape[2], v.shape[3]
     dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     sa = _stats_arg(stats, packed=False)
     structs = [_t4(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    _check(lib.sdpa_bwd_noalloc(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, float(scale), int(causal),
+    _check(lib.sdpa_bwd_noalloc(_dtype_code(q), B, Hq, Hkv, Sq, Sk, D, Dv, float(scale), int(causal),
                                 int(deterministic), gdt, *[ctypes.byref(x) for x in structs[:5]],
                                 ctypes.byref(sa), *[ctypes.byref(x) for x in structs[5:]],
                                 _stream_ptr(q.device)), "sdpa_bwd_noalloc")
@@ -368,11 +369,12 @@ def _cu_host(cu):
     return arr, len(cu)
 
 
-def bwd_varlen_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, deterministic) -> int:
+def bwd_varlen_workspace_size(dtype, cu_q, cu_kv, Hq, Hkv, D, deterministic, Dv=None) -> int:
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
     out = c_size(0)
-    _check(load().sdpa_bwd_varlen_workspace_size(dtype, n, aq, ak, Hq, Hkv, D, int(deterministic),
+    _check(load().sdpa_bwd_varlen_workspace_size(dtype, n, aq, ak, Hq, Hkv, D, D if Dv is None else Dv,
+                                                 int(deterministic),
                                                  ctypes.byref(out)), "sdpa_bwd_varlen_workspace_size")
     return out.value
 
@@ -385,16 +387,16 @@ def prepare_varlen(q, k, v, o, dout, stats, cu_q, cu_kv, scale: float, causal: b
     or a (max, sum) pair of (T, Hq[, 8]) tensors."""
     lib = load()
     Hq, D = q.shape[1], q.shape[2]
-    Hkv = k.shape[1]
+    Hkv, Dv = k.shape[1], v.shape[2]
     dt = _dtype_code(q)
     dq, dk, dv, gdt = _grads(q, k, v, dq, dk, dv, grad_dtype)
     aq, n = _cu_host(cu_q)
     ak, _ = _cu_host(cu_kv)
-    nbytes = bwd_varlen_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, deterministic)
+    nbytes = bwd_varlen_workspace_size(dt, cu_q, cu_kv, Hq, Hkv, D, deterministic, Dv)
     ws = _workspace(nbytes, q.device, workspace)
     sa = _stats_arg(stats, packed=True)
     structs = [_t3(x) for x in (q, k, v, o, dout, dq, dk, dv)]
-    args = (dt, n, aq, ak, Hq, Hkv, D, float(scale), int(causal), int(deterministic), gdt,
+    args = (dt, n, aq, ak, Hq, Hkv, D, Dv, float(scale), int(causal), int(deterministic), gdt,
             *structs[:5], ctypes.byref(sa), *structs[5:], ws.data_ptr(), ws.numel(),
             _stream_ptr(q.device))
     fn = lib.sdpa_bwd_varlen

@@ -106,11 +106,15 @@ Carve carve_bwd(int64_t rows, int64_t D, bool deterministic) {
 bool dq_mode_ok(int mode) { return mode >= 0 && mode <= 2; }
 bool dq_atomic(int mode, int64_t D) { (void)D; return mode == 2; }
 
-// Head dims of the dense and packed paths (equal for Q/K and V).  At D = 192
-// the key-tile kernel's tiles take 102 KB of LDS, which leaves no room for
-// the K and dS^T tiles of the atomic dQ form: dQ mode 2 is not offered there.
-bool dense_dim_ok(int64_t D) { return D == 64 || D == 128 || D == 192; }
-bool dense_mode_ok(int mode, int64_t D) { return !(D == 192 && mode == 2); }
+// Head dims of the dense and packed paths: D of Q and K, Dv of V, O and dO,
+// equal (64, 128, 192) or (192, 128), the pair the Ascend page names.  At
+// D = 192 the key-tile kernel's tiles take 102 KB of LDS, which leaves no
+// room for the K and dS^T tiles of the atomic dQ form: dQ mode 2 is not
+// offered there.
+bool dense_dims_ok(int64_t D, int64_t Dv) {
+    return (D == Dv && (D == 64 || D == 128 || D == 192)) || (D == 192 && Dv == 128);
+}
+bool dense_mode_ok(int mode, int64_t D, int64_t Dv) { return !(mode == 2 && (D == 192 || Dv != D)); }
 
 int check_stats(const sdpa_stats* s) {
     if (!s->lse_or_max) return SDPA_ERR_NULLPTR;
@@ -215,16 +219,16 @@ const char* sdpa_last_error(void) { return g_last_error.c_str(); }
 // ---------------------------------------------------------------------------
 
 int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk,
-                   int64_t D, double scale, int causal,
+                   int64_t D, int64_t Dv, double scale, int causal,
                    const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
                    const sdpa_tensor4* o_out, const sdpa_stats_out* lse_out, void* stream) {
     if (!q || !k || !v || !o_out || !lse_out) return SDPA_ERR_NULLPTR;
     if (!q->data || !k->data || !v->data || !o_out->data || !lse_out->lse) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
-    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
-    if (!dense_dim_ok(D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o_out})
         if (int s = tensor4_ok(t)) return s;
     if (Sq >= kMaxLen || Sk >= kMaxLen || B * Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
@@ -237,17 +241,17 @@ int sdpa_fwd_stats(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, in
     p.lse_sb = lse_out->stride_b; p.lse_sh = lse_out->stride_h; p.lse_ss = lse_out->stride_s;
     p.B = (int)B; p.Hq = (int)Hq; p.Hkv = (int)Hkv; p.Sq = (int)Sq; p.Sk = (int)Sk;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
-    hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)Sq, causal != 0, static_cast<hipStream_t>(stream));
+    hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)Dv, (int)Sq, causal != 0, static_cast<hipStream_t>(stream));
     if (log_enabled())
-        std::fprintf(stderr, "[sdpa_bwd] fwd_stats dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld causal=%d grid=(%lld,%lld)\n",
+        std::fprintf(stderr, "[sdpa_bwd] fwd_stats dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld Dv=%lld causal=%d grid=(%lld,%lld)\n",
                      dtype, (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq, (long long)Sk,
-                     (long long)D, causal, (long long)((Sq + 127) / 128), (long long)(B * Hq));
+                     (long long)D, (long long)Dv, causal, (long long)((Sq + 127) / 128), (long long)(B * Hq));
     if (e != hipSuccess) return fail_hip(e, "fwd launch");
     return SDPA_OK;
 }
 
 int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                          const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                           double scale, int causal, const sdpa_tensor3* q, const sdpa_tensor3* k,
                           const sdpa_tensor3* v, const sdpa_tensor3* o_out, const sdpa_stats_out* lse_out,
                           void* stream) {
@@ -255,11 +259,11 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
     if (!q || !k || !v || !o_out || !lse_out) return SDPA_ERR_NULLPTR;
     if (!q->data || !k->data || !v->data || !o_out->data || !lse_out->lse) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
-    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
-    if (!dense_dim_ok(D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o_out})
         if (int s = tensor3_ok(t)) return s;
     if (std::min<int64_t>(batch, sdpa::kMaxSeqArgs) * Hq > kMaxGridY) return SDPA_ERR_UNSUPPORTED;
@@ -289,7 +293,7 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
         }
         p.B = (int)(c1 - c0);
         if (mlq == 0) continue;
-        hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)mlq, causal != 0, static_cast<hipStream_t>(stream));
+        hipError_t e = sdpa::launch_fwd(p, dtype, (int)D, (int)Dv, (int)mlq, causal != 0, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail_hip(e, "fwd varlen launch");
     }
     return SDPA_OK;
@@ -300,20 +304,20 @@ int sdpa_fwd_stats_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_
 // ---------------------------------------------------------------------------
 
 int sdpa_bwd_workspace_size(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq,
-                            int64_t Sk, int64_t D, int deterministic, size_t* bytes) {
+                            int64_t Sk, int64_t D, int64_t Dv, int deterministic, size_t* bytes) {
     if (!bytes) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
-    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
-    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv) || !dense_mode_ok(deterministic, D, Dv)) return SDPA_ERR_UNSUPPORTED;
     *bytes = carve_bwd(B * Hq * Sq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
 
-static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool det,
+static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, int64_t Dv, bool causal, bool det,
                    const Packed* packed, int64_t B, int64_t Sq, int64_t Sk, hipStream_t st) {
     sdpa::BwdLaunch L{};
-    L.dtype = dtype; L.D = (int)D; L.causal = causal; L.deterministic = det;
+    L.dtype = dtype; L.D = (int)D; L.Dv = (int)Dv; L.causal = causal; L.deterministic = det;
     if (!packed) {
         p.varlen = 0;
         p.seqs.n = 0;
@@ -368,7 +372,7 @@ static int run_bwd(int dtype, sdpa::BwdParams& p, int64_t D, bool causal, bool d
 // The dense backward behind both entry points: `workspace` is the caller's
 // buffer (sdpa_bwd), or null for the library's own scratch array
 // (sdpa_bwd_noalloc), which is fetched only once the arguments are valid.
-static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
                      double scale, int causal, int deterministic, int grad_dtype,
                      const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
                      const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
@@ -381,12 +385,12 @@ static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
     if (!scratch && !workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
-    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1) return SDPA_ERR_INVALID;
+    if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1) return SDPA_ERR_INVALID;
     if (Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
-    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv) || !dense_mode_ok(deterministic, D, Dv)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor4* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor4_ok(t)) return s;
     if (int s = check_stats_stride(stats)) return s;
@@ -422,28 +426,28 @@ static int bwd_dense(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
     if (log_enabled())
-        std::fprintf(stderr, "[sdpa_bwd] bwd%s dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld causal=%d det=%d main_grid=(%lld,%lld)\n",
+        std::fprintf(stderr, "[sdpa_bwd] bwd%s dtype=%d B=%lld Hq=%lld Hkv=%lld Sq=%lld Sk=%lld D=%lld Dv=%lld causal=%d det=%d main_grid=(%lld,%lld)\n",
                      scratch ? "_noalloc" : "", dtype, (long long)B, (long long)Hq, (long long)Hkv, (long long)Sq,
-                     (long long)Sk, (long long)D, causal, (int)det, (long long)(B * Hkv), (long long)((Sk + 127) / 128));
-    return run_bwd(dtype, p, D, causal != 0, det, nullptr, B, Sq, Sk, static_cast<hipStream_t>(stream));
+                     (long long)Sk, (long long)D, (long long)Dv, causal, (int)det, (long long)(B * Hkv), (long long)((Sk + 127) / 128));
+    return run_bwd(dtype, p, D, Dv, causal != 0, det, nullptr, B, Sq, Sk, static_cast<hipStream_t>(stream));
 }
 
-int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+int sdpa_bwd(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
              double scale, int causal, int deterministic, int grad_dtype,
              const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
              const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
              const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv,
              void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
+    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
                      stats, dq, dk, dv, workspace, workspace_bytes, false, stream);
 }
 
-int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D, int64_t Dv,
                      double scale, int causal, int deterministic, int grad_dtype,
                      const sdpa_tensor4* q, const sdpa_tensor4* k, const sdpa_tensor4* v,
                      const sdpa_tensor4* o, const sdpa_tensor4* dout, const sdpa_stats* stats,
                      const sdpa_tensor4* dq, const sdpa_tensor4* dk, const sdpa_tensor4* dv, void* stream) {
-    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
+    return bwd_dense(dtype, B, Hq, Hkv, Sq, Sk, D, Dv, scale, causal, deterministic, grad_dtype, q, k, v, o, dout,
                      stats, dq, dk, dv, nullptr, 0, true, stream);
 }
 
@@ -453,20 +457,20 @@ int sdpa_bwd_noalloc(int dtype, int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, 
 
 int sdpa_bwd_varlen_workspace_size(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
                                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv,
-                                   int64_t D, int deterministic, size_t* bytes) {
+                                   int64_t D, int64_t Dv, int deterministic, size_t* bytes) {
     if (!bytes || !cu_seqlens_q_host || !cu_seqlens_kv_host) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
-    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
-    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv) || !dense_mode_ok(deterministic, D, Dv)) return SDPA_ERR_UNSUPPORTED;
     *bytes = carve_bwd(P.Tq * Hq, D, !dq_atomic(deterministic, D)).total;
     return SDPA_OK;
 }
 
 int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
-                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D,
+                    const int64_t* cu_seqlens_kv_host, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv,
                     double scale, int causal, int deterministic, int grad_dtype,
                     const sdpa_tensor3* q, const sdpa_tensor3* k, const sdpa_tensor3* v,
                     const sdpa_tensor3* o, const sdpa_tensor3* dout, const sdpa_stats* stats,
@@ -480,13 +484,13 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     if (!workspace) return SDPA_ERR_NULLPTR;
     if (dtype != SDPA_F16 && dtype != SDPA_BF16) return SDPA_ERR_INVALID;
     if (grad_dtype != dtype && grad_dtype != SDPA_F32) return SDPA_ERR_INVALID;
-    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
+    if (batch < 1 || Hq < 1 || Hkv < 1 || D < 1 || Dv < 1 || Hq % Hkv) return SDPA_ERR_INVALID;
     if (!std::isfinite(scale)) return SDPA_ERR_INVALID;
     if (!dq_mode_ok(deterministic)) return SDPA_ERR_INVALID;
     if (int s = check_stats_kind(stats)) return s;
     Packed P;
     if (int s = read_packed(batch, cu_seqlens_q_host, cu_seqlens_kv_host, P)) return s;
-    if (!dense_dim_ok(D) || !dense_mode_ok(deterministic, D)) return SDPA_ERR_UNSUPPORTED;
+    if (!dense_dims_ok(D, Dv) || !dense_mode_ok(deterministic, D, Dv)) return SDPA_ERR_UNSUPPORTED;
     for (const sdpa_tensor3* t : {q, k, v, o, dout, dq, dk, dv})
         if (int s = tensor3_ok(t)) return s;
     if (int s = check_stats_stride(stats)) return s;
@@ -515,10 +519,10 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
     p.scale = (float)scale;
     p.scale_log2 = (float)(scale * 1.4426950408889634);
     if (log_enabled())
-        std::fprintf(stderr, "[sdpa_bwd] bwd_varlen dtype=%d batch=%lld Tq=%lld Tk=%lld Hq=%lld Hkv=%lld D=%lld causal=%d det=%d\n",
+        std::fprintf(stderr, "[sdpa_bwd] bwd_varlen dtype=%d batch=%lld Tq=%lld Tk=%lld Hq=%lld Hkv=%lld D=%lld Dv=%lld causal=%d det=%d\n",
                      dtype, (long long)batch, (long long)P.Tq, (long long)P.Tk, (long long)Hq,
-                     (long long)Hkv, (long long)D, causal, (int)det);
-    return run_bwd(dtype, p, D, causal != 0, det, &P, batch, 0, 0, static_cast<hipStream_t>(stream));
+                     (long long)Hkv, (long long)D, (long long)Dv, causal, (int)det);
+    return run_bwd(dtype, p, D, Dv, causal != 0, det, &P, batch, 0, 0, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -7,7 +7,7 @@
 namespace sdpa {
 
 hipError_t launch_bwd_d128(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    return L.dtype == 0 ? launch_bwd_big_d<F16, 128>(p, L, st) : launch_bwd_big_d<BF16, 128>(p, L, st);
+    return L.dtype == 0 ? launch_bwd_big_d<F16, 128, 128>(p, L, st) : launch_bwd_big_d<BF16, 128, 128>(p, L, st);
 }
 
 hipError_t launch_bwd_d64_atomic(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {

@@ -85,37 +85,47 @@ __device__ __forceinline__ void xcd_group_order(int n_unit, int n_item, int L, i
     unit = (gi * kXcdGroup + s % gu) * 8 + xcd;
 }
 
-template <class T, int D, bool CAUSAL, bool DQ_ATOMIC>
-__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
+// DK: head dim of Q and K; DV: of V, O and dO (equal unless (192, 128)).
+template <class T, int DK, int DV, bool CAUSAL, bool DQ_ATOMIC>
+__global__ __launch_bounds__(256, (DK == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
+    static_assert(!DQ_ATOMIC || DK == DV, "the atomic dQ form takes equal head dims");
+    constexpr int D = DK;            // the atomic form's head dim
     constexpr int BC = 128;          // keys per workgroup: 4 wavefronts x 32
     constexpr int BR = 64;           // query rows per step
     constexpr int NW = 4;
-    constexpr int KS = D / 16;       // k-steps over the head dimension
+    constexpr int KSK = DK / 16, KSV = DV / 16;   // k-steps of S (over DK) and dP (over DV)
+    constexpr int KSM = KSK > KSV ? KSK : KSV;
     constexpr int MB = BR / 32;      // 32-row blocks of the query tile
-    constexpr int DB = D / 32;       // 32-row blocks of dK^T / dV^T
-    // row stride of Qs, dOs, Ks [row][d]: D=128 tiles are unpadded and
-    // chunk-swizzled (swz128), the others padded by 8 columns
-    constexpr bool SWZ = D == 128;
-    constexpr int QP = SWZ ? D : D + 8;
+    constexpr int DBK = DK / 32, DBV = DV / 32;   // 32-row blocks of dK^T and dV^T
+    constexpr int DBM = DBK > DBV ? DBK : DBV;
+    // row strides of Qs (and Ks) and dOs [row][d]: 128-column tiles are
+    // unpadded and chunk-swizzled (swz128), the others padded by 8 columns
+    constexpr bool SWQ = DK == 128, SWO = DV == 128;
+    constexpr int QPK = SWQ ? DK : DK + 8, QPV = SWO ? DV : DV + 8;
     constexpr int SP = BR + 8;       // row stride of dST          [j][i]
-    constexpr int CH = BR * D / 8 / 256;     // 16-byte chunks per thread per tile
-    constexpr int NBLK = MB * DB / NW;       // dQ 32x32 blocks per wavefront
-    static_assert(CH >= 1 && NBLK >= 1, "tile shape");
-    __shared__ __align__(16) uint16_t Qs[2][BR * QP];
-    __shared__ __align__(16) uint16_t dOs[2][BR * QP];
-    __shared__ __align__(16) uint16_t Ks[DQ_ATOMIC ? BC * QP : 8];
+    constexpr int CHK = BR * DK / 8 / 256, CHV = BR * DV / 8 / 256;   // 16-byte chunks per thread per tile
+    constexpr int NBLK = MB * DBK / NW;      // dQ 32x32 blocks per wavefront
+    static_assert(CHK >= 1 && CHV >= 1 && NBLK >= 1, "tile shape");
+    __shared__ __align__(16) uint16_t Qs[2][BR * QPK];
+    __shared__ __align__(16) uint16_t dOs[2][BR * QPV];
+    __shared__ __align__(16) uint16_t Ks[DQ_ATOMIC ? BC * QPK : 8];
     __shared__ __align__(16) uint16_t dST[DQ_ATOMIC ? BC * SP : 8];
     __shared__ __align__(16) float lse_s[2][BR];
     __shared__ __align__(16) float dlt_s[2][BR];
     // column position of (row, col) in a tile, and the transposed operand read
-    auto tcol = [](int row, int col) { return SWZ ? swz128_col(row, col) : col; };
-    auto ldt_acc = [&](const uint16_t* X, int k0, int n0, int ln) {
-        if constexpr (SWZ) return ld_tr_swz128<true>(X, k0, n0, ln);
-        else return ld_tr<true>(X, QP, k0, n0, ln);
+    auto tcolq = [](int row, int col) { return SWQ ? swz128_col(row, col) : col; };
+    auto tcolo = [](int row, int col) { return SWO ? swz128_col(row, col) : col; };
+    auto ldt_q = [&](const uint16_t* X, int k0, int n0, int ln) {
+        if constexpr (SWQ) return ld_tr_swz128<true>(X, k0, n0, ln);
+        else return ld_tr<true>(X, QPK, k0, n0, ln);
+    };
+    auto ldt_o = [&](const uint16_t* X, int k0, int n0, int ln) {
+        if constexpr (SWO) return ld_tr_swz128<true>(X, k0, n0, ln);
+        else return ld_tr<true>(X, QPV, k0, n0, ln);
     };
     auto ldt_row = [&](const uint16_t* X, int k0, int n0, int ln) {
-        if constexpr (SWZ) return ld_tr_swz128<false>(X, k0, n0, ln);
-        else return ld_tr<false>(X, QP, k0, n0, ln);
+        if constexpr (SWQ) return ld_tr_swz128<false>(X, k0, n0, ln);
+        else return ld_tr<false>(X, QPK, k0, n0, ln);
     };
 
     const int tid = threadIdx.x;
@@ -139,18 +149,21 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
 
     const int my_j = j0 + 32 * w + c;
     const bool col_ok = my_j < lk;
-    u32x4 kreg[KS], vreg[KS];
+    u32x4 kreg[KSK], vreg[KSV];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
+    for (int s = 0; s < KSM; ++s) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
-        vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
-        if (DQ_ATOMIC) st16(&Ks[(32 * w + c) * QP + tcol(32 * w + c, 16 * s + 8 * g)], kreg[s]);
+        if (s < KSK) kreg[s] = col_ok ? ld16(kbase + (int64_t)my_j * p.k.ss + 16 * s + 8 * g) : z;
+        if (s < KSV) vreg[s] = col_ok ? ld16(vbase + (int64_t)my_j * p.v.ss + 16 * s + 8 * g) : z;
+        if (DQ_ATOMIC && s < KSK) st16(&Ks[(32 * w + c) * QPK + tcolq(32 * w + c, 16 * s + 8 * g)], kreg[s]);
     }
 
-    f32x16 dva[DB], dka[DB];
+    f32x16 dva[DBV], dka[DBK];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dva[db] = zero16(); dka[db] = zero16(); }
+    for (int db = 0; db < DBM; ++db) {
+        if (db < DBV) dva[db] = zero16();
+        if (db < DBK) dka[db] = zero16();
+    }
 
     // steps: query heads of the group outer, query tiles from the causal start inner
     const int i_begin = CAUSAL ? (j0 / BR) * BR : 0;
@@ -162,17 +175,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     const uint32_t qss = 2u * (uint32_t)p.q.ss, doss = 2u * (uint32_t)p.dout.ss;
     const int64_t ws_ss = p.varlen ? p.Hq : 1;      // row stride of lse2 / delta
     const uint32_t wss = 4u * (uint32_t)ws_ss;
-    uint32_t qoff[CH], dooff[CH];
-    int crow[CH], ccol[CH];
+    // (chunk x of a Q tile: row e / (DK/8); of a dO tile: row e / (DV/8))
+    auto qrow = [&](int x) { return (tid + 256 * x) / (DK / 8); };
+    auto qcol = [&](int x) { return ((tid + 256 * x) % (DK / 8)) * 8; };
+    auto orow = [&](int x) { return (tid + 256 * x) / (DV / 8); };
+    auto ocol = [&](int x) { return ((tid + 256 * x) % (DV / 8)) * 8; };
+    uint32_t qoff[CHK], dooff[CHV];
 #pragma unroll
-    for (int x = 0; x < CH; ++x) {
-        const int e = tid + 256 * x;
-        const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-        crow[x] = r;
-        ccol[x] = cc;
-        qoff[x] = r * qss + 2 * cc;
-        dooff[x] = r * doss + 2 * cc;
-    }
+    for (int x = 0; x < CHK; ++x) qoff[x] = qrow(x) * qss + 2 * qcol(x);
+#pragma unroll
+    for (int x = 0; x < CHV; ++x) dooff[x] = orow(x) * doss + 2 * ocol(x);
 
     // Cursor of the tile to load next (head ld_h, rows from ld_i0): the query
     // rows of one head from i_begin to the end, then the next head of the
@@ -192,30 +204,29 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     // Tile loads are unconditional (rows past the end re-read the last row),
     // and nothing loaded is used before store_tile, so the prefetch of the next
     // tile is not waited for until the current step's products are issued.
-    u32x4 pq[CH], pdo[CH];
+    u32x4 pq[CHK], pdo[CHV];
     float pl = INFINITY, pd = 0.f;
     int pi0 = 0;
     auto load_tile = [&]() {
-        uint32_t oq[CH], odo[CH];
+        uint32_t oq[CHK], odo[CHV];
         uint32_t so = (uint32_t)(tid & (BR - 1)) * wss;
         if (ld_i0 + BR <= lq) {
 #pragma unroll
-            for (int x = 0; x < CH; ++x) { oq[x] = qoff[x]; odo[x] = dooff[x]; }
+            for (int x = 0; x < CHK; ++x) oq[x] = qoff[x];
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) odo[x] = dooff[x];
         } else {
             const int last = lq - 1 - ld_i0;
 #pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                const uint32_t r = min(crow[x], last);
-                oq[x] = r * qss + 2 * ccol[x];
-                odo[x] = r * doss + 2 * ccol[x];
-            }
+            for (int x = 0; x < CHK; ++x) oq[x] = (uint32_t)min(qrow(x), last) * qss + 2 * qcol(x);
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) odo[x] = (uint32_t)min(orow(x), last) * doss + 2 * ocol(x);
             so = (uint32_t)min(tid & (BR - 1), last) * wss;
         }
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            pq[x] = ld16_at(ld_q, oq[x]);
-            pdo[x] = ld16_at(ld_do, odo[x]);
-        }
+        for (int x = 0; x < CHK; ++x) pq[x] = ld16_at(ld_q, oq[x]);
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) pdo[x] = ld16_at(ld_do, odo[x]);
         pl = ldf_at(ld_l, so);
         pd = ldf_at(ld_d, so);
         pi0 = ld_i0;
@@ -230,12 +241,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            const int e = tid + 256 * x;
-            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
-            st16(&Qs[buf][r * QP + tcol(r, cc)], pq[x]);
-            st16(&dOs[buf][r * QP + tcol(r, cc)], pdo[x]);
-        }
+        for (int x = 0; x < CHK; ++x) st16(&Qs[buf][qrow(x) * QPK + tcolq(qrow(x), qcol(x))], pq[x]);
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) st16(&dOs[buf][orow(x) * QPV + tcolo(orow(x), ocol(x))], pdo[x]);
         if (tid < BR) {
             const bool ok = pi0 + tid < lq;     // a row past the end has P = 0
             lse_s[buf][tid] = ok ? pl : INFINITY;
@@ -282,10 +290,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     for (int r = 0; r < 4; ++r) pa[mb][4 * q + r] = nd[r];
                 }
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const int o = (mb * 32 + c) * QP + tcol(mb * 32 + c, 16 * s + 8 * g);
-                    sa[mb] = T::mma(ld16(&Qb[o]), kreg[s], sa[mb]);
-                    pa[mb] = T::mma(ld16(&dOb[o]), vreg[s], pa[mb]);
+                for (int s = 0; s < KSM; ++s) {
+                    const int row = mb * 32 + c, col = 16 * s + 8 * g;
+                    if (s < KSK) sa[mb] = T::mma(ld16(&Qb[row * QPK + tcolq(row, col)]), kreg[s], sa[mb]);
+                    if (s < KSV) pa[mb] = T::mma(ld16(&dOb[row * QPV + tcolo(row, col)]), vreg[s], pa[mb]);
                 }
             }
 #pragma unroll
@@ -300,9 +308,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     const u32x4 bP = acc_to_operand<T>(sa[mb], hh);
                     const u32x4 bS = acc_to_operand<T>(pa[mb], hh);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ldt_acc(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ldt_acc(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                    for (int db = 0; db < DBM; ++db) {
+                        if (db < DBV) dva[db] = T::mma(ldt_o(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        if (db < DBK) dka[db] = T::mma(ldt_q(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
                     }
                 }
             }
@@ -320,10 +328,10 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     for (int r = 0; r < 4; ++r) pa[4 * q + r] = nd[r];
                 }
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const int o = (mb * 32 + c) * QP + tcol(mb * 32 + c, 16 * s + 8 * g);
-                    sa = T::mma(ld16(&Qb[o]), kreg[s], sa);
-                    pa = T::mma(ld16(&dOb[o]), vreg[s], pa);
+                for (int s = 0; s < KSM; ++s) {
+                    const int row = mb * 32 + c, col = 16 * s + 8 * g;
+                    if (s < KSK) sa = T::mma(ld16(&Qb[row * QPK + tcolq(row, col)]), kreg[s], sa);
+                    if (s < KSV) pa = T::mma(ld16(&dOb[row * QPV + tcolo(row, col)]), vreg[s], pa);
                 }
                 if (masked)
                     softmax_grad_tile_nd<true>(sa, pa, &lse_s[buf][mb * 32], p.scale_log2, g, t_key - i0 - mb * 32);
@@ -335,9 +343,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
                     const u32x4 bP = acc_to_operand<T>(sa, hh);
                     const u32x4 bS = acc_to_operand<T>(pa, hh);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        dva[db] = T::mma(ldt_acc(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
-                        dka[db] = T::mma(ldt_acc(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
+                    for (int db = 0; db < DBM; ++db) {
+                        if (db < DBV) dva[db] = T::mma(ldt_o(dOb, mb * 32 + 16 * hh, db * 32, lane), bP, dva[db]);
+                        if (db < DBK) dka[db] = T::mma(ldt_q(Qb, mb * 32 + 16 * hh, db * 32, lane), bS, dka[db]);
                     }
                     // dS^T rows j = 32w + c; bS holds query rows 16hh + 4g + 0..3 and
                     // 16hh + 8 + 4g + 0..3 of this half tile, packed in pairs
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
             for (int ks = 0; ks < BC / 16; ++ks)
 #pragma unroll
                 for (int x = 0; x < NBLK; ++x) {
-                    const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
+                    const int blk = w + x * NW, ib = blk / DBK, db = blk % DBK;
                     acc[x] = T::mma(ld_tr<false>(dST, SP, 16 * ks, ib * 32, lane),
                                     ldt_row(Ks, 16 * ks, db * 32, lane), acc[x]);
                 }
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
             const bool full_rows = i0 + BR <= lq;
 #pragma unroll
             for (int x = 0; x < NBLK; ++x) {
-                const int blk = w + x * NW, ib = blk / DB, db = blk % DB;
+                const int blk = w + x * NW, ib = blk / DBK, db = blk % DBK;
                 float* base = dqa + (ib * 32 + 4 * g) * D + db * 32;
                 if (full_rows) {
 #pragma unroll
@@ -392,14 +400,16 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void bwd_main_kernel(BwdPar
     const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
     const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DBM; ++db)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int e = db * 32 + 8 * q + 4 * g;
-            st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
-                        dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
-            st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
-                        dva[db][4 * q + 3]);
+            if (db < DBK)
+                st_grad4<T>(p.dk.p, dko + e, p.grad_f32, dka[db][4 * q + 0] * p.scale, dka[db][4 * q + 1] * p.scale,
+                            dka[db][4 * q + 2] * p.scale, dka[db][4 * q + 3] * p.scale);
+            if (db < DBV)
+                st_grad4<T>(p.dv.p, dvo + e, p.grad_f32, dva[db][4 * q + 0], dva[db][4 * q + 1], dva[db][4 * q + 2],
+                            dva[db][4 * q + 3]);
         }
 }
 
@@ -422,9 +432,9 @@ __global__ __launch_bounds__(256) void bwd_dq_convert_kernel(BwdParams p) {
     st_grad8<T>(p.dq.p, toff(p.dq, L) + part * 8, p.grad_f32, x);
 }
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, (D > 128 ? 1 : 2)) void bwd_dq8_kernel(BwdParams p) {
-    __shared__ __align__(16) unsigned char arena[Dq8Lds<D>::BYTES];
+    __shared__ __align__(16) unsigned char arena[Dq8Lds<D, DV>::BYTES];
     // units: (sequence, query head), sharing K and V; items: query tiles,
     // the longest causal range (the last tile) first.  With the plain grid
     // each XCD took every eighth query tile of every head and so read every
@@ -432,7 +442,7 @@ __global__ __launch_bounds__(kThreads, (D > 128 ? 1 : 2)) void bwd_dq8_kernel(Bw
     // to 236 us.
     int unit, item;
     xcd_unit_order(gridDim.y, gridDim.x, blockIdx.y * gridDim.x + blockIdx.x, unit, item);
-    bwd_dq8_body<T, D, CAUSAL>(p, arena, gridDim.x - 1 - item, unit);
+    bwd_dq8_body<T, D, CAUSAL, DV>(p, arena, gridDim.x - 1 - item, unit);
 }
 
 // ---------------------------------------------------------------------------
@@ -452,33 +462,35 @@ static hipError_t launch_bwd_atomic_t(const BwdParams& p, const BwdLaunch& L, hi
     }
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
     if (main_grid.x > 0 && main_grid.y > 0)
-        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, D, CAUSAL, true>), main_grid, dim3(256), 0, st, p);
     if ((L.phase & BwdLaunch::kLast) && have_rows)
         PROF_LAUNCH(KID_BWD_DQ_CONVERT, st, (bwd_dq_convert_kernel<T, D>), row_grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
-template <class T, int D, bool CAUSAL>
+// DK: head dim of Q and K; DV: of V, O and dO.
+template <class T, int DK, int DV, bool CAUSAL>
 static hipError_t launch_bwd128_t(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    // D = 192: the host offers only the atomic-free dQ pass
-    if constexpr (D <= 128)
-        if (!L.deterministic) return launch_bwd_atomic_t<T, D, CAUSAL>(p, L, st);
+    // the atomic dQ form exists for equal head dims up to 128 (the host
+    // offers dQ mode 2 only there)
+    if constexpr (DK == DV && DK <= 128)
+        if (!L.deterministic) return launch_bwd_atomic_t<T, DK, CAUSAL>(p, L, st);
     if ((L.phase & BwdLaunch::kFirst) && p.rows > 0) {
-        const hipError_t e = launch_bwd_pre(p, L.dtype, D, false, st);
+        const hipError_t e = launch_bwd_pre(p, L.dtype, DV, false, st);
         if (e != hipSuccess) return e;
     }
     const dim3 main_grid(L.n_seq * p.Hkv, L.max_kv_tiles);
     if (main_grid.x > 0 && main_grid.y > 0)
-        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, D, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_BWD_MAIN, st, (bwd_main_kernel<T, DK, DV, CAUSAL, false>), main_grid, dim3(256), 0, st, p);
     const dim3 dq_grid(L.max_q_tiles64, L.n_seq * p.Hq);
     if (dq_grid.x > 0 && dq_grid.y > 0)
-        PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, D, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
+        PROF_LAUNCH(KID_BWD_DQ_DET, st, (bwd_dq8_kernel<T, DK, DV, CAUSAL>), dq_grid, dim3(kThreads), 0, st, p);
     return hipGetLastError();
 }
 
-template <class T, int D>
+template <class T, int DK, int DV>
 static hipError_t launch_bwd_big_d(const BwdParams& p, const BwdLaunch& L, hipStream_t st) {
-    return L.causal ? launch_bwd128_t<T, D, true>(p, L, st) : launch_bwd128_t<T, D, false>(p, L, st);
+    return L.causal ? launch_bwd128_t<T, DK, DV, true>(p, L, st) : launch_bwd128_t<T, DK, DV, false>(p, L, st);
 }
 
 }  // namespace sdpa

@@ -95,28 +95,33 @@ constexpr int kKeySlices = kWaves / 2;
 // wavefront accumulates dQ^T over its key slice; the two slices' partials are
 // summed through LDS at the end and dQ is written once, scaled and rounded.
 
-template <int D>
+// D: head dim of Q and K (and of dQ); DV: of V and dO.
+template <int D, int DV = D>
 struct Dq8Lds {
-    static constexpr int BK = 32 * kKeySlices, KP = D + 8, DB = D / 32;
-    static constexpr int TILE_B = BK * KP * 2;
-    static constexpr int LOOP_B = 4 * TILE_B;
+    static constexpr int BK = 32 * kKeySlices, KP = D + 8, KPV = DV + 8, DB = D / 32;
+    static constexpr int TILE_B = BK * KP * 2, TILE_VB = BK * KPV * 2;
+    static constexpr int LOOP_B = 2 * TILE_B + 2 * TILE_VB;
     static constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;
     static constexpr int BYTES = LOOP_B > RED_B ? LOOP_B : RED_B;
 };
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, int DV = D>
 __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* arena, int bx, int by) {
     constexpr int BQ = 64;           // query rows per workgroup
     constexpr int BK = 32 * kKeySlices;   // keys per step
-    constexpr int KS = D / 16;       // k-steps over the head dimension (32x32x16)
+    constexpr int KS = D / 16;       // k-steps of S over D (32x32x16)
+    constexpr int KSV = DV / 16;     // k-steps of dP over DV
+    constexpr int KSM = KS > KSV ? KS : KSV;
     constexpr int DB = D / 32;       // 32-row blocks of dQ^T
-    constexpr int KP = D + 8;        // row stride of Ks, Vs  [key][d]
-    constexpr int CH = BK * D / 8 / kThreads;   // 16-byte chunks per thread per key tile
-    constexpr int TILE_B = BK * KP * 2;
+    constexpr int KP = D + 8;        // row stride of Ks  [key][d]
+    constexpr int KPV = DV + 8;      // row stride of Vs  [key][dv]
+    constexpr int CH = BK * D / 8 / kThreads;     // 16-byte chunks per thread per K tile
+    constexpr int CHV = BK * DV / 8 / kThreads;   // and per V tile
+    constexpr int TILE_B = BK * KP * 2, TILE_VB = BK * KPV * 2;
     constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
-    constexpr int LOOP_B = 4 * TILE_B;
+    constexpr int LOOP_B = 2 * TILE_B + 2 * TILE_VB;
     constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;   // key slices 1.. of both row halves
-    static_assert(Dq8Lds<D>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
+    static_assert(Dq8Lds<D, DV>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
     uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
     uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
 
@@ -141,7 +146,7 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
 
     // byte offsets of this thread's chunks within a key tile
     const uint32_t kss = 2u * (uint32_t)p.k.ss, vss = 2u * (uint32_t)p.v.ss;
-    uint32_t koff[CH], voff[CH];
+    uint32_t koff[CH], voff[CHV];
     int crow[CH], ccol[CH];
 #pragma unroll
     for (int x = 0; x < CH; ++x) {
@@ -150,46 +155,48 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         crow[x] = r;
         ccol[x] = cc;
         koff[x] = r * kss + 2 * cc;
-        voff[x] = r * vss + 2 * cc;
     }
+    // chunk x of a V tile (the K tile's when DV == D)
+    auto vrow = [&](int x) { return (tid + kThreads * x) / (DV / 8); };
+    auto vcol = [&](int x) { return ((tid + kThreads * x) % (DV / 8)) * 8; };
+#pragma unroll
+    for (int x = 0; x < CHV; ++x) voff[x] = vrow(x) * vss + 2 * vcol(x);
     // Unconditional loads: keys past the end of the sequence re-read its last
     // key and are masked out (P = 0), so nothing is waited for before the tile
     // is stored after the step's products.
-    u32x4 pk[CH], pv[CH];
+    u32x4 pk[CH], pv[CHV];
     const uint16_t* kb = kbase;          // key tile being loaded, advanced per step
     const uint16_t* vb = vbase;
     const int64_t k_step = BK * p.k.ss, v_step = BK * p.v.ss;
     auto load_tile = [&](int st) {
         const int j0 = st * BK;
-        uint32_t ok_[CH], ov_[CH];
+        uint32_t ok_[CH], ov_[CHV];
         if (j0 + BK <= lk) {
 #pragma unroll
-            for (int x = 0; x < CH; ++x) { ok_[x] = koff[x]; ov_[x] = voff[x]; }
+            for (int x = 0; x < CH; ++x) ok_[x] = koff[x];
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) ov_[x] = voff[x];
         } else {
             const int last = lk - 1 - j0;
 #pragma unroll
-            for (int x = 0; x < CH; ++x) {
-                const uint32_t r = min(crow[x], last);
-                ok_[x] = r * kss + 2 * ccol[x];
-                ov_[x] = r * vss + 2 * ccol[x];
-            }
+            for (int x = 0; x < CH; ++x) ok_[x] = (uint32_t)min(crow[x], last) * kss + 2 * ccol[x];
+#pragma unroll
+            for (int x = 0; x < CHV; ++x) ov_[x] = (uint32_t)min(vrow(x), last) * vss + 2 * vcol(x);
         }
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            pk[x] = ld16_at(kb, ok_[x]);
-            pv[x] = ld16_at(vb, ov_[x]);
-        }
+        for (int x = 0; x < CH; ++x) pk[x] = ld16_at(kb, ok_[x]);
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) pv[x] = ld16_at(vb, ov_[x]);
         kb += k_step;
         vb += v_step;
     };
     auto store_tile = [&](int buf) {
         uint16_t* Kd = Ks0 + buf * (BK * KP);
-        uint16_t* Vd = Vs0 + buf * (BK * KP);
+        uint16_t* Vd = Vs0 + buf * (BK * KPV);
 #pragma unroll
-        for (int x = 0; x < CH; ++x) {
-            st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
-            st16(&Vd[crow[x] * KP + ccol[x]], pv[x]);
-        }
+        for (int x = 0; x < CH; ++x) st16(&Kd[crow[x] * KP + ccol[x]], pk[x]);
+#pragma unroll
+        for (int x = 0; x < CHV; ++x) st16(&Vd[vrow(x) * KPV + vcol(x)], pv[x]);
     };
 
     // Prologue: the first key tile and this lane's query row are requested
@@ -200,11 +207,11 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     // a row past the end of the sequence re-reads its last row; its LSE is
     // +inf (P = 0) and its dQ is not stored
     const int my_ic = min(my_i, lq - 1);
-    u32x4 qreg[KS], doreg[KS];
+    u32x4 qreg[KS], doreg[KSV];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
-        doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
+    for (int s = 0; s < KSM; ++s) {
+        if (s < KS) qreg[s] = ld16(qbase + (int64_t)my_ic * p.q.ss + 16 * s + 8 * g);
+        if (s < KSV) doreg[s] = ld16(dobase + (int64_t)my_ic * p.dout.ss + 16 * s + 8 * g);
     }
     // this row's log2-domain LSE and Delta from the row pass
     const int64_t ws = p.varlen ? (int64_t)(q0 + my_ic) * p.Hq + h : ((int64_t)b * p.Hq + h) * p.Sq + my_ic;
@@ -230,13 +237,13 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         const bool has_next = st + 1 < n_steps;
         if (has_next) load_tile(st + 1);
         const uint16_t* Kb = Ks0 + buf * (BK * KP);
-        const uint16_t* Vb = Vs0 + buf * (BK * KP);
+        const uint16_t* Vb = Vs0 + buf * (BK * KPV);
 
         f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
-            dp = T::mma(ld16(&Vb[(32 * kw + c) * KP + 16 * ks + 8 * g]), doreg[ks], dp);
+        for (int ks = 0; ks < KSM; ++ks) {
+            if (ks < KS) s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
+            if (ks < KSV) dp = T::mma(ld16(&Vb[(32 * kw + c) * KPV + 16 * ks + 8 * g]), doreg[ks], dp);
         }
         // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
         const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);

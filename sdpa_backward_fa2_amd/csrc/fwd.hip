@@ -14,16 +14,17 @@
 
 namespace sdpa {
 
-template <class T, int D, bool CAUSAL>
+// D: head dim of Q and K; DV: of V and O.
+template <class T, int D, int DV, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
     constexpr int BQ = 128;          // 4 wavefronts x 32 query rows
     constexpr int BK = 64;           // keys per LDS tile
-    constexpr int KS = D / 16;       // k-steps over the head dimension
-    constexpr int DB = D / 32;       // 32-row blocks of O^T
+    constexpr int KS = D / 16;       // k-steps over the Q/K head dimension
+    constexpr int DB = DV / 32;      // 32-row blocks of O^T
     constexpr int KP = D + 8;        // padded row stride of Ks  [key][d]
-    constexpr int VP = BK + 8;       // padded row stride of VT  [d][key]
+    constexpr int VP = BK + 8;       // padded row stride of VT  [dv][key]
     __shared__ __align__(16) uint16_t Ks[BK * KP];
-    __shared__ __align__(16) uint16_t VT[D * VP];
+    __shared__ __align__(16) uint16_t VT[DV * VP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -63,11 +64,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
             u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
             if (j < lk) {
                 kv = ld16(kp + (int64_t)j * p.k.ss + cc);
-                vv = ld16(vp + (int64_t)j * p.v.ss + cc);
+                if (DV == D) vv = ld16(vp + (int64_t)j * p.v.ss + cc);
             }
             st16(&Ks[r * KP + cc], kv);
+            if (DV == D) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) VT[(cc + t) * VP + r] = elem16(vv, t);
+                for (int t = 0; t < 8; ++t) VT[(cc + t) * VP + r] = elem16(vv, t);
+            }
+        }
+        if (DV != D) {
+            for (int e = tid; e < BK * DV / 8; e += 256) {
+                const int r = e / (DV / 8), cc = (e % (DV / 8)) * 8;
+                const int j = j0 + r;
+                u32x4 vv = {0u, 0u, 0u, 0u};
+                if (j < lk) vv = ld16(vp + (int64_t)j * p.v.ss + cc);
+#pragma unroll
+                for (int t = 0; t < 8; ++t) VT[(cc + t) * VP + r] = elem16(vv, t);
+            }
         }
         __syncthreads();
 
@@ -142,25 +155,27 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 }
 
 // grid.x covers the longest sequence (dense: Sq) in 128-row tiles
-template <class T, int D>
+template <class T, int D, int DV>
 static hipError_t launch_fwd_t(const FwdParams& p, int max_lq, bool causal, hipStream_t st) {
     dim3 grid((max_lq + 127) / 128, p.B * p.Hq);
     if (causal)
-        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, true>), grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, DV, true>), grid, dim3(256), 0, st, p);
     else
-        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, false>), grid, dim3(256), 0, st, p);
+        PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, DV, false>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
 template <class T>
-static hipError_t launch_fwd_dt(const FwdParams& p, int D, int max_lq, bool causal, hipStream_t st) {
-    if (D == 64) return launch_fwd_t<T, 64>(p, max_lq, causal, st);
-    if (D == 128) return launch_fwd_t<T, 128>(p, max_lq, causal, st);
-    return launch_fwd_t<T, 192>(p, max_lq, causal, st);
+static hipError_t launch_fwd_dt(const FwdParams& p, int D, int Dv, int max_lq, bool causal, hipStream_t st) {
+    if (D == 64) return launch_fwd_t<T, 64, 64>(p, max_lq, causal, st);
+    if (D == 128) return launch_fwd_t<T, 128, 128>(p, max_lq, causal, st);
+    if (Dv == 128) return launch_fwd_t<T, 192, 128>(p, max_lq, causal, st);
+    return launch_fwd_t<T, 192, 192>(p, max_lq, causal, st);
 }
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st) {
-    return dtype == 0 ? launch_fwd_dt<F16>(p, D, max_lq, causal, st) : launch_fwd_dt<BF16>(p, D, max_lq, causal, st);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int Dv, int max_lq, bool causal, hipStream_t st) {
+    return dtype == 0 ? launch_fwd_dt<F16>(p, D, Dv, max_lq, causal, st)
+                      : launch_fwd_dt<BF16>(p, D, Dv, max_lq, causal, st);
 }
 
 }  // namespace sdpa

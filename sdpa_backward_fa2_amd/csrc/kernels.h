@@ -15,7 +15,8 @@ inline bool row_stride_ok(int64_t s) { return s >= 0 && s < kMaxRowStride; }
 
 struct BwdLaunch {
     int dtype;            // 0 fp16, 1 bf16
-    int D;                // 64, 128 or 192
+    int D;                // head dim of Q and K: 64, 128 or 192
+    int Dv;               // of V, O and dO: D, or 128 with D = 192
     bool causal;
     bool deterministic;
     int n_seq;            // batch (dense) or number of packed sequences
@@ -29,7 +30,7 @@ struct BwdLaunch {
     int phase = kFirst | kLast;
 };
 
-hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int max_lq, bool causal, hipStream_t st);
+hipError_t launch_fwd(const FwdParams& p, int dtype, int D, int Dv, int max_lq, bool causal, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, const BwdLaunch& L, hipStream_t st);
 // The D=128 backward (bwd128.hip) and the D=192 backward (bwd192.hip);
 // launch_bwd hands those calls to them.

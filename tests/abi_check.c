@@ -34,21 +34,30 @@ static sdpa_tensor3 t3(int64_t st, int64_t sn) {
     return t;
 }
 
-static int dense(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int det, size_t ws, int noalloc) {
+static int dense2(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int64_t Dv, int det, size_t ws,
+                  int noalloc) {
     sdpa_tensor4 a = t4(S * H * D, D, H * D);
     sdpa_stats st = {SDPA_STATS_LSE, (const float*)FAKE, NULL, H * S, S, 1};
     if (noalloc)
-        return sdpa_bwd_noalloc(dtype, B, H, H, S, S, D, 0.125, 1, det, dtype, &a, &a, &a, &a, &a, &st, &a, &a,
-                                &a, NULL);
-    return sdpa_bwd(dtype, B, H, H, S, S, D, 0.125, 1, det, dtype, &a, &a, &a, &a, &a, &st, &a, &a, &a, FAKE, ws,
-                    NULL);
+        return sdpa_bwd_noalloc(dtype, B, H, H, S, S, D, Dv, 0.125, 1, det, dtype, &a, &a, &a, &a, &a, &st, &a,
+                                &a, &a, NULL);
+    return sdpa_bwd(dtype, B, H, H, S, S, D, Dv, 0.125, 1, det, dtype, &a, &a, &a, &a, &a, &st, &a, &a, &a, FAKE,
+                    ws, NULL);
+}
+
+static int dense(int dtype, int64_t B, int64_t H, int64_t S, int64_t D, int det, size_t ws, int noalloc) {
+    return dense2(dtype, B, H, S, D, D, det, ws, noalloc);
+}
+
+static int varlen2(int64_t n, const int64_t* cu, int64_t H, int64_t D, int64_t Dv, int det, size_t ws) {
+    sdpa_tensor3 a = t3(H * D, D);
+    sdpa_stats st = {SDPA_STATS_MAX_SUM, (const float*)FAKE, (const float*)FAKE, 0, 1, H};
+    return sdpa_bwd_varlen(SDPA_BF16, n, cu, cu, H, H, D, Dv, 0.088, 1, det, SDPA_BF16, &a, &a, &a, &a, &a, &st, &a,
+                           &a, &a, FAKE, ws, NULL);
 }
 
 static int varlen(int64_t n, const int64_t* cu, int64_t H, int64_t D, int det, size_t ws) {
-    sdpa_tensor3 a = t3(H * D, D);
-    sdpa_stats st = {SDPA_STATS_MAX_SUM, (const float*)FAKE, (const float*)FAKE, 0, 1, H};
-    return sdpa_bwd_varlen(SDPA_BF16, n, cu, cu, H, H, D, 0.088, 1, det, SDPA_BF16, &a, &a, &a, &a, &a, &st, &a,
-                           &a, &a, FAKE, ws, NULL);
+    return varlen2(n, cu, H, D, D, det, ws);
 }
 
 static int selected(int64_t n, const int64_t* cu, int64_t bs, int64_t count, const void* mask, int64_t ms,
@@ -63,17 +72,21 @@ static int selected(int64_t n, const int64_t* cu, int64_t bs, int64_t count, con
 int main(void) {
     size_t n = 0;
     /* dense */
-    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 0, &n), SDPA_OK);
+    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 64, 0, &n), SDPA_OK);
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 64, 0, n, 0), SDPA_ERR_HIP);
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 64, 0, n - 1, 0), SDPA_ERR_WORKSPACE);
     EXPECT(dense(7, 4, 12, 1024, 64, 0, n, 0), SDPA_ERR_INVALID);
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 96, 0, n, 0), SDPA_ERR_UNSUPPORTED);
+    EXPECT(dense2(SDPA_F16, 4, 12, 1024, 192, 128, 0, n, 0), SDPA_ERR_HIP);          /* Dqk 192, Dv 128 */
+    EXPECT(dense2(SDPA_F16, 4, 12, 1024, 128, 64, 0, n, 0), SDPA_ERR_UNSUPPORTED);
+    EXPECT(dense2(SDPA_F16, 4, 12, 1024, 192, 128, 2, n, 0), SDPA_ERR_UNSUPPORTED);   /* no atomic dQ */
+    EXPECT(dense2(SDPA_F16, 4, 12, 1024, 64, 0, 0, n, 0), SDPA_ERR_INVALID);
     EXPECT(dense(SDPA_F16, -1, 12, 1024, 64, 0, n, 0), SDPA_ERR_INVALID);
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 64, 3, n, 0), SDPA_ERR_INVALID);
     EXPECT(dense(SDPA_F16, 4, 12, (int64_t)1 << 40, 64, 0, n, 0), SDPA_ERR_UNSUPPORTED);   /* huge S */
-    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 2, &n), SDPA_OK);
+    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 64, 2, &n), SDPA_OK);
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 64, 2, n, 0), SDPA_ERR_HIP);
-    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 0, NULL), SDPA_ERR_NULLPTR);
+    EXPECT(sdpa_bwd_workspace_size(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 64, 0, NULL), SDPA_ERR_NULLPTR);
     /* allocation-free variant: fixed scratch */
     EXPECT(dense(SDPA_F16, 4, 12, 1024, 64, 0, 0, 1), SDPA_ERR_HIP);
     EXPECT(dense(SDPA_F16, 64, 64, 1024, 64, 0, 0, 1), SDPA_ERR_WORKSPACE);
@@ -81,11 +94,13 @@ int main(void) {
     {
         const int64_t cu[3] = {300, 700, 1500};
         const int64_t bad[3] = {300, 200, 1500};
-        EXPECT(sdpa_bwd_varlen_workspace_size(SDPA_BF16, 3, cu, cu, 32, 32, 128, 0, &n), SDPA_OK);
+        EXPECT(sdpa_bwd_varlen_workspace_size(SDPA_BF16, 3, cu, cu, 32, 32, 128, 128, 0, &n), SDPA_OK);
         EXPECT(varlen(3, cu, 32, 128, 0, n), SDPA_ERR_HIP);
         EXPECT(varlen(3, bad, 32, 128, 0, n), SDPA_ERR_INVALID);
         EXPECT(varlen(3, cu, 32, 96, 0, n), SDPA_ERR_UNSUPPORTED);
         EXPECT(varlen(3, cu, 32, 192, 2, n), SDPA_ERR_UNSUPPORTED);   /* no atomic dQ at D=192 */
+        EXPECT(varlen2(3, cu, 32, 192, 128, 0, (size_t)1 << 40), SDPA_ERR_HIP);
+        EXPECT(varlen2(3, cu, 32, 64, 128, 0, (size_t)1 << 40), SDPA_ERR_UNSUPPORTED);
         EXPECT(varlen(3, cu, 32, 128, 0, 8), SDPA_ERR_WORKSPACE);
         EXPECT(varlen(3, cu, 40000, 128, 0, (size_t)1 << 40), SDPA_ERR_UNSUPPORTED);
         EXPECT(varlen(0, cu, 32, 128, 0, n), SDPA_ERR_INVALID);
@@ -113,9 +128,9 @@ int main(void) {
     {
         sdpa_tensor4 a = t4(1024 * 12 * 64, 64, 12 * 64);
         sdpa_stats_out so = {(float*)FAKE, 12 * 1024, 1024, 1};
-        EXPECT(sdpa_fwd_stats(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 0.125, 1, &a, &a, &a, &a, &so, NULL),
+        EXPECT(sdpa_fwd_stats(SDPA_F16, 4, 12, 12, 1024, 1024, 64, 64, 0.125, 1, &a, &a, &a, &a, &so, NULL),
                SDPA_ERR_HIP);
-        EXPECT(sdpa_fwd_stats(SDPA_F16, 4, 12, 5, 1024, 1024, 64, 0.125, 1, &a, &a, &a, &a, &so, NULL),
+        EXPECT(sdpa_fwd_stats(SDPA_F16, 4, 12, 5, 1024, 1024, 64, 64, 0.125, 1, &a, &a, &a, &a, &so, NULL),
                SDPA_ERR_INVALID);
     }
     for (int s = 0; s < 6; ++s)

@@ -38,13 +38,14 @@ def t4(ptr=FAKE, strides=(16384, 8192, 64, 1)):
 
 
 def dense_call(**kw):
-    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, scale=0.125, causal=0, det=0, grad=None,
+    a = dict(dtype=0, B=1, Hq=2, Hkv=2, Sq=128, Sk=128, D=64, Dv=None, scale=0.125, causal=0, det=0, grad=None,
              q=t4(), k=t4(), v=t4(), o=t4(), do=t4(), dq=t4(), dk=t4(), dv=t4(),
              stats=sb.Stats(0, FAKE, None, 256, 128, 1), ws=FAKE, ws_bytes=1 << 30)
     a.update(kw)
     ref = lambda x: ctypes.byref(x) if x is not None else None  # noqa: E731
     grad = a["dtype"] if a["grad"] is None else a["grad"]
-    return lib().sdpa_bwd(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"],
+    dv = a["D"] if a["Dv"] is None else a["Dv"]
+    return lib().sdpa_bwd(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], dv, a["scale"],
                           a["causal"], a["det"], grad, ref(a["q"]), ref(a["k"]), ref(a["v"]), ref(a["o"]),
                           ref(a["do"]), ref(a["stats"]), ref(a["dq"]), ref(a["dk"]), ref(a["dv"]),
                           a["ws"], a["ws_bytes"], None)
@@ -92,7 +93,7 @@ def test_workspace_size_query():
 
     def size(D, mode):
         n = ctypes.c_size_t(0)
-        assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, D, mode, ctypes.byref(n)) == OK
+        assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, D, D, mode, ctypes.byref(n)) == OK
         return n.value
     # atomic-free modes: LSE and Delta rows; the atomic mode adds the fp32 dQ
     # accumulator
@@ -102,11 +103,11 @@ def test_workspace_size_query():
     # D=192: the atomic-free modes only
     assert size(192, 0) == size(192, 1) >= rows * 8
     m = ctypes.c_size_t(0)
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 192, 2, ctypes.byref(m)) == UNSUPPORTED
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 256, 0, ctypes.byref(m)) == UNSUPPORTED
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 3, ctypes.byref(m)) == INVALID
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 0, ctypes.byref(m)) == UNSUPPORTED
-    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 0, None) == NULLPTR
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 192, 192, 2, ctypes.byref(m)) == UNSUPPORTED
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 256, 256, 0, ctypes.byref(m)) == UNSUPPORTED
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 64, 3, ctypes.byref(m)) == INVALID
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 80, 80, 0, ctypes.byref(m)) == UNSUPPORTED
+    assert lib().sdpa_bwd_workspace_size(0, 4, 12, 12, 1024, 1024, 64, 64, 0, None) == NULLPTR
 
 
 def noalloc_call(**kw):
@@ -114,7 +115,8 @@ def noalloc_call(**kw):
              stats=sb.Stats(0, FAKE, None, 256, 128, 1))
     a.update(kw)
     ts = [t4() for _ in range(8)]
-    return lib().sdpa_bwd_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["scale"],
+    return lib().sdpa_bwd_noalloc(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], a["D"],
+                                  a["scale"],
                                   a["causal"], a["det"], a["dtype"], *[ctypes.byref(t) for t in ts[:5]],
                                   ctypes.byref(a["stats"]), *[ctypes.byref(t) for t in ts[5:]], None)
 
@@ -130,7 +132,7 @@ def test_noalloc_validation():
     assert b"16777216" in lib().sdpa_last_error()
     assert noalloc_call(Hq=16, Hkv=16, Sq=4096, det=2) == WORKSPACE                # + 4*D B per row, mode 2
     n = ctypes.c_size_t(0)
-    assert lib().sdpa_bwd_workspace_size(0, 1, 16, 16, 4096, 4096, 64, 2, ctypes.byref(n)) == OK
+    assert lib().sdpa_bwd_workspace_size(0, 1, 16, 16, 4096, 4096, 64, 64, 2, ctypes.byref(n)) == OK
     assert n.value > (16 << 20)
 
 
@@ -145,13 +147,14 @@ def t3(ptr=FAKE, strides=(32 * 128, 128, 1)):
 
 
 def varlen_call(cu_q, cu_k, **kw):
-    a = dict(dtype=1, Hq=32, Hkv=32, D=128, scale=0.088, causal=1, det=0, grad=1, ws_bytes=1 << 34)
+    a = dict(dtype=1, Hq=32, Hkv=32, D=128, Dv=None, scale=0.088, causal=1, det=0, grad=1, ws_bytes=1 << 34)
     a.update(kw)
     aq = (ctypes.c_int64 * len(cu_q))(*cu_q)
     ak = (ctypes.c_int64 * len(cu_k))(*cu_k)
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
     ts = [t3() for _ in range(8)]
-    return lib().sdpa_bwd_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], a["scale"],
+    dv = a["D"] if a["Dv"] is None else a["Dv"]
+    return lib().sdpa_bwd_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], dv, a["scale"],
                                  a["causal"], a["det"], a["grad"], *[ctypes.byref(t) for t in ts[:5]],
                                  ctypes.byref(st), *[ctypes.byref(t) for t in ts[5:]], FAKE,
                                  a["ws_bytes"], None)
@@ -166,9 +169,9 @@ def test_varlen_validation():
     assert varlen_call([100, 300], [100, 300], ws_bytes=8) == WORKSPACE
     n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 2)(100, 300)
-    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 0, ctypes.byref(n)) == OK
+    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 128, 0, ctypes.byref(n)) == OK
     assert n.value >= 300 * 32 * 8                      # LSE and Delta per (token, head)
-    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 2, ctypes.byref(n)) == OK
+    assert lib().sdpa_bwd_varlen_workspace_size(1, 2, cu, cu, 32, 32, 128, 128, 2, ctypes.byref(n)) == OK
     assert n.value >= 300 * 32 * (8 + 128 * 4)         # plus the fp32 dQ accumulator
     assert varlen_call([100, 300], [100, 300], det=5) == INVALID
     # (sequence, query head) of a chunk of sequences must fit grid y (65535)
@@ -178,7 +181,7 @@ def test_varlen_validation():
     st = sb.Stats(1, FAKE, FAKE, 0, 1, 32)
     ts = [t3() for _ in range(8)]
     ts[2] = big
-    assert lib().sdpa_bwd_varlen(1, 2, cu, cu, 32, 32, 128, 0.088, 1, 0, 1,
+    assert lib().sdpa_bwd_varlen(1, 2, cu, cu, 32, 32, 128, 128, 0.088, 1, 0, 1,
                                  *[ctypes.byref(t) for t in ts[:5]], ctypes.byref(st),
                                  *[ctypes.byref(t) for t in ts[5:]], FAKE, 1 << 34, None) == UNSUPPORTED
 
@@ -191,10 +194,11 @@ def test_varlen_valid_without_device():
 
 
 def fwd_call(**kw):
-    a = dict(dtype=0, B=1, Hq=2, Hkv=1, Sq=64, Sk=64, D=64, scale=0.1, causal=1)
+    a = dict(dtype=0, B=1, Hq=2, Hkv=1, Sq=64, Sk=64, D=64, Dv=None, scale=0.1, causal=1)
     a.update(kw)
     so = sb.StatsOut(FAKE, 128, 64, 1)
-    return lib().sdpa_fwd_stats(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"],
+    dv = a["D"] if a["Dv"] is None else a["Dv"]
+    return lib().sdpa_fwd_stats(a["dtype"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"], dv,
                                 a["scale"], a["causal"], ctypes.byref(t4()), ctypes.byref(t4()),
                                 ctypes.byref(t4()), ctypes.byref(t4()), ctypes.byref(so), None)
 
@@ -206,13 +210,14 @@ def test_fwd_validation():
 
 
 def fwd_varlen_call(cu_q, cu_k, **kw):
-    a = dict(dtype=1, Hq=4, Hkv=2, D=128, scale=0.088, causal=1, lse=FAKE)
+    a = dict(dtype=1, Hq=4, Hkv=2, D=128, Dv=None, scale=0.088, causal=1, lse=FAKE)
     a.update(kw)
     aq = (ctypes.c_int64 * len(cu_q))(*cu_q)
     ak = (ctypes.c_int64 * len(cu_k))(*cu_k)
     so = sb.StatsOut(a["lse"], 0, 1, 4)
     ts = [t3() for _ in range(4)]
-    return lib().sdpa_fwd_stats_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], a["scale"],
+    dv = a["D"] if a["Dv"] is None else a["Dv"]
+    return lib().sdpa_fwd_stats_varlen(a["dtype"], len(cu_q), aq, ak, a["Hq"], a["Hkv"], a["D"], dv, a["scale"],
                                        a["causal"], *[ctypes.byref(t) for t in ts], ctypes.byref(so), None)
 
 

@@ -29,12 +29,14 @@ def _run_bwd(q, k, v, o, do, lse, scale, causal, det):
     return dq, dk, dv
 
 
-def _random_case(B, Hq, Hkv, Sq, Sk, D, dtype, layout, seed):
-    """Small random problem: physical layout bshd or bhsd, N(0,1) inputs."""
+def _random_case(B, Hq, Hkv, Sq, Sk, D, dtype, layout, seed, Dv=None):
+    """Small random problem: physical layout bshd or bhsd, N(0,1) inputs; V and
+    dO have head dim Dv (default D)."""
     rng = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
     out = {}
-    for name, H, S in (("q", Hq, Sq), ("k", Hkv, Sk), ("v", Hkv, Sk), ("do", Hq, Sq)):
-        shape = (B, S, H, D) if layout == "bshd" else (B, H, S, D)
+    for name, H, S, d in (("q", Hq, Sq, D), ("k", Hkv, Sk, D), ("v", Hkv, Sk, Dv), ("do", Hq, Sq, Dv)):
+        shape = (B, S, H, d) if layout == "bshd" else (B, H, S, d)
         bits = synth.encode(rng.standard_normal(shape), dtype)
         t = to_device(bits, dtype)
         x = synth.decode(bits, dtype)
@@ -44,13 +46,13 @@ def _random_case(B, Hq, Hkv, Sq, Sk, D, dtype, layout, seed):
     return out
 
 
-def _check_case(B, Hq, Hkv, Sq, Sk, D, dtype, causal, layout, seed=0, stats="gpu"):
-    case = _random_case(B, Hq, Hkv, Sq, Sk, D, dtype, layout, seed)
+def _check_case(B, Hq, Hkv, Sq, Sk, D, dtype, causal, layout, seed=0, stats="gpu", Dv=None):
+    case = _random_case(B, Hq, Hkv, Sq, Sk, D, dtype, layout, seed, Dv)
     (q, qx), (k, kx), (v, vx), (do, dox) = case["q"], case["k"], case["v"], case["do"]
     scale = 1.0 / math.sqrt(D)
     f = oracle.dense_forward(qx, kx, vx, scale, causal)
     if stats == "gpu":
-        o = _nan_like(q)
+        o = _nan_like(do)
         lse = torch.full((B, Hq, Sq), float("nan"), device="cuda")
         sb.fwd_stats(q, k, v, scale, causal, o=o, lse=lse)
         torch.cuda.synchronize()
@@ -60,15 +62,15 @@ def _check_case(B, Hq, Hkv, Sq, Sk, D, dtype, causal, layout, seed=0, stats="gpu
         o = to_device(synth.encode(f["O"], dtype), dtype)
         lse = torch.tensor(f["lse"], dtype=torch.float32, device="cuda")
     g = oracle.dense_backward(qx, kx, vx, dox, scale, causal)
-    for det in _modes(D):
+    for det in _modes(D, v.shape[-1]):
         dq, dk, dv = _run_bwd(q, k, v, o, do, lse, scale, causal, det)
         for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
             assert_rel(to_f64(got), ref, dtype, f"{name} det={det}")
 
 
-def _modes(D):
-    """dQ modes offered at head dim D (no fp32-atomic form at D=192)."""
-    return (0, 1) if D == 192 else (0, 1, 2)
+def _modes(D, Dv=None):
+    """dQ modes offered at head dims (D, Dv): no fp32-atomic form at D=192."""
+    return (0, 1) if D == 192 or (Dv is not None and Dv != D) else (0, 1, 2)
 
 
 # ----------------------------------------------------------------------------
@@ -224,6 +226,47 @@ def test_d192_atomic_mode_is_unsupported():
     case = _random_case(1, 2, 2, 64, 64, 192, "f16", "bhsd", 1)
     q, k, v, do = (case[n][0] for n in ("q", "k", "v", "do"))
     o, lse = sb.fwd_stats(q, k, v, 0.1, True)
+    with pytest.raises(sb.SdpaError) as e:
+        sb.bwd(q, k, v, o, do, lse, 0.1, True, deterministic=2)
+    assert e.value.status == 3   # SDPA_ERR_UNSUPPORTED
+
+
+# ----------------------------------------------------------------------------
+# Query/key head dim 192 with value head dim 128
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("S", [1, 37, 128, 200, 385])
+def test_dqk192_dv128_square(dtype, causal, S):
+    _check_case(2, 2, 2, S, S, 192, dtype, causal, "bshd", seed=S + 320, Dv=128)
+
+
+@pytest.mark.parametrize("Sq,Sk", [(64, 300), (257, 129), (5, 1), (130, 131)])
+def test_dqk192_dv128_rectangular_causal(Sq, Sk):
+    _check_case(1, 3, 3, Sq, Sk, 192, "bf16", True, "bhsd", seed=Sq + Sk, Dv=128)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 2), (6, 1)])
+def test_dqk192_dv128_gqa(Hq, Hkv):
+    _check_case(2, Hq, Hkv, 160, 160, 192, "f16", True, "bshd", seed=Hq * 7, Dv=128)
+
+
+def test_dqk192_dv128_longer_causal():
+    """Several key tiles and a ragged tail; O and LSE from the library's forward."""
+    _check_case(2, 4, 2, 700, 700, 192, "bf16", True, "bshd", seed=1920, Dv=128)
+
+
+def test_dqk192_dv128_oracle_stats():
+    """Statistics and O from the oracle instead of the library's forward."""
+    _check_case(1, 2, 2, 300, 300, 192, "f16", False, "bhsd", seed=5, stats="oracle", Dv=128)
+
+
+def test_dqk192_dv128_atomic_mode_is_unsupported():
+    case = _random_case(1, 2, 2, 64, 64, 192, "f16", "bhsd", 1, Dv=128)
+    q, k, v, do = (case[n][0] for n in ("q", "k", "v", "do"))
+    o, lse = sb.fwd_stats(q, k, v, 0.1, True)
+    assert o.shape[-1] == 128
     with pytest.raises(sb.SdpaError) as e:
         sb.bwd(q, k, v, o, do, lse, 0.1, True, deterministic=2)
     assert e.value.status == 3   # SDPA_ERR_UNSUPPORTED

@@ -31,15 +31,16 @@ def _check_lse(got, ref, what):
         assert e <= STATS_ABS_TOL, f"{what}: max|LSE err| = {e:.3e}"
 
 
-def _fwd_case(lq, lk, Hq, Hkv, D, dtype, causal, seed, backward=True):
+def _fwd_case(lq, lk, Hq, Hkv, D, dtype, causal, seed, backward=True, Dv=None):
     rng = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
     cu_q, cu_k = np.cumsum(lq), np.cumsum(lk)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
     q, qx = _packed(Tq, Hq, D, dtype, rng)
     k, kx = _packed(Tk, Hkv, D, dtype, rng)
-    v, vx = _packed(Tk, Hkv, D, dtype, rng)
+    v, vx = _packed(Tk, Hkv, Dv, dtype, rng)
     scale = 1 / math.sqrt(D)
-    o = torch.full_like(q, float("nan"))
+    o = torch.full((Tq, Hq, Dv), float("nan"), dtype=q.dtype, device="cuda")
     lse = torch.full((Tq, Hq), float("nan"), dtype=torch.float32, device="cuda")
     sb.fwd_stats_varlen(q, k, v, cu_q, cu_k, scale, causal, o=o, lse=lse)
     torch.cuda.synchronize()
@@ -48,7 +49,7 @@ def _fwd_case(lq, lk, Hq, Hkv, D, dtype, causal, seed, backward=True):
     _check_lse(to_f64(lse), f["lse"], "LSE")
     if not backward:
         return
-    do, dox = _packed(Tq, Hq, D, dtype, rng)
+    do, dox = _packed(Tq, Hq, Dv, dtype, rng)
     g = oracle.varlen_backward(qx, kx, vx, dox, cu_q, cu_k, scale, causal)
     dq, dk, dv = sb.bwd_varlen(q, k, v, o, do, lse, cu_q, cu_k, scale, causal)
     torch.cuda.synchronize()
@@ -105,3 +106,10 @@ def test_config4_packed_forward_matches_per_sequence_dense():
         torch.cuda.synchronize()
         assert torch.equal(o[sl].view(torch.int16), od.view(torch.int16))
         assert torch.equal(lse[sl].t().contiguous(), ld[0])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dqk192_dv128(causal):
+    """Query/key head dim 192, value head dim 128: O is (T, H, 128)."""
+    _fwd_case([1, 200, 0, 129, 64, 300], [1, 200, 5, 129, 64, 300], 4, 2, 192, "bf16", causal, seed=192128,
+              Dv=128)

@@ -30,14 +30,15 @@ def _run(q, k, v, o, do, stats, cu_q, cu_k, scale, causal, det):
     return dq, dk, dv
 
 
-def _case(lq, lk, Hq, Hkv, D, dtype, causal, seed, stats_form="max_sum", dets=(0, 1, 2)):
+def _case(lq, lk, Hq, Hkv, D, dtype, causal, seed, stats_form="max_sum", dets=(0, 1, 2), Dv=None):
     rng = np.random.default_rng(seed)
+    Dv = D if Dv is None else Dv
     cu_q, cu_k = np.cumsum(lq), np.cumsum(lk)
     Tq, Tk = int(cu_q[-1]), int(cu_k[-1])
     q, qx = _packed(Tq, Hq, D, dtype, rng)
     k, kx = _packed(Tk, Hkv, D, dtype, rng)
-    v, vx = _packed(Tk, Hkv, D, dtype, rng)
-    do, dox = _packed(Tq, Hq, D, dtype, rng)
+    v, vx = _packed(Tk, Hkv, Dv, dtype, rng)
+    do, dox = _packed(Tq, Hq, Dv, dtype, rng)
     scale = 1 / math.sqrt(D)
     f = oracle.varlen_forward(qx, kx, vx, cu_q, cu_k, scale, causal)
     o = to_device(synth.encode(f["O"], dtype), dtype)
@@ -131,3 +132,15 @@ def test_more_sequences_than_one_launch_holds():
     lengths = [int(x) for x in rng.integers(0, 40, size=70)]
     lengths[0] = 33
     _case(lengths, lengths, 2, 2, 64, "f16", True, seed=13)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_dqk192_dv128_ragged_causal(dtype):
+    """Query/key head dim 192, value head dim 128, packed."""
+    lengths = [1, 200, 0, 129, 64, 300]
+    _case(lengths, lengths, 2, 2, 192, dtype, True, seed=321, dets=(0, 1), Dv=128)
+
+
+def test_dqk192_dv128_unequal_lengths_gqa():
+    _case([100, 1, 250, 0, 64], [37, 300, 129, 20, 0], 4, 2, 192, "bf16", True, seed=322, dets=(0, 1), Dv=128)
+    _case([130, 257], [90, 300], 4, 1, 192, "f16", False, seed=323, dets=(0, 1), Dv=128)
