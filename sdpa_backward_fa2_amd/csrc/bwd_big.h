@@ -396,6 +396,53 @@ __global__ __launch_bounds__(256, (DK == 64 ? 2 : 1)) void bwd_main_kernel(BwdPa
         if (i0 >= lq) { i0 = i_begin; ++h; }
     }
 
+    if (!p.grad_f32) {
+        // 16-bit gradients leave through LDS (the Q/dO tiles are free after
+        // the loop's last barrier): in the accumulator layout a store
+        // instruction covers 8 bytes of each of 32 rows; staged, each covers
+        // whole rows.  Row r's 16-byte chunk ch sits at position (ch + r) mod
+        // the row's chunk count, so the staging writes of a wavefront's 32
+        // rows spread over the banks.
+        constexpr int NCK = DK / 8, NCV = DV / 8;
+        static_assert(2 * BR * QPK >= BC * DK && 2 * BR * QPV >= BC * DV, "staging fits the tile buffers");
+        static_assert((BC * NCK) % 256 == 0 && (BC * NCV) % 256 == 0, "whole chunks per thread");
+        uint16_t* sk = &Qs[0][0];       // [BC][DK]
+        uint16_t* sv = &dOs[0][0];      // [BC][DV]
+        const int r = 32 * w + c;
+#pragma unroll
+        for (int db = 0; db < DBM; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = 4 * db + q;
+                if (db < DBK) {
+                    u32x2 x;
+                    x[0] = T::pack(f32_round(dka[db][4 * q + 0] * p.scale), f32_round(dka[db][4 * q + 1] * p.scale));
+                    x[1] = T::pack(f32_round(dka[db][4 * q + 2] * p.scale), f32_round(dka[db][4 * q + 3] * p.scale));
+                    st8(&sk[r * DK + ((ch + r) % NCK) * 8 + 4 * g], x);
+                }
+                if (db < DBV) {
+                    u32x2 x;
+                    x[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
+                    x[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
+                    st8(&sv[r * DV + ((ch + r) % NCV) * 8 + 4 * g], x);
+                }
+            }
+        __syncthreads();
+        const int nrow = min(BC, lk - j0);
+        uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + j0) * p.dk.ss;
+        uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + j0) * p.dv.ss;
+#pragma unroll
+        for (int x = 0; x < BC * NCK / 256; ++x) {
+            const int e = tid + 256 * x, row = e / NCK, ch = e % NCK;
+            if (row < nrow) st16(dkp + (int64_t)row * p.dk.ss + ch * 8, ld16(&sk[row * DK + ((ch + row) % NCK) * 8]));
+        }
+#pragma unroll
+        for (int x = 0; x < BC * NCV / 256; ++x) {
+            const int e = tid + 256 * x, row = e / NCV, ch = e % NCV;
+            if (row < nrow) st16(dvp + (int64_t)row * p.dv.ss + ch * 8, ld16(&sv[row * DV + ((ch + row) % NCV) * 8]));
+        }
+        return;
+    }
     if (!col_ok) return;
     const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
     const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;

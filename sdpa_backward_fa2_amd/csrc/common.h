@@ -95,6 +95,14 @@ struct BF16 {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// The value as an fp32 result: keeps the compiler from fusing the product that
+// made it into a later conversion to 16 bits (v_fma_mix*, one rounding), so a
+// 16-bit output equals the fp32 output of the same call rounded to 16 bits.
+__device__ __forceinline__ float f32_round(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 // lane exchange inside a row of 16 lanes (DPP control word CTRL)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
