@@ -845,6 +845,45 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
         i0_k = i0_k1;
     }
 
+    if (!p.grad_f32) {
+        // 16-bit dK and dV leave through LDS as whole rows (the Q/dO tiles
+        // are free after the loop's last barrier): in the accumulator layout
+        // a store instruction covers 8 bytes of each of 32 rows.  Row r's
+        // 16-byte chunk j sits at (j + r) mod D/8, spreading the staging
+        // writes of a wavefront's 32 rows over the banks.
+        constexpr int NC = D / 8;
+        static_assert(2 * BC * D <= 2 * L::NBUF * TILE, "staging fits the tile buffers");
+        static_assert((BC * NC) % k2Threads == 0, "whole chunks per thread");
+        uint16_t* sk = Qs0;                 // [BC][D]
+        uint16_t* sv = Qs0 + BC * D;        // [BC][D]
+        const int r = 32 * kw + c;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ch = (4 * db + q + r) % NC;
+                u32x2 x;
+                x[0] = T::pack(f32_round(dka[db][4 * q + 0] * p.scale), f32_round(dka[db][4 * q + 1] * p.scale));
+                x[1] = T::pack(f32_round(dka[db][4 * q + 2] * p.scale), f32_round(dka[db][4 * q + 3] * p.scale));
+                st8(&sk[r * D + ch * 8 + 4 * g], x);
+                x[0] = T::pack(dva[db][4 * q + 0], dva[db][4 * q + 1]);
+                x[1] = T::pack(dva[db][4 * q + 2], dva[db][4 * q + 3]);
+                st8(&sv[r * D + ch * 8 + 4 * g], x);
+            }
+        __syncthreads();
+        const int nrow = min(BC, lk - j0);
+        uint16_t* dkp = p.dk.p + b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + j0) * p.dk.ss;
+        uint16_t* dvp = p.dv.p + b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + j0) * p.dv.ss;
+#pragma unroll
+        for (int x = 0; x < BC * NC / k2Threads; ++x) {
+            const int e = tid + k2Threads * x, row = e / NC, ch = e % NC, pos = (ch + row) % NC;
+            if (row < nrow) {
+                st16(dkp + (int64_t)row * p.dk.ss + ch * 8, ld16(&sk[row * D + pos * 8]));
+                st16(dvp + (int64_t)row * p.dv.ss + ch * 8, ld16(&sv[row * D + pos * 8]));
+            }
+        }
+        return;
+    }
     if (!col_ok) return;
     const int64_t dko = b * p.dk.sb + hk * p.dk.sh + (int64_t)(k0 + my_j) * p.dk.ss;
     const int64_t dvo = b * p.dv.sb + hk * p.dv.sh + (int64_t)(k0 + my_j) * p.dv.ss;
