@@ -18,6 +18,8 @@
 // aclnnNsaSelectedAttentionGrad page, "Formula" section), with
 // dS = P o (dP - Delta), Delta_i = sum_j P_ij dP_ij = sum_d dO_id O_id, the
 // softmax gradient written with the forward output instead of P.
+#include <type_traits>
+
 #include "bwd_shared.h"
 #include "common.h"
 #include "kernels.h"
@@ -823,15 +825,21 @@ __device__ __forceinline__ void bwd_key2_body(const BwdParams& p, unsigned char*
         for (int rb = 0; rb < 2; ++rb) {
             const int r0 = i0_k + 32 * rb;
             const bool masked = (CAUSAL && r0 < j0 + BC) || !full_cols;
-            if (masked)
-                softmax_grad_tile_nd<true>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, t_key - r0);
-            else
-                softmax_grad_tile_nd<false>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, 0);
+            // fp16: dS from the 16-bit P and dP - Delta operands, two products per instruction
+            constexpr bool PK = std::is_same<T, F16>::value;
+            if (masked) {
+                if constexpr (PK) softmax_p_tile_nd<true>(sab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, t_key - r0);
+                else softmax_grad_tile_nd<true>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, t_key - r0);
+            } else {
+                if constexpr (PK) softmax_p_tile_nd<false>(sab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, 0);
+                else softmax_grad_tile_nd<false>(sab[rb], pab[rb], &lse_s[buf * BR + 32 * rb], p.scale_log2, g, 0);
+            }
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const u32x4 bP = acc_to_operand<T>(sab[rb], hh);
-                const u32x4 bS = acc_to_operand<T>(pab[rb], hh);
+                u32x4 bS = acc_to_operand<T>(pab[rb], hh);
+                if constexpr (PK) bS = mul_f16x8(bP, bS);
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     dva[db] = T::mma(ld_tr<true>(dOb, QP, 32 * rb + 16 * hh, db * 32, lane), bP, dva[db]);

@@ -72,6 +72,37 @@ __device__ __forceinline__ void softmax_grad_tile_nd(f32x16& sa, f32x16& pa, con
     }
 }
 
+// The same softmax step leaving pa = dP - Delta: the caller forms dS = P o
+// (dP - Delta) from the two 16-bit operands with packed fp16 products (two
+// per instruction, rounded to nearest like the operands).
+template <bool MASKED>
+__device__ __forceinline__ void softmax_p_tile_nd(f32x16& sa, const float* lse_row, float scale_log2, int g, int t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 Lr = *reinterpret_cast<const f32x4*>(&lse_row[8 * q + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rg = 4 * q + r;
+            float pv = fast_exp2(__builtin_fmaf(sa[rg], scale_log2, -Lr[r]));
+            if (MASKED) pv = (8 * q + r >= t) ? pv : 0.f;
+            sa[rg] = pv;
+        }
+    }
+}
+
+// (Each element is copied to a scalar before its bit_cast: a bit_cast of the
+// indexed vector element itself compiled to four copies of element 0.)
+__device__ __forceinline__ u32x4 mul_f16x8(u32x4 a, u32x4 b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = a[i], y = b[i];
+        r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * __builtin_bit_cast(h2, y));
+    }
+    return r;
+}
+
 // Wavefronts per workgroup of the D=64 kernel and the dQ body: two row halves
 // of kKeySlices key slices.  Four wavefronts let two workgroups share a CU (two
 // wavefronts per SIMD), so one workgroup's memory waits and barriers overlap

@@ -51,10 +51,12 @@ struct F16 {
         return (float)__builtin_bit_cast(_Float16, x);
     }
     // MFMA operands built from fp32 intermediates (P, dS): one instruction per
-    // pair, rounding toward zero (outputs use the round-to-nearest `pack`).
+    // pair (gfx950's v_cvt_pk_f16_f32), rounding to nearest even like the
+    // outputs, so the 16-bit operands carry no rounding bias.
     static __device__ __forceinline__ uint32_t pack_op(float lo, float hi) {
-        typedef __fp16 h2 __attribute__((ext_vector_type(2)));
-        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
     }
     // c + a.lo*b.lo + a.hi*b.hi in fp32 (one v_dot2 instruction)
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
