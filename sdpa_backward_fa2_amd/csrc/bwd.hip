@@ -537,7 +537,10 @@ __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* 
         // every key of the step after every row of this wavefront: P = 0
         const bool dead = CAUSAL && j0 > w_row0 + 31;
 
-        f32x16 ds[2];
+        // dS^T as 16-bit B operands; fp16 forms it from the 16-bit P and
+        // dP - Delta with packed products, bf16 in fp32 then rounds
+        constexpr bool PK = std::is_same<T, F16>::value;
+        u32x4 ds[2][2];
         if (!dead) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -556,14 +559,22 @@ __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* 
                     for (int rg = 0; rg < 16; ++rg) {
                         float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
                         pvv = (8 * (rg >> 2) + (rg & 3) <= t) ? pvv : 0.f;
-                        dp[rg] = pvv * dp[rg];
+                        if constexpr (PK) s[rg] = pvv;
+                        else dp[rg] = pvv * dp[rg];
                     }
                 } else {
 #pragma unroll
-                    for (int rg = 0; rg < 16; ++rg)
-                        dp[rg] = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2)) * dp[rg];
+                    for (int rg = 0; rg < 16; ++rg) {
+                        const float pvv = fast_exp2(__builtin_fmaf(s[rg], p.scale_log2, -l2));
+                        if constexpr (PK) s[rg] = pvv;
+                        else dp[rg] = pvv * dp[rg];
+                    }
                 }
-                ds[kh] = dp;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    if constexpr (PK) ds[kh][hh] = mul_f16x8(acc_to_operand<T>(s, hh), acc_to_operand<T>(dp, hh));
+                    else ds[kh][hh] = acc_to_operand<T>(dp, hh);
+                }
             }
         }
         if (has_next) store_tile(buf ^ 1);
@@ -573,7 +584,7 @@ __device__ __forceinline__ void bwd_dqw_body(const BwdParams& p, unsigned char* 
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    const u32x4 bS = acc_to_operand<T>(ds[kh], hh);
+                    const u32x4 bS = ds[kh][hh];
 #pragma unroll
                     for (int db = 0; db < DB; ++db)
                         dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kh + 16 * hh, db * 32, lane), bS, dq[db]);
