@@ -126,10 +126,20 @@ constexpr int kKeySlices = kWaves / 2;
 // wavefront accumulates dQ^T over its key slice; the two slices' partials are
 // summed through LDS at the end and dQ is written once, scaled and rounded.
 
-// D: head dim of Q and K (and of dQ); DV: of V and dO.
+// D: head dim of Q and K (and of dQ); DV: of V and dO.  At D = DV = 128 the
+// key tiles go from global memory straight to LDS (global_load_lds_dwordx4,
+// no staging registers) into unpadded rows whose 16-byte chunk j of row r
+// sits at j ^ swz128(r): the MFMA operand reads of the dS and dQ products
+// then meet distinct banks (the padded rows of the register-staged form left
+// 26 M bank-conflict cycles against 23 M LDS instructions at S=4096, and its
+// 255 registers had no room for the swizzle's address arithmetic).
+template <int D, int DV>
+constexpr bool dq8_direct() { return D == 128 && DV == 128; }
+
 template <int D, int DV = D>
 struct Dq8Lds {
-    static constexpr int BK = 32 * kKeySlices, KP = D + 8, KPV = DV + 8, DB = D / 32;
+    static constexpr int BK = 32 * kKeySlices, DB = D / 32;
+    static constexpr int KP = dq8_direct<D, DV>() ? D : D + 8, KPV = dq8_direct<D, DV>() ? DV : DV + 8;
     static constexpr int TILE_B = BK * KP * 2, TILE_VB = BK * KPV * 2;
     static constexpr int LOOP_B = 2 * TILE_B + 2 * TILE_VB;
     static constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;
@@ -144,15 +154,16 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
     constexpr int KSV = DV / 16;     // k-steps of dP over DV
     constexpr int KSM = KS > KSV ? KS : KSV;
     constexpr int DB = D / 32;       // 32-row blocks of dQ^T
-    constexpr int KP = D + 8;        // row stride of Ks  [key][d]
-    constexpr int KPV = DV + 8;      // row stride of Vs  [key][dv]
+    constexpr bool DIRECT = dq8_direct<D, DV>();   // direct-to-LDS, swizzled tiles
+    constexpr int KP = Dq8Lds<D, DV>::KP;          // row stride of Ks  [key][d]
+    constexpr int KPV = Dq8Lds<D, DV>::KPV;        // row stride of Vs  [key][dv]
     constexpr int CH = BK * D / 8 / kThreads;     // 16-byte chunks per thread per K tile
     constexpr int CHV = BK * DV / 8 / kThreads;   // and per V tile
     constexpr int TILE_B = BK * KP * 2, TILE_VB = BK * KPV * 2;
     constexpr int OFF_K = 0, OFF_V = 2 * TILE_B;
     constexpr int LOOP_B = 2 * TILE_B + 2 * TILE_VB;
     constexpr int RED_B = (kKeySlices - 1) * 2 * 64 * (DB * 16) * 4;   // key slices 1.. of both row halves
-    static_assert(Dq8Lds<D, DV>::BYTES == (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
+    static_assert(Dq8Lds<D, DV>::BYTES >= (LOOP_B > RED_B ? LOOP_B : RED_B), "arena size");
     uint16_t* Ks0 = reinterpret_cast<uint16_t*>(arena + OFF_K);
     uint16_t* Vs0 = reinterpret_cast<uint16_t*>(arena + OFF_V);
 
@@ -229,10 +240,38 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
 #pragma unroll
         for (int x = 0; x < CHV; ++x) st16(&Vd[vrow(x) * KPV + vcol(x)], pv[x]);
     };
+    // Direct form: wavefront w fills 1 KiB blocks w*CH .. w*CH + CH-1 of
+    // each tile; lane l of block m writes tile chunk position 64m + l (row
+    // (64m + l) / 16, position (64m + l) % 16), which holds the row's
+    // global chunk position ^ swz128(row).  Keys past the end re-read the
+    // last key (masked out, P = 0).
+    static_assert(!DIRECT || (CH == CHV && D / 8 == 16), "direct tiles: 16 chunks per row");
+    auto dma_tile = [&](int st, int buf) {
+        if constexpr (DIRECT) {
+            const int j0 = st * BK, last = lk - 1 - j0;
+            const unsigned char* kt = reinterpret_cast<const unsigned char*>(kbase + (int64_t)j0 * p.k.ss);
+            const unsigned char* vt = reinterpret_cast<const unsigned char*>(vbase + (int64_t)j0 * p.v.ss);
+#pragma unroll
+            for (int x = 0; x < CH; ++x) {
+                const int m = w * CH + x, q = 64 * m + lane, r = q >> 4;
+                const uint32_t col = (uint32_t)(((q & 15) ^ swz128(r)) * 16);
+                const uint32_t rr = (uint32_t)min(r, last);
+                __builtin_amdgcn_global_load_lds(kt + rr * kss + col,
+                                                 (__attribute__((address_space(3))) void*)(Ks0 + buf * (BK * KP) + 512 * m),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vt + rr * vss + col,
+                                                 (__attribute__((address_space(3))) void*)(Vs0 + buf * (BK * KPV) + 512 * m),
+                                                 16, 0, 0);
+            }
+        }
+    };
 
     // Prologue: the first key tile and this lane's query row are requested
     // before anything waits for memory.
-    if (n_steps > 0) load_tile(0);
+    if (n_steps > 0) {
+        if constexpr (DIRECT) dma_tile(0, 0);
+        else load_tile(0);
+    }
     const int my_i = i0 + 32 * rh + c;
     const bool row_ok = my_i < lq;
     // a row past the end of the sequence re-reads its last row; its LSE is
@@ -255,7 +294,9 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndl16[r] = -dl;
 
-    if (n_steps > 0) store_tile(0);
+    if constexpr (!DIRECT) {
+        if (n_steps > 0) store_tile(0);
+    }
     wait_all_memory();
     __syncthreads();
 
@@ -266,15 +307,21 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
         const int buf = st & 1;
         const int j0 = st * BK;
         const bool has_next = st + 1 < n_steps;
-        if (has_next) load_tile(st + 1);
+        if (has_next) {
+            // the other buffer's tile was last read before the previous step's barrier
+            if constexpr (DIRECT) dma_tile(st + 1, buf ^ 1);
+            else load_tile(st + 1);
+        }
         const uint16_t* Kb = Ks0 + buf * (BK * KP);
         const uint16_t* Vb = Vs0 + buf * (BK * KPV);
 
         f32x16 s = zero16(), dp = ndl16;   // dP^T accumulates onto -Delta
+        const int kr = 32 * kw + c;
 #pragma unroll
         for (int ks = 0; ks < KSM; ++ks) {
-            if (ks < KS) s = T::mma(ld16(&Kb[(32 * kw + c) * KP + 16 * ks + 8 * g]), qreg[ks], s);
-            if (ks < KSV) dp = T::mma(ld16(&Vb[(32 * kw + c) * KPV + 16 * ks + 8 * g]), doreg[ks], dp);
+            const int col = 16 * ks + 8 * g;
+            if (ks < KS) s = T::mma(ld16(&Kb[kr * KP + (DIRECT ? swz128_col(kr, col) : col)]), qreg[ks], s);
+            if (ks < KSV) dp = T::mma(ld16(&Vb[kr * KPV + (DIRECT ? swz128_col(kr, col) : col)]), doreg[ks], dp);
         }
         // element (rg): key j = j0 + 32kw + 8(rg/4) + 4g + rg%4, query my_i
         const bool masked = (CAUSAL && j0 + BK > i0) || (j0 + BK > lk);
@@ -293,16 +340,24 @@ __device__ __forceinline__ void bwd_dq8_body(const BwdParams& p, unsigned char* 
                 dp[rg] = pvv * dp[rg];
             }
         }
-        if (has_next) store_tile(buf ^ 1);
+        if constexpr (!DIRECT) {
+            if (has_next) store_tile(buf ^ 1);
+        }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const u32x4 bS = acc_to_operand<T>(dp, hh);
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-                dq[db] = T::mma(ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane), bS, dq[db]);
+            for (int db = 0; db < DB; ++db) {
+                u32x4 a;
+                if constexpr (DIRECT) a = ld_tr_swz128<true>(Kb, 32 * kw + 16 * hh, db * 32, lane);
+                else a = ld_tr<true>(Kb, KP, 32 * kw + 16 * hh, db * 32, lane);
+                dq[db] = T::mma(a, bS, dq[db]);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
+        // direct form: the next tile's loads land in LDS before the barrier
+        if constexpr (DIRECT) wait_all_memory();
         __syncthreads();
     }
 
