@@ -487,8 +487,13 @@ __global__ __launch_bounds__(kThreads, (D > 128 ? 1 : 2)) void bwd_dq8_kernel(Bw
     // each XCD took every eighth query tile of every head and so read every
     // head's K and V; per-unit order took the S=4096, D=128 dQ pass from 325
     // to 236 us.
+    // Dense batches take the key-tile kernel's grouped order (item-major
+    // across an XCD's units, so its longest query tiles go first): 225.7 ->
+    // 221.9 us at B2 H16 S4096; packed batches, whose units differ in length,
+    // keep the unit-major order (249.3 us; grouped, 253.2 us on 8 sequences).
     int unit, item;
-    xcd_unit_order(gridDim.y, gridDim.x, blockIdx.y * gridDim.x + blockIdx.x, unit, item);
+    if (p.varlen) xcd_unit_order(gridDim.y, gridDim.x, blockIdx.y * gridDim.x + blockIdx.x, unit, item);
+    else xcd_group_order(gridDim.y, gridDim.x, blockIdx.y * gridDim.x + blockIdx.x, unit, item);
     bwd_dq8_body<T, D, CAUSAL, DV>(p, arena, gridDim.x - 1 - item, unit);
 }
 
