@@ -39,52 +39,6 @@ namespace sdpa {
 // causal diagonal, a ragged last key tile); ragged query rows carry LSE = +inf
 // and so contribute P = 0 without a mask.
 
-// Dispatch places consecutive workgroups (x fastest) on consecutive XCDs of
-// the eight.  For a grid of n_unit units (heads, whose workgroups share their
-// tensors) of n_item items each, linear slot L is mapped so that XCD L % 8
-// runs the items of one unit after another: its concurrently running
-// workgroups then share a unit's data in that XCD's L2, instead of every XCD
-// reading every unit.  Needs n_unit % 8 == 0 (else the plain mapping).  A
-// bijection on [0, n_unit * n_item).
-__device__ __forceinline__ void xcd_unit_order(int n_unit, int n_item, int L, int& unit, int& item) {
-    if (n_unit & 7) {
-        unit = L % n_unit;
-        item = L / n_unit;
-        return;
-    }
-    const int xcd = L & 7, slot = L >> 3;
-    unit = (slot / n_item) * 8 + xcd;
-    item = slot % n_item;
-}
-
-// The key-tile kernel's order.  Units (sequence, KV head) share Q and dO;
-// items are a unit's key tiles, longest causal range first.  With n_unit a
-// multiple of 8, unit u runs on XCD u % 8, and each XCD takes its units in
-// groups of kXcdGroup: all items of a group, item-major across its units,
-// before the next group, so that the workgroups an XCD runs at once read few
-// units' rows from its L2.  Packed sequences come sorted by decreasing length
-// (the host sorts them), so the longest units go first.  Plain order (units
-// fastest) otherwise.  A bijection on [0, n_unit * n_item).  With four units
-// per XCD (B2 H16 S4096) a group is the whole XCD share and the order is the
-// plain one.  On 8 packed sequences x 32 heads (32 units per XCD) it cut the
-// kernel's HBM reads from 1121 to 336 MB per launch (FETCH_SIZE); the time
-// stayed 387-391 us, which the one-wavefront-per-SIMD kernel spends on
-// latency, not bandwidth.  Groups of 2 were slower (401 us), of 8 the same.
-constexpr int kXcdGroup = 4;
-__device__ __forceinline__ void xcd_group_order(int n_unit, int n_item, int L, int& unit, int& item) {
-    if (n_unit & 7) {
-        unit = L % n_unit;
-        item = L / n_unit;
-        return;
-    }
-    const int xcd = L & 7, slot = L >> 3;
-    const int per_xcd = n_unit >> 3;
-    const int gi = slot / (kXcdGroup * n_item), s = slot % (kXcdGroup * n_item);
-    const int gu = min(kXcdGroup, per_xcd - gi * kXcdGroup);   // units in this group
-    item = s / gu;
-    unit = (gi * kXcdGroup + s % gu) * 8 + xcd;
-}
-
 // DK: head dim of Q and K; DV: of V, O and dO (equal unless (192, 128)).
 template <class T, int DK, int DV, bool CAUSAL, bool DQ_ATOMIC>
 __global__ __launch_bounds__(256, (DK == 64 ? 2 : 1)) void bwd_main_kernel(BwdParams p) {
