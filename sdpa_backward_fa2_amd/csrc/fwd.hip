@@ -25,7 +25,12 @@ namespace sdpa {
 // masked, rows past the end re-read the last row and are not stored.
 template <int D, int DV>
 struct FwdLds {
-    static constexpr int BK = 64, KP = D + 8, VP = DV + 8;
+    // SWV: at D = DV = 128 the V tiles are unpadded with their chunks
+    // swizzled (swz128), so that the transposing reads meet distinct banks:
+    // S=4096 causal 235 -> 229 us.  (At (192, 128) it was slower, 341 -> 353
+    // us, and a 64-column swizzle at D = 64 changed nothing.)
+    static constexpr bool SWV = D == 128 && DV == 128;
+    static constexpr int BK = 64, KP = D + 8, VP = SWV ? DV : DV + 8;
 };
 
 // D: head dim of Q and K; DV: of V and O.
@@ -37,6 +42,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     constexpr int KS = D / 16;       // k-steps of S over the Q/K head dimension
     constexpr int DB = DV / 32;      // 32-row blocks of O^T
     constexpr int KP = FwdLds<D, DV>::KP, VP = FwdLds<D, DV>::VP;   // row strides [key][d]
+    constexpr bool SWV = FwdLds<D, DV>::SWV;
     constexpr int CHK = BK * D / 8 / NT, CHV = BK * DV / 8 / NT;    // 16-byte chunks per thread per tile
     static_assert(CHK * NT * 8 == BK * D && CHV * NT * 8 == BK * DV, "whole chunks per thread");
     __shared__ __align__(16) uint16_t Ks[2][BK * KP];
@@ -77,6 +83,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
         vrow[x] = e / (DV / 8);
         vcol[x] = (e % (DV / 8)) * 8;
     }
+    auto vcol_lds = [&](int x) { return SWV ? swz128_col(vrow[x], vcol[x]) : vcol[x]; };
     u32x4 pk[CHK], pv[CHV];
     auto load_tile = [&](int st) {
         const int j0 = st * BK, last = lk - 1 - j0;
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int x = 0; x < CHK; ++x) st16(&Ks[buf][krow[x] * KP + kcol[x]], pk[x]);
 #pragma unroll
-        for (int x = 0; x < CHV; ++x) st16(&Vs[buf][vrow[x] * VP + vcol[x]], pv[x]);
+        for (int x = 0; x < CHV; ++x) st16(&Vs[buf][vrow[x] * VP + vcol_lds(x)], pv[x]);
     };
 
     if (n_steps > 0) load_tile(0);
@@ -182,8 +189,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
             for (int hh = 0; hh < 2; ++hh) {
                 const u32x4 bop = acc_to_operand<T>(s[kb], hh);
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    o[db] = T::mma(ld_tr<true>(Vb, VP, 32 * kb + 16 * hh, db * 32, lane), bop, o[db]);
+                for (int db = 0; db < DB; ++db) {
+                    u32x4 a;
+                    if constexpr (SWV) a = ld_tr_swz128<true>(Vb, 32 * kb + 16 * hh, db * 32, lane);
+                    else a = ld_tr<true>(Vb, VP, 32 * kb + 16 * hh, db * 32, lane);
+                    o[db] = T::mma(a, bop, o[db]);
+                }
             }
         if (has_next) store_tile(buf ^ 1);
         __syncthreads();
@@ -207,12 +218,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_kernel(FwdParams p) {
     }
 }
 
-// grid: (query tiles of the longest sequence, batch x heads); two-wavefront
-// workgroups at D = 64 (64-row tiles, twice as many workgroups for the
-// small head dim), four otherwise
+// grid: (query tiles of the longest sequence, batch x heads).  Four
+// wavefronts (128-row tiles) at every head dim: at D = 64 two-wavefront
+// workgroups, twice as many, were no faster on the GPT-2 shape (31.0 against
+// 30.3 us).
 template <class T, int D, int DV>
 static hipError_t launch_fwd_t(const FwdParams& p, int max_lq, bool causal, hipStream_t st) {
-    constexpr int NW = (D == 64 && DV == 64) ? 2 : 4;
+    constexpr int NW = 4;
     dim3 grid((max_lq + 32 * NW - 1) / (32 * NW), p.B * p.Hq);
     if (causal)
         PROF_LAUNCH(KID_FWD, st, (fwd_kernel<T, D, DV, true, NW>), grid, dim3(64 * NW), 0, st, p);
