@@ -63,12 +63,17 @@ struct NsaParams {
     int32_t* pieces;      // [max_pieces][3]: bucket, first entry, end entry
     int tt, n_tiles;      // index build: tokens per tile, tiles (ceil(Tq / tt))
     int32_t* hist;        // [N2][NB][n_tiles] per-tile block totals, then their prefixes
-    int32_t* rank;        // [N2][Tq * count] entry ranks within their tile and block
+    int32_t* rank;        // [N2][Tq * count] entry ranks within their tile and block; after the
+                          // scatter, each entry's position in the entries array (-1: none)
     // backward
     TensorArg q, k, v, dout, dq, dk, dv;
     const float* lse2;
     const float* delta;
     float* partial;       // [max_pieces][halves][64][D] for dK then dV
+    // stored dS (16 query heads per KV head, Dqk = Dv = 128; null: the dQ
+    // kernel recomputes it): [entry position][key of the block][16 heads in
+    // the order 0-3, 8-11, 4-7, 12-15], 16-bit
+    uint16_t* ds;
     int halves;           // ceil(bs / 64)
     int sparse_mode;
     int t_base;           // forward: first token of this launch (grid x counts from it)
@@ -301,7 +306,7 @@ __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
     const int t0 = tile * p.tt, t1 = min(p.Tq, t0 + p.tt);
     const int e_begin = t0 * p.count, e_end = t1 * p.count;
     const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
-    const int32_t* rank = p.rank + (int64_t)h2 * p.Tq * p.count;
+    int32_t* rank = p.rank + (int64_t)h2 * p.Tq * p.count;
     const int32_t* hist = p.hist + (int64_t)h2 * p.NB * p.n_tiles;
     const int32_t* off = p.offsets + h2 * p.NB;
     int s_cur = seq_of_token(p.seqs, t0);
@@ -320,8 +325,13 @@ __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
         for (int u = 0; u < kIdxBatch; ++u)
             pos[u] = g[u] >= 0 ? off[g[u]] + hist[(int64_t)g[u] * p.n_tiles + tile] + rk[u] : -1;
 #pragma unroll
-        for (int u = 0; u < kIdxBatch; ++u)
-            if (g[u] >= 0) p.entries[pos[u]] = cb + 64 * u + lane;
+        for (int u = 0; u < kIdxBatch; ++u) {
+            const int e = cb + 64 * u + lane;
+            if (g[u] >= 0) p.entries[pos[u]] = e;
+            // each entry's list position replaces its rank (read above by
+            // this lane only): the stored-dS dQ kernel finds its dS by it
+            if (e < e_end) rank[e] = pos[u];
+        }
     }
 }
 
@@ -626,6 +636,15 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             for (int hh = 0; hh < 2; ++hh) {
                 const u32x4 bP = acc_to_operand<T>(sa, hh);
                 const u32x4 bS = acc_to_operand<T>(pa, hh);
+                if constexpr (DK == 128 && DV == 128) {
+                    // 16 heads per entry: rows r0 + 16hh .. +15 are one
+                    // entry; this lane holds 8 of its heads for key myk
+                    if (p.ds && col_ok) {
+                        const int li = st * E + (r0 + 16 * hh) / 16;
+                        if (li < n_e)
+                            st16(p.ds + ((int64_t)(eb + li) * p.bs + kb0 + myk) * 16 + 8 * g, bS);
+                    }
+                }
 #pragma unroll
                 for (int db = 0; db < DBM; ++db) {
                     if (db < DBV) dva[db] = T::mma(ld_tr<true>(dOb, QPV, r0 + 16 * hh, db * 32, lane), bP, dva[db]);
@@ -982,6 +1001,101 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
     for (int db = 0; db < DB; ++db)
         st_grad4<T>(p.dq.p, dqo + 16 * db + 4 * G16, p.grad_f32, dq[db][0] * p.scale, dq[db][1] * p.scale,
                     dq[db][2] * p.scale, dq[db][3] * p.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dQ from the stored dS (16 query heads per KV head, Dqk = Dv = 128)
+// ---------------------------------------------------------------------------
+//
+// dQ_t = scale * sum over the token's gathered keys j of dS_tj K_j, with dS
+// as the dK/dV kernel stored it (one 16-head x block_size tile per entry),
+// so this pass gathers K only and recomputes neither S nor dP.  Workgroup
+// (four wavefronts) per (token, KV head); the gathered keys go 128 at a time
+// (block_size divides 128): the chunk's K rows and dS^T rows are loaded into
+// registers during the previous chunk and staged in LDS; wavefront w forms
+// dQ^T for head dims 32w .. 32w+31 as K^T dS^T (v_mfma_f32_16x16x32, both
+// operands by transposing LDS reads), so no partials are reduced.  A choice
+// outside the sequence has no entry and contributes zero.
+template <class T>
+__global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p) {
+    constexpr int D = 128, BK = 128;
+    constexpr int KP = D + 8;                    // K rows in LDS, padded
+    constexpr int DP = 16;                       // dS^T rows: 16 heads
+    constexpr int CHK = BK * D / 8 / 256;        // 16-byte K chunks per thread
+    __shared__ __align__(16) uint16_t Ks[BK * KP];
+    __shared__ __align__(16) uint16_t Ds[BK * DP];
+    __shared__ int blk_s[128];                   // the token's chosen blocks (-1: none)
+    __shared__ int pos_s[128];                   // their entries' list positions
+
+    const int t = blockIdx.x, h2 = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int col = lane & 15, G16 = lane >> 4;
+    const int s_idx = seq_of_token(p.seqs, t);
+    if (s_idx < 0) return;
+    const SeqRow sq = seq_row(p.seqs, s_idx);
+    const int krow0 = sq.k0;
+    const int nblk = sq.lk / p.bs;
+    const int nk = p.count * p.bs;
+    const int32_t* tk = p.topk + (int64_t)t * p.tk_st + (int64_t)h2 * p.tk_sn;
+    const int32_t* pos_of = p.rank + (int64_t)h2 * p.Tq * p.count + (int64_t)t * p.count;
+    for (int i = tid; i < p.count; i += 256) {
+        const int blk = tk[(int64_t)i * p.tk_sk];
+        const bool ok = blk >= 0 && blk < nblk;
+        blk_s[i] = ok ? blk : -1;
+        pos_s[i] = ok ? pos_of[i] : -1;
+    }
+    __syncthreads();
+
+    const int kss = (int)p.k.ss;
+    const uint16_t* const kh = p.k.p + (int64_t)h2 * p.k.sh;
+    u32x4 kv[CHK], dv;
+    // Unconditional loads: a key of no block, or past the gathered keys,
+    // re-reads key row krow0 and entry 0's dS, and its dS is zeroed.
+    auto load_chunk = [&](int c0) {
+#pragma unroll
+        for (int x = 0; x < CHK; ++x) {
+            const int e = tid + 256 * x;
+            const int r = e / (D / 8), cc = (e % (D / 8)) * 8;
+            const int n = c0 + r;
+            const int slot = min(n / p.bs, p.count - 1);
+            const int blk = blk_s[slot];
+            const int row = krow0 + ((n < nk && blk >= 0) ? blk * p.bs + n % p.bs : 0);
+            kv[x] = ld16(kh + (int64_t)row * kss + cc);
+        }
+        const int n = c0 + (tid >> 1);
+        const int slot = min(n / p.bs, p.count - 1);
+        const int pos = n < nk ? pos_s[slot] : -1;
+        dv = ld16(p.ds + ((int64_t)max(pos, 0) * p.bs + n % p.bs) * 16 + 8 * (tid & 1));
+        if (pos < 0) dv = u32x4{0u, 0u, 0u, 0u};
+    };
+    f32x4 dq[2] = {zero4(), zero4()};
+    load_chunk(0);
+    for (int c0 = 0; c0 < nk; c0 += BK) {
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < CHK; ++x) {
+            const int e = tid + 256 * x;
+            st16(&Ks[(e / (D / 8)) * KP + (e % (D / 8)) * 8], kv[x]);
+        }
+        st16(&Ds[(tid >> 1) * DP + 8 * (tid & 1)], dv);
+        __syncthreads();
+        if (c0 + BK < nk) load_chunk(c0 + BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 32; ++ks) {
+            const u32x4 b = ld_tr16x16(Ds, DP, 32 * ks, 0, lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                dq[j] = T::mma16(ld_tr16x16(Ks, KP, 32 * ks, 32 * w + 16 * j, lane), b, dq[j]);
+        }
+    }
+    // dQ^T tiles: lane holds stored head slot `col` (head 0-3, 8-11, 4-7,
+    // 12-15 in slot order), head dims 32w + 16j + 4*G16 + r
+    const int h = h2 * 16 + ((col & 4) ? (col >> 3) * 4 + 8 + (col & 3) : (col >> 3) * 4 + (col & 3));
+    const int64_t dqo = (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+        st_grad4<T>(p.dq.p, dqo + 32 * w + 16 * j + 4 * G16, p.grad_f32, dq[j][0] * p.scale, dq[j][1] * p.scale,
+                    dq[j][2] * p.scale, dq[j][3] * p.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -1458,10 +1572,16 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     // zeros and there is no dQ row to write
     if (p.Tq > 0) {
         const dim3 grid(p.Tq, p.N2 * ((p.G + 15) / 16));
-        if constexpr (DK > 128)
+        if constexpr (DK > 128) {
             PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_wave_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
-        else
+        } else if constexpr (DK == 128 && DV == 128) {
+            if (p.ds)
+                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_ds_kernel<T>), dim3(p.Tq, p.N2), dim3(256), 0, st, p);
+            else
+                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
+        } else {
             PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
+        }
     }
     return hipGetLastError();
 }
@@ -1488,7 +1608,8 @@ size_t up(size_t x) { return (x + kAlignN - 1) / kAlignN * kAlignN; }
 struct NsaLayout {
     int64_t NB = 0, nbk = 0, E = 0, chunk = 1, max_pieces = 0, halves = 1, tt = 16, n_tiles = 0;
     size_t counts = 0, offsets = 0, entries = 0, pstart = 0, pieces = 0, hist = 0, rank = 0, lse2 = 0, delta = 0,
-           partial = 0, seqtab = 0, total = 0;
+           partial = 0, seqtab = 0, ds = 0, total = 0;
+    bool use_ds = false;      // the dK/dV kernel stores dS for the dQ pass
 };
 
 struct Seqs {
@@ -1568,6 +1689,11 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.lse2 = o; o = up(o + S.Tq * Hq * 4);
     L.delta = o; o = up(o + S.Tq * Hq * 4);
     L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
+    // stored dS for a dQ pass without recomputation: 16 query heads per KV
+    // head at Dqk = Dv = 128, block sizes that divide 128, up to 1 GiB
+    const size_t ds_bytes = (size_t)std::max<int64_t>(L.E, 1) * bs * 16 * 2;
+    L.use_ds = G == 16 && D == 128 && Dv == 128 && 128 % bs == 0 && ds_bytes <= ((size_t)1 << 30);
+    L.ds = o; o = up(o + (L.use_ds ? ds_bytes : 0));
     // more sequences than the kernel arguments carry: a table in the workspace
     const int64_t n = (int64_t)S.q0.size();
     L.seqtab = o; o = up(o + (n > sdpa::kMaxSeqArgs ? (size_t)n * 16 : 0));
@@ -1778,6 +1904,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     p.lse2 = reinterpret_cast<float*>(ws + L.lse2);
     p.delta = reinterpret_cast<float*>(ws + L.delta);
     p.partial = reinterpret_cast<float*>(ws + L.partial);
+    p.ds = L.use_ds ? reinterpret_cast<uint16_t*>(ws + L.ds) : nullptr;
     p.sparse_mode = sparse_mode;
     p.mask = atten_mask; p.mask_ss = atten_mask_stride;
     p.scale = (float)scale;

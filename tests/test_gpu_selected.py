@@ -137,6 +137,11 @@ def test_config5_nsa_selected():
     ((512,), 1, 1, 128, 3),
     ((384, 192), 16, 1, 64, 3),
     ((96, 192), 2, 1, 48, 2),      # block size that does not divide a 128-key chunk
+    # 16 query heads per KV head: at Dqk = Dv = 128 the dQ pass reads the dS
+    # the dK/dV kernel stored (two KV heads; 32-key blocks, four to a 128-key
+    # chunk; 128-key blocks, two 64-key halves each)
+    ((256, 384), 16, 2, 32, 4),
+    ((512,), 16, 1, 128, 3),
 ])
 def test_selected_small(dtype, D, Dv, mode, lengths, G, N2, bs, count):
     """D: head dim of Q and K, Dv: of V and dO (192/128: the page's unequal
