@@ -28,6 +28,9 @@
 //                            order (deterministic); zero-fills unselected blocks
 //   nsa_dq_kernel            per (token, KV head, 16-head tile): dQ over the
 //                            gathered keys, without atomics
+//   nsa_dq_ds_kernel         16 query heads per KV head, Dqk = Dv = 128: dQ
+//                            from the dS that nsa_kv_kernel stored (K gathered,
+//                            S and dP not recomputed)
 //   nsa_fwd_kernel           the forward: O and (max, sum) per (token, head)
 //                            over the gathered keys, same tiling as nsa_dq
 #include <hip/hip_runtime.h>
