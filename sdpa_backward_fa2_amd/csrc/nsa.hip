@@ -1668,13 +1668,51 @@ int check_selected(int64_t batch, const int64_t* cuq, const int64_t* cuk, int64_
     return SDPA_OK;
 }
 
+// Compute units of the current device (256 if the query fails).
+int device_cus() {
+    constexpr int kMaxDev = 64;
+    static int cached[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    if (cached[dev] == 0) {
+        int cu = 0;
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) return 256;
+        cached[dev] = cu;
+    }
+    return cached[dev];
+}
+
 NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t Dv, int64_t bs, int64_t count) {
     NsaLayout L;
     L.NB = S.Tk / bs;
     L.nbk = Hkv * L.NB;
     L.E = S.Tq * Hkv * count;
     const int64_t G = Hq / Hkv;
-    L.chunk = std::max<int64_t>(1, 2048 / G);
+    // Entries per work piece of the dK/dV kernel: k steps of BR rows (BR / G
+    // entries each), k chosen to minimise an estimate of the kernel's span,
+    // the rounds of pieces over the device's workgroup slots times k steps,
+    // plus a small cost per piece for its partial sums (the pieces' count is
+    // bounded by one partial piece per bucket).  On the NSA workload (65536
+    // entries, 64 buckets, 256 slots) pieces of 16 steps took 199 us, of 12
+    // steps 182 us, of 10 steps 197 us and of 8 steps 191 us: the rounds, not
+    // the piece length, set the span.  At most 1.5x the pieces (and partial
+    // workspace) of the longest pieces.
+    const int64_t BR = (D == 128 && Dv == 128) ? 128 : 64;      // the kernel's rows per step
+    const int64_t per_step = std::max<int64_t>(1, BR / G);
+    const int64_t slots = (int64_t)device_cus() * (D == 64 ? 2 : 1);
+    const int64_t kmax = 2048 / BR;                  // a piece's tokens fit the kernel's 2048 / G table
+    const int64_t np_cap = 3 * (L.nbk + (L.E + kmax * per_step - 1) / (kmax * per_step)) / 2;
+    double best = -1.0;
+    for (int64_t k = kmax; k >= 4; --k) {
+        const int64_t ch = k * per_step;
+        const int64_t np = L.nbk + (L.E + ch - 1) / ch;
+        if (k < kmax && np > np_cap) break;
+        const double cost = (double)((np + slots - 1) / slots) * k * BR + 0.4 * np;
+        if (best < 0.0 || cost < best) {
+            best = cost;
+            L.chunk = ch;
+        }
+    }
     L.max_pieces = L.nbk + (L.E + L.chunk - 1) / L.chunk;
     L.halves = (bs + 63) / 64;
     // index tiles: 16 tokens, doubled until blocks x tiles is at most 2^22
