@@ -738,16 +738,15 @@ template <int DK, int DV>
 constexpr int reduce_key_groups() { return 64 / (256 / reduce_lanes<DK, DV>()); }
 
 template <class T, int DK, int DV>
-__global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
+__device__ __forceinline__ void kv_reduce_body(const NsaParams& p, int bucket, int half, int group) {
     constexpr int LPR = reduce_lanes<DK, DV>();   // threads per key row, 8 columns each
-    const int bucket = blockIdx.x, half = blockIdx.y;
     const int h2 = bucket / p.NB, blk = bucket % p.NB;
     const int kb0 = half * 64;
     if (kb0 >= p.bs) return;
     const int ps = p.pstart[bucket], np = p.pstart[bucket + 1] - ps;
     if (np == 1) return;
     const int nkeys = min(64, p.bs - kb0);
-    const int key = blockIdx.z * (256 / LPR) + threadIdx.x / LPR, d0 = (threadIdx.x % LPR) * 8;
+    const int key = group * (256 / LPR) + threadIdx.x / LPR, d0 = (threadIdx.x % LPR) * 8;
     const bool has_k = d0 < DK, has_v = d0 < DV;
     if (key >= nkeys || !(has_k || has_v)) return;
     float ak[8], av[8];
@@ -782,6 +781,11 @@ __global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
     const int64_t row = (int64_t)blk * p.bs + kb0 + key;
     if (has_k) st_grad8<T>(p.dk.p, h2 * p.dk.sh + row * p.dk.ss + d0, p.grad_f32, ak);
     if (has_v) st_grad8<T>(p.dv.p, h2 * p.dv.sh + row * p.dv.ss + d0, p.grad_f32, av);
+}
+
+template <class T, int DK, int DV>
+__global__ __launch_bounds__(256) void nsa_kv_reduce_kernel(NsaParams p) {
+    kv_reduce_body<T, DK, DV>(p, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -1020,7 +1024,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 // operands by transposing LDS reads), so no partials are reduced.  A choice
 // outside the sequence has no entry and contributes zero.
 template <class T>
-__global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p) {
+__device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
     constexpr int D = 128, BK = 128;
     constexpr int KP = D + 8;                    // K rows in LDS, padded
     constexpr int DP = 16;                       // dS^T rows: 16 heads
@@ -1030,7 +1034,6 @@ __global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p) {
     __shared__ int blk_s[128];                   // the token's chosen blocks (-1: none)
     __shared__ int pos_s[128];                   // their entries' list positions
 
-    const int t = blockIdx.x, h2 = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int col = lane & 15, G16 = lane >> 4;
     const int s_idx = seq_of_token(p.seqs, t);
@@ -1099,6 +1102,22 @@ __global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p) {
     for (int j = 0; j < 2; ++j)
         st_grad4<T>(p.dq.p, dqo + 32 * w + 16 * j + 4 * G16, p.grad_f32, dq[j][0] * p.scale, dq[j][1] * p.scale,
                     dq[j][2] * p.scale, dq[j][3] * p.scale);
+}
+
+// One launch for the stored-dS dQ pass and the partial-sum reduction of
+// dK/dV (independent of each other; both follow the dK/dV kernel): the dQ
+// items first, one per (token, KV head), then the reduction's items, which
+// fill the CUs the dQ pass's last round leaves idle.
+template <class T>
+__global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p, int n_dq) {
+    const int id = blockIdx.x;
+    if (id < n_dq) {
+        dq_ds_body<T>(p, id / p.N2, id % p.N2);
+        return;
+    }
+    constexpr int NG = reduce_key_groups<128, 128>();
+    const int r = id - n_dq;
+    kv_reduce_body<T, 128, 128>(p, r / (p.halves * NG), (r / NG) % p.halves, r % NG);
 }
 
 // ---------------------------------------------------------------------------
@@ -1569,6 +1588,17 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     else
         PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
                     st, p);
+    if constexpr (DK == 128 && DV == 128) {
+        if (p.ds) {
+            // the dQ pass and the reduction in one launch
+            const long n_dq = (long)p.Tq * p.N2;
+            const long n_red = (long)p.N2 * p.NB * p.halves * reduce_key_groups<128, 128>();
+            if (n_dq + n_red > 0)
+                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_ds_kernel<T>), dim3((unsigned)(n_dq + n_red)), dim3(256), 0, st, p,
+                            (int)n_dq);
+            return hipGetLastError();
+        }
+    }
     PROF_LAUNCH(KID_NSA_KV_REDUCE, st, (nsa_kv_reduce_kernel<T, DK, DV>),
                 dim3(p.N2 * p.NB, p.halves, reduce_key_groups<DK, DV>()), dim3(256), 0, st, p);
     // with no query token (every query length 0) dK and dV are the reduction's
@@ -1577,11 +1607,6 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
         const dim3 grid(p.Tq, p.N2 * ((p.G + 15) / 16));
         if constexpr (DK > 128) {
             PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_wave_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
-        } else if constexpr (DK == 128 && DV == 128) {
-            if (p.ds)
-                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_ds_kernel<T>), dim3(p.Tq, p.N2), dim3(256), 0, st, p);
-            else
-                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
         } else {
             PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_kernel<T, DK, DV>), grid, dim3(256), 0, st, p);
         }
