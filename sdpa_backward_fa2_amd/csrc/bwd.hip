@@ -31,65 +31,12 @@ namespace sdpa {
 // Preprocess
 // ---------------------------------------------------------------------------
 
-// Grid, LPR lanes per row (a power of two; 16 elements per lane at D=64 and
-// 128, 24 at D=192): dense, x = chunks of rows of one (batch, head) = y;
-// packed, x = chunks of the (token, head) rows in memory order (the heads of
-// a token are adjacent in the packed layout).
-template <int D>
-constexpr int pre_lanes() { return D == 64 ? 4 : 8; }
 template <int D>
 constexpr int pre_rows_per_block() { return 256 / pre_lanes<D>(); }
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p, int zero_dq) {
-    constexpr int LPR = pre_lanes<D>();
-    constexpr int EPL = D / LPR;                 // elements per lane
-    constexpr int NC = EPL / 8;                  // 16-byte chunks per lane
-    static_assert(EPL % 8 == 0 && (LPR & (LPR - 1)) == 0, "row split");
-    constexpr int RPB = pre_rows_per_block<D>();
-    const int part = threadIdx.x % LPR;
-    int64_t R;
-    bool ok;
-    RowLoc L;
-    if (p.varlen) {
-        R = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-        ok = R < p.rows;
-        const int64_t Rc = ok ? R : p.rows - 1;           // rows past the end re-read the last
-        L = RowLoc{0, Rc % p.Hq, Rc / p.Hq};
-    } else {
-        const int i = blockIdx.x * RPB + threadIdx.x / LPR;
-        const int y = blockIdx.y;
-        ok = i < p.Sq;
-        R = (int64_t)y * p.Sq + i;
-        L = RowLoc{y / p.Hq, y % p.Hq, min(i, p.Sq - 1)};
-    }
-    const uint16_t* op = p.o.p + toff(p.o, L) + part * EPL;
-    const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * EPL;
-    u32x4 oc[NC], dc[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        oc[c] = ld16(op + 8 * c);
-        dc[c] = ld16(dp + 8 * c);
-    }
-    const int64_t so = L.b * p.st_sb + L.h * p.st_sh + L.i * p.st_ss;
-    const float sa = p.st_a[so];
-    const float sb = p.stats_kind ? p.st_b[so] : 0.f;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc = dot8<T>(dc[c], oc[c], acc);
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (!ok) return;
-    if (part == 0) {
-        p.delta[R] = acc;
-        p.lse2[R] = stats_to_lse2(p.stats_kind, sa, sb);
-    }
-    if (zero_dq) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * EPL);
-#pragma unroll
-        for (int c = 0; c < EPL / 4; ++c) dst[c] = z;
-    }
+    row_pass_rows<T, D, 256>(p, zero_dq, blockIdx.x, blockIdx.y);
 }
 
 template <class T, int D>

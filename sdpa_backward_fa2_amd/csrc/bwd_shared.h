@@ -51,6 +51,67 @@ __device__ __forceinline__ int64_t toff(const TensorArg& t, const RowLoc& L) {
     return L.b * t.sb + L.h * t.sh + L.i * t.ss;
 }
 
+// The row pass (Delta = sum_d dO*O, the statistics as log2-domain LSE and,
+// in the atomic dQ mode, the fp32 accumulator row cleared) over the rows of
+// workgroup (bx, by) of NT threads, LPR lanes per row (a power of two; 16
+// elements per lane at D=64 and 128, 24 at D=192): dense, bx = chunks of rows
+// of one (batch, head) = by; packed, bx = chunks of the (token, head) rows in
+// memory order (the heads of a token are adjacent in the packed layout).
+template <int D>
+constexpr int pre_lanes() { return D == 64 ? 4 : 8; }
+
+template <class T, int D, int NT>
+__device__ __forceinline__ void row_pass_rows(const BwdParams& p, int zero_dq, int bx, int by) {
+    constexpr int LPR = pre_lanes<D>();
+    constexpr int EPL = D / LPR;                 // elements per lane
+    constexpr int NC = EPL / 8;                  // 16-byte chunks per lane
+    static_assert(EPL % 8 == 0 && (LPR & (LPR - 1)) == 0, "row split");
+    constexpr int RPB = NT / LPR;                // rows per workgroup
+    const int part = threadIdx.x % LPR;
+    int64_t R;
+    bool ok;
+    RowLoc L;
+    if (p.varlen) {
+        R = (int64_t)bx * RPB + threadIdx.x / LPR;
+        ok = R < p.rows;
+        const int64_t Rc = ok ? R : p.rows - 1;           // rows past the end re-read the last
+        L = RowLoc{0, Rc % p.Hq, Rc / p.Hq};
+    } else {
+        const int i = bx * RPB + threadIdx.x / LPR;
+        const int y = by;
+        ok = i < p.Sq;
+        R = (int64_t)y * p.Sq + i;
+        L = RowLoc{y / p.Hq, y % p.Hq, min(i, p.Sq - 1)};
+    }
+    const uint16_t* op = p.o.p + toff(p.o, L) + part * EPL;
+    const uint16_t* dp = p.dout.p + toff(p.dout, L) + part * EPL;
+    u32x4 oc[NC], dc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        oc[c] = ld16(op + 8 * c);
+        dc[c] = ld16(dp + 8 * c);
+    }
+    const int64_t so = L.b * p.st_sb + L.h * p.st_sh + L.i * p.st_ss;
+    const float sa = p.st_a[so];
+    const float sb = p.stats_kind ? p.st_b[so] : 0.f;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc = dot8<T>(dc[c], oc[c], acc);
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (!ok) return;
+    if (part == 0) {
+        p.delta[R] = acc;
+        p.lse2[R] = stats_to_lse2(p.stats_kind, sa, sb);
+    }
+    if (zero_dq) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4* dst = reinterpret_cast<f32x4*>(p.dqacc + acc_row(p, L, R) * D + part * EPL);
+#pragma unroll
+        for (int c = 0; c < EPL / 4; ++c) dst[c] = z;
+    }
+}
+
 // P = exp2(S*scale*log2e - LSE*log2e) and dS = P * (dP - Delta) for one 32x32
 // C tile held as (sa, pa), whose dP accumulator started from -Delta (pa
 // already holds dP - Delta); rows 8q + 4g + r of the tile, this lane's key.  Element (q, r) is kept when 8q + r >= t, with t the first

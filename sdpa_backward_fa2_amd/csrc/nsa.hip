@@ -43,6 +43,7 @@
 #include <vector>
 
 #include "../../include/sdpa_bwd.h"
+#include "bwd_shared.h"
 #include "common.h"
 #include "kernels.h"
 #include "prof.h"
@@ -213,9 +214,9 @@ __device__ __forceinline__ int step_block(const NsaParams& p, int v, int c, int 
     return c + lane < e_end ? g : -1;
 }
 
-__global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
+__device__ __forceinline__ void rank_body(const NsaParams& p, int tile, int h2) {
     __shared__ int cnt[kIdxWin];
-    const int tile = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
+    const int lane = threadIdx.x;
     const int t0 = tile * p.tt, t1 = min(p.Tq, t0 + p.tt);
     const int e_begin = t0 * p.count, e_end = t1 * p.count;
     const int sa = seq_of_token(p.seqs, t0), sb = seq_of_token(p.seqs, t1 - 1);
@@ -264,6 +265,20 @@ __global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
         for (int i = lane; i < nw; i += 64) hist[(int64_t)(w0 + i) * p.n_tiles + tile] = cnt[i];
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
+}
+
+__global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
+    rank_body(p, blockIdx.x, blockIdx.y);
+}
+
+// The rank pass and the backward's row pass (Delta and log2-LSE of every
+// (token, head) row, which the index does not need) in one launch: the rank
+// items first, then row-pass items of 64 threads.
+template <class T, int DV>
+__global__ __launch_bounds__(64) void nsa_rank_pre_kernel(NsaParams p, BwdParams bp, int n_rank) {
+    const int id = blockIdx.x;
+    if (id < n_rank) rank_body(p, id % p.n_tiles, id / p.n_tiles);
+    else row_pass_rows<T, DV, 64>(bp, 0, id - n_rank, 0);
 }
 
 // One wavefront, one (block, KV head) = bucket: exclusive prefixes over the
@@ -1578,9 +1593,20 @@ static hipError_t launch_nsa_fwd_dims(const NsaParams& p, int D, int Dv, hipStre
 // DK: head dim of Q and K, DV: of V, O and dO (the row pass reduces dO o O)
 template <class T, int DK, int DV>
 static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStream_t st) {
-    hipError_t e = launch_index(p, st);
-    if (e != hipSuccess) return e;
-    e = launch_bwd_pre(bp, std::is_same<T, F16>::value ? 0 : 1, DV, false, st);
+    // the index build with the row pass in its first launch (the two are
+    // independent): one launch fewer than index + row pass
+    {
+        const long n_rank = (long)p.n_tiles * p.N2;
+        const long n_pre = (bp.rows + 64 / pre_lanes<DV>() - 1) / (64 / pre_lanes<DV>());
+        if (n_rank + n_pre > 0)
+            PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_rank_pre_kernel<T, DV>), dim3((unsigned)(n_rank + n_pre)), dim3(64), 0,
+                        st, p, bp, (int)n_rank);
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_hist_scan_kernel, dim3(p.NB, p.N2), dim3(64), 0, st, p);
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
+        if (p.n_tiles > 0)
+            PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+    }
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.mask)
         PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, true>), dim3(p.max_pieces, p.halves), dim3(256), 0,
