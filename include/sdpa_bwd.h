@@ -340,8 +340,10 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
  * and the number of launches launches[k], and disables timing.  Kernel ids:
  * 0 forward, 1 backward preprocess, 2 backward key-tile kernel (D=128; D=64
  * in dQ mode 2), 3 dQ convert,
- * 4 deterministic dQ (D=128), 5 NSA index build (four launches), 6 NSA dK/dV,
- * 7 NSA dQ, 8 fused dK/dV and dQ (D=64), 9 NSA dK/dV partial reduction,
+ * 4 deterministic dQ (D=128), 5 NSA index build (four launches; in the
+ * selected backward the first also carries the row pass), 6 NSA dK/dV,
+ * 7 NSA dQ (with the dK/dV partial reduction where the dQ pass reads stored
+ * dS), 8 fused dK/dV and dQ (D=64), 9 NSA dK/dV partial reduction,
  * 10 fused dK/dV and dQ, two-wavefront form (D=64);
  * sdpa_kernel_name(id) gives the kernel's symbol name stem.  Not thread-safe
  * with respect to concurrent begin/end calls from several threads.
