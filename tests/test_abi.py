@@ -292,12 +292,18 @@ def test_bwd_selected_validation():
     assert bwd_selected_call(D=128, Dv=64) == UNSUPPORTED
     assert bwd_selected_call(mask=FAKE, mask_stride=256) == INVALID     # row shorter than the KV length
     assert bwd_selected_call(mask=FAKE, mask_stride=1 << 31) == UNSUPPORTED
-    n = ctypes.c_size_t(0)
     cu = (ctypes.c_int64 * 1)(512)
-    assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 192, 128, 64, 4, 0, ctypes.byref(n)) == OK
-    m = ctypes.c_size_t(0)
-    assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, 16, 1, 128, 128, 64, 4, 0, ctypes.byref(m)) == OK
-    assert n.value > m.value                             # wider dK partials
+
+    def ws(Hq, D, Dv):
+        n = ctypes.c_size_t(0)
+        assert lib().sdpa_bwd_selected_workspace_size(1, 1, cu, cu, Hq, 1, D, Dv, 64, 4, 0, ctypes.byref(n)) == OK
+        return n.value
+    assert ws(16, 192, 192) > ws(16, 192, 128)          # wider dV partials, same pieces
+    # 16 query heads per KV head at 128/128: the dK/dV kernel stores dS for
+    # the dQ pass, one 16-bit 16-head x 64-key tile per (token, slot) entry
+    stored_ds = 512 * 4 * 16 * 64 * 2
+    assert ws(16, 128, 128) >= stored_ds
+    assert ws(16, 192, 128) < stored_ds and ws(8, 128, 128) < stored_ds
     assert fwd_selected_call(D=128, Dv=192) == UNSUPPORTED
 
 
