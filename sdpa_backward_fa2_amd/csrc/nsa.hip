@@ -28,7 +28,7 @@
 //                            order (deterministic); zero-fills unselected blocks
 //   nsa_dq_kernel            per (token, KV head, 16-head tile): dQ over the
 //                            gathered keys, without atomics
-//   nsa_dq_ds_kernel         16 query heads per KV head, Dqk = Dv = 128: dQ
+//   nsa_dq_ds_kernel         16 query heads per KV head, Dqk 128 or 192: dQ
 //                            from the dS that nsa_kv_kernel stored (K gathered,
 //                            S and dP not recomputed)
 //   nsa_fwd_kernel           the forward: O and (max, sum) per (token, head)
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             for (int hh = 0; hh < 2; ++hh) {
                 const u32x4 bP = acc_to_operand<T>(sa, hh);
                 const u32x4 bS = acc_to_operand<T>(pa, hh);
-                if constexpr (DK == 128 && DV == 128) {
+                if constexpr (DK >= 128) {
                     // 16 heads per entry: rows r0 + 16hh .. +15 are one
                     // entry; this lane holds 8 of its heads for key myk
                     if (p.ds && col_ok) {
@@ -1026,7 +1026,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ from the stored dS (16 query heads per KV head, Dqk = Dv = 128)
+// dQ from the stored dS (16 query heads per KV head, Dqk = 128 or 192)
 // ---------------------------------------------------------------------------
 //
 // dQ_t = scale * sum over the token's gathered keys j of dS_tj K_j, with dS
@@ -1035,12 +1035,14 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 // (four wavefronts) per (token, KV head); the gathered keys go 128 at a time
 // (block_size divides 128): the chunk's K rows and dS^T rows are loaded into
 // registers during the previous chunk and staged in LDS; wavefront w forms
-// dQ^T for head dims 32w .. 32w+31 as K^T dS^T (v_mfma_f32_16x16x32, both
-// operands by transposing LDS reads), so no partials are reduced.  A choice
-// outside the sequence has no entry and contributes zero.
-template <class T>
+// dQ^T for head dims D/4 * w .. + D/4 - 1 as K^T dS^T (v_mfma_f32_16x16x32,
+// both operands by transposing LDS reads), so no partials are reduced.  A
+// choice outside the sequence has no entry and contributes zero.
+template <class T, int D>
 __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
-    constexpr int D = 128, BK = 128;
+    static_assert(D == 128 || D == 192, "stored-dS dQ: Dqk 128 or 192");
+    constexpr int BK = 128;
+    constexpr int NJ = D / 64;                   // 16-column dQ^T tiles per wavefront
     constexpr int KP = D + 8;                    // K rows in LDS, padded
     constexpr int DP = 16;                       // dS^T rows: 16 heads
     constexpr int CHK = BK * D / 8 / 256;        // 16-byte K chunks per thread
@@ -1089,7 +1091,9 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
         dv = ld16(p.ds + ((int64_t)max(pos, 0) * p.bs + n % p.bs) * 16 + 8 * (tid & 1));
         if (pos < 0) dv = u32x4{0u, 0u, 0u, 0u};
     };
-    f32x4 dq[2] = {zero4(), zero4()};
+    f32x4 dq[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dq[j] = zero4();
     load_chunk(0);
     for (int c0 = 0; c0 < nk; c0 += BK) {
         __syncthreads();
@@ -1105,17 +1109,17 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
         for (int ks = 0; ks < BK / 32; ++ks) {
             const u32x4 b = ld_tr16x16(Ds, DP, 32 * ks, 0, lane);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                dq[j] = T::mma16(ld_tr16x16(Ks, KP, 32 * ks, 32 * w + 16 * j, lane), b, dq[j]);
+            for (int j = 0; j < NJ; ++j)
+                dq[j] = T::mma16(ld_tr16x16(Ks, KP, 32 * ks, 16 * (NJ * w + j), lane), b, dq[j]);
         }
     }
     // dQ^T tiles: lane holds stored head slot `col` (head 0-3, 8-11, 4-7,
-    // 12-15 in slot order), head dims 32w + 16j + 4*G16 + r
+    // 12-15 in slot order), head dims 16 (NJ w + j) + 4*G16 + r
     const int h = h2 * 16 + ((col & 4) ? (col >> 3) * 4 + 8 + (col & 3) : (col >> 3) * 4 + (col & 3));
     const int64_t dqo = (int64_t)t * p.dq.ss + (int64_t)h * p.dq.sh;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-        st_grad4<T>(p.dq.p, dqo + 32 * w + 16 * j + 4 * G16, p.grad_f32, dq[j][0] * p.scale, dq[j][1] * p.scale,
+    for (int j = 0; j < NJ; ++j)
+        st_grad4<T>(p.dq.p, dqo + 16 * (NJ * w + j) + 4 * G16, p.grad_f32, dq[j][0] * p.scale, dq[j][1] * p.scale,
                     dq[j][2] * p.scale, dq[j][3] * p.scale);
 }
 
@@ -1123,16 +1127,16 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
 // dK/dV (independent of each other; both follow the dK/dV kernel): the dQ
 // items first, one per (token, KV head), then the reduction's items, which
 // fill the CUs the dQ pass's last round leaves idle.
-template <class T>
+template <class T, int DK, int DV>
 __global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p, int n_dq) {
     const int id = blockIdx.x;
     if (id < n_dq) {
-        dq_ds_body<T>(p, id / p.N2, id % p.N2);
+        dq_ds_body<T, DK>(p, id / p.N2, id % p.N2);
         return;
     }
-    constexpr int NG = reduce_key_groups<128, 128>();
+    constexpr int NG = reduce_key_groups<DK, DV>();
     const int r = id - n_dq;
-    kv_reduce_body<T, 128, 128>(p, r / (p.halves * NG), (r / NG) % p.halves, r % NG);
+    kv_reduce_body<T, DK, DV>(p, r / (p.halves * NG), (r / NG) % p.halves, r % NG);
 }
 
 // ---------------------------------------------------------------------------
@@ -1614,14 +1618,14 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     else
         PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
                     st, p);
-    if constexpr (DK == 128 && DV == 128) {
+    if constexpr (DK >= 128) {
         if (p.ds) {
             // the dQ pass and the reduction in one launch
             const long n_dq = (long)p.Tq * p.N2;
-            const long n_red = (long)p.N2 * p.NB * p.halves * reduce_key_groups<128, 128>();
+            const long n_red = (long)p.N2 * p.NB * p.halves * reduce_key_groups<DK, DV>();
             if (n_dq + n_red > 0)
-                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_ds_kernel<T>), dim3((unsigned)(n_dq + n_red)), dim3(256), 0, st, p,
-                            (int)n_dq);
+                PROF_LAUNCH(KID_NSA_DQ, st, (nsa_dq_ds_kernel<T, DK, DV>), dim3((unsigned)(n_dq + n_red)), dim3(256), 0,
+                            st, p, (int)n_dq);
             return hipGetLastError();
         }
     }
@@ -1782,9 +1786,9 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.delta = o; o = up(o + S.Tq * Hq * 4);
     L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
     // stored dS for a dQ pass without recomputation: 16 query heads per KV
-    // head at Dqk = Dv = 128, block sizes that divide 128, up to 1 GiB
+    // head at Dqk = 128 or 192, block sizes that divide 128, up to 1 GiB
     const size_t ds_bytes = (size_t)std::max<int64_t>(L.E, 1) * bs * 16 * 2;
-    L.use_ds = G == 16 && D == 128 && Dv == 128 && 128 % bs == 0 && ds_bytes <= ((size_t)1 << 30);
+    L.use_ds = G == 16 && D >= 128 && 128 % bs == 0 && ds_bytes <= ((size_t)1 << 30);
     L.ds = o; o = up(o + (L.use_ds ? ds_bytes : 0));
     // more sequences than the kernel arguments carry: a table in the workspace
     const int64_t n = (int64_t)S.q0.size();
