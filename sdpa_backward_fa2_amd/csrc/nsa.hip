@@ -12,14 +12,17 @@
 // Kernels, all on the caller's stream:
 //   nsa_rank_kernel          per (token tile, KV head): each (token, slot)
 //                            entry's rank within its tile and block, and the
-//                            tile's per-block totals (LDS counters, no atomics)
+//                            tile's per-block totals (LDS counters, no atomics);
+//                            in the backward nsa_rank_pre_kernel, which also
+//                            runs the row pass (Delta and log2-LSE per
+//                            (token, head))
 //   nsa_hist_scan_kernel     per (KV block, KV head): prefixes of those totals
 //                            over the tiles, and the block's entry count
 //   nsa_scan_kernel          CSR offsets of the lists and a table of work
 //                            pieces (at most `chunk` entries of one block each)
 //   nsa_scatter_kernel       stores each entry in its block's list, which so
-//                            comes out in (token, slot) order
-//   bwd_pre_kernel           Delta and log2-LSE per (token, head)  [bwd.hip]
+//                            comes out in (token, slot) order; up to 4096
+//                            buckets nsa_scan_scatter_kernel does the scan too
 //   nsa_kv_kernel            per piece and 64-key half of its block: dK, dV
 //                            over the piece's tokens (G heads per token form
 //                            the query rows of a step); a block with one piece
@@ -318,15 +321,14 @@ __global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
 }
 
 // One wavefront per (tile, KV head): entry e goes to offset + tile prefix +
-// rank of its block's list.
-__global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
-    const int tile = blockIdx.x, h2 = blockIdx.y, lane = threadIdx.x;
+// rank of its block's list (off: the KV head's CSR offsets).
+__device__ __forceinline__ void scatter_body(const NsaParams& p, int tile, int h2, const int32_t* off) {
+    const int lane = threadIdx.x;
     const int t0 = tile * p.tt, t1 = min(p.Tq, t0 + p.tt);
     const int e_begin = t0 * p.count, e_end = t1 * p.count;
     const int32_t* tk = p.topk + (int64_t)h2 * p.tk_sn;
     int32_t* rank = p.rank + (int64_t)h2 * p.Tq * p.count;
     const int32_t* hist = p.hist + (int64_t)h2 * p.NB * p.n_tiles;
-    const int32_t* off = p.offsets + h2 * p.NB;
     int s_cur = seq_of_token(p.seqs, t0);
     for (int cb = e_begin; cb < e_end; cb += 64 * kIdxBatch) {
         int v[kIdxBatch], rk[kIdxBatch], g[kIdxBatch], pos[kIdxBatch];
@@ -351,6 +353,64 @@ __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
             if (e < e_end) rank[e] = pos[u];
         }
     }
+}
+
+__global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
+    scatter_body(p, blockIdx.x, blockIdx.y, p.offsets + blockIdx.y * p.NB);
+}
+
+// Index builds of at most kScanScatterMax buckets: the offsets scan rides in
+// the scatter launch.  Every workgroup scans the buckets' entry counts itself
+// (a run of consecutive buckets per lane) into LDS offsets, and workgroup
+// (0, 0) also writes the CSR offsets, the pieces' starts and the work pieces,
+// which the kernels after the index build read.
+constexpr int kScanScatterMax = 4096;
+__global__ __launch_bounds__(64) void nsa_scan_scatter_kernel(NsaParams p) {
+    __shared__ int32_t off_s[kScanScatterMax];
+    const int lane = threadIdx.x;
+    const int nb = p.N2 * p.NB;
+    const int per = (nb + 63) / 64;
+    const int a = min(nb, lane * per), b = min(nb, a + per);
+    int sum = 0, psum = 0;
+    for (int i = a; i < b; ++i) {
+        const int c = p.counts[i];
+        sum += c;
+        psum += (c + p.chunk - 1) / p.chunk;
+    }
+    int x = sum, y = psum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int xs = __shfl_up(x, o), ys = __shfl_up(y, o);
+        if (lane >= o) {
+            x += xs;
+            y += ys;
+        }
+    }
+    int run = x - sum, prun = y - psum;
+    const bool writer = blockIdx.x == 0 && blockIdx.y == 0;
+    for (int i = a; i < b; ++i) {
+        const int c = p.counts[i];
+        off_s[i] = run;
+        if (writer) {
+            const int np = (c + p.chunk - 1) / p.chunk;
+            p.offsets[i] = run;
+            p.pstart[i] = prun;
+            for (int k = 0; k < np; ++k) {
+                p.pieces[(prun + k) * 3 + 0] = i;
+                p.pieces[(prun + k) * 3 + 1] = run + k * p.chunk;
+                p.pieces[(prun + k) * 3 + 2] = min(run + (k + 1) * p.chunk, run + c);
+            }
+            prun += np;
+        }
+        run += c;
+    }
+    const int total = __shfl(x, 63), ptotal = __shfl(y, 63);
+    if (writer && lane == 0) {
+        p.offsets[nb] = total;
+        p.pstart[nb] = ptotal;
+    }
+    __syncthreads();
+    scatter_body(p, blockIdx.x, blockIdx.y, off_s + blockIdx.y * p.NB);
 }
 
 // Block-wide exclusive scan of one value per thread (1024 threads); returns the
@@ -1570,13 +1630,23 @@ __global__ __launch_bounds__(256) void nsa_fwd_kernel(NsaParams p) {
 // Launch
 // ---------------------------------------------------------------------------
 
+// The offsets scan and the scatter: one launch when the buckets fit the
+// fused kernel's LDS and there are entries to scatter, else two.
+static void launch_scan_scatter(const NsaParams& p, hipStream_t st) {
+    if (p.n_tiles > 0 && (int64_t)p.N2 * p.NB <= kScanScatterMax) {
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+        return;
+    }
+    PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
+    if (p.n_tiles > 0)
+        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+}
+
 static hipError_t launch_index(const NsaParams& p, hipStream_t st) {
     if (p.n_tiles > 0)
         PROF_LAUNCH(KID_NSA_INDEX, st, nsa_rank_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
     PROF_LAUNCH(KID_NSA_INDEX, st, nsa_hist_scan_kernel, dim3(p.NB, p.N2), dim3(64), 0, st, p);
-    PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
-    if (p.n_tiles > 0)
-        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+    launch_scan_scatter(p, st);
     return hipGetLastError();
 }
 
@@ -1606,9 +1676,7 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
             PROF_LAUNCH(KID_NSA_INDEX, st, (nsa_rank_pre_kernel<T, DV>), dim3((unsigned)(n_rank + n_pre)), dim3(64), 0,
                         st, p, bp, (int)n_rank);
         PROF_LAUNCH(KID_NSA_INDEX, st, nsa_hist_scan_kernel, dim3(p.NB, p.N2), dim3(64), 0, st, p);
-        PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scan_kernel, dim3(1), dim3(1024), 0, st, p);
-        if (p.n_tiles > 0)
-            PROF_LAUNCH(KID_NSA_INDEX, st, nsa_scatter_kernel, dim3(p.n_tiles, p.N2), dim3(64), 0, st, p);
+        launch_scan_scatter(p, st);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
