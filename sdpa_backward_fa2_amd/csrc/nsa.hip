@@ -1092,16 +1092,21 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 // dQ_t = scale * sum over the token's gathered keys j of dS_tj K_j, with dS
 // as the dK/dV kernel stored it (one 16-head x block_size tile per entry),
 // so this pass gathers K only and recomputes neither S nor dP.  Workgroup
-// (four wavefronts) per (token, KV head); the gathered keys go 128 at a time
-// (block_size divides 128): the chunk's K rows and dS^T rows are loaded into
-// registers during the previous chunk and staged in LDS; wavefront w forms
+// (four wavefronts) per (token, KV head); the gathered keys go 64 at a time:
+// the chunk's K rows and dS^T rows are loaded into registers during the
+// previous chunk and staged in LDS; wavefront w forms
 // dQ^T for head dims D/4 * w .. + D/4 - 1 as K^T dS^T (v_mfma_f32_16x16x32,
 // both operands by transposing LDS reads), so no partials are reduced.  A
-// choice outside the sequence has no entry and contributes zero.
+// choice outside the sequence has no entry and contributes zero.  The pass
+// is bound by the latency of its gathered loads, so it is sized for
+// occupancy: 64-key chunks (20 KB of LDS at D = 128) and 72 registers at
+// D = 128, six workgroups per CU: NSA workload 95 -> 86 us at Dqk = 128
+// and 185 -> 140 us at 192 against 128-key chunks at four (two-buffer
+// 128-key chunks at two workgroups per CU: 136 us).
 template <class T, int D>
 __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
     static_assert(D == 128 || D == 192, "stored-dS dQ: Dqk 128 or 192");
-    constexpr int BK = 128;
+    constexpr int BK = 64;
     constexpr int NJ = D / 64;                   // 16-column dQ^T tiles per wavefront
     constexpr int KP = D + 8;                    // K rows in LDS, padded
     constexpr int DP = 16;                       // dS^T rows: 16 heads
@@ -1145,7 +1150,7 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
             const int row = krow0 + ((n < nk && blk >= 0) ? blk * p.bs + n % p.bs : 0);
             kv[x] = ld16(kh + (int64_t)row * kss + cc);
         }
-        const int n = c0 + (tid >> 1);
+        const int n = c0 + ((tid >> 1) & (BK - 1));
         const int slot = min(n / p.bs, p.count - 1);
         const int pos = n < nk ? pos_s[slot] : -1;
         dv = ld16(p.ds + ((int64_t)max(pos, 0) * p.bs + n % p.bs) * 16 + 8 * (tid & 1));
@@ -1162,7 +1167,7 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
             const int e = tid + 256 * x;
             st16(&Ks[(e / (D / 8)) * KP + (e % (D / 8)) * 8], kv[x]);
         }
-        st16(&Ds[(tid >> 1) * DP + 8 * (tid & 1)], dv);
+        if (tid < 2 * BK) st16(&Ds[(tid >> 1) * DP + 8 * (tid & 1)], dv);
         __syncthreads();
         if (c0 + BK < nk) load_chunk(c0 + BK);
 #pragma unroll
@@ -1188,7 +1193,7 @@ __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
 // items first, one per (token, KV head), then the reduction's items, which
 // fill the CUs the dQ pass's last round leaves idle.
 template <class T, int DK, int DV>
-__global__ __launch_bounds__(256, 2) void nsa_dq_ds_kernel(NsaParams p, int n_dq) {
+__global__ __launch_bounds__(256, 6) void nsa_dq_ds_kernel(NsaParams p, int n_dq) {
     const int id = blockIdx.x;
     if (id < n_dq) {
         dq_ds_body<T, DK>(p, id / p.N2, id % p.N2);
