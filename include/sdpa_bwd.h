@@ -267,6 +267,9 @@ int sdpa_bwd_varlen(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host,
  *   and head strides of every tensor below 2^23 elements.  Topk
  *   values outside the sequence's blocks select nothing (those slots are
  *   ignored); the statistics must then describe the same reduced key set.
+ *   Checked mode: with the environment variable SDPA_BWD_CHECK set (not
+ *   "0"), the selected calls copy topk to the host, which synchronises
+ *   `stream`, and return SDPA_ERR_INVALID for such a value instead.
  *   Every kernel of this path is deterministic; the flag (0, 1 or 2, else
  *   SDPA_ERR_INVALID) is accepted for symmetry with the other entry points.
  *   grad_dtype: `dtype` or SDPA_F32, as for sdpa_bwd.

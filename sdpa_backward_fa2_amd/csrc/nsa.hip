@@ -41,6 +41,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -1924,6 +1925,40 @@ int device_ok() {
     return SDPA_OK;
 }
 
+// Checked mode (environment SDPA_BWD_CHECK set and not "0", read at every
+// call): the selected calls copy the top-k values to the host, a copy that
+// synchronises the caller's stream, and reject a value outside its token's
+// sequence's blocks with SDPA_ERR_INVALID instead of ignoring that slot.
+// (Negative strides are not checked.)
+int check_topk(const Seqs& S, int64_t Hkv, const int32_t* topk, int64_t st, int64_t sn, int64_t sk, int64_t bs,
+               int64_t count, void* stream) {
+    const char* env = std::getenv("SDPA_BWD_CHECK");
+    if (!env || !env[0] || env[0] == '0' || S.Tq == 0) return SDPA_OK;
+    if (st < 0 || sn < 0 || sk < 0) return SDPA_OK;
+    const size_t n = (size_t)((S.Tq - 1) * st + (Hkv - 1) * sn + (count - 1) * sk + 1);
+    std::vector<int32_t> h(n);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(h.data(), topk, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "top-k check copy");
+    for (size_t b = 0; b < S.q0.size(); ++b) {
+        const int64_t nblk = S.lk[b] / bs;
+        for (int64_t t = S.q0[b]; t < S.q0[b] + S.lq[b]; ++t)
+            for (int64_t h2 = 0; h2 < Hkv; ++h2)
+                for (int64_t i = 0; i < count; ++i) {
+                    const int32_t v = h[(size_t)(t * st + h2 * sn + i * sk)];
+                    if (v < 0 || v >= nblk) {
+                        g_nsa_err = "topk[" + std::to_string(t) + ", " + std::to_string(h2) + ", " + std::to_string(i) +
+                                    "] = " + std::to_string(v) + " is outside the sequence's " + std::to_string(nblk) +
+                                    " blocks";
+                        sdpa::set_last_error(g_nsa_err.c_str());
+                        return SDPA_ERR_INVALID;
+                    }
+                }
+    }
+    return SDPA_OK;
+}
+
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int t3_ok(const sdpa_tensor3* t) {
@@ -1996,6 +2031,7 @@ int sdpa_fwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     for (const sdpa_tensor3* t : {q, k, v, o_out})
         if (int s = t3_ok(t)) return s;
     if (int s = device_ok()) return s;
+    if (int s = check_topk(S, Hkv, topk, tk_st, tk_sn, tk_sk, block_size, block_count, stream)) return s;
     if (S.Tq == 0) return SDPA_OK;
 
     sdpa::NsaParams p{};
@@ -2062,6 +2098,7 @@ int sdpa_bwd_selected(int dtype, int64_t batch, const int64_t* cu_seqlens_q_host
     const NsaLayout L = nsa_layout(S, Hq, Hkv, D, Dv, block_size, block_count);
     if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
     if (int s = device_ok()) return s;
+    if (int s = check_topk(S, Hkv, topk, tk_st, tk_sn, tk_sk, block_size, block_count, stream)) return s;
     if (S.Tk == 0) return SDPA_OK;
 
     char* ws = static_cast<char*>(workspace);
@@ -2116,6 +2153,7 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
     const NsaLayout L = nsa_layout(S, Hkv, Hkv, 128, 128, block_size, block_count);
     if (workspace_bytes < L.total) return SDPA_ERR_WORKSPACE;
     if (int s = device_ok()) return s;
+    if (int s = check_topk(S, Hkv, topk, tk_st, tk_sn, tk_sk, block_size, block_count, stream)) return s;
     if (L.nbk == 0) return SDPA_OK;
     char* ws = static_cast<char*>(workspace);
     sdpa::NsaParams p{};

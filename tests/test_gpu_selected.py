@@ -227,3 +227,29 @@ def test_many_sequences(mode):
     dq, dk, dv = _run_selected(t["q"], t["k"], t["v"], o_ref, t["do"], stats, topk, cu, bs, scale, mode)
     for name, got, ref in (("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"])):
         assert_rel(to_f64(got), ref, dtype, f"{name}, 70 sequences")
+
+
+def test_checked_mode_rejects_out_of_range_topk(monkeypatch):
+    """SDPA_BWD_CHECK=1: a top-k value outside the token's sequence's blocks
+    is an SDPA_ERR_INVALID error (copied to the host and checked) instead of
+    an ignored slot; valid values pass unchanged."""
+    rng = np.random.default_rng(5)
+    lengths = np.array([256, 128])
+    cu = np.cumsum(lengths)
+    T, G, bs, count, dtype = int(cu[-1]), 2, 64, 2, "bf16"
+    topk = synth.draw_topk(lengths, 1, bs, count, config_id=31)
+    bits = {n: synth.encode(rng.standard_normal(shape), dtype)
+            for n, shape in (("q", (T, G, 128)), ("k", (T, 1, 128)), ("v", (T, 1, 128)), ("do", (T, G, 128)))}
+    t = {n: to_device(b, dtype) for n, b in bits.items()}
+    monkeypatch.setenv("SDPA_BWD_CHECK", "1")
+    o, m, l = sb.fwd_selected(t["q"], t["k"], t["v"], _topk_dev(topk), cu, cu, bs, 0.1, 2)
+    sb.bwd_selected(t["q"], t["k"], t["v"], o, t["do"], (m, l), _topk_dev(topk), cu, cu, bs, 0.1, 2)
+    torch.cuda.synchronize()
+    bad = topk.copy()
+    bad[300, 0, 1] = 2          # token 300 is in the 128-token sequence: blocks 0 and 1 only
+    for call in (lambda: sb.fwd_selected(t["q"], t["k"], t["v"], _topk_dev(bad), cu, cu, bs, 0.1, 2),
+                 lambda: sb.bwd_selected(t["q"], t["k"], t["v"], o, t["do"], (m, l), _topk_dev(bad), cu, cu, bs,
+                                         0.1, 2)):
+        with pytest.raises(sb.SdpaError) as e:
+            call()
+        assert e.value.status == 2    # SDPA_ERR_INVALID
