@@ -30,15 +30,16 @@ def pytest_collection_modifyitems(config, items):
 
 
 def pytest_sessionfinish(session, exitstatus):
-    """After a GPU run, write every parity comparison's error and bound to
-    gpurun_out/parity_margins.txt (worst ratio first), when that folder
-    exists: the margin under the bound, not only pass or fail."""
+    """After a GPU run, write every parity comparison's error and bound
+    (worst ratio first) to the file the environment variable
+    SDPA_PARITY_MARGINS names, when it is set: the margin under the bound,
+    not only pass or fail."""
     gu = sys.modules.get("gpu_util")
-    out_dir = os.path.join(ROOT, "gpurun_out")
-    if gu is None or not getattr(gu, "MARGINS", None) or not os.path.isdir(out_dir):
+    path = os.environ.get("SDPA_PARITY_MARGINS")
+    if gu is None or not getattr(gu, "MARGINS", None) or not path:
         return
     rows = sorted(gu.MARGINS, key=lambda r: -r[3] / r[4])
-    with open(os.path.join(out_dir, "parity_margins.txt"), "w") as fh:
+    with open(path, "w") as fh:
         fh.write("# err/bound  err  bound  dtype  what  test\n")
         for test, what, dtype, e, tol in rows:
             fh.write(f"{e / tol:.3f} {e:.3e} {tol:.0e} {dtype} {what} {test}\n")
