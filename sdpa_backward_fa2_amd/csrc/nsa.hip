@@ -31,7 +31,7 @@
 //                            order (deterministic); zero-fills unselected blocks
 //   nsa_dq_kernel            per (token, KV head, 16-head tile): dQ over the
 //                            gathered keys, without atomics
-//   nsa_dq_ds_kernel         16 query heads per KV head, Dqk 128 or 192: dQ
+//   nsa_dq_ds_kernel         16 query heads per KV head: dQ
 //                            from the dS that nsa_kv_kernel stored (K gathered,
 //                            S and dP not recomputed)
 //   nsa_fwd_kernel           the forward: O and (max, sum) per (token, head)
@@ -715,7 +715,7 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             for (int hh = 0; hh < 2; ++hh) {
                 const u32x4 bP = acc_to_operand<T>(sa, hh);
                 const u32x4 bS = acc_to_operand<T>(pa, hh);
-                if constexpr (DK >= 128) {
+                {
                     // 16 heads per entry: rows r0 + 16hh .. +15 are one
                     // entry; this lane holds 8 of its heads for key myk
                     if (p.ds && col_ok) {
@@ -1087,7 +1087,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ from the stored dS (16 query heads per KV head, Dqk = 128 or 192)
+// dQ from the stored dS (16 query heads per KV head)
 // ---------------------------------------------------------------------------
 //
 // dQ_t = scale * sum over the token's gathered keys j of dS_tj K_j, with dS
@@ -1106,7 +1106,7 @@ __global__ __launch_bounds__(256) void nsa_dq_kernel(NsaParams p) {
 // 128-key chunks at two workgroups per CU: 136 us).
 template <class T, int D>
 __device__ __forceinline__ void dq_ds_body(const NsaParams& p, int t, int h2) {
-    static_assert(D == 128 || D == 192, "stored-dS dQ: Dqk 128 or 192");
+    static_assert(D == 64 || D == 128 || D == 192, "stored-dS dQ: Dqk 64, 128 or 192");
     constexpr int BK = 64;
     constexpr int NJ = D / 64;                   // 16-column dQ^T tiles per wavefront
     constexpr int KP = D + 8;                    // K rows in LDS, padded
@@ -1692,7 +1692,7 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     else
         PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
                     st, p);
-    if constexpr (DK >= 128) {
+    {
         if (p.ds) {
             // the dQ pass and the reduction in one launch
             const long n_dq = (long)p.Tq * p.N2;
@@ -1860,9 +1860,9 @@ NsaLayout nsa_layout(const Seqs& S, int64_t Hq, int64_t Hkv, int64_t D, int64_t 
     L.delta = o; o = up(o + S.Tq * Hq * 4);
     L.partial = o; o = up(o + (size_t)L.max_pieces * L.halves * 64 * (D + Dv) * 4);   // dK, dV partials
     // stored dS for a dQ pass without recomputation: 16 query heads per KV
-    // head at Dqk = 128 or 192, block sizes that divide 128, up to 1 GiB
+    // head, block sizes that divide 128, up to 1 GiB
     const size_t ds_bytes = (size_t)std::max<int64_t>(L.E, 1) * bs * 16 * 2;
-    L.use_ds = G == 16 && D >= 128 && 128 % bs == 0 && ds_bytes <= ((size_t)1 << 30);
+    L.use_ds = G == 16 && 128 % bs == 0 && ds_bytes <= ((size_t)1 << 30);
     L.ds = o; o = up(o + (L.use_ds ? ds_bytes : 0));
     // more sequences than the kernel arguments carry: a table in the workspace
     const int64_t n = (int64_t)S.q0.size();
