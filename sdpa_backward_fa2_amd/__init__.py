@@ -304,7 +304,8 @@ def _stats_arg(stats, packed: bool) -> Stats:
 def prepare_bwd(q, k, v, o, dout, stats, scale: float, causal: bool, deterministic: int = DQ_FASTEST,
                 dq=None, dk=None, dv=None, workspace=None, grad_dtype=None):
     """Marshal the arguments of one dense backward once; returns (call, (dq, dk, dv))
-    where call() enqueues the backward on the current stream.  The tensors must
+    where call() enqueues the backward on the stream that was current when it
+    was prepared (prepare inside a capture stream to graph it).  The tensors must
     stay alive and unmoved while call is used.  Gradients are q's dtype or
     float32 (given tensors, else grad_dtype)."""
     lib = load()
