@@ -65,3 +65,43 @@ def test_noalloc_two_calls_second_smaller(mode):
                 assert torch.equal(a.view(torch.int16), r.view(torch.int16)), f"{name} differs from sdpa_bwd"
             assert_rel(to_f64(a), x, dtype, f"noalloc {name} mode={mode} S={S}")
 
+
+
+@pytest.mark.parametrize("mode", [0, 2])
+def test_noalloc_graph_replay(mode):
+    """The caller this entry point is for: a HIP graph that captures it.  The
+    captured call is replayed three times with eager device work between
+    replays; each replay matches the eager call (bitwise in the atomic-free
+    mode, within the parity bound with fp32 atomics)."""
+    B, H, S, D, dtype, causal = 2, 4, 512, 128, "bf16", True
+    print(f"noalloc graph mode={mode} B={B} H={H} S={S} D={D} {dtype}", flush=True)
+    ts, _xs, o, lse, scale = _case(B, H, S, D, dtype, causal, 21)
+    q, k, v, do = ts["q"], ts["k"], ts["v"], ts["do"]
+    eager = sb.bwd_noalloc(q, k, v, o, do, lse, scale, causal, deterministic=mode,
+                           dq=_nan(q), dk=_nan(k), dv=_nan(v))
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in eager]
+    outs = (_nan(q), _nan(k), _nan(v))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        sb.bwd_noalloc(q, k, v, o, do, lse, scale, causal, deterministic=mode, dq=outs[0], dk=outs[1], dv=outs[2])
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            sb.bwd_noalloc(q, k, v, o, do, lse, scale, causal, deterministic=mode,
+                           dq=outs[0], dk=outs[1], dv=outs[2])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for replay in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("dq", "dk", "dv"), outs, eager):
+            if mode == 0:
+                assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {replay}: {name}"
+            else:
+                e = float((got.float() - ref.float()).abs().max() / ref.float().abs().max())
+                assert e <= REL_TOL[dtype], f"replay {replay}: {name} {e}"
