@@ -47,7 +47,7 @@ def kernel_sources(kernel: str) -> list:
     """The files a kernel's code comes from: its sources (NSA kernels also use
     the dense preprocess) and the build script, which holds the compiler flags."""
     base = ("common.h", "bwd_shared.h", "bwd.hip", "bwd_big.h", "bwd128.hip", "bwd192.hip")
-    files = base + ("nsa.hip",) if kernel.startswith("nsa") else base
+    files = base + ("nsa.hip", "nsa_kv.hip") if kernel.startswith("nsa") else base
     return [os.path.join(ROOT, "sdpa_backward_fa2_amd", "csrc", f) for f in files] + [
         os.path.join(ROOT, "sdpa_backward_fa2_amd", "build.py")]
 

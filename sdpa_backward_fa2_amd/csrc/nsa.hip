@@ -158,6 +158,7 @@ __device__ __forceinline__ int seq_of_block(const SeqTable& s, int key_row) { re
 __device__ __forceinline__ int seq_of_token(const SeqTable& s, int t) { return seq_of<0>(s, t); }
 
 // Writes rows first .. first + chunk.n - 1 of the workspace sequence table.
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(64) void nsa_seqtab_kernel(SeqTable chunk, int32_t* table, int first) {
     const int i = threadIdx.x;
     if (i >= chunk.n) return;
@@ -165,6 +166,8 @@ __global__ __launch_bounds__(64) void nsa_seqtab_kernel(SeqTable chunk, int32_t*
     v[0] = chunk.q0[i]; v[1] = chunk.k0[i]; v[2] = chunk.lq[i]; v[3] = chunk.lk[i];
     *reinterpret_cast<i32x4*>(table + 4 * (first + i)) = v;
 }
+#endif
+
 
 // ---------------------------------------------------------------------------
 // Inverse index: a stable counting sort of the (token, slot) entries by block
@@ -271,9 +274,12 @@ __device__ __forceinline__ void rank_body(const NsaParams& p, int tile, int h2) 
     }
 }
 
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(64) void nsa_rank_kernel(NsaParams p) {
     rank_body(p, blockIdx.x, blockIdx.y);
 }
+#endif
+
 
 // The rank pass and the backward's row pass (Delta and log2-LSE of every
 // (token, head) row, which the index does not need) in one launch: the rank
@@ -315,11 +321,14 @@ __device__ __forceinline__ int hist_scan_bucket(const NsaParams& p, int bucket, 
     return __shfl(x, 63);
 }
 
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(64) void nsa_hist_scan_kernel(NsaParams p) {
     const int bucket = blockIdx.y * p.NB + blockIdx.x;
     const int n = hist_scan_bucket(p, bucket, threadIdx.x);
     if (threadIdx.x == 0) p.counts[bucket] = n;
 }
+#endif
+
 
 // One wavefront per (tile, KV head): entry e goes to offset + tile prefix +
 // rank of its block's list (off: the KV head's CSR offsets).
@@ -356,9 +365,12 @@ __device__ __forceinline__ void scatter_body(const NsaParams& p, int tile, int h
     }
 }
 
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
     scatter_body(p, blockIdx.x, blockIdx.y, p.offsets + blockIdx.y * p.NB);
 }
+#endif
+
 
 // Index builds of at most kScanScatterMax buckets: the offsets scan rides in
 // the scatter launch.  Every workgroup scans the buckets' entry counts itself
@@ -366,6 +378,7 @@ __global__ __launch_bounds__(64) void nsa_scatter_kernel(NsaParams p) {
 // (0, 0) also writes the CSR offsets, the pieces' starts and the work pieces,
 // which the kernels after the index build read.
 constexpr int kScanScatterMax = 4096;
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(64) void nsa_scan_scatter_kernel(NsaParams p) {
     __shared__ int32_t off_s[kScanScatterMax];
     const int lane = threadIdx.x;
@@ -413,6 +426,8 @@ __global__ __launch_bounds__(64) void nsa_scan_scatter_kernel(NsaParams p) {
     __syncthreads();
     scatter_body(p, blockIdx.x, blockIdx.y, off_s + blockIdx.y * p.NB);
 }
+#endif
+
 
 // Block-wide exclusive scan of one value per thread (1024 threads); returns the
 // exclusive prefix and writes the block total to *total.
@@ -442,6 +457,7 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* wsum, int* total
     return r;
 }
 
+#ifndef SDPA_NSA_KV_UNIT
 __global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
     __shared__ int wsum[17];
     const int nb = p.N2 * p.NB;
@@ -471,6 +487,8 @@ __global__ __launch_bounds__(1024) void nsa_scan_kernel(NsaParams p) {
         p.pstart[nb] = carry_p;
     }
 }
+#endif
+
 
 // ---------------------------------------------------------------------------
 // dK / dV: key-block outer over pieces of the inverse lists
@@ -796,6 +814,35 @@ __global__ __launch_bounds__(256) void nsa_kv_kernel(NsaParams p) {
             }
     }
 }
+
+#ifdef SDPA_NSA_KV_UNIT
+// The dK/dV kernel's launch, compiled in its own translation unit (nsa_kv.hip)
+// so that the build can give the kernel scheduler options of its own.
+template <class T, int DK, int DV>
+hipError_t launch_nsa_kv(const NsaParams& p, hipStream_t st) {
+    if (p.mask)
+        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, true>), dim3(p.max_pieces, p.halves), dim3(256), 0,
+                    st, p);
+    else
+        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
+                    st, p);
+    return hipGetLastError();
+}
+#define SDPA_NSA_KV_INST(T)                                                      \
+    template hipError_t launch_nsa_kv<T, 64, 64>(const NsaParams&, hipStream_t);   \
+    template hipError_t launch_nsa_kv<T, 128, 128>(const NsaParams&, hipStream_t); \
+    template hipError_t launch_nsa_kv<T, 192, 192>(const NsaParams&, hipStream_t); \
+    template hipError_t launch_nsa_kv<T, 192, 128>(const NsaParams&, hipStream_t);
+SDPA_NSA_KV_INST(F16)
+SDPA_NSA_KV_INST(BF16)
+#undef SDPA_NSA_KV_INST
+
+}  // namespace sdpa
+#else   // the rest of the selected-attention kernels and the entry points
+
+// Defined in nsa_kv.hip.
+template <class T, int DK, int DV>
+hipError_t launch_nsa_kv(const NsaParams& p, hipStream_t st);
 
 // Sum the partials of blocks split into several pieces, in piece order; a
 // block no token chose (no piece) gets zeros, and a block with one piece was
@@ -1686,12 +1733,8 @@ static hipError_t launch_nsa_t(const NsaParams& p, const BwdParams& bp, hipStrea
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.mask)
-        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, true>), dim3(p.max_pieces, p.halves), dim3(256), 0,
-                    st, p);
-    else
-        PROF_LAUNCH(KID_NSA_KV, st, (nsa_kv_kernel<T, DK, DV, false>), dim3(p.max_pieces, p.halves), dim3(256), 0,
-                    st, p);
+    e = launch_nsa_kv<T, DK, DV>(p, st);
+    if (e != hipSuccess) return e;
     {
         if (p.ds) {
             // the dQ pass and the reduction in one launch
@@ -2168,3 +2211,5 @@ int sdpa_selected_build_index(int64_t batch, const int64_t* cu_seqlens_q_host,
 }
 
 }  // extern "C"
+
+#endif  // SDPA_NSA_KV_UNIT
